@@ -1,0 +1,290 @@
+"""Plain float64 reference of the verification hot path (test infrastructure only; see package doc).
+
+Sources, by page title:
+  [SSD]  "论文阅读：Speculative Speculative Decoding — 消除推测解码的最后一个顺序瓶颈"
+         (xiaohongrsx.github.io/posts/ssd-paper-reading)
+  [SD7.3] "7.3 Speculative Decoding：投机采样加速" (aiknowledge.cn)
+  [HW]   "推测解码：用一个“小模型”骗出 3 倍推理速度" (bbs.huaweicloud.com/blogs/510880)
+
+Readings where the pages are silent or garbled (each the plainest one the rest supports):
+  * temperature: both distributions are softmax(z / T) with one T > 0;
+  * acceptance: accept x iff u * q'(x) < p(x), u in [0, 1) (so p >= q' always accepts);
+  * a rejection resamples from the normalised residual max(p - q', 0), the only choice that keeps
+    the output distribution equal to p as all three pages assert;
+  * the bonus uses its own uniform u[K]; the inverse CDF runs in ascending token order and picks the
+    first token whose cumulative residual exceeds u * R;
+  * if every draft token is accepted, the bonus is drawn from the target row K (0-based) with R = 1;
+    an all-zero residual (reachable only through rounding) falls back to the target row, R = 1;
+  * Saguaro: the draft probability of each token of the set S is multiplied by C, the others keep
+    their weight, and the row is renormalised;
+  * top-F orders raw logits descending, ties to the smaller index, never returns -inf, pads with -1;
+  * geometric acceptance law P(k) = (1 - a) a^k for k < K and a^K for k = K; power-law miss model
+    sum_k P(k) F_k^-r; integer fan-out by largest remainder, ties to the smaller k.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------------------------
+# inputs
+# ----------------------------------------------------------------------------------------------
+def logits_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored logits: fp32 arrays, or bf16 carried as uint16 bit patterns."""
+    if dtype == "bf16":
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# distributions
+# ----------------------------------------------------------------------------------------------
+def softmax_t(z: np.ndarray, T: float) -> np.ndarray:
+    """Temperature softmax of one logit row: each position's output is a probability distribution
+    over the vocabulary ([SSD] "为什么大模型能并行验证"; [SD7.3] 7.3.3 names q(x), p(x))."""
+    if not (T > 0.0 and math.isfinite(T)):
+        raise ValueError("temperature must be finite and > 0")
+    y = np.asarray(z, dtype=np.float64) / T
+    m = np.max(y)
+    e = np.exp(y - m)
+    return e / np.sum(e)
+
+
+def _valid_set(S: Optional[Sequence[int]], V: int) -> list:
+    """Distinct in-range entries of a Saguaro set, in their given order (-1 and duplicates ignored)."""
+    out = []
+    if S is None:
+        return out
+    for s in S:
+        s = int(s)
+        if 0 <= s < V and s not in out:
+            out.append(s)
+    return out
+
+
+def saguaro(q: np.ndarray, S: Optional[Sequence[int]], C: float):
+    """Saguaro sampling ([SSD] "Saguaro 优化二", "解法：操纵草稿分布"): multiply the draft probability
+    of the F cached tokens by C, leave the rest, renormalise.
+
+    Returns (q', sigma, N) with sigma = sum_{s in S} q(s) and N = 1 - (1 - C) sigma.
+    """
+    if not (0.0 <= C <= 1.0):
+        raise ValueError("C must lie in [0, 1]")
+    V = q.shape[0]
+    idx = _valid_set(S, V)
+    sigma = float(np.sum(q[idx])) if idx else 0.0
+    N = 1.0 - (1.0 - C) * sigma
+    if not N > 0.0:
+        raise ValueError("Saguaro normaliser is not positive")
+    w = np.ones(V)
+    w[idx] = C
+    return q * w / N, sigma, N
+
+
+# ----------------------------------------------------------------------------------------------
+# verification of one sequence
+# ----------------------------------------------------------------------------------------------
+@dataclass
+class VerifyResult:
+    k: int                 # accepted draft tokens, 0..K
+    bonus: int             # the token emitted after them
+    a: np.ndarray          # [K] min(1, p_i(x_i) / q'_i(x_i)) at every position
+    R: float               # residual mass at the rejected position (1.0 when k == K)
+    c_lo: float            # cumulative residual fraction just before the bonus token
+    c_hi: float            # ... and including it (decision boundaries of the bonus uniform)
+    fallback: bool         # residual was all zero and the target row was used instead
+
+
+def verify_sequence(zq: np.ndarray, zp: np.ndarray, x: Sequence[int], u: Sequence[float], T: float,
+                    sets: Optional[Sequence[Sequence[int]]] = None, C: float = 1.0) -> VerifyResult:
+    """Verify K draft tokens of one sequence.
+
+    zq [K, V]   draft logits of the K drafted positions (float64 values)
+    zp [K+1, V] target logits; row K scores the position after the last draft token
+    x  [K]      draft tokens;  u [K+1] uniforms, u[K] samples the bonus token
+    sets        per-position Saguaro sets (or None), C the Saguaro factor
+
+    Steps ([SD7.3] 7.3.2 steps 3-4 and 7.3.3; [HW] "三、接受概率为什么是对的"; [SSD] "接受-拒绝机制"):
+    accept x_i with probability min(1, p(x_i)/q(x_i)); stop at the first rejection and discard the
+    later drafts; on a rejection sample the bonus from the normalised max(p - q, 0); if every draft
+    is accepted, sample it from the target's extra position.
+    """
+    K = len(x)
+    V = zq.shape[1]
+    assert zq.shape[0] >= K and zp.shape == (K + 1, V) and len(u) == K + 1
+    p = [softmax_t(zp[i], T) for i in range(K + 1)]
+    qd = []
+    for i in range(K):
+        q = softmax_t(zq[i], T)
+        if sets is not None:
+            q, _, _ = saguaro(q, sets[i], C)
+        qd.append(q)
+
+    a = np.empty(K)
+    k = K
+    for i in range(K):
+        xi = int(x[i])
+        px, qx = p[i][xi], qd[i][xi]
+        if qx > 0.0:
+            a[i] = min(1.0, px / qx)
+        else:
+            a[i] = 1.0 if px > 0.0 else 0.0
+        if k == K and not (float(u[i]) * qx < px):
+            k = i  # first rejection: positions after it are discarded
+
+    fallback = False
+    if k < K:
+        r = np.maximum(p[k] - qd[k], 0.0)
+        R = float(np.sum(r))
+        R_out = R
+        if R == 0.0:
+            r, R, fallback = p[k], 1.0, True
+    else:
+        r, R, R_out = p[K], 1.0, 1.0
+
+    cum = np.cumsum(r)
+    target = float(u[K]) * R
+    t = int(np.searchsorted(cum, target, side="right"))  # first index with cum > target
+    if t >= V:
+        t = int(np.nonzero(r > 0.0)[0][-1])
+    c_lo = (cum[t - 1] if t > 0 else 0.0) / R
+    c_hi = cum[t] / R
+    return VerifyResult(k=k, bonus=t, a=a, R=R_out, c_lo=float(c_lo), c_hi=float(c_hi),
+                        fallback=fallback)
+
+
+def verify_batch(draft: np.ndarray, target: np.ndarray, dtype: str, x: np.ndarray, u: np.ndarray,
+                 T: float, sets: Optional[np.ndarray] = None, C: float = 1.0, seqs=None):
+    """verify_sequence over sequences of stored logits; draft [B, >=K, V], target [B, K+1, V]."""
+    B, K = x.shape
+    seqs = range(B) if seqs is None else seqs
+    out = {}
+    for b in seqs:
+        zq = logits_f64(draft[b, :K], dtype)
+        zp = logits_f64(target[b], dtype)
+        out[b] = verify_sequence(zq, zp, x[b], u[b], T, None if sets is None else sets[b], C)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# SSD: bonus-token guesses, fan-out, speculation cache
+# ----------------------------------------------------------------------------------------------
+def topf(z: np.ndarray, F: int, exclude: int = -1) -> np.ndarray:
+    """Top-F bonus-token guesses of one draft row, excluding the sampled token
+    ([SSD] "怎么猜奖励 token"). Raw logits descending, ties to the smaller index; -inf never
+    returned; -1 pads when fewer than F tokens remain."""
+    z = np.asarray(z, dtype=np.float64)
+    V = z.shape[0]
+    order = np.lexsort((np.arange(V), -z))
+    keep = [int(v) for v in order if v != exclude and z[v] > -np.inf]
+    out = np.full(F, -1, dtype=np.int64)
+    take = keep[:F]
+    out[: len(take)] = take
+    return out
+
+
+def geometric_pk(K: int, a: float) -> np.ndarray:
+    """Geometric acceptance law ([SSD] "最优扇出度分配"): P(k) = (1-a) a^k for k < K, a^K for k = K."""
+    P = np.array([(1.0 - a) * a ** k for k in range(K)] + [a ** K], dtype=np.float64)
+    return P
+
+
+def fanout(K: int, a: float, r: float, budget: int):
+    """Geometric fan-out ([SSD] "最优扇出度分配"): minimise sum_k P(k) F_k^-r subject to
+    sum_k F_k = budget. Setting the Lagrangian's derivative in F_k to zero gives
+    F_k proportional to P(k)^(1/(1+r)); substituting P gives F_k = F_0 a^(k/(1+r)) for k < K.
+
+    Returns (integer F [K+1], continuous F [K+1]). Integers: floor, then the remaining units to the
+    largest fractional parts, ties to the smaller k.
+    """
+    if K < 0 or not (0.0 < a < 1.0) or not (r > 0.0) or budget < 0:
+        raise ValueError("bad fan-out arguments")
+    P = geometric_pk(K, a)
+    ratio = (P / P[0]) ** (1.0 / (1.0 + r))   # F_k / F_0
+    F0 = budget / np.sum(ratio)              # from the budget constraint
+    Fc = F0 * ratio
+    Fi = np.floor(Fc).astype(np.int64)
+    left = budget - int(Fi.sum())
+    frac = Fc - Fi
+    order = sorted(range(K + 1), key=lambda k: (-frac[k], k))
+    for k in order[:left]:
+        Fi[k] += 1
+    return Fi, Fc
+
+
+def cache_keys(guesses: Sequence[Sequence[int]], F: Sequence[int]):
+    """Keys of one sequence's speculation cache ([SSD] "SSD 的核心思想": an outcome is (k, t), k
+    drafts accepted and t the bonus token). For each k the F_k guesses of draft position k
+    (0-based; position K is the extra draft row) occupy consecutive slots; a missing guess (-1)
+    leaves its slot empty as (-1, -1)."""
+    kk, tt = [], []
+    for k, Fk in enumerate(F):
+        for j in range(int(Fk)):
+            t = int(guesses[k][j]) if j < len(guesses[k]) else -1
+            kk.append(k if t >= 0 else -1)
+            tt.append(t if t >= 0 else -1)
+    return np.array(kk, dtype=np.int64), np.array(tt, dtype=np.int64)
+
+
+def cache_lookup(keys_k: np.ndarray, keys_t: np.ndarray, k: int, bonus: int) -> int:
+    """First slot holding the outcome (k, bonus), or -1 on a miss."""
+    for j in range(len(keys_k)):
+        if int(keys_k[j]) == k and int(keys_t[j]) == bonus:
+            return j
+    return -1
+
+
+def all_hit_probability(h: float, B: int) -> float:
+    """[SSD] "问题：大 batch 下缓存未命中不可避免": the batch proceeds with zero wait only if every
+    one of its B sequences hits; with independent per-sequence hit rate h that is h^B."""
+    return float(h) ** int(B)
+
+
+def branch_layout(budget: int, K: int) -> dict:
+    """Shape arithmetic of the cache build ([SSD] "并行生成所有分支", "两层 batch"): each of the
+    `budget` outcomes owns a K-token continuation; drafting them one token at a time across all
+    branches takes K batched forwards of `budget` rows instead of budget*K serial ones."""
+    return dict(branches=budget, K=K, serial_forwards=budget * K, batched_forwards=K,
+                batch_size=budget, branch_rows=budget * K)
+
+
+def ssd_round(draft, target, dtype, x, u, T, sets, C, F, branch=None, seqs=None):
+    """One SSD round for the sampled sequences:
+    guesses (top-F_k of draft row k excluding x_k for k < K, of the extra row K without exclusion),
+    cache keys, Saguaro verification, cache lookup; and, for the branch rows, the Saguaro set
+    (top-F of the row) with its mass and normaliser.
+
+    Returns {b: dict(k, bonus, guesses, keys_k, keys_t, slot, branch_sigma, branch_N)}.
+    """
+    B, K = x.shape
+    seqs = range(B) if seqs is None else seqs
+    out = {}
+    for b in seqs:
+        zq = logits_f64(draft[b], dtype)
+        zp = logits_f64(target[b], dtype)
+        res = verify_sequence(zq[:K], zp, x[b], u[b], T, None if sets is None else sets[b], C)
+        guesses = [topf(zq[i], int(F[i]), int(x[b, i])) for i in range(K)]
+        guesses.append(topf(zq[K], int(F[K])))
+        kk, tt = cache_keys(guesses, F)
+        slot = cache_lookup(kk, tt, res.k, res.bonus)
+        d = dict(verify=res, k=res.k, bonus=res.bonus, guesses=guesses, keys_k=kk, keys_t=tt, slot=slot)
+        if branch is not None:
+            nbr = branch.shape[1]
+            sig = np.empty((nbr, K))
+            nrm = np.empty((nbr, K))
+            sets_b = np.empty((nbr, K, max(1, int(max(F[:K])))), dtype=np.int64)
+            for j in range(nbr):
+                for i in range(K):
+                    zb = logits_f64(branch[b, j, i], dtype)
+                    S = topf(zb, int(F[i]))
+                    sets_b[j, i, :] = -1
+                    sets_b[j, i, : len(S)] = S
+                    _, sig[j, i], nrm[j, i] = saguaro(softmax_t(zb, T), S, C)
+            d.update(branch_sets=sets_b, branch_sigma=sig, branch_N=nrm)
+        out[b] = d
+    return out
