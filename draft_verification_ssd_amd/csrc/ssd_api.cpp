@@ -1,0 +1,293 @@
+// extern "C" entry points: argument validation (before any HIP call), workspace carving, launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "ssd.h"
+#include "ssd_launch.hpp"
+#include "ssd_plan.hpp"
+
+using namespace ssd;
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634073599246810018921;
+
+int elem_size(ssd_dtype d) { return d == SSD_BF16 ? 2 : 4; }
+bool dtype_ok(int d) { return d == SSD_F32 || d == SSD_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0 && have >= need;
+}
+bool temp_ok(float T) { return std::isfinite(T) && T > 0.f; }
+bool c_ok(float C) { return C >= 0.f && C <= 1.f; }  // false for NaN
+template <class P>
+P* at(void* base, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported dtype";
+    case SSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SSD_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max) {
+  if (B < 0 || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || topf_F_max < 0 ||
+      topf_F_max > SSD_MAX_F)
+    return 0;
+  return verify_layout(B, K, V, topf_F_max).total;
+}
+
+ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
+                      int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
+                      float temperature, const int32_t* draft_tokens, const float* uniforms,
+                      const int32_t* sag_set, int sag_F, float sag_C, const int32_t* topf_F,
+                      int topf_F_max, int32_t* topf_out, int32_t* accepted_len,
+                      int32_t* bonus_token, float* accept_prob, float* residual_mass,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
+  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V)
+    return SSD_ERR_INVALID_ARG;
+  if (!temp_ok(temperature)) return SSD_ERR_INVALID_ARG;
+  if (sag_F < 0 || sag_F > SSD_MAX_F || (sag_F > 0 && (!sag_set || !c_ok(sag_C))))
+    return SSD_ERR_INVALID_ARG;
+  if (topf_F_max < 0 || topf_F_max > SSD_MAX_F || (topf_F_max > 0 && !topf_out))
+    return SSD_ERR_INVALID_ARG;
+  if (topf_F)
+    for (int i = 0; i < K; ++i)
+      if (topf_F[i] < 0 || topf_F[i] > topf_F_max) return SSD_ERR_INVALID_ARG;
+  if (draft_seq_stride < int64_t(K) * V || target_seq_stride < int64_t(K + 1) * V)
+    return SSD_ERR_INVALID_ARG;
+  if (B == 0) return SSD_OK;
+  if (!draft_logits || !target_logits || !draft_tokens || !uniforms || !accepted_len ||
+      !bonus_token)
+    return SSD_ERR_INVALID_ARG;
+  const VerifyLayout L = verify_layout(B, K, V, topf_F_max);
+  if (!ws_ok(workspace, workspace_bytes, L.total)) return SSD_ERR_WORKSPACE;
+
+  const int es = elem_size(dtype);
+  VerifyArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.draft = draft_logits;
+  a.dstride = draft_seq_stride;
+  a.target = target_logits;
+  a.tstride = target_seq_stride;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.c2 = float(kLog2e / double(temperature));
+  a.x = draft_tokens;
+  a.u = uniforms;
+  a.sset = sag_F > 0 ? sag_set : nullptr;
+  a.sF = sag_F;
+  a.C = sag_F > 0 ? sag_C : 1.f;
+  for (int i = 0; i < K; ++i) a.topfF[i] = topf_F ? topf_F[i] : topf_F_max;
+  a.topfFmax = topf_F_max;
+  a.topf_out = topf_out;
+  a.k_out = accepted_len;
+  a.bonus_out = bonus_token;
+  a.aprob_out = accept_prob;
+  a.rmass_out = residual_mass;
+  a.flags = at<uint32_t>(workspace, 0);
+  a.cnt = at<uint32_t>(workspace, L.off_cnt);
+  a.stats = at<float2>(workspace, L.off_stats);
+  a.cand = at<void>(workspace, L.off_cand);
+  a.res = at<float>(workspace, L.off_res);
+  a.n1 = L.rp.n1;
+  a.chunk1 = L.rp.chunk1;
+  a.aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
+              (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;
+  return hip_status(launch_verify(a, L.n2, dtype == SSD_BF16, stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t ssd_topf_workspace_bytes(int R, int V, int F_max) {
+  if (R < 0 || V < 1 || V > SSD_MAX_V || F_max < 1 || F_max > SSD_MAX_F) return 0;
+  return topf_layout(R, V, F_max).total;
+}
+
+ssd_status ssd_topf_guess(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                          const int32_t* exclude, const int32_t* F_per_row, int F_max,
+                          int32_t* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
+  if (R < 0 || R > (1 << 24) || V < 1 || V > SSD_MAX_V || F_max < 1 || F_max > SSD_MAX_F ||
+      row_stride < V)
+    return SSD_ERR_INVALID_ARG;
+  if (R == 0) return SSD_OK;
+  if (!logits || !out) return SSD_ERR_INVALID_ARG;
+  const TopfLayout L = topf_layout(R, V, F_max);
+  if (!ws_ok(workspace, workspace_bytes, L.total)) return SSD_ERR_WORKSPACE;
+  const int es = elem_size(dtype);
+  TopfArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.R = R;
+  a.V = V;
+  a.exclude = exclude;
+  a.F_per_row = F_per_row;
+  a.Fmax = F_max;
+  a.out = out;
+  a.flags = at<uint32_t>(workspace, 0);
+  a.cand = at<void>(workspace, L.off_cand);
+  a.n1 = L.rp.n1;
+  a.chunk1 = L.rp.chunk1;
+  a.aligned = aligned16(logits) && (row_stride * es) % 16 == 0;
+  return hip_status(launch_topf(a, dtype == SSD_BF16, stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t ssd_saguaro_workspace_bytes(int R, int V) {
+  if (R < 0 || V < 1 || V > SSD_MAX_V) return 0;
+  return saguaro_layout(R, V).total;
+}
+
+ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                              float temperature, const int32_t* set, int F, float C,
+                              float* out_probs, float* out_set_mass, float* out_norm,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
+  if (R < 0 || R > 65535 || V < 1 || V > SSD_MAX_V || row_stride < V || !temp_ok(temperature) ||
+      F < 0 || F > SSD_MAX_F || (F > 0 && !set) || !c_ok(C))
+    return SSD_ERR_INVALID_ARG;
+  if (R == 0) return SSD_OK;
+  if (!logits) return SSD_ERR_INVALID_ARG;
+  const SaguaroLayout L = saguaro_layout(R, V);
+  if (!ws_ok(workspace, workspace_bytes, L.total)) return SSD_ERR_WORKSPACE;
+  const int es = elem_size(dtype);
+  SagArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.R = R;
+  a.V = V;
+  a.c2 = float(kLog2e / double(temperature));
+  a.set = set;
+  a.F = F;
+  a.C = C;
+  a.out_probs = out_probs;
+  a.out_set_mass = out_set_mass;
+  a.out_norm = out_norm;
+  a.flags = at<uint32_t>(workspace, 0);
+  a.stats = at<float2>(workspace, L.off_stats);
+  a.n1 = L.rp.n1;
+  a.chunk1 = L.rp.chunk1;
+  a.n_out = L.n_out;
+  a.chunk_out = L.chunk_out;
+  a.aligned = aligned16(logits) && (row_stride * es) % 16 == 0;
+  a.out_aligned = out_probs && aligned16(out_probs) && V % 4 == 0;
+  return hip_status(launch_saguaro(a, dtype == SSD_BF16, stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+ssd_status ssd_fanout_alloc(int K, double a, double r, int budget, int32_t* out_F,
+                            double* out_F_cont) {
+  if (K < 0 || K > 4096 || !(a > 0.0 && a < 1.0) || !(r > 0.0) || !std::isfinite(r) ||
+      budget < 0 || !out_F)
+    return SSD_ERR_INVALID_ARG;
+  // P(k): geometric acceptance law; F_k / F_0 = (P(k) / P(0))^(1/(1+r)) from the stationarity of
+  // the Lagrangian of sum_k P(k) F_k^-r + lambda (sum_k F_k - budget).
+  std::vector<double> w(K + 1);
+  double total = 0.0;
+  for (int k = 0; k <= K; ++k) {
+    const double Pk = (k < K) ? (1.0 - a) * std::pow(a, k) : std::pow(a, K);
+    const double P0 = (K > 0) ? (1.0 - a) : 1.0;
+    w[k] = std::pow(Pk / P0, 1.0 / (1.0 + r));
+    total += w[k];
+  }
+  std::vector<double> frac(K + 1);
+  int64_t used = 0;
+  for (int k = 0; k <= K; ++k) {
+    const double f = double(budget) * w[k] / total;
+    if (out_F_cont) out_F_cont[k] = f;
+    const double fl = std::floor(f);
+    out_F[k] = int32_t(fl);
+    frac[k] = f - fl;
+    used += out_F[k];
+  }
+  // largest remainders first, ties to the smaller k
+  for (int64_t left = budget - used; left > 0; --left) {
+    int best = -1;
+    for (int k = 0; k <= K; ++k)
+      if (frac[k] >= 0.0 && (best < 0 || frac[k] > frac[best])) best = k;
+    if (best < 0) break;
+    out_F[best] += 1;
+    frac[best] = -1.0;
+  }
+  return SSD_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* fanout,
+                          int budget, int32_t* cache_k, int32_t* cache_tok, hipStream_t stream) {
+  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || G_max < 1 || G_max > SSD_MAX_F ||
+      budget < 0 || !fanout)
+    return SSD_ERR_INVALID_ARG;
+  CacheKeysArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int64_t off = 0;
+  for (int k = 0; k <= K; ++k) {
+    if (fanout[k] < 0 || fanout[k] > G_max) return SSD_ERR_INVALID_ARG;
+    a.off[k] = int(off);
+    off += fanout[k];
+  }
+  if (off != budget) return SSD_ERR_INVALID_ARG;
+  a.off[K + 1] = budget;
+  if (B == 0 || budget == 0) return SSD_OK;
+  if (!guesses || !cache_k || !cache_tok) return SSD_ERR_INVALID_ARG;
+  a.B = B;
+  a.K = K;
+  a.Gmax = G_max;
+  a.budget = budget;
+  a.guesses = guesses;
+  a.cache_k = cache_k;
+  a.cache_tok = cache_tok;
+  return hip_status(launch_cache_keys(a, stream));
+}
+
+ssd_status ssd_cache_lookup(int B, int budget, const int32_t* cache_k, const int32_t* cache_tok,
+                            const int32_t* accepted_len, const int32_t* bonus_token,
+                            int32_t* out_slot, int32_t* out_miss_count, hipStream_t stream) {
+  if (B < 0 || B > SSD_MAX_B || budget < 0 || !out_miss_count) return SSD_ERR_INVALID_ARG;
+  if (B > 0 && (!accepted_len || !bonus_token || !out_slot)) return SSD_ERR_INVALID_ARG;
+  if (B > 0 && budget > 0 && (!cache_k || !cache_tok)) return SSD_ERR_INVALID_ARG;
+  CacheLookupArgs a;
+  a.B = B;
+  a.budget = budget;
+  a.cache_k = cache_k;
+  a.cache_tok = cache_tok;
+  a.k = accepted_len;
+  a.tok = bonus_token;
+  a.out_slot = out_slot;
+  a.out_miss = out_miss_count;
+  return hip_status(launch_cache_lookup(a, stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+ssd_status ssd_read_flags(void* workspace, uint32_t* out_flags, int clear, hipStream_t stream) {
+  if (!workspace || !out_flags) return SSD_ERR_INVALID_ARG;
+  uint32_t host = 0;
+  if (hipMemcpyAsync(&host, workspace, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SSD_ERR_HIP;
+  *out_flags = host;
+  if (clear) return hip_status(launch_clear_flags(static_cast<uint32_t*>(workspace), stream));
+  return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Kernel argument blocks and launchers (internal to the library). Arguments are passed by value
+// as one kernarg struct per launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct VerifyArgs {
+  const void* draft;
+  int64_t dstride;  // elements between consecutive sequences
+  const void* target;
+  int64_t tstride;
+  int B, K, V;
+  float c2;  // log2(e) / T
+  const int32_t* x;
+  const float* u;
+  const int32_t* sset;
+  int sF;
+  float C;
+  int topfF[16];
+  int topfFmax;
+  int32_t* topf_out;
+  int32_t* k_out;
+  int32_t* bonus_out;
+  float* aprob_out;
+  float* rmass_out;
+  // workspace views
+  uint32_t* flags;
+  uint32_t* cnt;  // per-sequence arrival counters, 64-byte stride
+  float2* stats;  // [B (2K+1)][n1]
+  void* cand;     // [B K][n1][topfFmax] (value, index)
+  float* res;     // [B][n2]
+  int n1, chunk1;
+  int aligned;  // every logit row starts 16-byte aligned
+};
+
+struct TopfArgs {
+  const void* logits;
+  int64_t row_stride;
+  int R, V;
+  const int32_t* exclude;
+  const int32_t* F_per_row;
+  int Fmax;
+  int32_t* out;
+  uint32_t* flags;
+  void* cand;
+  int n1, chunk1;
+  int aligned;
+};
+
+struct SagArgs {
+  const void* logits;
+  int64_t row_stride;
+  int R, V;
+  float c2;
+  const int32_t* set;
+  int F;
+  float C;
+  float* out_probs;
+  float* out_set_mass;
+  float* out_norm;
+  uint32_t* flags;
+  float2* stats;
+  int n1, chunk1;
+  int n_out, chunk_out;
+  int aligned;
+  int out_aligned;
+};
+
+struct CacheKeysArgs {
+  int B, K, Gmax, budget;
+  const int32_t* guesses;
+  int off[18];  // slot offset of each position k (prefix sums of the fan-out), off[K+1] = budget
+  int32_t* cache_k;
+  int32_t* cache_tok;
+};
+
+struct CacheLookupArgs {
+  int B, budget;
+  const int32_t* cache_k;
+  const int32_t* cache_tok;
+  const int32_t* k;
+  const int32_t* tok;
+  int32_t* out_slot;
+  int32_t* out_miss;
+};
+
+hipError_t launch_verify(const VerifyArgs& a, int n2, bool bf16, hipStream_t st);
+hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st);
+hipError_t launch_cache_lookup(const CacheLookupArgs& a, hipStream_t st);
+hipError_t launch_clear_flags(uint32_t* flags, hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,97 @@
+// Host-side launch planning: how rows are cut into workgroup chunks, and the workspace layout
+// that those chunks need. The *_workspace_bytes entry points and the launchers both use these
+// functions, so a workspace sized by the helper always fits the launch.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPlanMaxChunks = 64;
+constexpr int kPlanTargetGroups = 2048;  // enough workgroups to cover 256 CUs several times over
+constexpr int kPlanMinChunk = 2048;      // elements per workgroup, at least one vector per thread
+constexpr int kPlanSub = 2048;           // phase-2 sub-chunk (256 threads x 8 elements)
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct RowPlan {
+  int n1;      // chunks per row
+  int chunk1;  // elements per chunk (multiple of 8)
+};
+
+// Cut `rows` rows of V elements into chunks: aim for kPlanTargetGroups workgroups in total while
+// keeping each chunk at least kPlanMinChunk elements and at most kPlanMaxChunks per row.
+inline RowPlan plan_rows(int64_t rows, int V) {
+  int64_t n1 = ceil_div(kPlanTargetGroups, rows > 0 ? rows : 1);
+  int64_t cap = ceil_div(V, kPlanMinChunk);
+  if (cap > kPlanMaxChunks) cap = kPlanMaxChunks;
+  if (n1 > cap) n1 = cap;
+  if (n1 < 1) n1 = 1;
+  int64_t chunk = ceil_div(ceil_div(V, n1), 8) * 8;
+  RowPlan p;
+  p.chunk1 = int(chunk);
+  p.n1 = int(ceil_div(V, chunk));
+  return p;
+}
+
+struct VerifyLayout {
+  RowPlan rp;
+  int n2;  // phase-2 sub-chunks per sequence
+  size_t off_cnt, off_stats, off_cand, off_res, total;
+};
+
+// Workspace: [flags | per-sequence counters | row stats | top-F candidates | residual sums]
+inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
+  VerifyLayout L;
+  const int64_t rows = int64_t(B) * (2 * K + 1);
+  L.rp = plan_rows(rows, V);
+  L.n2 = int(ceil_div(V, kPlanSub));
+  size_t off = kAlign;  // flags word lives at offset 0
+  L.off_cnt = off;
+  off = align_up(off + size_t(B) * 64);
+  L.off_stats = off;
+  off = align_up(off + size_t(rows) * L.rp.n1 * 8);
+  L.off_cand = off;
+  off = align_up(off + size_t(B) * K * L.rp.n1 * topf_F_max * 8);
+  L.off_res = off;
+  off = align_up(off + size_t(B) * L.n2 * 4);
+  L.total = off;
+  return L;
+}
+
+struct TopfLayout {
+  RowPlan rp;
+  size_t off_cand, total;
+};
+
+inline TopfLayout topf_layout(int R, int V, int F_max) {
+  TopfLayout L;
+  L.rp = plan_rows(R, V);
+  L.off_cand = kAlign;
+  L.total = align_up(L.off_cand + size_t(R) * L.rp.n1 * F_max * 8);
+  return L;
+}
+
+struct SaguaroLayout {
+  RowPlan rp;
+  int n_out;  // materialisation chunks per row
+  int chunk_out;
+  size_t off_stats, total;
+};
+
+inline SaguaroLayout saguaro_layout(int R, int V) {
+  SaguaroLayout L;
+  L.rp = plan_rows(R, V);
+  RowPlan o = plan_rows(R, V);
+  L.n_out = o.n1;
+  L.chunk_out = o.chunk1;
+  L.off_stats = kAlign;
+  L.total = align_up(L.off_stats + size_t(R) * L.rp.n1 * 8);
+  return L;
+}
+
+}  // namespace ssd

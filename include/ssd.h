@@ -1,0 +1,197 @@
+/*
+ * ssd.h — C ABI of the MI355X (gfx950) library for batched lossless draft verification and the
+ * speculative-speculative-decoding (SSD / Saguaro) pieces around it.
+ *
+ * Sources (page titles):
+ *   [SSD]   "论文阅读：Speculative Speculative Decoding — 消除推测解码的最后一个顺序瓶颈"
+ *           (xiaohongrsx.github.io/posts/ssd-paper-reading)
+ *   [SD7.3] "7.3 Speculative Decoding：投机采样加速" (aiknowledge.cn)
+ *   [HW]    "推测解码：用一个“小模型”骗出 3 倍推理速度" (bbs.huaweicloud.com/blogs/510880)
+ *
+ * Conventions shared by every entry point
+ *   - Every device pointer is caller-owned device memory (e.g. a torch tensor's storage). The
+ *     library allocates nothing and keeps no global state; calls on different streams with
+ *     different workspaces are independent.
+ *   - Device calls enqueue work on `stream` and return once it is launched; nothing synchronises.
+ *   - Arguments are validated on the host before any launch. Any error code means nothing was
+ *     launched, except SSD_ERR_HIP (a launch was rejected by the runtime).
+ *   - Device data is not validated up front (that would need a synchronisation). Out-of-range
+ *     token ids are never dereferenced: the kernel records a flag in the workspace instead (see
+ *     ssd_read_flags) and treats the position as rejected.
+ *   - Logit rows hold V values of `dtype`, contiguous. Every row must have at least one finite
+ *     logit; NaN and +inf logits give undefined results.
+ *   - Sizes: 1 <= K <= SSD_MAX_K, 1 <= V <= SSD_MAX_V, 0 <= B <= SSD_MAX_B. A batch of zero rows
+ *     or sequences is a successful no-op.
+ *   - Workspaces: device memory of at least the size the matching *_workspace_bytes helper
+ *     returns, 256-byte aligned. Its first 4 bytes hold the sticky device-error flags; the rest is
+ *     scratch that each call rewrites before reading. One workspace serves one call at a time.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_MAX_K 16
+#define SSD_MAX_F 16
+#define SSD_MAX_V (1 << 22)
+#define SSD_MAX_B 65535
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1,
+  SSD_ERR_UNSUPPORTED = 2,
+  SSD_ERR_WORKSPACE = 3,
+  SSD_ERR_HIP = 4
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Device-error flag bits (sticky, OR-ed into the workspace's first word). */
+#define SSD_FLAG_BAD_TOKEN 0x1u     /* a draft token id outside [0, V) */
+#define SSD_FLAG_SAGUARO_NORM 0x2u  /* Saguaro normaliser N <= 0 (C = 0 with S holding all mass) */
+#define SSD_FLAG_BAD_F 0x4u         /* a per-row F outside [0, F_max] (clamped) */
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_verify — one round of verification for B sequences.
+ *
+ * Defines: [SD7.3] 7.3.2 (steps 3-4) and 7.3.3; [HW] "二、猜 + 验" and "三、接受概率为什么是对的";
+ * [SSD] "接受-拒绝机制" and "SSD 的核心思想" (the outcome (k, t)).
+ *   q_i = softmax(draft row i / T), p_i = softmax(target row i / T).
+ *   With a Saguaro set S_i ([SSD] "Saguaro 优化二"): q'_i = q_i * (C on S_i, 1 elsewhere) / N_i,
+ *   N_i = 1 - (1 - C) * sum_{s in S_i} q_i(s); without one, q'_i = q_i.
+ *   Position i accepts x_i iff u_i * q'_i(x_i) < p_i(x_i); k = number of leading accepts.
+ *   If k < K the bonus token is drawn from r = max(p_k - q'_k, 0) / R, R = sum r, by inverse CDF
+ *   with u_K: the first token t (ascending id) whose cumulative r exceeds u_K * R. If k = K it is
+ *   drawn the same way from p_K (R = 1). An all-zero residual (rounding only) falls back to p_k.
+ *   Optionally, the top-F guesses of every verified draft row ([SSD] "怎么猜奖励 token"): the F
+ *   largest raw logits excluding x_i, ties to the smaller id, -1 padded, -inf never returned.
+ *
+ * Arguments (row (b, i) of a logits array starts at element b * seq_stride + i * V):
+ *   draft_logits      device [B, >=K rows, V] of dtype; rows i < K are read. draft_seq_stride >= K*V.
+ *   target_logits     device [B, >=K+1 rows, V]; rows i <= K. target_seq_stride >= (K+1)*V.
+ *   dtype             SSD_F32 or SSD_BF16 (both arrays).
+ *   temperature       T, finite and > 0.
+ *   draft_tokens      device int32 [B, K].
+ *   uniforms          device fp32 [B, K+1], each in [0, 1); column K samples the bonus.
+ *   sag_set, sag_F    device int32 [B, K, sag_F] Saguaro sets (entries < 0, >= V or repeated are
+ *                     ignored), or NULL with sag_F = 0. 0 <= sag_F <= SSD_MAX_F.
+ *   sag_C             C in [0, 1]; ignored when sag_F = 0.
+ *   topf_F            host int32 [K]: guesses wanted per draft position (0..topf_F_max), or NULL
+ *                     (= topf_F_max everywhere).
+ *   topf_F_max        0..SSD_MAX_F; 0 disables the guesses.
+ *   topf_out          device int32 [B, K, topf_F_max] or NULL when topf_F_max = 0.
+ *   accepted_len      device int32 [B] out: k in 0..K.
+ *   bonus_token       device int32 [B] out.
+ *   accept_prob       device fp32 [B, K] out or NULL: min(1, p_i(x_i) / q'_i(x_i)) at every i.
+ *   residual_mass     device fp32 [B] out or NULL: R (1 when k = K).
+ *   workspace         device scratch of ssd_verify_workspace_bytes(B, K, V, topf_F_max) bytes.
+ * Errors: SSD_ERR_INVALID_ARG (null required pointer, bad size/stride/T/C/F), SSD_ERR_UNSUPPORTED
+ * (dtype), SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
+ * ------------------------------------------------------------------------------------------- */
+size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max);
+
+ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
+                      const void* target_logits, int64_t target_seq_stride,
+                      ssd_dtype dtype, int B, int K, int V, float temperature,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const int32_t* sag_set, int sag_F, float sag_C,
+                      const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                      int32_t* accepted_len, int32_t* bonus_token,
+                      float* accept_prob, float* residual_mass,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_topf_guess — top-F bonus-token guesses of R rows ([SSD] "怎么猜奖励 token"): per row the
+ * F largest raw logits, excluding one token, ties to the smaller id; -inf never returned; -1 pads.
+ *   logits      device [R rows, V] of dtype; row r starts at element r * row_stride (>= V).
+ *   exclude     device int32 [R] (-1 = none) or NULL.
+ *   F_per_row   device int32 [R] in [0, F_max] or NULL (= F_max). Out-of-range values are clamped
+ *               and flagged (SSD_FLAG_BAD_F).
+ *   F_max       1..SSD_MAX_F.
+ *   out         device int32 [R, F_max].
+ *   workspace   ssd_topf_workspace_bytes(R, V, F_max) bytes.
+ * ------------------------------------------------------------------------------------------- */
+size_t ssd_topf_workspace_bytes(int R, int V, int F_max);
+
+ssd_status ssd_topf_guess(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                          const int32_t* exclude, const int32_t* F_per_row, int F_max,
+                          int32_t* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_saguaro_adjust — Saguaro down-weighting of R draft rows ([SSD] "Saguaro 优化二",
+ * "解法：操纵草稿分布"): q = softmax(row / T); sigma = sum_{s in S} q(s) over the distinct in-range
+ * entries of S; N = 1 - (1 - C) sigma; q' = q * (C on S, 1 elsewhere) / N.
+ *   logits        device [R rows, V]; row r at element r * row_stride (>= V).
+ *   set, F        device int32 [R, F] (-1 pads; out-of-range and repeated entries ignored), F in
+ *                 0..SSD_MAX_F (set may be NULL iff F = 0).
+ *   C             in [0, 1].
+ *   out_probs     device fp32 [R, V] q' or NULL (then nothing of size V is written).
+ *   out_set_mass  device fp32 [R] sigma, or NULL.
+ *   out_norm      device fp32 [R] N, or NULL. N <= 0 is flagged (SSD_FLAG_SAGUARO_NORM).
+ *   workspace     ssd_saguaro_workspace_bytes(R, V) bytes.
+ * ------------------------------------------------------------------------------------------- */
+size_t ssd_saguaro_workspace_bytes(int R, int V);
+
+ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                              float temperature, const int32_t* set, int F, float C,
+                              float* out_probs, float* out_set_mass, float* out_norm,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_fanout_alloc — geometric fan-out of a cache budget ([SSD] "最优扇出度分配"). Host only,
+ * synchronous. P(k) = (1-a) a^k for k < K and a^K for k = K; minimising sum_k P(k) F_k^-r under
+ * sum_k F_k = budget gives F_k proportional to P(k)^(1/(1+r)). Integers: floor, then the leftover
+ * units go to the largest fractional parts, ties to the smaller k.
+ *   K >= 0, 0 < a < 1, r > 0, budget >= 0.
+ *   out_F       host int32 [K+1].
+ *   out_F_cont  host double [K+1] continuous optimum, or NULL.
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_fanout_alloc(int K, double a, double r, int budget, int32_t* out_F,
+                            double* out_F_cont);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_cache_keys — keys of each sequence's speculation cache ([SSD] "SSD 的核心思想": an outcome
+ * (k, t) is k accepted drafts and bonus t; "怎么猜奖励 token"). For k = 0..K the F_k guesses of
+ * draft position k occupy consecutive slots (position K is the draft row after the last drafted
+ * token); a guess of -1 leaves an empty slot (-1, -1).
+ *   guesses     device int32 [B, K+1, G_max] (-1 padded), F_k <= G_max.
+ *   fanout      host int32 [K+1], sum = budget.
+ *   cache_k, cache_tok  device int32 [B, budget] out.
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* fanout,
+                          int budget, int32_t* cache_k, int32_t* cache_tok, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_cache_lookup — look the verification outcome up in each sequence's cache ([SSD]
+ * "SSD 的核心思想": a hit means the next draft is ready with zero wait; "Saguaro 优化三": the batch
+ * waits for every miss). out_slot[b] = first slot j with (cache_k, cache_tok)[b, j] =
+ * (accepted_len[b], bonus_token[b]), else -1; out_miss_count[0] = number of -1 (deterministic).
+ *   cache_k, cache_tok  device int32 [B, budget] (k = -1 marks an empty slot); budget >= 0.
+ *   accepted_len, bonus_token  device int32 [B].
+ *   out_slot    device int32 [B];  out_miss_count  device int32 [1].
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_cache_lookup(int B, int budget, const int32_t* cache_k, const int32_t* cache_tok,
+                            const int32_t* accepted_len, const int32_t* bonus_token,
+                            int32_t* out_slot, int32_t* out_miss_count, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_read_flags — copy a workspace's device-error flags to *out_flags (host) and, if clear != 0,
+ * reset them. Synchronises `stream`.
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_read_flags(void* workspace, uint32_t* out_flags, int clear, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ssd_status_string(ssd_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

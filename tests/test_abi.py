@@ -1,0 +1,145 @@
+"""C-ABI contract tests that need no GPU: exports, argument validation, host-side fan-out.
+
+No call here reaches a kernel launch: every device entry point is called with at least one invalid
+argument, and the workspace pointer is NULL wherever the expected error comes earlier, so a
+validation slip surfaces as a wrong status code rather than a launch.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import draft_verification_ssd_amd as ssd
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "ssd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ssd.LIB_PATH), reason="libssd.so not built")
+
+OK, INV, UNS, WS = ssd.SSD_OK, ssd.SSD_ERR_INVALID_ARG, ssd.SSD_ERR_UNSUPPORTED, ssd.SSD_ERR_WORKSPACE
+FAKE = 0x1000          # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ssd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(ssd.EXPORTS) == names
+
+
+def test_status_strings():
+    L = ssd.lib()
+    for s in range(5):
+        assert L.ssd_status_string(s)
+    assert L.ssd_status_string(99) == b"unknown status"
+
+
+def _verify(**over):
+    B, K, V = 2, 4, 1000
+    a = dict(draft=FAKE, dstride=K * V, target=FAKE, tstride=(K + 1) * V, dtype=ssd.SSD_F32, B=B, K=K,
+             V=V, T=1.0, x=FAKE, u=FAKE, sset=None, sF=0, C=1.0, topfF=None, topfFmax=0, topf_out=None,
+             k=FAKE, bonus=FAKE, aprob=None, rmass=None, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return ssd.lib().ssd_verify(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(dtype=7), UNS),
+    (dict(B=-1), INV), (dict(B=70000), INV),
+    (dict(K=0), INV), (dict(K=17), INV),
+    (dict(V=0), INV), (dict(V=(1 << 22) + 1), INV),
+    (dict(T=0.0), INV), (dict(T=-1.0), INV), (dict(T=float("inf")), INV), (dict(T=float("nan")), INV),
+    (dict(sF=-1), INV), (dict(sF=17), INV), (dict(sF=2, sset=None), INV),
+    (dict(sF=2, sset=FAKE, C=1.5), INV), (dict(sF=2, sset=FAKE, C=float("nan")), INV),
+    (dict(topfFmax=17, topf_out=FAKE), INV), (dict(topfFmax=3, topf_out=None), INV),
+    (dict(dstride=3999), INV), (dict(tstride=4999), INV),
+    (dict(draft=None), INV), (dict(target=None), INV), (dict(x=None), INV), (dict(u=None), INV),
+    (dict(k=None), INV), (dict(bonus=None), INV),
+    (dict(), WS),                                       # no workspace
+    (dict(ws=FAKE + 8, wsb=1 << 30), WS),               # misaligned workspace
+    (dict(ws=FAKE * 16, wsb=64), WS),                   # too small
+    (dict(B=0), OK),                                    # empty batch: nothing to do
+])
+def test_verify_argument_validation(over, want):
+    assert _verify(**over) == want
+
+
+def test_verify_topf_per_position_range_is_checked():
+    F = (ctypes.c_int32 * 4)(1, 2, 4, 1)                  # 4 > topf_F_max = 3
+    assert _verify(topfF=ctypes.addressof(F), topfFmax=3, topf_out=FAKE) == INV
+    F2 = (ctypes.c_int32 * 4)(1, -1, 2, 1)
+    assert _verify(topfF=ctypes.addressof(F2), topfFmax=3, topf_out=FAKE) == INV
+
+
+def test_topf_and_saguaro_validation():
+    L = ssd.lib()
+    assert L.ssd_topf_guess(FAKE, 100, 9, 4, 100, None, None, 3, FAKE, None, 0, None) == UNS
+    assert L.ssd_topf_guess(FAKE, 99, 0, 4, 100, None, None, 3, FAKE, None, 0, None) == INV
+    assert L.ssd_topf_guess(FAKE, 100, 0, 4, 100, None, None, 0, FAKE, None, 0, None) == INV
+    assert L.ssd_topf_guess(FAKE, 100, 0, 4, 100, None, None, 17, FAKE, None, 0, None) == INV
+    assert L.ssd_topf_guess(None, 100, 0, 4, 100, None, None, 3, FAKE, None, 0, None) == INV
+    assert L.ssd_topf_guess(FAKE, 100, 0, 4, 100, None, None, 3, None, None, 0, None) == INV
+    assert L.ssd_topf_guess(FAKE, 100, 0, 4, 100, None, None, 3, FAKE, None, 0, None) == WS
+    assert L.ssd_topf_guess(FAKE, 100, 0, 0, 100, None, None, 3, FAKE, None, 0, None) == OK
+    sag = L.ssd_saguaro_adjust
+    assert sag(FAKE, 100, 0, 4, 100, 0.0, None, 0, 0.5, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, None, 2, 0.5, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 2, -0.1, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 17, 0.5, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 99, 0, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == WS
+    assert sag(FAKE, 100, 5, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == UNS
+    assert sag(FAKE, 100, 0, 0, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == OK
+
+
+def test_cache_validation():
+    L = ssd.lib()
+    F = (ctypes.c_int32 * 5)(3, 2, 2, 2, 3)
+    # fan-out must sum to the budget and fit the guess width
+    assert L.ssd_cache_keys(2, 4, 3, FAKE, ctypes.addressof(F), 11, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 2, FAKE, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 3, FAKE, None, 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 3, None, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(0, 4, 3, FAKE, ctypes.addressof(F), 12, FAKE, FAKE, None) == OK
+    assert L.ssd_cache_lookup(2, 12, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == INV
+    assert L.ssd_cache_lookup(2, 12, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_lookup(-1, 12, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INV
+    assert L.ssd_read_flags(None, FAKE, 1, None) == INV
+
+
+def test_workspace_sizes():
+    a = ssd.ssd_verify_workspace_bytes(16, 4, 128256, 3)
+    b = ssd.ssd_verify_workspace_bytes(128, 8, 152064, 4)
+    assert 0 < a < b and a % 256 == 0
+    assert ssd.ssd_verify_workspace_bytes(16, 0, 128256, 3) == 0
+    assert ssd.ssd_topf_workspace_bytes(768, 128256, 3) > 0
+    assert ssd.ssd_saguaro_workspace_bytes(8192, 128256) > 0
+
+
+@pytest.mark.parametrize("K,a,r,budget", [(4, 0.7, 1.0, 12), (4, 0.7, 1.0, 32), (8, 0.55, 0.5, 100),
+                                          (2, 0.9, 2.0, 7), (0, 0.5, 1.0, 5), (6, 0.3, 1.5, 0),
+                                          (16, 0.8, 1.0, 1000), (3, 0.99, 0.1, 9)])
+def test_fanout_matches_the_oracle(K, a, r, budget):
+    F, Fc = ssd.ssd_fanout_alloc(K, a, r, budget)
+    Fo, Fco = O.fanout(K, a, r, budget)
+    assert F == [int(v) for v in Fo]
+    np.testing.assert_allclose(Fc, Fco, rtol=1e-12, atol=1e-12)
+
+
+def test_fanout_validation():
+    L = ssd.lib()
+    out = (ctypes.c_int32 * 5)()
+    for args in [(4, 1.0, 1.0, 3), (4, 0.0, 1.0, 3), (4, 0.5, 0.0, 3), (4, 0.5, 1.0, -1), (-1, 0.5, 1.0, 3)]:
+        assert L.ssd_fanout_alloc(*args, ctypes.addressof(out), None) == INV
+    assert L.ssd_fanout_alloc(4, 0.5, 1.0, 3, None, None) == INV

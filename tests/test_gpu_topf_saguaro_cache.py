@@ -1,0 +1,156 @@
+"""GPU parity of the standalone top-F guesses, Saguaro adjust and speculation-cache calls."""
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_ssd_amd as ssd
+import oracle as O
+import synth
+from gpu_helpers import DEV, PROB_ATOL, logits_to_device, oracle_topf_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def tie_heavy_rows(R, V, dtype, seed):
+    rng = np.random.default_rng(seed)
+    z = rng.integers(-4, 5, size=(R, V)).astype(np.float32) * np.float32(0.5)
+    z[rng.random((R, V)) < 0.05] = -np.inf
+    return synth.f32_to_bf16_bits(z) if dtype == "bf16" else z
+
+
+@pytest.mark.parametrize("R,V,F,dtype", [(1, 1, 1, "f32"), (3, 5, 7, "bf16"), (5, 300, 3, "f32"),
+                                         (17, 2049, 4, "bf16"), (4, 40000, 16, "f32"),
+                                         (300, 9000, 8, "bf16"), (2, 128256, 3, "bf16"),
+                                         (3, 77777, 5, "f32")])
+def test_topf_matches_oracle_with_ties_masks_and_exclusion(R, V, F, dtype):
+    print(f"[case] topf R{R} V{V} F{F} {dtype}", flush=True)
+    z = tie_heavy_rows(R, V, dtype, seed=R * 7 + V)
+    rng = np.random.default_rng(V)
+    ex = rng.integers(-1, V, size=R).astype(np.int32)
+    Fr = rng.integers(0, F + 1, size=R).astype(np.int32)
+    zd = logits_to_device(z, dtype)
+    got = ssd.ssd_topf_guess(zd, F, exclude=torch.from_numpy(ex).to(DEV),
+                             F_per_row=torch.from_numpy(Fr).to(DEV)).cpu().numpy()
+    z64 = O.logits_f64(z, dtype)
+    for r in range(R):
+        want = list(O.topf(z64[r], int(Fr[r]), int(ex[r]))) + [-1] * (F - int(Fr[r]))
+        assert list(got[r]) == want, f"row {r}"
+
+
+def test_topf_on_a_strided_row_view():
+    bt = synth.make_verify_batch(6, 4, 20000, synth.BF16, 2)
+    d = logits_to_device(bt.draft, bt.dtype)                 # [B, K+1, V]
+    view = d[:, bt.K, :]                                      # row K of every sequence
+    print("[case] topf strided view", flush=True)
+    got = ssd.ssd_topf_guess(view, 4).cpu().numpy()
+    want = oracle_topf_rows(O.logits_f64(bt.draft[:, bt.K], bt.dtype), 4)
+    assert np.array_equal(got, want)
+
+
+def test_topf_bad_f_is_clamped_and_flagged():
+    z = tie_heavy_rows(3, 500, "f32", 1)
+    Fr = np.array([2, 9, -1], dtype=np.int32)
+    ws = ssd.Workspace(ssd.ssd_topf_workspace_bytes(3, 500, 4))
+    print("[case] topf bad F", flush=True)
+    got = ssd.ssd_topf_guess(logits_to_device(z, "f32"), 4, F_per_row=torch.from_numpy(Fr).to(DEV),
+                             workspace=ws).cpu().numpy()
+    assert ssd.ssd_read_flags(ws) & ssd.FLAG_BAD_F
+    z64 = O.logits_f64(z, "f32")
+    assert list(got[0]) == list(O.topf(z64[0], 2)) + [-1, -1]
+    assert list(got[1]) == list(O.topf(z64[1], 4))
+    assert list(got[2]) == [-1] * 4
+
+
+@pytest.mark.parametrize("R,V,F,C,T,dtype", [(4, 1000, 3, 0.5, 1.0, "f32"), (7, 4099, 8, 0.0, 0.7, "bf16"),
+                                             (3, 32000, 4, 1.0, 1.0, "f32"), (9, 128256, 5, 0.3, 1.0, "bf16"),
+                                             (2, 777, 0, 0.5, 1.0, "f32"), (5, 2048, 16, 0.9, 2.0, "bf16")])
+def test_saguaro_matches_oracle(R, V, F, C, T, dtype):
+    print(f"[case] saguaro R{R} V{V} F{F} C{C} {dtype}", flush=True)
+    rng = np.random.default_rng(R + V)
+    z = (rng.normal(0, 2, size=(R, V))).astype(np.float32)
+    if dtype == "bf16":
+        z = synth.f32_to_bf16_bits(z)
+    z64 = O.logits_f64(z, dtype)
+    sets = np.full((R, max(F, 1)), -1, dtype=np.int32)
+    for r in range(R):
+        s = O.topf(z64[r], F) if F else []
+        sets[r, : len(s)] = s
+        if F >= 3 and r % 2 == 0:
+            sets[r, 2] = sets[r, 0]          # repeated entry: ignored
+        if F >= 2 and r % 3 == 0:
+            sets[r, 1] = V + 3               # out of range: ignored
+    zd = logits_to_device(z, dtype)
+    sd = torch.from_numpy(sets[:, :F].copy()).to(DEV) if F else None
+    qp, sig, N = ssd.ssd_saguaro_adjust(zd, T, sd, C, materialise=True)
+    qp, sig, N = qp.cpu().numpy(), sig.cpu().numpy(), N.cpu().numpy()
+    for r in range(R):
+        q = O.softmax_t(z64[r], T)
+        want, s_ref, n_ref = O.saguaro(q, sets[r, :F] if F else None, C)
+        assert abs(sig[r] - s_ref) < PROB_ATOL and abs(N[r] - n_ref) < PROB_ATOL
+        np.testing.assert_allclose(qp[r], want, atol=PROB_ATOL, rtol=0)
+
+
+def test_saguaro_compact_outputs_only():
+    z = np.random.default_rng(3).normal(0, 2, size=(5, 3001)).astype(np.float32)
+    sets = np.array([O.topf(z[r].astype(np.float64), 2) for r in range(5)], dtype=np.int32)
+    print("[case] saguaro compact", flush=True)
+    qp, sig, N = ssd.ssd_saguaro_adjust(logits_to_device(z, "f32"), 1.0, torch.from_numpy(sets).to(DEV), 0.5)
+    assert qp is None
+    for r in range(5):
+        _, s_ref, n_ref = O.saguaro(O.softmax_t(z[r].astype(np.float64), 1.0), sets[r], 0.5)
+        assert abs(sig[r].item() - s_ref) < PROB_ATOL and abs(N[r].item() - n_ref) < PROB_ATOL
+
+
+def test_saguaro_degenerate_normaliser_is_flagged():
+    z = np.full((1, 4), -np.inf, dtype=np.float32)
+    z[0, :2] = 0.0
+    sets = np.array([[0, 1]], dtype=np.int32)
+    ws = ssd.Workspace(ssd.ssd_saguaro_workspace_bytes(1, 4))
+    print("[case] saguaro N<=0", flush=True)
+    ssd.ssd_saguaro_adjust(logits_to_device(z, "f32"), 1.0, torch.from_numpy(sets).to(DEV), 0.0, workspace=ws)
+    assert ssd.ssd_read_flags(ws) & ssd.FLAG_SAGUARO_NORM
+
+
+@pytest.mark.parametrize("B,K,G,fan", [(3, 4, 3, [3, 2, 2, 2, 3]), (5, 4, 8, [8, 7, 5, 5, 7]),
+                                       (2, 2, 2, [0, 2, 1]), (1, 1, 1, [1, 0])])
+def test_cache_keys_and_lookup_match_oracle(B, K, G, fan):
+    print(f"[case] cache B{B} K{K} fan{fan}", flush=True)
+    rng = np.random.default_rng(B * 10 + K)
+    guesses = np.full((B, K + 1, G), -1, dtype=np.int32)
+    for b in range(B):
+        for k in range(K + 1):
+            n = rng.integers(0, G + 1)
+            guesses[b, k, :n] = rng.permutation(50)[:n]
+    ck, ct = ssd.ssd_cache_keys(torch.from_numpy(guesses).to(DEV), fan)
+    ck, ct = ck.cpu().numpy(), ct.cpu().numpy()
+    kk_all, tt_all = [], []
+    for b in range(B):
+        kk, tt = O.cache_keys([list(guesses[b, k]) for k in range(K + 1)], fan)
+        assert list(ck[b]) == list(kk) and list(ct[b]) == list(tt)
+        kk_all.append(kk)
+        tt_all.append(tt)
+    # outcomes: half of them drawn from the cache, half at random
+    acc = np.empty(B, dtype=np.int32)
+    bon = np.empty(B, dtype=np.int32)
+    for b in range(B):
+        valid = np.nonzero(ck[b] >= 0)[0]
+        if b % 2 == 0 and len(valid):
+            j = rng.choice(valid)
+            acc[b], bon[b] = ck[b, j], ct[b, j]
+        else:
+            acc[b], bon[b] = rng.integers(0, K + 1), rng.integers(0, 50)
+    slot, miss = ssd.ssd_cache_lookup(torch.from_numpy(ck).to(DEV), torch.from_numpy(ct).to(DEV),
+                                      torch.from_numpy(acc).to(DEV), torch.from_numpy(bon).to(DEV))
+    slot = slot.cpu().numpy()
+    want = [O.cache_lookup(kk_all[b], tt_all[b], int(acc[b]), int(bon[b])) for b in range(B)]
+    assert list(slot) == want
+    assert int(miss.item()) == sum(s < 0 for s in want)
+
+
+def test_lookup_with_empty_cache_counts_every_miss():
+    B = 1000
+    z = torch.zeros(B, dtype=torch.int32, device=DEV)
+    ck = torch.empty((B, 0), dtype=torch.int32, device=DEV)
+    print("[case] lookup empty cache", flush=True)
+    slot, miss = ssd.ssd_cache_lookup(ck, ck, z, z)
+    assert int(miss.item()) == B and bool((slot == -1).all())
