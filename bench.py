@@ -1,0 +1,205 @@
+"""Throughput of the verification hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one verification round over one batch: every draft and target logit row of the batch
+is streamed once (temperature softmax statistics, fused top-F guesses), the accept decisions and
+first rejection are taken, the residual is formed and normalised and the bonus token is drawn by
+inverse CDF. Inputs are seeded synthetic logits (see synth/gen.py) resident in HBM before timing;
+the timed loop rotates over enough input replicas (>= 512 MB per cycle) that the 256 MB Infinity
+Cache cannot serve them. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified logit rows/sec and achieved HBM GB/s (B=16,K=4,V=128256)"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 512 << 20
+KERNEL_SOURCES = ["draft_verification_ssd_amd/csrc/ssd_verify.hip",
+                  "draft_verification_ssd_amd/csrc/ssd_device.hpp",
+                  "draft_verification_ssd_amd/csrc/ssd_plan.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="b16_k4_v128256_bf16_top3")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(B, K, V, esize, topf):
+    logits = (2 * K + 1) * B * V * esize          # every draft (K) and target (K+1) row read once
+    small = B * K * 4 + B * (K + 1) * 4           # draft tokens, uniforms
+    outs = 2 * B * 4 + B * K * topf * 4           # accepted length, bonus, guesses
+    return logits + small + outs
+
+
+def make_replica(bt, dev, topf, workspace):
+    import numpy as np
+    import torch
+
+    import draft_verification_ssd_amd as ssd
+
+    def lg(a):
+        a = np.ascontiguousarray(a)
+        if bt.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    draft = lg(bt.draft[:, : bt.K])
+    target = lg(bt.target)
+    x = torch.from_numpy(bt.x).to(dev)
+    u = torch.from_numpy(bt.u).to(dev)
+    return ssd.VerifyCall(draft, target, x, u, bt.T, topf_F_max=topf, workspace=workspace)
+
+
+def cpu_baseline(bt, topf, seconds):
+    """The float64 oracle on a bounded sample of the same workload (single thread)."""
+    import oracle as O
+
+    t0 = time.perf_counter()
+    seqs = 0
+    B, K = bt.B, bt.K
+    while True:
+        b = seqs % B
+        zq = O.logits_f64(bt.draft[b, :K], bt.dtype)
+        zp = O.logits_f64(bt.target[b], bt.dtype)
+        O.verify_sequence(zq, zp, bt.x[b], bt.u[b], bt.T)
+        for i in range(K):
+            O.topf(zq[i], topf, int(bt.x[b, i]))
+        seqs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    rows = seqs * (2 * K + 1)
+    return dict(value=rows / el, unit="rows/s", cores=1, kind="oracle",
+                sample=f"{seqs} sequences of the workload (seed 0), {rows} logit rows, "
+                       f"float64 NumPy oracle verify + top-{topf} guesses, {el:.1f} s on 1 thread")
+
+
+def load_traffic(workload, khash):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_hash") != khash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
+              f"sequence across GPUs, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import draft_verification_ssd_amd as ssd
+    import synth
+
+    spec = synth.workload(args.workload)
+    B, K, V, dtype = spec["B"], spec["K"], spec["V"], spec["dtype"]
+    topf = spec.get("topf", 0)
+    esize = 2 if dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    bt = synth.make_verify_batch(B, K, V, dtype, args.seed, T=spec["T"],
+                                 noise_sigma=spec.get("noise_sigma", 0.5), zipf_s=spec.get("zipf_s"))
+    step_bytes = algorithmic_bytes(B, K, V, esize, topf)
+    logit_bytes = (2 * K + 1) * B * V * esize
+    n_rep = max(1, math.ceil(ROTATE_BYTES / logit_bytes))
+    ws = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, topf), dev)
+    calls = [make_replica(bt, dev, topf, ws) for _ in range(n_rep)]
+    stream = torch.cuda.current_stream(dev)
+
+    for i in range(args.warmup):
+        calls[i % n_rep]()
+    torch.cuda.synchronize()
+
+    # per-step event pairs on the launch stream give the kernels' own duration per launch;
+    # the outer pair gives whole-loop throughput
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        e0, e1 = evs[i]
+        e0.record(stream)
+        calls[i % n_rep]()
+        e1.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    flags = ssd.ssd_read_flags(ws)
+    if flags:
+        print(f"device flags {flags:#x}", file=sys.stderr)
+        sys.exit(3)
+
+    rows = (2 * K + 1) * B
+    value = rows / (ms_per_step * 1e-3)
+    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    khash = kernel_hash()
+    traffic = load_traffic(args.workload, khash)
+
+    k_hist = np.bincount(calls[0].outputs["accepted_len"].cpu().numpy(), minlength=K + 1).tolist()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "K": K, "V": V, "T": spec["T"], "topf": topf,
+                   "rows_per_step": rows, "algorithmic_bytes_per_step": step_bytes,
+                   "input_replicas": n_rep, "sequences_per_s": round(B / (ms_per_step * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "verify_fused_kernel",
+                     "launch_ms": round(launch_ms, 6), "kernel_hash": khash},
+        "accepted_len_hist": k_hist,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(bt, topf, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_F32, SSD_BF16 = 0, 1
-SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 22, 65535
-FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F = 0x1, 0x2, 0x4
+SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 20, 65535
+FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT = 0x1, 0x2, 0x4, 0x8
 
 EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify", "ssd_topf_workspace_bytes", "ssd_topf_guess",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",

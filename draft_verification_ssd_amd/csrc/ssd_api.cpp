@@ -31,6 +31,10 @@ ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_
 
 }  // namespace
 
+#ifdef SSD_TRACE
+static void* ssd_trace_buffer = nullptr;
+#endif
+
 extern "C" {
 
 const char* ssd_status_string(ssd_status s) {
@@ -89,6 +93,7 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.B = B;
   a.K = K;
   a.V = V;
+  a.T = L.T;
   a.c2 = float(kLog2e / double(temperature));
   a.x = draft_tokens;
   a.u = uniforms;
@@ -104,15 +109,24 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.rmass_out = residual_mass;
   a.flags = at<uint32_t>(workspace, 0);
   a.cnt = at<uint32_t>(workspace, L.off_cnt);
-  a.stats = at<float2>(workspace, L.off_stats);
-  a.cand = at<void>(workspace, L.off_cand);
+  a.stats = at<uint64_t>(workspace, L.off_stats);
+  a.cand = at<uint64_t>(workspace, L.off_cand);
   a.res = at<float>(workspace, L.off_res);
-  a.n1 = L.rp.n1;
-  a.chunk1 = L.rp.chunk1;
+  a.spin_limit = 1 << 20;
   a.aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
               (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;
-  return hip_status(launch_verify(a, L.n2, dtype == SSD_BF16, stream));
+#ifdef SSD_TRACE
+  a.trace = static_cast<uint64_t*>(ssd_trace_buffer);
+#endif
+  const hipError_t e = launch_verify(a, dtype == SSD_BF16, stream);
+  if (e == hipErrorInvalidConfiguration) return SSD_ERR_UNSUPPORTED;
+  return hip_status(e);
 }
+
+#ifdef SSD_TRACE
+// analysis builds only: device buffer of 8 timestamps per verification workgroup
+void ssd_set_trace_buffer(void* device_buffer) { ssd_trace_buffer = device_buffer; }
+#endif
 
 // ------------------------------------------------------------------------------------------------
 size_t ssd_topf_workspace_bytes(int R, int V, int F_max) {

@@ -17,11 +17,58 @@ constexpr int kMaxF = 16;
 constexpr int kMaxChunks = 64;           // phase-1 chunks per row
 constexpr int kSubElems = 8;             // phase-2 elements per thread (contiguous)
 constexpr int kSub = kThreads * kSubElems;  // phase-2 sub-chunk width
-constexpr int kMaxSubs = (1 << 22) / kSub;  // sub-chunks of the largest supported row
+constexpr int kMaxV = 1 << 20;             // largest supported vocabulary
+constexpr int kMaxTiles = kMaxV / kSub;     // tiles of the largest supported row
 
 constexpr uint32_t kFlagBadToken = 0x1u;
 constexpr uint32_t kFlagSaguaroNorm = 0x2u;
 constexpr uint32_t kFlagBadF = 0x4u;
+constexpr uint32_t kFlagTimeout = 0x8u;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Cand {
+  float v;
+  int i;
+};
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
+// ---------------------------------------------------------------------------------------------
+// DPP lane exchanges inside 16-lane rows: xor 1, xor 2 (quad permutes), then the half-row and row
+// mirrors. Applied in that order, a commutative combine leaves every lane of the row holding the
+// bit-identical row result, with no LDS traffic.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return v;
+}
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
@@ -274,6 +321,114 @@ __device__ __forceinline__ void block_merge_top(const TopList<FM>& tl, int F, ui
       out_i[r] = (bh != 0) ? int(~bl) : -1;
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Row tiles: thread t of a 256-thread block owns the kSubElems contiguous tokens starting at
+// c0 + 8 t of each row. load_raw keeps them packed (one uint4 per 16 bytes); positions at or past
+// V read as -inf. Vector loads need the row 16-byte aligned.
+// ---------------------------------------------------------------------------------------------
+template <class ET>
+struct RawTile {
+  static constexpr int kWords = kSubElems * sizeof(typename ET::T) / 16;  // uint4 per thread
+  uint4 w[kWords];
+};
+
+// Vector path: the thread's 8 tokens are whole and 16-byte aligned. Decided once per thread, so a
+// run of row loads compiles to back-to-back vector loads with no waits in between.
+template <class ET>
+__device__ __forceinline__ void load_raw_vec(const typename ET::T* __restrict__ row, int e0,
+                                             RawTile<ET>& r) {
+#pragma unroll
+  for (int h = 0; h < RawTile<ET>::kWords; ++h) r.w[h] = load16(row + e0 + h * ET::kVec);
+}
+
+template <class ET>
+__device__ __forceinline__ void load_raw_scalar(const typename ET::T* __restrict__ row,
+                                                          int e0, int V, RawTile<ET>& r) {
+  constexpr int NW = RawTile<ET>::kWords;
+  uint32_t words[NW * 4];
+  if (sizeof(typename ET::T) == 4) {
+#pragma unroll
+    for (int e = 0; e < kSubElems; ++e)
+      words[e] = (e0 + e < V) ? __float_as_uint(ET::one(row, e0 + e)) : 0xFF800000u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSubElems; e += 2) {
+      const uint32_t lo = (e0 + e < V) ? (__float_as_uint(ET::one(row, e0 + e)) >> 16) : 0xFF80u;
+      const uint32_t hi = (e0 + e + 1 < V) ? (__float_as_uint(ET::one(row, e0 + e + 1)) >> 16) : 0xFF80u;
+      words[e / 2] = lo | (hi << 16);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < NW; ++h)
+    r.w[h] = make_uint4(words[4 * h], words[4 * h + 1], words[4 * h + 2], words[4 * h + 3]);
+}
+
+template <class ET>
+__device__ __forceinline__ void load_raw(const typename ET::T* __restrict__ row, int e0, int V,
+                                         bool aligned, RawTile<ET>& r) {
+  if (aligned && e0 + kSubElems <= V)
+    load_raw_vec<ET>(row, e0, r);
+  else
+    load_raw_scalar<ET>(row, e0, V, r);
+}
+
+template <class ET>
+__device__ __forceinline__ void unpack_tile(const RawTile<ET>& r, float (&z)[kSubElems]) {
+#pragma unroll
+  for (int h = 0; h < RawTile<ET>::kWords; ++h) ET::unpack(r.w[h], z + h * ET::kVec);
+}
+
+// Residual (qrow != nullptr) or target-row values of this thread's tokens of a tile:
+// r = max(p - q w / N, 0) with w = C on the Saguaro set (w_in = C / N, w_out = 1 / N), or r = p.
+template <class ET>
+__device__ __forceinline__ void sub_values(const typename ET::T* __restrict__ prow,
+                                           const typename ET::T* __restrict__ qrow, int c0, int V,
+                                           bool aligned, float c, float Lp, float Lq, float w_out,
+                                           float w_in, const int* set_entries, int n_set,
+                                           float (&r)[kSubElems]) {
+  const int e0 = c0 + threadIdx.x * kSubElems;
+  RawTile<ET> rp, rq;
+  load_raw<ET>(prow, e0, V, aligned, rp);
+  if (qrow) load_raw<ET>(qrow, e0, V, aligned, rq);
+  float zp[kSubElems], zq[kSubElems];
+  unpack_tile<ET>(rp, zp);
+  if (qrow) unpack_tile<ET>(rq, zq);
+  uint32_t in_set = 0;  // bit e: token e0 + e belongs to the Saguaro set
+  for (int f = 0; f < n_set; ++f) {
+    const unsigned d = unsigned(set_entries[f] - e0);
+    if (d < unsigned(kSubElems)) in_set |= 1u << d;
+  }
+#pragma unroll
+  for (int e = 0; e < kSubElems; ++e) {
+    const float pv = ex2(fmaf(zp[e], c, -Lp));
+    if (qrow) {
+      const float w = ((in_set >> e) & 1u) ? w_in : w_out;
+      const float qv = ex2(fmaf(zq[e], c, -Lq)) * w;
+      r[e] = fmaxf(pv - qv, 0.f);
+    } else {
+      r[e] = pv;
+    }
+    if (e0 + e >= V) r[e] = 0.f;
+  }
+}
+
+// Scan this thread's values, then the block: per-element inclusive prefixes (relative to the tile
+// start) in pre[], tile total returned (equal to the last thread's last inclusive prefix).
+__device__ __forceinline__ float sub_scan(const float (&r)[kSubElems], float (&pre)[kSubElems],
+                                          float* shf) {
+  float run = 0.f;
+#pragma unroll
+  for (int e = 0; e < kSubElems; ++e) {
+    run += r[e];
+    pre[e] = run;
+  }
+  float total;
+  const float excl = block_excl_scan(run, shf, total);
+#pragma unroll
+  for (int e = 0; e < kSubElems; ++e) pre[e] = excl + pre[e];
+  return total;
 }
 
 }  // namespace ssd

@@ -13,6 +13,8 @@ struct VerifyArgs {
   const void* target;
   int64_t tstride;
   int B, K, V;
+  int b0;    // first sequence of this launch
+  int T;     // 2048-token tiles per row
   float c2;  // log2(e) / T
   const int32_t* x;
   const float* u;
@@ -28,12 +30,13 @@ struct VerifyArgs {
   float* rmass_out;
   // workspace views
   uint32_t* flags;
-  uint32_t* cnt;  // per-sequence arrival counters, 64-byte stride
-  float2* stats;  // [B (2K+1)][n1]
-  void* cand;     // [B K][n1][topfFmax] (value, index)
-  float* res;     // [B][n2]
-  int n1, chunk1;
+  uint32_t* cnt;     // per sequence: [b*64] tile arrivals after phase 1, [b*64+32] after phase 2
+  uint64_t* stats;   // [B][2K+1][T] (max c, sum) per tile
+  uint64_t* cand;    // [B][K][T][topfFmax] candidate keys per tile
+  float* res;        // [B][T] residual mass per tile
+  int spin_limit;
   int aligned;  // every logit row starts 16-byte aligned
+  uint64_t* trace;  // per-workgroup phase timestamps (analysis builds only), or null
 };
 
 struct TopfArgs {
@@ -87,7 +90,7 @@ struct CacheLookupArgs {
   int32_t* out_miss;
 };
 
-hipError_t launch_verify(const VerifyArgs& a, int n2, bool bf16, hipStream_t st);
+hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st);

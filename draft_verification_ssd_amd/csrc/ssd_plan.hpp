@@ -38,27 +38,27 @@ inline RowPlan plan_rows(int64_t rows, int V) {
   return p;
 }
 
+constexpr int kPlanTile = 2048;  // tokens per verification tile (256 threads x 8)
+
 struct VerifyLayout {
-  RowPlan rp;
-  int n2;  // phase-2 sub-chunks per sequence
+  int T;  // tiles per row
   size_t off_cnt, off_stats, off_cand, off_res, total;
 };
 
-// Workspace: [flags | per-sequence counters | row stats | top-F candidates | residual sums]
+// Workspace: [flags | per-sequence counters (256 B each) | tile stats | top-F candidate keys |
+// tile residual masses]. The counters must start at zero; every call leaves them at zero.
 inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
   VerifyLayout L;
-  const int64_t rows = int64_t(B) * (2 * K + 1);
-  L.rp = plan_rows(rows, V);
-  L.n2 = int(ceil_div(V, kPlanSub));
+  L.T = int(ceil_div(V, kPlanTile));
   size_t off = kAlign;  // flags word lives at offset 0
   L.off_cnt = off;
-  off = align_up(off + size_t(B) * 64);
+  off = align_up(off + size_t(B) * 256);
   L.off_stats = off;
-  off = align_up(off + size_t(rows) * L.rp.n1 * 8);
+  off = align_up(off + size_t(B) * (2 * K + 1) * L.T * 8);
   L.off_cand = off;
-  off = align_up(off + size_t(B) * K * L.rp.n1 * topf_F_max * 8);
+  off = align_up(off + size_t(B) * K * L.T * topf_F_max * 8);
   L.off_res = off;
-  off = align_up(off + size_t(B) * L.n2 * 4);
+  off = align_up(off + size_t(B) * L.T * 4);
   L.total = off;
   return L;
 }

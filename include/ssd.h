@@ -10,8 +10,9 @@
  *
  * Conventions shared by every entry point
  *   - Every device pointer is caller-owned device memory (e.g. a torch tensor's storage). The
- *     library allocates nothing and keeps no global state; calls on different streams with
- *     different workspaces are independent.
+ *     library allocates nothing; its only global state is a per-device cache of how many
+ *     verification workgroups fit the device at once. Calls on different streams with different
+ *     workspaces are independent.
  *   - Device calls enqueue work on `stream` and return once it is launched; nothing synchronises.
  *   - Arguments are validated on the host before any launch. Any error code means nothing was
  *     launched, except SSD_ERR_HIP (a launch was rejected by the runtime).
@@ -23,8 +24,11 @@
  *   - Sizes: 1 <= K <= SSD_MAX_K, 1 <= V <= SSD_MAX_V, 0 <= B <= SSD_MAX_B. A batch of zero rows
  *     or sequences is a successful no-op.
  *   - Workspaces: device memory of at least the size the matching *_workspace_bytes helper
- *     returns, 256-byte aligned. Its first 4 bytes hold the sticky device-error flags; the rest is
- *     scratch that each call rewrites before reading. One workspace serves one call at a time.
+ *     returns, 256-byte aligned, zero-filled before its first use. Its first 4 bytes hold the
+ *     sticky device-error flags; ssd_verify keeps per-sequence arrival counters in it that each
+ *     call returns to zero (re-zero the workspace after an SSD_FLAG_TIMEOUT). The rest is scratch
+ *     that each call rewrites before reading. One workspace serves one call at a time: calls that
+ *     share a workspace must be ordered on one stream.
  */
 #ifndef SSD_H_
 #define SSD_H_
@@ -39,7 +43,7 @@ extern "C" {
 
 #define SSD_MAX_K 16
 #define SSD_MAX_F 16
-#define SSD_MAX_V (1 << 22)
+#define SSD_MAX_V (1 << 20)
 #define SSD_MAX_B 65535
 
 typedef enum ssd_status {
@@ -56,6 +60,7 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 #define SSD_FLAG_BAD_TOKEN 0x1u     /* a draft token id outside [0, V) */
 #define SSD_FLAG_SAGUARO_NORM 0x2u  /* Saguaro normaliser N <= 0 (C = 0 with S holding all mass) */
 #define SSD_FLAG_BAD_F 0x4u         /* a per-row F outside [0, F_max] (clamped) */
+#define SSD_FLAG_TIMEOUT 0x8u       /* a wait between workgroups gave up (workspace needs re-zeroing) */
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_verify — one round of verification for B sequences.
@@ -91,8 +96,12 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   accept_prob       device fp32 [B, K] out or NULL: min(1, p_i(x_i) / q'_i(x_i)) at every i.
  *   residual_mass     device fp32 [B] out or NULL: R (1 when k = K).
  *   workspace         device scratch of ssd_verify_workspace_bytes(B, K, V, topf_F_max) bytes.
+ * Launch: one kernel per round of sequences, each round as many whole sequences (ceil(V / 2048)
+ * workgroups each) as the device keeps resident at once; the workgroups of a sequence wait for
+ * each other with bounded spins (SSD_FLAG_TIMEOUT instead of a hang).
  * Errors: SSD_ERR_INVALID_ARG (null required pointer, bad size/stride/T/C/F), SSD_ERR_UNSUPPORTED
- * (dtype), SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
+ * (dtype, or a vocabulary whose 2048-token tiles cannot all be resident on the device),
+ * SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
  * ------------------------------------------------------------------------------------------- */
 size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max);
 

@@ -58,7 +58,7 @@ def _verify(**over):
     (dict(dtype=7), UNS),
     (dict(B=-1), INV), (dict(B=70000), INV),
     (dict(K=0), INV), (dict(K=17), INV),
-    (dict(V=0), INV), (dict(V=(1 << 22) + 1), INV),
+    (dict(V=0), INV), (dict(V=(1 << 20) + 1), INV),
     (dict(T=0.0), INV), (dict(T=-1.0), INV), (dict(T=float("inf")), INV), (dict(T=float("nan")), INV),
     (dict(sF=-1), INV), (dict(sF=17), INV), (dict(sF=2, sset=None), INV),
     (dict(sF=2, sset=FAKE, C=1.5), INV), (dict(sF=2, sset=FAKE, C=float("nan")), INV),

@@ -1,0 +1,151 @@
+"""Full-size workloads on the GPU against the oracle on sampled sequences / rows:
+
+  * SSD cache build: B=16 outer x 12 branches, K=4, V=128256 bf16, fan-out budget 12 (a=0.7, r=1),
+    Saguaro C=0.5 — guesses, keys, Saguaro verification, branch-row Saguaro, lookup and hit rate;
+  * large batch: B=128, K=8, V=152064 fp32 Zipf-shaped rows, T=0.7, top-4 guesses (several launch
+    rounds of the verification kernel);
+  * full SSD round: B=64 x budget 32 = 2048 branches (8192 branch rows) plus the outer rows,
+    V=128256 fp32, C=0.3 — Saguaro adjust on every branch row, verification, lookup, miss count.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_verification_ssd_amd as ssd
+import oracle as O
+import synth
+from gpu_helpers import DEV, PROB_ATOL, compare_verify, logits_to_device, report
+
+pytestmark = pytest.mark.gpu
+
+
+def ssd_round_gpu(bt, fan, branch=None, branch_sample=None):
+    """One SSD round through the library: guesses of the outer draft rows (verify-fused for rows
+    0..K-1, standalone for row K), cache keys, Saguaro verification, lookup; and Saguaro adjust of
+    the branch rows with sets = their top-F_j guesses."""
+    B, K, V = bt.B, bt.K, bt.V
+    draft = logits_to_device(bt.draft, bt.dtype)          # [B, K+1, V]
+    target = logits_to_device(bt.target, bt.dtype)
+    x = torch.from_numpy(bt.x).to(DEV)
+    u = torch.from_numpy(bt.u).to(DEV)
+    sets = torch.from_numpy(bt.sets).to(DEV)
+    Gm = max(fan)
+    guesses = torch.full((B, K + 1, Gm), -1, dtype=torch.int32, device=DEV)
+    topf = torch.empty((B, K, Gm), dtype=torch.int32, device=DEV)
+    out = ssd.ssd_verify(draft, target, x, u, bt.T, sag_set=sets, sag_C=bt.C, topf_F=fan[:K],
+                         topf_F_max=Gm, topf_out=topf,
+                         accept_prob=torch.empty((B, K), device=DEV), residual_mass=torch.empty(B, device=DEV))
+    guesses[:, :K] = topf
+    if fan[K] > 0:
+        guesses[:, K, : fan[K]] = ssd.ssd_topf_guess(draft[:, K, :], fan[K])
+    ck, ct = ssd.ssd_cache_keys(guesses.contiguous(), fan)
+    slot, miss = ssd.ssd_cache_lookup(ck, ct, out["accepted_len"], out["bonus_token"])
+    res = dict(k=out["accepted_len"], bonus=out["bonus_token"], guesses=guesses, ck=ck, ct=ct,
+               slot=slot, miss=miss, out=out)
+    if branch is not None:
+        nb = branch.shape[1]
+        bd = logits_to_device(branch, bt.dtype).view(B * nb * K, V)
+        Fr = torch.tensor(fan[:K], dtype=torch.int32, device=DEV).repeat(B * nb)
+        bsets = ssd.ssd_topf_guess(bd, Gm, F_per_row=Fr)
+        _, sig, N = ssd.ssd_saguaro_adjust(bd, bt.T, bsets, bt.C)
+        res.update(branch_sets=bsets.view(B, nb, K, Gm), branch_sigma=sig.view(B, nb, K),
+                   branch_N=N.view(B, nb, K))
+    torch.cuda.synchronize()
+    return res
+
+
+def check_round(bt, fan, res, seqs, branch=None, branch_seqs=(), name=""):
+    ref = O.ssd_round(bt.draft, bt.target, bt.dtype, bt.x, bt.u, bt.T, bt.sets, bt.C, fan,
+                      branch=None, seqs=seqs)
+    st = compare_verify(bt, res["out"], {b: ref[b]["verify"] for b in seqs},
+                        res["out"]["accept_prob"], res["out"]["residual_mass"])
+    g = res["guesses"].cpu().numpy()
+    ck, ct, slot = res["ck"].cpu().numpy(), res["ct"].cpu().numpy(), res["slot"].cpu().numpy()
+    k_gpu, t_gpu = res["k"].cpu().numpy(), res["bonus"].cpu().numpy()
+    for b in seqs:
+        d = ref[b]
+        for i in range(bt.K + 1):
+            assert list(g[b, i, : fan[i]]) == list(d["guesses"][i]), f"guesses seq {b} pos {i}"
+        assert list(ck[b]) == list(d["keys_k"]) and list(ct[b]) == list(d["keys_t"]), f"keys seq {b}"
+        # lookup must agree with the oracle's lookup of the GPU's own outcome (bit-exact int work)
+        assert slot[b] == O.cache_lookup(d["keys_k"], d["keys_t"], int(k_gpu[b]), int(t_gpu[b]))
+    miss = int(res["miss"].item())
+    assert miss == int((slot < 0).sum())
+    if branch is not None:
+        bs = res["branch_sets"].cpu().numpy()
+        sig = res["branch_sigma"].cpu().numpy()
+        nrm = res["branch_N"].cpu().numpy()
+        for b, j in branch_seqs:
+            for i in range(bt.K):
+                zb = O.logits_f64(branch[b, j, i], bt.dtype)
+                S = O.topf(zb, fan[i])
+                assert list(bs[b, j, i, : fan[i]]) == list(S), f"branch set {b},{j},{i}"
+                _, s_ref, n_ref = O.saguaro(O.softmax_t(zb, bt.T), S, bt.C)
+                assert abs(sig[b, j, i] - s_ref) < PROB_ATOL and abs(nrm[b, j, i] - n_ref) < PROB_ATOL
+    st["hits"] = int((slot >= 0).sum())
+    st["miss_count"] = miss
+    report(name, st)
+    return st
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ssd_cache_build_b16x12_k4_v128256_bf16(seed):
+    w = synth.workload("ssd_build_b16x12_k4_v128256_bf16")
+    fan, _ = ssd.ssd_fanout_alloc(w["K"], w["a"], w["r"], w["budget"])
+    fo, _ = O.fanout(w["K"], w["a"], w["r"], w["budget"])
+    assert fan == [int(v) for v in fo] == [3, 2, 2, 2, 3]
+    bt = synth.make_verify_batch(w["B"], w["K"], w["V"], w["dtype"], seed, T=w["T"], sag_sizes=fan[: w["K"]],
+                                 C=w["C"])
+    branch = synth.make_branch_rows(w["B"], w["budget"], w["K"], w["V"], w["dtype"], seed)
+    print(f"[case] ssd cache build seed {seed}", flush=True)
+    res = ssd_round_gpu(bt, fan, branch)
+    check_round(bt, fan, res, range(w["B"]), branch, [(b, j) for b in (0, 7, 15) for j in (0, 5, 11)],
+                name=f"ssd_build seed{seed}")
+
+
+@pytest.mark.parametrize("seed", [0])
+def test_large_batch_b128_k8_v152064_f32_zipf_top4(seed):
+    w = synth.workload("b128_k8_v152064_f32_zipf_top4")
+    bt = synth.make_verify_batch(w["B"], w["K"], w["V"], w["dtype"], seed, T=w["T"], zipf_s=w["zipf_s"],
+                                 noise_sigma=w["noise_sigma"])
+    print("[case] b128_k8_v152064 verify", flush=True)
+    draft = logits_to_device(bt.draft[:, : bt.K], bt.dtype)
+    target = logits_to_device(bt.target, bt.dtype)
+    B, K = bt.B, bt.K
+    aprob = torch.empty((B, K), device=DEV)
+    rmass = torch.empty(B, device=DEV)
+    out = ssd.ssd_verify(draft, target, torch.from_numpy(bt.x).to(DEV), torch.from_numpy(bt.u).to(DEV), bt.T,
+                         topf_F_max=w["topf"], accept_prob=aprob, residual_mass=rmass)
+    torch.cuda.synchronize()
+    seqs = list(range(0, B, 11)) + [B - 1]
+    ref = O.verify_batch(bt.draft, bt.target, bt.dtype, bt.x, bt.u, bt.T, seqs=seqs)
+    st = compare_verify(bt, out, ref, aprob, rmass)
+    g = out["topf"].cpu().numpy()
+    for b in seqs:
+        for i in range(K):
+            want = O.topf(O.logits_f64(bt.draft[b, i], bt.dtype), w["topf"], int(bt.x[b, i]))
+            assert list(g[b, i]) == list(want), f"top-F seq {b} pos {i}"
+    # every sequence: accepted lengths in range and bonus tokens inside the vocabulary
+    k = out["accepted_len"].cpu().numpy()
+    t = out["bonus_token"].cpu().numpy()
+    assert np.all((k >= 0) & (k <= K)) and np.all((t >= 0) & (t < bt.V))
+    report("b128_k8_v152064_f32_zipf", st)
+
+
+def test_full_ssd_round_b64x32_k4_v128256_f32():
+    w = synth.workload("ssd_round_b64x32_k4_v128256_f32")
+    fan, _ = ssd.ssd_fanout_alloc(w["K"], w["a"], w["r"], w["budget"])
+    assert fan == [int(v) for v in O.fanout(w["K"], w["a"], w["r"], w["budget"])[0]] == [8, 7, 5, 5, 7]
+    bt = synth.make_verify_batch(w["B"], w["K"], w["V"], w["dtype"], 0, T=w["T"], sag_sizes=fan[: w["K"]],
+                                 C=w["C"])
+    branch = synth.make_branch_rows(w["B"], w["budget"], w["K"], w["V"], w["dtype"], 0)
+    print("[case] full ssd round b64x32", flush=True)
+    res = ssd_round_gpu(bt, fan, branch)
+    seqs = list(range(0, w["B"], 9)) + [w["B"] - 1]
+    st = check_round(bt, fan, res, seqs, branch, [(0, 0), (13, 31), (40, 17), (63, 5)],
+                     name="ssd_round b64x32")
+    # host-side choice of the path from the miss count ([SSD] Saguaro 优化三): zero-wait only if
+    # every sequence hit
+    miss = st["miss_count"]
+    path = "zero-wait" if miss == 0 else "fallback"
+    print(f"[ssd round] misses {miss}/{w['B']} -> {path} path", flush=True)
