@@ -109,39 +109,87 @@ struct BF16T {
 };
 
 // ---------------------------------------------------------------------------------------------
-// wave64 reductions (xor butterflies: every lane ends with the bit-identical result)
+// wave64 reductions without LDS: DPP inside each 16-lane row (every lane of the row ends with the
+// bit-identical row result), then the four row results are read into scalar registers and
+// combined in the fixed order (row0 . row1) . (row2 . row3). Every lane returns the same bits.
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = row16_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+// min over the four rows of a value that is already uniform within each row
+__device__ __forceinline__ float rows_min(float v) {
+  return fminf(fminf(readlane_f(v, 0), readlane_f(v, 16)), fminf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
-// lexicographic max of (hi, lo) key pairs
+template <int CTRL>
+__device__ __forceinline__ void key_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);
+  const bool take = oh > hi || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+__device__ __forceinline__ bool key_gt(uint32_t ah, uint32_t al, uint32_t bh, uint32_t bl) {
+  return ah > bh || (ah == bh && al > bl);
+}
+// lexicographic max of (hi, lo) key pairs over the wave
 __device__ __forceinline__ void wave_max_key(uint32_t& hi, uint32_t& lo) {
+  key_step<kDppXor1>(hi, lo);
+  key_step<kDppXor2>(hi, lo);
+  key_step<kDppHalfMirror>(hi, lo);
+  key_step<kDppMirror>(hi, lo);
+  uint32_t bh = __builtin_amdgcn_readlane(hi, 0), bl = __builtin_amdgcn_readlane(lo, 0);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t oh = __shfl_xor(hi, o, 64);
-    const uint32_t ol = __shfl_xor(lo, o, 64);
-    if (oh > hi || (oh == hi && ol > lo)) {
-      hi = oh;
-      lo = ol;
+  for (int r = 16; r < 64; r += 16) {
+    const uint32_t oh = __builtin_amdgcn_readlane(hi, r), ol = __builtin_amdgcn_readlane(lo, r);
+    if (key_gt(oh, ol, bh, bl)) {
+      bh = oh;
+      bl = ol;
     }
   }
+  hi = bh;
+  lo = bl;
+}
+
+// Inclusive scan over the wave: Hillis-Steele inside each row (DPP row shifts 1, 2, 4, 8), then
+// row 0's total is added to row 1 and row 2's to row 3 (row_bcast:15), and row 1's running total
+// to rows 2 and 3 (row_bcast:31). Lanes a shift would read from outside the row add 0.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143, kDppWaveShr1 = 0x138;
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowShr1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowShr2, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowShr4, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowShr8, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppBcast15, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppBcast31, 0xC, 0xF, false));
+  return v;
+}
+// value of the previous lane (0 in lane 0)
+__device__ __forceinline__ float wave_shift_up1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppWaveShr1, 0xF, 0xF, false));
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -188,18 +236,13 @@ __device__ __forceinline__ int block_max_i(int v, int* sh) {
 // the block total as fl(excl[last] + v[last]) so that it equals the last thread's inclusive value.
 __device__ __forceinline__ float block_excl_scan(float v, float* sh, float& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
+  const float inc = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) sh[w] = inc;
   __syncthreads();
   float base = 0.f;
   for (int i = 0; i < w; ++i) base += sh[i];
-  const float excl_lane = __shfl_up(inc, 1, 64);
+  const float excl_lane = wave_shift_up1(inc);
   const float excl = (lane == 0) ? base : base + excl_lane;
   // total: computed by the last thread, broadcast
   __syncthreads();

@@ -7,6 +7,8 @@
 
 namespace ssd {
 
+constexpr int kGzPerSeq = 2 * 16 + 16 * 16;  // 2 K_max token logits + K_max F_max set logits
+
 struct VerifyArgs {
   const void* draft;
   int64_t dstride;  // elements between consecutive sequences
@@ -30,10 +32,13 @@ struct VerifyArgs {
   float* rmass_out;
   // workspace views
   uint32_t* flags;
-  uint32_t* cnt;     // per sequence: [b*64] tile arrivals after phase 1, [b*64+32] after phase 2
+  uint32_t* ctl;     // per sequence, 64 words: the phase-1 arrival counter (zero between calls)
+  uint64_t* dec;     // per sequence, 32 tagged words: the decision record (k, log-normalisers, set)
+  float* gz;         // per sequence, kGzPerSeq floats: logits at the draft and set tokens
   uint64_t* stats;   // [B][2K+1][T] (max c, sum) per tile
   uint64_t* cand;    // [B][K][T][topfFmax] candidate keys per tile
-  float* res;        // [B][T] residual mass per tile
+  uint64_t* res;     // [B][T] residual mass per tile, tagged with the call
+  uint32_t epoch;    // this call's tag (never 0): marks the record and mass words it writes
   int spin_limit;
   int aligned;  // every logit row starts 16-byte aligned
   uint64_t* trace;  // per-workgroup phase timestamps (analysis builds only), or null
