@@ -1,6 +1,9 @@
 """Throughput of the verification hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py ... --copy-calibration      (also runs a plain device copy of known size)
+    python bench.py --traffic-from FETCH.csv WRITE.csv   (no GPU: turns two rocprofv3 --pmc
+                                                          counter files into profiles/traffic_*.json)
 
 A step is one verification round over one batch: every draft and target logit row of the batch
 is streamed once (temperature softmax statistics, fused top-F guesses), the accept decisions and
@@ -25,6 +28,8 @@ sys.path.insert(0, ROOT)
 METRIC = "verified logit rows/sec and achieved HBM GB/s (B=16,K=4,V=128256)"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes exactly this many bytes per launch
+VERIFY_KERNEL = "verify_fused_kernel"
 KERNEL_SOURCES = ["draft_verification_ssd_amd/csrc/ssd_verify.hip",
                   "draft_verification_ssd_amd/csrc/ssd_device.hpp",
                   "draft_verification_ssd_amd/csrc/ssd_plan.hpp"]
@@ -47,6 +52,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed loop, copy COPY_BYTES device-to-device a few times so a "
+                         "counter run sees the copy kernel beside the verification kernel")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     return ap.parse_args()
 
 
@@ -111,8 +120,49 @@ def load_traffic(workload, khash):
     return d.get("bytes_per_launch")
 
 
+def _counter_rows(path):
+    """(kernel name, counter name, value in KiB) per dispatch from a rocprofv3 counter CSV."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_traffic(fetch_csv, write_csv, workload):
+    """HBM bytes per launch of the verification kernel, each counter scaled by what it reads for
+    the calibration copy (COPY_BYTES read and COPY_BYTES written per launch)."""
+    import statistics
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r[1] == name]
+        ver = [v for k, _, v in rows if VERIFY_KERNEL in k]
+        # the copy is the launch whose counter comes closest to COPY_BYTES (torch names it
+        # differently across versions); it must be one of the non-verification kernels
+        other = [v for k, _, v in rows if VERIFY_KERNEL not in k]
+        if not ver or not other:
+            raise SystemExit(f"{path}: no {name} rows for the verification kernel or the copy")
+        copy_kib = min(other, key=lambda v: abs(v * 1024 - COPY_BYTES))
+        scale = COPY_BYTES / (copy_kib * 1024)
+        out[name] = dict(raw_kib_per_launch=statistics.median(ver), copy_raw_kib=copy_kib, scale=scale,
+                         bytes_per_launch=statistics.median(ver) * 1024 * scale, launches=len(ver))
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    d = dict(workload=workload, kernel=VERIFY_KERNEL, kernel_hash=kernel_hash(), bytes_per_launch=round(total),
+             fetch=out["FETCH_SIZE"], write=out["WRITE_SIZE"],
+             note="median over dispatches; each counter scaled by its reading for a plain "
+                  f"{COPY_BYTES >> 20} MiB device copy")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
               f"sequence across GPUs, see DESIGN.md)", file=sys.stderr)
@@ -161,6 +211,13 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     flags = ssd.ssd_read_flags(ws)
     if flags:
