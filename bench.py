@@ -179,6 +179,7 @@ def main():
     esize = 2 if dtype == "bf16" else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
 
     bt = synth.make_verify_batch(B, K, V, dtype, args.seed, T=spec["T"],
                                  noise_sigma=spec.get("noise_sigma", 0.5), zipf_s=spec.get("zipf_s"))
@@ -187,29 +188,34 @@ def main():
     n_rep = max(1, math.ceil(ROTATE_BYTES / logit_bytes))
     ws = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, topf), dev)
     calls = [make_replica(bt, dev, topf, ws) for _ in range(n_rep)]
-    stream = torch.cuda.current_stream(dev)
 
     for i in range(args.warmup):
         calls[i % n_rep]()
     torch.cuda.synchronize()
 
-    # per-step event pairs on the launch stream give the kernels' own duration per launch;
-    # the outer pair gives whole-loop throughput
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # whole-loop throughput: K back-to-back steps bracketed by one event pair
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        e0, e1 = evs[i]
-        e0.record(stream)
         calls[i % n_rep]()
-        e1.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+
+    # per-launch duration of the kernel: an event pair on the launch stream around each step
+    n_ev = min(args.steps, 500)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        e0, e1 = evs[i]
+        e0.record(stream)
+        calls[i % n_rep]()
+        e1.record(stream)
+    torch.cuda.synchronize()
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     if args.copy_calibration:

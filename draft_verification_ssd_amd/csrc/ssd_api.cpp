@@ -1,7 +1,6 @@
 // extern "C" entry points: argument validation (before any HIP call), workspace carving, launch.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -30,15 +29,6 @@ P* at(void* base, size_t off) {
 }
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
-// Tag of one ssd_verify call: the kernel stamps the words it publishes for other workgroups with
-// it, so a stale word left by an earlier call on the same workspace is never taken as current.
-// Process-wide, never 0 (a zero-filled workspace holds tag 0); repeats after 2^32 - 1 calls.
-uint32_t next_call_tag() {
-  static std::atomic<uint32_t> counter{0};
-  uint32_t v = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  while (v == 0) v = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  return v;
-}
 
 }  // namespace
 
@@ -121,11 +111,10 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.flags = at<uint32_t>(workspace, 0);
   a.ctl = at<uint32_t>(workspace, L.off_ctl);
   a.dec = at<uint64_t>(workspace, L.off_dec);
-  a.gz = at<float>(workspace, L.off_gz);
   a.stats = at<uint64_t>(workspace, L.off_stats);
   a.cand = at<uint64_t>(workspace, L.off_cand);
   a.res = at<uint64_t>(workspace, L.off_res);
-  a.epoch = next_call_tag();
+  a.cready = at<uint64_t>(workspace, L.off_cready);
   a.spin_limit = 1 << 20;
   a.aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
               (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;

@@ -187,6 +187,15 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppBcast31, 0xC, 0xF, false));
   return v;
 }
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast31, 0xC, 0xF, false);
+  return v;
+}
 // value of the previous lane (0 in lane 0)
 __device__ __forceinline__ float wave_shift_up1(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppWaveShr1, 0xF, 0xF, false));

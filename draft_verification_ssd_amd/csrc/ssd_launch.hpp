@@ -7,7 +7,6 @@
 
 namespace ssd {
 
-constexpr int kGzPerSeq = 2 * 16 + 16 * 16;  // 2 K_max token logits + K_max F_max set logits
 
 struct VerifyArgs {
   const void* draft;
@@ -32,13 +31,12 @@ struct VerifyArgs {
   float* rmass_out;
   // workspace views
   uint32_t* flags;
-  uint32_t* ctl;     // per sequence, 64 words: the phase-1 arrival counter (zero between calls)
+  uint32_t* ctl;     // per sequence, 64 words: arrival counter (zero between calls), last call tag
   uint64_t* dec;     // per sequence, 32 tagged words: the decision record (k, log-normalisers, set)
-  float* gz;         // per sequence, kGzPerSeq floats: logits at the draft and set tokens
   uint64_t* stats;   // [B][2K+1][T] (max c, sum) per tile
   uint64_t* cand;    // [B][K][T][topfFmax] candidate keys per tile
   uint64_t* res;     // [B][T] residual mass per tile, tagged with the call
-  uint32_t epoch;    // this call's tag (never 0): marks the record and mass words it writes
+  uint64_t* cready;  // [B][T] per tile: its top-F candidates are in (tagged with the call)
   int spin_limit;
   int aligned;  // every logit row starts 16-byte aligned
   uint64_t* trace;  // per-workgroup phase timestamps (analysis builds only), or null

@@ -38,16 +38,17 @@ inline RowPlan plan_rows(int64_t rows, int V) {
   return p;
 }
 
-constexpr int kPlanTile = 2048;  // tokens per verification tile (256 threads x 8)
+constexpr int kPlanTile = 4096;  // tokens per verification tile (256 threads x 16)
 
 struct VerifyLayout {
   int T;  // tiles per row
-  size_t off_ctl, off_dec, off_gz, off_stats, off_cand, off_res, total;
+  size_t off_ctl, off_dec, off_stats, off_cand, off_res, off_cready, total;
 };
 
 // Workspace: [flags | per-sequence control words (256 B) | per-sequence decision records (256 B) |
-// per-sequence token logits (288 floats) | tile stats | top-F candidate keys | tile residual
-// masses (tagged)]. The control words must start at zero; every call leaves them at zero.
+// tile stats | top-F candidate keys | tile residual
+// masses (tagged) | per-tile candidates-ready words (tagged)]. The control words must start at
+// zero; every call leaves them at zero.
 inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
   VerifyLayout L;
   L.T = int(ceil_div(V, kPlanTile));
@@ -56,13 +57,13 @@ inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
   off = align_up(off + size_t(B) * 256);
   L.off_dec = off;
   off = align_up(off + size_t(B) * 256);
-  L.off_gz = off;
-  off = align_up(off + size_t(B) * (2 * 16 + 16 * 16) * 4);
   L.off_stats = off;
   off = align_up(off + size_t(B) * (2 * K + 1) * L.T * 8);
   L.off_cand = off;
   off = align_up(off + size_t(B) * K * L.T * topf_F_max * 8);
   L.off_res = off;
+  off = align_up(off + size_t(B) * L.T * 8);
+  L.off_cready = off;
   off = align_up(off + size_t(B) * L.T * 8);
   L.total = off;
   return L;

@@ -1,24 +1,32 @@
 // Batched lossless draft verification on gfx950: one launch per round of sequences.
 //
-// Work unit: one 256-thread workgroup per (sequence b, tile of 2048 tokens). A tile covers the
+// Work unit: one 256-thread workgroup per (sequence b, tile of kTileTok tokens). A tile covers the
 // same token range of all 2K+1 rows of its sequence (K draft rows, K+1 target rows), so the T
-// tiles of a sequence together stream every logit of it exactly once.
+// tiles of a sequence together stream every logit of it exactly once. Inside a tile, wave w owns
+// tokens [w * 64 kE, (w + 1) * 64 kE); lane l holds kE of them in 16-byte chunks j: chunk j of lane
+// l starts at token j * 64 VEC + l VEC of the wave's range (VEC tokens per 16 bytes), so every
+// load instruction of a wave reads 1 KB of contiguous memory.
 //
-//  phase 1   Each thread loads 8 contiguous tokens of every row (16-byte vector loads, all rows of
-//            a load group in flight together), forms max and sum 2^(z c - max) per row with
-//            c = log2(e)/T, and merges them over 16-lane groups with DPP. The threads that hold a
-//            draft token or a Saguaro-set token publish its logit straight from registers. On
-//            draft rows the tile's top-F candidates are filtered against a wave threshold and
-//            compacted into LDS. Partials go out with write-through (agent-coherent) stores; once
-//            they have completed, one atomic per tile counts the tile in.
-//  decide    The tile that arrives last merges the row statistics in one fixed order, takes the
-//            accept decisions and k, writes k and the accept probabilities, and publishes a small
-//            decision record behind a flag that the other tiles wait for.
+//  phase 1   Each lane loads its chunks of every row of a load group at once, forms max and
+//            sum 2^(z c - max) per row with c = log2(e)/T, and merges them over 16-lane groups with
+//            DPP. Partials go out with write-through (agent-coherent) stores; once they have
+//            completed, one atomic per tile counts the tile in.
+//  top-F     While it waits for the decision, a tile re-reads its draft rows from cache and keeps
+//            the candidates of each wave that pass a threshold every top-F token of the wave
+//            passes (from the same DPP maxima), selects the tile's best F per row and publishes them.
+//  decide    The tile that arrives last merges the row statistics in one fixed order, gathers the
+//            logits at the draft tokens, takes the accept decisions and k, writes k and the accept
+//            probabilities, and publishes a small decision record of words tagged with the call,
+//            which the other tiles poll.
 //  residual  Every tile sums r = max(p_k - q'_k, 0) (or p_K when all drafts pass) over its token
-//            range, re-reading the two rows from cache, keeps r in registers and publishes the sum.
+//            range, re-reading the two rows from cache, keeps r and its prefix sums in registers
+//            and publishes the tagged sum.
 //  bonus     Every tile scans the T sums in the same order (the same bits everywhere); the tile
 //            whose range holds u_K R finds the token in its registers. Tiles 0..K-1 merge the
 //            top-F guesses of draft row = tile while the sums come in.
+//
+// Code size matters here: the hot loops stay compact (only the all-vector load mode is unrolled
+// over rows; tail tiles and unaligned rows take rolled loops) so they fit the instruction cache.
 //
 // The waits are bounded spins (a timeout is flagged, never hung). They need every tile of a
 // sequence resident at once, so one launch covers only as many sequences as the device keeps
@@ -26,27 +34,142 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
+#include "ssd_plan.hpp"
 
 namespace ssd {
 
-constexpr int kTile = kSub;  // 2048 tokens
+constexpr int kE = 16;                   // tokens per lane per row
+constexpr int kTileTok = kThreads * kE;  // tokens per tile
+static_assert(kTileTok == kPlanTile, "host plan and kernel disagree on the tile size");
+constexpr int kMaxVT = (kMaxV + kTileTok - 1) / kTileTok;  // tiles of the longest row
 constexpr int kMaxR2 = 2 * kMaxK + 1;
 constexpr int kGroupsPerBlock = kThreads / 16;
 constexpr int kCandW = 40;  // filtered top-F candidates kept per draft row per wave
 constexpr int kCandSel = (kWaves * kCandW + 63) / 64;  // candidates per lane at selection
 static_assert(kCandW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
 
-// per-sequence control words (64 x uint32): the phase-1 arrival counter
-constexpr int kCtlArrive = 0;
+// Per-sequence control words (64 x uint32): the phase-1 arrival counter, and the tag of the
+// sequence's last call. A call's tag is the last tag + 1 (never 0, the value of a zero-filled
+// workspace), so it advances on every launch, graph replays included, with no host state.
+constexpr int kCtlArrive = 0, kCtlTag = 16;
 // Per-sequence decision record: 64-bit words (call tag << 32 | value), each written once per
 // call, so a reader knows a word is current when its tag matches the call's.
 constexpr int kDecK = 0, kDecLp = 1, kDecLq = 2, kDecWout = 3, kDecWin = 4, kDecNset = 5,
               kDecSet = 6, kDecWords = kDecSet + kMaxF;
-static_assert(kDecWords <= 32 && kDecWords <= 64, "decision record exceeds its 256 bytes");
-static_assert(kGzPerSeq >= 2 * kMaxK + kMaxK * kMaxF, "token-logit slots too small");
+static_assert(kDecWords <= 32, "decision record exceeds its 256 bytes");
+
+// token layout of one lane's kE tokens of a row
+template <class ET>
+struct Lay {
+  static constexpr int VEC = 16 / int(sizeof(typename ET::T));  // tokens per 16-byte chunk
+  static constexpr int NV = kE / VEC;                           // chunks per lane
+  static constexpr int WTOK = 64 * kE;                          // tokens per wave
+  static constexpr int CTOK = 64 * VEC;                         // tokens per chunk across a wave
+  // element q of a lane whose first token is bl
+  __device__ static __forceinline__ int tok(int bl, int q) { return bl + (q / VEC) * CTOK + (q % VEC); }
+  // element of token x in the lane whose first token is bl, or -1
+  __device__ static __forceinline__ int elem(int bl, int x) {
+    const int d = x - bl;
+    if (d < 0) return -1;
+    const int j = d / CTOK, rem = d - j * CTOK;
+    return (j < NV && rem < VEC) ? j * VEC + rem : -1;
+  }
+};
+
+template <class ET>
+struct RowRaw {
+  uint4 w[Lay<ET>::NV];
+};
+
+template <class ET>
+__device__ __forceinline__ void row_load_vec(const typename ET::T* row, int bl, RowRaw<ET>& r) {
+#pragma unroll
+  for (int j = 0; j < Lay<ET>::NV; ++j) r.w[j] = load16(row + bl + j * Lay<ET>::CTOK);
+}
+
+// one 16-byte chunk element by element; positions at or past V read as -inf. Every element is
+// loaded (from a clamped index) and masked afterwards, so no load waits behind a branch.
+template <class ET>
+__device__ __forceinline__ uint4 chunk_scalar(const typename ET::T* row, int tok0, int V) {
+  uint32_t wd[4];
+  if (sizeof(typename ET::T) == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = __float_as_uint(ET::one(row, min(tok0 + i, V - 1)));
+      wd[i] = (tok0 + i < V) ? v : 0xFF800000u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __float_as_uint(ET::one(row, min(tok0 + 2 * i, V - 1))) >> 16;
+      const uint32_t hi = __float_as_uint(ET::one(row, min(tok0 + 2 * i + 1, V - 1))) >> 16;
+      wd[i] = ((tok0 + 2 * i < V) ? lo : 0xFF80u) | (((tok0 + 2 * i + 1 < V) ? hi : 0xFF80u) << 16);
+    }
+  }
+  return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+}
+
+template <class ET>
+__device__ __forceinline__ void row_load_scalar(const typename ET::T* row, int bl, int V, RowRaw<ET>& r) {
+#pragma unroll
+  for (int j = 0; j < Lay<ET>::NV; ++j) r.w[j] = chunk_scalar<ET>(row, bl + j * Lay<ET>::CTOK, V);
+}
+
+template <class ET>
+__device__ __forceinline__ void row_unpack(const RowRaw<ET>& r, float (&z)[kE]) {
+#pragma unroll
+  for (int j = 0; j < Lay<ET>::NV; ++j) ET::unpack(r.w[j], z + j * Lay<ET>::VEC);
+}
+
+// Rows whose length is a whole number of chunks (16-byte aligned rows): a chunk lies wholly
+// inside or wholly past the row. The load reads a clamped, valid chunk; mask_tail then turns the
+// chunks past V into -inf once they are unpacked (so no second copy of the words stays live).
+template <class ET>
+__device__ __forceinline__ void row_load_clamped(const typename ET::T* row, int bl, int V, RowRaw<ET>& r) {
+#pragma unroll
+  for (int j = 0; j < Lay<ET>::NV; ++j)
+    r.w[j] = load16(row + min(bl + j * Lay<ET>::CTOK, V - Lay<ET>::VEC));
+}
+template <class ET>
+__device__ __forceinline__ void mask_tail(float (&z)[kE], int bl, int V) {
+#pragma unroll
+  for (int j = 0; j < Lay<ET>::NV; ++j) {
+    const bool in = bl + j * Lay<ET>::CTOK < V;
+#pragma unroll
+    for (int e = 0; e < Lay<ET>::VEC; ++e) z[j * Lay<ET>::VEC + e] = in ? z[j * Lay<ET>::VEC + e] : -INFINITY;
+  }
+}
+
+// Load modes, chosen per tile: 0 every chunk whole (vector loads), 1 aligned rows with chunks past
+// V (clamped vector loads; mask_tail after unpacking), 2 rows not 16-byte aligned (element
+// loads, masked as they load).
+template <class ET, int MODE>
+__device__ __forceinline__ void row_load_m(const typename ET::T* row, int bl, int V, RowRaw<ET>& r) {
+  if (MODE == 0)
+    row_load_vec<ET>(row, bl, r);
+  else if (MODE == 1)
+    row_load_clamped<ET>(row, bl, V, r);
+  else
+    row_load_scalar<ET>(row, bl, V, r);
+}
+// row load and unpack with a runtime mode (the residual pass)
+template <class ET>
+__device__ __forceinline__ void row_fetch(const typename ET::T* row, int bl, int V, int mode, float (&z)[kE]) {
+  RowRaw<ET> r;
+  if (mode == 2)
+    row_load_scalar<ET>(row, bl, V, r);
+  else if (mode == 1)
+    row_load_clamped<ET>(row, bl, V, r);
+  else
+    row_load_vec<ET>(row, bl, r);
+  row_unpack<ET>(r, z);
+  if (mode == 1) mask_tail<ET>(z, bl, V);
+}
+
 
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
   return uint64_t(__float_as_uint(a)) | (uint64_t(__float_as_uint(b)) << 32);
@@ -68,19 +191,11 @@ __device__ __forceinline__ P ld_agent(const P* p) {
 // wait for this thread's outstanding vector-memory operations (stores included) to complete
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// store the logit of token `tok` to *dst if this thread holds it (one conditional store per
-// element: selecting the element by index would send the thread's tokens through scratch memory)
-__device__ __forceinline__ void store_if_held(float* dst, const float (&z)[kSubElems], int e0, int tok) {
-#pragma unroll
-  for (int e = 0; e < kSubElems; ++e)
-    if (e0 + e == tok) st_agent(dst, z[e]);
-}
-
 #ifdef SSD_TRACE
 // phase timestamps per workgroup (100 MHz clock), for performance analysis builds only
 #define TRACE(i)                                                                      \
   do {                                                                                \
-    if (threadIdx.x == 0 && a.trace) a.trace[blockIdx.x * 16 + (i)] = wall_clock64(); \
+    if (threadIdx.x == 0 && a.trace) a.trace[blockIdx.x * 32 + (i)] = wall_clock64(); \
   } while (0)
 #else
 #define TRACE(i) \
@@ -99,9 +214,9 @@ struct Shared {
   int ncw[kMaxK][kWaves];
   uint64_t cand[kMaxK][kWaves][kCandW];
   uint64_t best[kMaxK][kMaxF];
+  uint64_t spare[kWaves][64];  // where the compaction's failing tokens are written
   int leader;
   // decision (last tile to arrive)
-  float2 part[kThreads];
   float L[kMaxR2];
   float zg[2 * kMaxK];      // logits at the draft tokens: draft rows 0..K-1, then target rows
   float zs[kMaxK * kMaxF];  // draft logits at the set entries
@@ -110,30 +225,92 @@ struct Shared {
   int k, nset;
   float Lp, Lq, w_out, w_in;
   int myset[kMaxF];
-  // bonus
-  float res[kMaxTiles];
+  // residual and bonus
+  float wt[kWaves];
+  float res[kMaxVT];
   int cstar, clamp, fallback, first, lastp;
   float base, target, R;
   uint64_t wtop[kWaves][kMaxF];
-  float shf[8];
-  int shi[8];
-  uint32_t shk[2 * kWaves];
 };
 
-template <class ET, int FM>
-__global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a) {
+// Residual values of a lane's kE tokens of one tile and their prefix sums in token order, relative
+// to the tile start: r = max(p - q w / N, 0) with w = C on the Saguaro set (w_in = C / N,
+// w_out = 1 / N), or r = p when qrow is null. Returns the tile total (every lane, same bits).
+// Token order inside a tile is (wave, chunk, lane, element); the sums follow it: element sums per
+// chunk, a DPP scan over lanes per chunk, chunk bases per wave, wave bases per tile.
+template <class ET>
+__device__ __forceinline__ float tile_residual(const typename ET::T* prow, const typename ET::T* qrow,
+                                               int bl, int V, int mode, float c, float Lp, float Lq,
+                                               float w_out, float w_in, const int* set, int n_set,
+                                               float* wt_sh, float (&rv)[kE], float (&pre)[kE]) {
+  using LY = Lay<ET>;
+  float zp[kE], zq[kE];
+  row_fetch<ET>(prow, bl, V, mode, zp);
+  if (qrow) row_fetch<ET>(qrow, bl, V, mode, zq);
+  uint32_t in_set = 0;  // bit q: element q is a Saguaro-set token
+  for (int f = 0; f < n_set; ++f) {
+    const int q = LY::elem(bl, set[f]);
+    if (q >= 0) in_set |= 1u << q;
+  }
+#pragma unroll
+  for (int q = 0; q < kE; ++q) {
+    const float pv = ex2(fmaf(zp[q], c, -Lp));
+    if (qrow) {
+      const float w = ((in_set >> q) & 1u) ? w_in : w_out;
+      rv[q] = fmaxf(pv - ex2(fmaf(zq[q], c, -Lq)) * w, 0.f);
+    } else {
+      rv[q] = pv;
+    }
+    if (LY::tok(bl, q) >= V) rv[q] = 0.f;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float pin[LY::NV], cb[LY::NV + 1];
+#pragma unroll
+  for (int j = 0; j < LY::NV; ++j) {
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < LY::VEC; ++e) sum += rv[j * LY::VEC + e];
+    pin[j] = wave_incl_scan(sum);
+  }
+  cb[0] = 0.f;
+#pragma unroll
+  for (int j = 0; j < LY::NV; ++j) cb[j + 1] = cb[j] + readlane_f(pin[j], 63);
+  __syncthreads();
+  if (lane == 0) wt_sh[w] = cb[LY::NV];
+  __syncthreads();
+  float wb = 0.f, total = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i == w) wb = total;
+    total += wt_sh[i];
+  }
+#pragma unroll
+  for (int j = 0; j < LY::NV; ++j) {
+    float p = wb + cb[j] + wave_shift_up1(pin[j]);
+#pragma unroll
+    for (int e = 0; e < LY::VEC; ++e) {
+      p += rv[j * LY::VEC + e];
+      pre[j * LY::VEC + e] = p;
+    }
+  }
+  return total;
+}
+
+template <class ET, int FM, int G>
+__global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a) {
   using T = typename ET::T;
-  constexpr int G = (sizeof(T) == 2) ? 9 : 5;  // rows per load group (36-40 VGPRs of payload)
+  using LY = Lay<ET>;
   __shared__ Shared sh;
 
-  const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
+  const int t = threadIdx.x, lane = t & 63, grp = t >> 4, w = t >> 6;
   const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF;
   const float cc = a.c2;
   const bool aligned = a.aligned != 0;
   const int tile = blockIdx.x % nT;
   const int b = a.b0 + int(blockIdx.x) / nT;
-  const int c0 = tile * kTile;
-  const int e0 = c0 + t * kSubElems;
+  const int c0 = tile * kTileTok;
+  const int wb0 = c0 + w * LY::WTOK;     // first token of this wave
+  const int bl = wb0 + lane * LY::VEC;   // first token of this lane
   const T* draft = reinterpret_cast<const T*>(a.draft) + int64_t(b) * a.dstride;
   const T* target = reinterpret_cast<const T*>(a.target) + int64_t(b) * a.tstride;
   auto row_ptr = [&](int r) -> const T* {
@@ -141,81 +318,117 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
   };
   uint32_t* ctl = a.ctl + int64_t(b) * 64;
   uint64_t* dec = a.dec + int64_t(b) * 32;
-  const uint32_t tag = a.epoch;
-  float* gz = a.gz + int64_t(b) * kGzPerSeq;  // [0, 2K) token logits, [2K, 2K + K sF) set logits
+  const uint32_t tag_ld = ld_agent(ctl + kCtlTag);  // read before this tile arrives (see below)
 
-  // Per-sequence inputs, one copy per wave in registers (lane i holds position i, entry q of the
-  // Saguaro sets sits in lane q % 64 of sv_v[q / 64]). They are loaded before the rows and read
-  // with readlane, so no row waits on LDS or on a scalar load.
-  const int x_v = a.x[b * K + min(lane, K - 1)];
-  const float u_v = a.u[b * (K + 1) + min(lane, K)];
-  int sv0 = -1, sv1 = -1, sv2 = -1, sv3 = -1;  // K * sF <= 256 entries: four per lane at most
-  if (sF > 0) {
-    const int nS = K * sF;
-    const int* ss = a.sset + int64_t(b) * nS;
-    sv0 = ss[min(lane, nS - 1)];
-    if (nS > 64) sv1 = ss[min(lane + 64, nS - 1)];
-    if (nS > 128) sv2 = ss[min(lane + 128, nS - 1)];
-    if (nS > 192) sv3 = ss[min(lane + 192, nS - 1)];
-  }
+  // per-sequence inputs, loaded before the rows and staged to LDS after phase 1
+  const int x_v = (t < K) ? a.x[b * K + t] : -1;
+  const float u_v = (t <= K) ? a.u[b * (K + 1) + t] : 0.f;
+  int sv_v = -1;
+  if (t < K * sF) sv_v = a.sset[int64_t(b) * K * sF + t];
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the row loads
-  auto set_entry = [&](int q) -> int {  // q wave-uniform
-    if (q < 64) return __builtin_amdgcn_readlane(sv0, q);
-    if (q < 128) return __builtin_amdgcn_readlane(sv1, q - 64);
-    if (q < 192) return __builtin_amdgcn_readlane(sv2, q - 128);
-    return __builtin_amdgcn_readlane(sv3, q - 192);
-  };
 
-  // ---- phase 1: statistics, token logits and top-F candidates of this tile
+  // load mode of this tile (uniform): whole vector chunks everywhere but in a row's last tile
+  const int mode = !aligned ? 2 : (c0 + kTileTok <= V ? 0 : 1);
+
+  // ---- phase 1: row statistics of this tile
   TRACE(0);
-  const int w = t >> 6;
-  const int Fp = a.topfFmax + 1;  // candidates kept per wave: one more than the guesses
-  const bool vec = aligned && e0 + kSubElems <= V;  // this thread's tokens load as vectors
-  auto row_group = [&](int g0) __attribute__((always_inline)) {
-    RawTile<ET> raw[G];
-    // every slot of the group is loaded (past the last row: the last row again, a cache hit) and
-    // consumed below, so no load is left pending at the loop's back edge
-    if (vec) {
+  // max and sum 2^(z c - max) of one row over the lane's tokens, merged over 16-lane groups
+  auto row_stats = [&](const float (&z)[kE], int r) __attribute__((always_inline)) {
+    float m = z[0];
+#pragma unroll
+    for (int q = 1; q < kE; ++q) m = fmaxf(m, z[q]);
+    float s = 0.f;
+    const float mc = m * cc;
+    if (m > -INFINITY) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int q = 0; q < kE; q += 4) {
+        s0 += ex2(fmaf(z[q], cc, -mc));
+        s1 += ex2(fmaf(z[q + 1], cc, -mc));
+        s2 += ex2(fmaf(z[q + 2], cc, -mc));
+        s3 += ex2(fmaf(z[q + 3], cc, -mc));
+      }
+      s = (s0 + s1) + (s2 + s3);
+    }
+    const float M = row16_max(m);
+    const float Mc = M * cc;
+    const float S = row16_sum((s > 0.f) ? s * ex2(mc - Mc) : 0.f);
+    if ((t & 15) == 0) sh.g16[r][grp] = make_float2(Mc, S);
+  };
+  if (mode != 2) {
+    // aligned rows: every row of a group in flight at once, consumed in load order; chunks past V
+    // (a row's last tile) are loaded from a clamped address and masked
+    for (int g0 = 0; g0 < R2; g0 += G) {
+      RowRaw<ET> raw[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        load_raw_vec<ET>(row_ptr(min(g0 + j, R2 - 1)), e0, raw[j]);
-        __builtin_amdgcn_sched_barrier(0);  // issue in row order: row j is consumed j-th
+        row_load_clamped<ET>(row_ptr(min(g0 + j, R2 - 1)), bl, V, raw[j]);
+        __builtin_amdgcn_sched_barrier(0);  // issue in row order
       }
-    } else {
 #pragma unroll
-      for (int j = 0; j < G; ++j) load_raw_scalar<ET>(row_ptr(min(g0 + j, R2 - 1)), e0, V, raw[j]);
+      for (int j = 0; j < G; ++j) {
+        float z[kE];
+        row_unpack<ET>(raw[j], z);
+        if (mode == 1) mask_tail<ET>(z, bl, V);
+        if (g0 + j < R2) row_stats(z, g0 + j);
+        if (j == 0 && g0 == 0) TRACE(8);
+      }
     }
+  } else {
+    // rows not 16-byte aligned: one row at a time
+#pragma unroll 1
+    for (int r = 0; r < R2; ++r) {
+      float z[kE];
+      row_fetch<ET>(row_ptr(r), bl, V, mode, z);
+      row_stats(z, r);
+    }
+  }
+  TRACE(9);
+  if (t < K) {
+    sh.xe[t] = x_v;
+    sh.F[t] = a.topfF[t];
+  }
+  if (t <= K) sh.u[t] = u_v;
+  if (t < K * sF) sh.sv[t] = sv_v;
+  __syncthreads();
+
+  // ---- publish the tile's partials; once they have completed, count the tile in
+  if (t < R2) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int r = g0 + j;
-      float z[kSubElems];
-      unpack_tile<ET>(raw[j], z);
-      float m = z[0];
+    for (int q = 0; q < kGroupsPerBlock; ++q) M = fmaxf(M, sh.g16[t][q].x);
+    float S = 0.f;
 #pragma unroll
-      for (int e = 1; e < kSubElems; ++e) m = fmaxf(m, z[e]);
-      float s = 0.f;
-      const float mc = m * cc;
-      if (m > -INFINITY) {
-        float s0 = 0.f, s1 = 0.f;
+    for (int q = 0; q < kGroupsPerBlock; ++q) {
+      const float2 v = sh.g16[t][q];
+      if (v.y > 0.f) S += v.y * ex2(v.x - M);
+    }
+    st_agent(a.stats + (int64_t(b) * R2 + t) * nT + tile, pack2(M, S));
+  }
+  wait_vmem();
+  __syncthreads();
+  if (t == 0) sh.leader = (atomicAdd(ctl + kCtlArrive, 1u) == unsigned(nT - 1));
+  // Every tile read the last tag before its arrival (its loads completed before the atomic), so
+  // the leader may advance it now.
+  const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
+  __syncthreads();
+  TRACE(1);
+
+  // ---- top-F guesses, per tile: each draft row's candidates are filtered into per-wave LDS regions,
+  // the tile's best F per row go to the workspace, then a word tagged with the call says they are
+  // in. Run while the tile would otherwise wait (non-leaders before the decision record, the
+  // leader after publishing its residual mass), re-reading the draft rows from cache.
+  const int Fp = a.topfFmax + 1;  // candidates kept per wave: one more than the guesses
+  // Top-F candidates of draft row r of this tile into this wave's LDS region.
+  auto row_filter = [&](const float (&z)[kE], int r) __attribute__((always_inline)) {
+    float m = z[0];
 #pragma unroll
-        for (int e = 0; e < kSubElems; e += 2) {
-          s0 += ex2(fmaf(z[e], cc, -mc));
-          s1 += ex2(fmaf(z[e + 1], cc, -mc));
-        }
-        s = s0 + s1;
-      }
-      // row16_max, keeping the 4- and 8-lane group maxima for the top-F threshold
-      const float m2 = fmaxf(m, dpp_f<kDppXor1>(m));
-      const float m4 = fmaxf(m2, dpp_f<kDppXor2>(m2));
-      const float m8 = fmaxf(m4, dpp_f<kDppHalfMirror>(m4));
-      const float M = fmaxf(m8, dpp_f<kDppMirror>(m8));
-      const float Mc = M * cc;
-      const float sc = (s > 0.f) ? s * ex2(mc - Mc) : 0.f;
-      const float S = row16_sum(sc);
-      if ((t & 15) == 0 && r < R2) sh.g16[r][grp] = make_float2(Mc, S);
-      if (j == 0 && g0 == 0) TRACE(8);
-      if (FM == 0 || r >= K) continue;
-      // Top-F candidates of a draft row into this wave's region. The sampled token is dropped
+    for (int q = 1; q < kE; ++q) m = fmaxf(m, z[q]);
+    const float m2 = fmaxf(m, dpp_f<kDppXor1>(m));
+    const float m4 = fmaxf(m2, dpp_f<kDppXor2>(m2));
+    const float m8 = fmaxf(m4, dpp_f<kDppHalfMirror>(m4));
+    const float M = fmaxf(m8, dpp_f<kDppMirror>(m8));
+    // Top-F candidates of a draft row into this wave's region. The sampled token is dropped
       // only at selection, so the filter keeps the wave's top Fp = F_max + 1 tokens. Threshold:
       // the smallest maximum over the non-empty groups of the coarsest grouping (16, 8, 4 or 1
       // lanes) that has at least Fp non-empty groups; Fp groups then each hold a token at least
@@ -233,8 +446,8 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
         const float h = (m8 > -kInf) ? m8 : kInf;
         g = fminf(h, dpp_f<kDppMirror>(h));
       } else if (lvl == 2) {
-        const float q = (m4 > -kInf) ? m4 : kInf;
-        g = fminf(q, dpp_f<kDppHalfMirror>(q));
+        const float q4 = (m4 > -kInf) ? m4 : kInf;
+        g = fminf(q4, dpp_f<kDppHalfMirror>(q4));
         g = fminf(g, dpp_f<kDppMirror>(g));
       } else {
         g = (m > -kInf) ? m : kInf;
@@ -245,164 +458,141 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
       }
       const bool few = lvl == 3 && __popcll(__ballot(m > -kInf)) < Fp;
       const float thr = few ? -__FLT_MAX__ : rows_min(g);
-      int total = 0;
+      // Compaction without a scalar round trip per token: per-lane counts, a DPP scan for each
+      // lane's first slot, then one LDS write per token, the tokens that fail going to a
+      // per-lane spare slot. An entry holds the raw float bits and ~token.
+      int cnt = 0;
 #pragma unroll
-      for (int e = 0; e < kSubElems; ++e) total += __popcll(__ballot(z[e] >= thr));
+      for (int q = 0; q < kE; ++q) cnt += (z[q] >= thr) ? 1 : 0;
+      const int incl = wave_incl_scan_i(cnt);
+      int total = __builtin_amdgcn_readlane(incl, 63);
       uint64_t* region = sh.cand[r][w];
-      if (total <= kCandW) {  // compaction: slot = running count + lanes below in the mask
-        int base = 0;
+      if (total <= kCandW) {
+        int slot = incl - cnt;
+        uint64_t* spare = &sh.spare[w][lane];
 #pragma unroll
-        for (int e = 0; e < kSubElems; ++e) {
-          const bool pass = z[e] >= thr;
-          const uint64_t mk = __ballot(pass);
-          if (mk) {
-            if (pass) {
-              const int slot = base + int(__builtin_amdgcn_mbcnt_hi(
-                                          uint32_t(mk >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mk), 0u)));
-              region[slot] = cand_key(z[e], e0 + e);
-            }
-            base += __popcll(mk);
-          }
+        for (int q = 0; q < kE; ++q) {
+          const bool pass = z[q] >= thr;
+          uint64_t* dst = pass ? region + slot : spare;
+          *dst = (uint64_t(__float_as_uint(z[q])) << 32) | uint64_t(~uint32_t(LY::tok(bl, q)));
+          slot += pass ? 1 : 0;
         }
       } else {  // too many pass (ties, a short last tile): the wave's exact top Fp from registers
         uint32_t ph = 0xFFFFFFFFu, pl = 0xFFFFFFFFu;
+#pragma unroll 1
         for (int f = 0; f < Fp; ++f) {
-          uint32_t bh = 0, bl = 0;
+          uint32_t bh = 0, blo = 0;
 #pragma unroll
-          for (int e = 0; e < kSubElems; ++e) {
-            const bool ok = z[e] > -INFINITY;
-            const uint32_t kh = ok ? ordered_key(z[e]) : 0u;
-            const uint32_t kl = ok ? ~uint32_t(e0 + e) : 0u;
-            if (key_gt(ph, pl, kh, kl) && key_gt(kh, kl, bh, bl)) {
+          for (int q = 0; q < kE; ++q) {
+            const bool ok = z[q] > -INFINITY;
+            const uint32_t kh = ok ? ordered_key(z[q]) : 0u;
+            const uint32_t kl = ok ? ~uint32_t(LY::tok(bl, q)) : 0u;
+            if (key_gt(ph, pl, kh, kl) && key_gt(kh, kl, bh, blo)) {
               bh = kh;
-              bl = kl;
+              blo = kl;
             }
           }
-          wave_max_key(bh, bl);
-          if (lane == 0) region[f] = (uint64_t(bh) << 32) | bl;
+          wave_max_key(bh, blo);
+          if (lane == 0)  // raw float bits, as the compaction writes them (0 = none)
+            region[f] = bh ? (uint64_t(__float_as_uint(key_to_float(bh))) << 32) | blo : 0ull;
           ph = bh;
-          pl = bl;
+          pl = blo;
         }
         total = Fp;
       }
       if (lane == 0) sh.ncw[r][w] = total;
-    }
-    // Token logits once the group's rows have landed (the per-sequence registers are read only
-    // now, so no row waits on them). A tile stores only tokens in its own range.
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int r = g0 + j;
-      if (r >= 2 * K) continue;
-      const int xr = __builtin_amdgcn_readlane(x_v, r < K ? r : r - K);
-      const bool own_x = (xr >> 11) == tile && xr < V;
-      bool own_set = false;
-      if (r < K)
-        for (int f = 0; f < sF; ++f) {
-          const int sv = set_entry(r * sF + f);
-          own_set |= (sv >> 11) == tile && sv < V;
-        }
-      if (!own_x && !own_set) continue;
-      // unpack again rather than keep the statistics pass's floats alive (an empty asm hides the
-      // packed words' provenance; it emits no instruction)
-#pragma unroll
-      for (int h = 0; h < RawTile<ET>::kWords; ++h)
-        asm volatile("" : "+v"(raw[j].w[h].x), "+v"(raw[j].w[h].y), "+v"(raw[j].w[h].z), "+v"(raw[j].w[h].w));
-      float z[kSubElems];
-      unpack_tile<ET>(raw[j], z);
-      if (own_x && unsigned(xr - e0) < unsigned(kSubElems)) store_if_held(gz + r, z, e0, xr);
-      if (own_set)
-        for (int f = 0; f < sF; ++f) {
-          const int sv = set_entry(r * sF + f);
-          if (unsigned(sv - e0) < unsigned(kSubElems) && sv < V)
-            store_if_held(gz + 2 * K + r * sF + f, z, e0, sv);
-        }
-    }
   };
-  // A single group runs outside any loop, so the per-sequence loads above stay visibly older
-  // than the row loads and reading them waits only for them.
-  if (R2 <= G) {
-    row_group(0);
-  } else {
-    for (int g0 = 0; g0 < R2; g0 += G) row_group(g0);
-  }
-  TRACE(9);
-  if (t < K) {
-    sh.xe[t] = x_v;
-    sh.F[t] = a.topfF[t];
-  }
-  if (t <= K) sh.u[t] = u_v;
-  if (t < 64) {
-    if (t < K * sF) sh.sv[t] = sv0;
-    if (t + 64 < K * sF) sh.sv[t + 64] = sv1;
-    if (t + 128 < K * sF) sh.sv[t + 128] = sv2;
-    if (t + 192 < K * sF) sh.sv[t + 192] = sv3;
-  }
-  __syncthreads();
-  if (FM > 0) {  // wave w selects the F best candidates (value desc, index asc) of rows w, w+4, ...
-    for (int r = w; r < K; r += kWaves) {
-      const int F = sh.F[r];
-      const int xs = sh.xe[r];
-      uint64_t key[kCandSel];  // candidate q = lane + 64 i is entry q % kCandW of wave q / kCandW
+  auto topf_tile = [&]() __attribute__((always_inline)) {
+    if (mode != 2) {
+      // four draft rows in flight at once, then filtered one after another
+      constexpr int kQ = 4;
+#pragma unroll 1
+      for (int r0 = 0; r0 < K; r0 += kQ) {
+        RowRaw<ET> raw[kQ];
 #pragma unroll
-      for (int i = 0; i < kCandSel; ++i) {
-        const int q = lane + 64 * i, ww = q / kCandW, sl = q - ww * kCandW;
-        key[i] = (ww < kWaves && sl < sh.ncw[r][ww]) ? sh.cand[r][ww][sl] : 0ull;
-        if (uint32_t(key[i]) == ~uint32_t(xs)) key[i] = 0;  // the sampled token is never a guess
+        for (int j = 0; j < kQ; ++j) {
+          row_load_clamped<ET>(row_ptr(min(r0 + j, K - 1)), bl, V, raw[j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) {
+          if (r0 + j >= K) continue;
+          float z[kE];
+          row_unpack<ET>(raw[j], z);
+          if (mode == 1) mask_tail<ET>(z, bl, V);
+          if (r0 + j == 0) TRACE(16);
+          row_filter(z, r0 + j);
+          if (r0 + j == 0) TRACE(17);
+        }
       }
-      for (int f = 0; f < F; ++f) {
-        uint64_t mine = key[0];
-#pragma unroll
-        for (int i = 1; i < kCandSel; ++i) mine = (key[i] > mine) ? key[i] : mine;
-        uint32_t hi = uint32_t(mine >> 32), lo = uint32_t(mine);
-        wave_max_key(hi, lo);
-        const uint64_t win = (uint64_t(hi) << 32) | lo;
-        if (lane == 0) sh.best[r][f] = win;
-#pragma unroll
-        for (int i = 0; i < kCandSel; ++i)
-          if (key[i] == win) key[i] = 0;  // keys are unique: only the winner is cleared
+    } else {
+#pragma unroll 1
+      for (int r = 0; r < K; ++r) {
+        float z[kE];
+        row_fetch<ET>(row_ptr(r), bl, V, mode, z);
+        row_filter(z, r);
       }
     }
     __syncthreads();
-  }
-  TRACE(10);
-
-  // ---- publish the tile's partials; once they have completed, count the tile in
-  if (t < R2) {
-    float M = -INFINITY;
+    if (FM > 0) {  // wave w selects the F best candidates (value desc, index asc) of rows w, w+4, ...
+      for (int r = w; r < K; r += kWaves) {
+        const int F = sh.F[r];
+        const int xs = sh.xe[r];
+        uint64_t key[kCandSel];  // candidate q = lane + 64 i is entry q % kCandW of wave q / kCandW
 #pragma unroll
-    for (int q = 0; q < kGroupsPerBlock; ++q) M = fmaxf(M, sh.g16[t][q].x);
-    float S = 0.f;
+        for (int i = 0; i < kCandSel; ++i) {
+          const int q = lane + 64 * i, ww = q / kCandW, sl = q - ww * kCandW;
+          const uint64_t e = (ww < kWaves && sl < sh.ncw[r][ww]) ? sh.cand[r][ww][sl] : 0ull;
+          key[i] = uint32_t(e) ? (uint64_t(ordered_key(__uint_as_float(uint32_t(e >> 32)))) << 32) |
+                                     uint32_t(e)
+                               : 0ull;
+          if (uint32_t(key[i]) == ~uint32_t(xs)) key[i] = 0;  // the sampled token is never a guess
+        }
+        for (int f = 0; f < F; ++f) {
+          uint64_t mine = key[0];
 #pragma unroll
-    for (int q = 0; q < kGroupsPerBlock; ++q) {
-      const float2 v = sh.g16[t][q];
-      if (v.y > 0.f) S += v.y * ex2(v.x - M);
+          for (int i = 1; i < kCandSel; ++i) mine = (key[i] > mine) ? key[i] : mine;
+          uint32_t hi = uint32_t(mine >> 32), lo = uint32_t(mine);
+          wave_max_key(hi, lo);
+          const uint64_t win = (uint64_t(hi) << 32) | lo;
+          if (lane == 0) sh.best[r][f] = win;
+#pragma unroll
+          for (int i = 0; i < kCandSel; ++i)
+            if (key[i] == win) key[i] = 0;  // keys are unique: only the winner is cleared
+        }
+      }
+      __syncthreads();
     }
-    st_agent(a.stats + (int64_t(b) * R2 + t) * nT + tile, pack2(M, S));
-  }
-  if (FM > 0 && t < K * a.topfFmax) {
-    const int r = t / a.topfFmax, f = t - r * a.topfFmax;
-    if (f < sh.F[r])
-      st_agent(a.cand + ((int64_t(b) * K + r) * nT + tile) * a.topfFmax + f, sh.best[r][f]);
-  }
-  wait_vmem();
-  __syncthreads();
-  if (t == 0) sh.leader = (atomicAdd(ctl + kCtlArrive, 1u) == unsigned(nT - 1));
-  __syncthreads();
-  TRACE(1);
+    TRACE(19);
+    if (t < K * a.topfFmax) {
+      const int r = t / a.topfFmax, f = t - r * a.topfFmax;
+      if (f < sh.F[r])
+        st_agent(a.cand + ((int64_t(b) * K + r) * nT + tile) * a.topfFmax + f, sh.best[r][f]);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (t == 0) st_agent(a.cready + int64_t(b) * nT + tile, tagged(tag, 1u));
+  };
+  if (FM > 0 && !sh.leader) topf_tile();
+  TRACE(10);
 
   // ---- decide: the last tile to arrive merges the statistics and publishes the decision
   if (sh.leader) {
-    if (t == 0) st_agent(ctl + kCtlArrive, 0u);  // every tile has arrived: ready for the next call
-    // token logits first, so their loads overlap the statistics loads
+    if (t == 0) {  // every tile has arrived: ready for the next call
+      st_agent(ctl + kCtlArrive, 0u);
+      st_agent(ctl + kCtlTag, tag);
+    }
+    // logits at the draft tokens (draft and target rows 0..K-1) and at the Saguaro-set tokens,
+    // gathered from the rows; issued first, so they overlap the statistics loads
     float zg_v = 0.f, zs_v = 0.f;
     int set_v = -1;
     if (t < 2 * K) {
       const int xr = sh.xe[t < K ? t : t - K];
-      if (unsigned(xr) < unsigned(V)) zg_v = ld_agent(gz + t);
+      if (unsigned(xr) < unsigned(V)) zg_v = ET::one(row_ptr(t), xr);
     }
     if (t < K * sF) {
       set_v = (unsigned(sh.sv[t]) < unsigned(V)) ? sh.sv[t] : -1;
-      if (set_v >= 0) zs_v = ld_agent(gz + 2 * K + t);
+      if (set_v >= 0) zs_v = ET::one(row_ptr(t / sF), set_v);
     }
     // 16-lane group g merges rows g, g + 16, g + 32: lane l takes tiles l, l + 16, ..., then the
     // group combines its lanes with DPP (a fixed order, the same bits on every run)
@@ -471,14 +661,14 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
         accept = false;
         ai = 0.f;
       } else {
-        const float w = xin ? C : 1.f;
+        const float wx = xin ? C : 1.f;
         const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
         const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
-        if (w == 0.f || dq == -INFINITY) {             // q'(x) = 0: accept iff p(x) > 0
+        if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
           accept = dp > -INFINITY;
           ai = accept ? 1.f : 0.f;
         } else {
-          const float ratio = ex2(dp - dq) * (Nn / w);  // p(x) / q'(x)
+          const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
           accept = sh.u[i] < ratio;
           ai = fminf(1.f, ratio);
         }
@@ -548,16 +738,33 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
   const float Lp = sh.Lp, Lq = sh.Lq, w_out = sh.w_out, w_in = sh.w_in;
   const int nset = resid ? min(max(sh.nset, 0), kMaxF) : 0;
 
-  // ---- residual mass of this tile (the values stay in registers), published
-  float rv[kSubElems], pre[kSubElems];
-  sub_values<ET>(prow, qrow, c0, V, aligned, cc, Lp, Lq, w_out, w_in, sh.myset, nset, rv);
-  const float total = sub_scan(rv, pre, sh.shf);
+  // ---- residual mass of this tile (values and prefix sums stay in registers), published
+  float rv[kE], pre[kE];
+  const float total = tile_residual<ET>(prow, qrow, bl, V, mode, cc, Lp, Lq, w_out, w_in, sh.myset,
+                                        nset, sh.wt, rv, pre);
   if (t == 0) st_agent(a.res + int64_t(b) * nT + tile, tagged(tag, __float_as_uint(total)));
   TRACE(4);
+  if (FM > 0 && sh.leader) topf_tile();
 
   // ---- top-F guesses of draft rows tile, tile + T, ... while the other tiles finish: each
   // wave takes its own top F of the tiles' candidates, then wave 0 merges the four lists. Keys
   // are unique (a token lives in one tile), so round f picks the largest key below round f-1's.
+  if (FM > 0 && tile < K) {  // every tile's candidates must be in
+    const int per = (nT + kThreads - 1) / kThreads;
+    const int q0 = min(t * per, nT), q1 = min(nT, q0 + per);
+    const uint64_t* cr = a.cready + int64_t(b) * nT;
+    for (int spins = 0;; ++spins) {
+      bool ok = true;
+      for (int q = q0; q < q1; ++q) ok = ok && uint32_t(ld_agent(cr + q) >> 32) == tag;
+      if (__all(ok)) break;
+      if (spins > a.spin_limit) {
+        if (lane == 0) atomicOr(a.flags, kFlagTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __syncthreads();
+  }
   for (int r = tile; FM > 0 && r < K; r += nT) {
     const int F = sh.F[r];
     int32_t* out = a.topf_out + (int64_t(b) * K + r) * a.topfFmax;
@@ -668,10 +875,11 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
   if (!sh.fallback && sh.cstar == tile) {
     int first = INT_MAX, lastp = -1;
 #pragma unroll
-    for (int e = 0; e < kSubElems; ++e)
-      if (rv[e] > 0.f) {
-        lastp = e0 + e;
-        if (first == INT_MAX && !sh.clamp && sh.base + pre[e] > sh.target) first = e0 + e;
+    for (int q = 0; q < kE; ++q)
+      if (rv[q] > 0.f) {
+        const int tk = LY::tok(bl, q);
+        lastp = max(lastp, tk);
+        if (!sh.clamp && sh.base + pre[q] > sh.target) first = min(first, tk);
       }
     first = wave_min_i(first);
     lastp = wave_max_i(lastp);
@@ -690,20 +898,33 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
     float run = 0.f;
     int found = -1, lastp = -1;
     for (int q = 0; q < nT && found < 0; ++q) {
-      sub_values<ET>(prow, nullptr, q * kTile, V, aligned, cc, Lp, 0.f, 1.f, 1.f, sh.myset, 0, rv);
-      const float tot = sub_scan(rv, pre, sh.shf);
-      const int f0 = q * kTile + t * kSubElems;
+      const int blq = q * kTileTok + w * LY::WTOK + lane * LY::VEC;
+      const int mq = !aligned ? 2 : ((q + 1) * kTileTok <= V ? 0 : 1);
+      const float tot = tile_residual<ET>(prow, nullptr, blq, V, mq, cc, Lp, 0.f, 1.f, 1.f, sh.myset, 0,
+                                          sh.wt, rv, pre);
       int first = INT_MAX, lp = -1;
 #pragma unroll
-      for (int e = 0; e < kSubElems; ++e)
+      for (int e = 0; e < kE; ++e)
         if (rv[e] > 0.f) {
-          lp = f0 + e;
-          if (first == INT_MAX && run + pre[e] > target_v) first = f0 + e;
+          const int tk = LY::tok(blq, e);
+          lp = max(lp, tk);
+          if (run + pre[e] > target_v) first = min(first, tk);
         }
-      first = block_min_i(first, sh.shi);
-      lp = block_max_i(lp, sh.shi);
-      if (lp >= 0) lastp = lp;
-      if (first != INT_MAX) found = first;
+      first = wave_min_i(first);
+      lp = wave_max_i(lp);
+      __syncthreads();
+      if (t == 0) {
+        sh.first = INT_MAX;
+        sh.lastp = -1;
+      }
+      __syncthreads();
+      if (lane == 0) {
+        if (first != INT_MAX) atomicMin(&sh.first, first);
+        if (lp >= 0) atomicMax(&sh.lastp, lp);
+      }
+      __syncthreads();
+      if (sh.lastp >= 0) lastp = sh.lastp;
+      if (sh.first != INT_MAX) found = sh.first;
       run += tot;
     }
     if (t == 0) {
@@ -712,14 +933,13 @@ __global__ __launch_bounds__(kThreads, 4) void verify_fused_kernel(VerifyArgs a)
     }
   }
   TRACE(6);
-
   TRACE(7);
 }
 
 // ---------------------------------------------------------------------------------------------
 // launch: grids of whole sequences whose tiles all fit the device at once
 // ---------------------------------------------------------------------------------------------
-template <class ET, int FM>
+template <class ET, int FM, int G>
 static int capacity_blocks() {
   static std::mutex mu;
   static int cache[64] = {0};
@@ -729,7 +949,7 @@ static int capacity_blocks() {
   if (cache[dev] == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(verify_fused_kernel<ET, FM>), kThreads, 0) != hipSuccess)
+            &per_cu, reinterpret_cast<const void*>(verify_fused_kernel<ET, FM, G>), kThreads, 0) != hipSuccess)
       return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     cache[dev] = per_cu * cus;
@@ -737,28 +957,36 @@ static int capacity_blocks() {
   return cache[dev];
 }
 
-template <class ET, int FM>
+template <class ET, int FM, int G>
 static hipError_t launch_fused(VerifyArgs a, hipStream_t st) {
-  const int cap = capacity_blocks<ET, FM>();
+  const int cap = capacity_blocks<ET, FM, G>();
   if (cap < a.T) return hipErrorInvalidConfiguration;
   const int per_round = cap / a.T;  // whole sequences whose tiles are all resident at once
   const int B = a.B;
   for (int b0 = 0; b0 < B; b0 += per_round) {
     const int nb = (B - b0 < per_round) ? (B - b0) : per_round;
     a.b0 = b0;
-    hipLaunchKernelGGL((verify_fused_kernel<ET, FM>), dim3(unsigned(nb * a.T)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_fused_kernel<ET, FM, G>), dim3(unsigned(nb * a.T)), dim3(kThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+// Rows per load group: bf16 9 (K <= 4 in one group, 8 VGPRs of payload per row and lane), fp32 5
+// (16 VGPRs per row). Larger K runs several groups; a smaller K loads the last row again for the
+// unused slots (cache hits) and skips their arithmetic.
+template <class ET, int FM>
+static hipError_t launch_g(const VerifyArgs& a, hipStream_t st) {
+  return launch_fused<ET, FM, (sizeof(typename ET::T) == 2 ? 9 : 5)>(a, st);
+}
+
 template <class ET>
 static hipError_t launch_verify_e(const VerifyArgs& a, hipStream_t st) {
-  if (a.topfFmax == 0) return launch_fused<ET, 0>(a, st);
-  if (a.topfFmax <= 4) return launch_fused<ET, 4>(a, st);
-  if (a.topfFmax <= 8) return launch_fused<ET, 8>(a, st);
-  return launch_fused<ET, 16>(a, st);
+  if (a.topfFmax == 0) return launch_g<ET, 0>(a, st);
+  if (a.topfFmax <= 4) return launch_g<ET, 4>(a, st);
+  if (a.topfFmax <= 8) return launch_g<ET, 8>(a, st);
+  return launch_g<ET, 16>(a, st);
 }
 
 hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t st) {
