@@ -114,7 +114,6 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.stats = at<uint64_t>(workspace, L.off_stats);
   a.cand = at<uint64_t>(workspace, L.off_cand);
   a.res = at<uint64_t>(workspace, L.off_res);
-  a.cready = at<uint64_t>(workspace, L.off_cready);
   a.spin_limit = 1 << 20;
   a.aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
               (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;

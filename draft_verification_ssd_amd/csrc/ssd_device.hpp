@@ -144,33 +144,60 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
-template <int CTRL>
-__device__ __forceinline__ void key_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);
-  const bool take = oh > hi || (oh == hi && ol > lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
-}
 __device__ __forceinline__ bool key_gt(uint32_t ah, uint32_t al, uint32_t bh, uint32_t bl) {
   return ah > bh || (ah == bh && al > bl);
 }
+// 64-bit DPP move: both halves through the same lane pattern; lanes the row mask leaves out keep v
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = int(uint32_t(v)), hi = int(uint32_t(v >> 32));
+  const uint32_t l = uint32_t(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false));
+  const uint32_t h = uint32_t(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false));
+  return (uint64_t(h) << 32) | l;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// unsigned 64-bit maximum over the wave, all in vector registers: DPP inside 16-lane rows, then
+// row_bcast:15 and row_bcast:31 carry rows 0..2 into row 3, whose last lane holds the result
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<kDppXor1>(v));
+  v = max_u64(v, dpp_u64<kDppXor2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppMirror>(v));
+  v = max_u64(v, dpp_u64<0x142, 0xA>(v));  // row_bcast:15 into rows 1 and 3
+  v = max_u64(v, dpp_u64<0x143, 0xC>(v));  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
+  return (uint64_t(hi) << 32) | lo;
+}
 // lexicographic max of (hi, lo) key pairs over the wave
 __device__ __forceinline__ void wave_max_key(uint32_t& hi, uint32_t& lo) {
-  key_step<kDppXor1>(hi, lo);
-  key_step<kDppXor2>(hi, lo);
-  key_step<kDppHalfMirror>(hi, lo);
-  key_step<kDppMirror>(hi, lo);
-  uint32_t bh = __builtin_amdgcn_readlane(hi, 0), bl = __builtin_amdgcn_readlane(lo, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) {
-    const uint32_t oh = __builtin_amdgcn_readlane(hi, r), ol = __builtin_amdgcn_readlane(lo, r);
-    if (key_gt(oh, ol, bh, bl)) {
-      bh = oh;
-      bl = ol;
-    }
-  }
-  hi = bh;
-  lo = bl;
+  const uint64_t m = wave_max_u64((uint64_t(hi) << 32) | lo);
+  hi = uint32_t(m >> 32);
+  lo = uint32_t(m);
+}
+
+// Unsigned maxima of quads and minima of 16-lane rows (DPP; every lane of the group ends with
+// the group result), and the number of values in a lane's 16-lane row strictly larger than its
+// own (each of the 15 row rotations compared once).
+__device__ __forceinline__ uint32_t quad_max_u(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  return max(v, dpp_u<kDppXor2>(v));
+}
+__device__ __forceinline__ uint32_t row16_min_u(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  return min(v, dpp_u<kDppMirror>(v));
+}
+template <int D>
+__device__ __forceinline__ int larger_at_rotation(uint32_t v) {  // DPP row_ror:D
+  return dpp_u<0x120 + D>(v) > v ? 1 : 0;
+}
+__device__ __forceinline__ int row16_count_larger(uint32_t v) {
+  return ((larger_at_rotation<1>(v) + larger_at_rotation<2>(v)) + (larger_at_rotation<3>(v) + larger_at_rotation<4>(v))) +
+         ((larger_at_rotation<5>(v) + larger_at_rotation<6>(v)) + (larger_at_rotation<7>(v) + larger_at_rotation<8>(v))) +
+         ((larger_at_rotation<9>(v) + larger_at_rotation<10>(v)) + (larger_at_rotation<11>(v) + larger_at_rotation<12>(v))) +
+         ((larger_at_rotation<13>(v) + larger_at_rotation<14>(v)) + larger_at_rotation<15>(v));
 }
 
 // Inclusive scan over the wave: Hillis-Steele inside each row (DPP row shifts 1, 2, 4, 8), then

@@ -15,7 +15,7 @@ struct VerifyArgs {
   int64_t tstride;
   int B, K, V;
   int b0;    // first sequence of this launch
-  int T;     // 2048-token tiles per row
+  int T;     // 4096-token tiles per row
   float c2;  // log2(e) / T
   const int32_t* x;
   const float* u;
@@ -31,12 +31,11 @@ struct VerifyArgs {
   float* rmass_out;
   // workspace views
   uint32_t* flags;
-  uint32_t* ctl;     // per sequence, 64 words: arrival counter (zero between calls), last call tag
+  uint32_t* ctl;     // per sequence, 64 words: the last call's tag
   uint64_t* dec;     // per sequence, 32 tagged words: the decision record (k, log-normalisers, set)
-  uint64_t* stats;   // [B][2K+1][T] (max c, sum) per tile
-  uint64_t* cand;    // [B][K][T][topfFmax] candidate keys per tile
+  uint64_t* stats;   // [B][2K+1][T][2] tagged max c and sum per tile
+  uint64_t* cand;    // [B][K][T][topfFmax][2] candidate keys per tile, two tagged halves each
   uint64_t* res;     // [B][T] residual mass per tile, tagged with the call
-  uint64_t* cready;  // [B][T] per tile: its top-F candidates are in (tagged with the call)
   int spin_limit;
   int aligned;  // every logit row starts 16-byte aligned
   uint64_t* trace;  // per-workgroup phase timestamps (analysis builds only), or null

@@ -42,13 +42,13 @@ constexpr int kPlanTile = 4096;  // tokens per verification tile (256 threads x 
 
 struct VerifyLayout {
   int T;  // tiles per row
-  size_t off_ctl, off_dec, off_stats, off_cand, off_res, off_cready, total;
+  size_t off_ctl, off_dec, off_stats, off_cand, off_res, total;
 };
 
 // Workspace: [flags | per-sequence control words (256 B) | per-sequence decision records (256 B) |
-// tile stats | top-F candidate keys | tile residual
-// masses (tagged) | per-tile candidates-ready words (tagged)]. The control words must start at
-// zero; every call leaves them at zero.
+// tile statistics (two tagged words per row and tile) | top-F candidate keys (two tagged words
+// each) | tile residual masses (tagged)]. A zero-filled workspace is a valid start; every call
+// leaves it valid for the next.
 inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
   VerifyLayout L;
   L.T = int(ceil_div(V, kPlanTile));
@@ -58,12 +58,10 @@ inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
   L.off_dec = off;
   off = align_up(off + size_t(B) * 256);
   L.off_stats = off;
-  off = align_up(off + size_t(B) * (2 * K + 1) * L.T * 8);
+  off = align_up(off + size_t(B) * (2 * K + 1) * L.T * 16);
   L.off_cand = off;
-  off = align_up(off + size_t(B) * K * L.T * topf_F_max * 8);
+  off = align_up(off + size_t(B) * K * L.T * topf_F_max * 16);
   L.off_res = off;
-  off = align_up(off + size_t(B) * L.T * 8);
-  L.off_cready = off;
   off = align_up(off + size_t(B) * L.T * 8);
   L.total = off;
   return L;

@@ -48,14 +48,25 @@ static_assert(kTileTok == kPlanTile, "host plan and kernel disagree on the tile 
 constexpr int kMaxVT = (kMaxV + kTileTok - 1) / kTileTok;  // tiles of the longest row
 constexpr int kMaxR2 = 2 * kMaxK + 1;
 constexpr int kGroupsPerBlock = kThreads / 16;
-constexpr int kCandW = 40;  // filtered top-F candidates kept per draft row per wave
-constexpr int kCandSel = (kWaves * kCandW + 63) / 64;  // candidates per lane at selection
-static_assert(kCandW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
+// Per draft row and wave, the top-F candidates live in an LDS region of kRegW 64-bit words:
+// either the raw chunks of the wave's hot lanes (at most kHot of them, see hot_dump), or a list of
+// (float bits << 32 | ~token) entries from the compaction filter.
+constexpr int kRegW = 48;
+constexpr int kSel = 8;  // dumped elements per lane at selection: up to 32 slots of 16
+static_assert(kRegW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
+static_assert(kRegW <= 64, "a key-list region gives at most one entry per lane");
+template <class ET>
+constexpr int hot_slots() {
+  return (kRegW * 8 / (kE * int(sizeof(typename ET::T)))) < 8 ? (kRegW * 8 / (kE * int(sizeof(typename ET::T))))
+                                                               : 8;
+}
+static_assert(kWaves * 8 * kE <= 64 * kSel, "selection registers must cover the hot-lane dumps");
 
-// Per-sequence control words (64 x uint32): the phase-1 arrival counter, and the tag of the
-// sequence's last call. A call's tag is the last tag + 1 (never 0, the value of a zero-filled
-// workspace), so it advances on every launch, graph replays included, with no host state.
-constexpr int kCtlArrive = 0, kCtlTag = 16;
+// Per-sequence control words (64 x uint32): word kCtlTag holds the tag of the sequence's last
+// call. A call's tag is the last tag + 1 (never 0, the value of a zero-filled workspace), so it
+// advances on every launch, graph replays included, with no host state.
+constexpr int kCtlTag = 16;
+
 // Per-sequence decision record: 64-bit words (call tag << 32 | value), each written once per
 // call, so a reader knows a word is current when its tag matches the call's.
 constexpr int kDecK = 0, kDecLp = 1, kDecLq = 2, kDecWout = 3, kDecWin = 4, kDecNset = 5,
@@ -197,7 +208,14 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
   do {                                                                                \
     if (threadIdx.x == 0 && a.trace) a.trace[blockIdx.x * 32 + (i)] = wall_clock64(); \
   } while (0)
+#define TRACEV(i, v)                                                                  \
+  do {                                                                                \
+    if (threadIdx.x == 0 && a.trace) a.trace[blockIdx.x * 32 + (i)] = (v);            \
+  } while (0)
 #else
+#define TRACEV(i, v) \
+  do {               \
+  } while (0)
 #define TRACE(i) \
   do {           \
   } while (0)
@@ -211,11 +229,15 @@ struct Shared {
   int sv[kMaxK * kMaxF];  // Saguaro-set entries
   // phase 1
   float2 g16[kMaxR2][kGroupsPerBlock];  // (max c, sum) per 16-lane group
-  int ncw[kMaxK][kWaves];
-  uint64_t cand[kMaxK][kWaves][kCandW];
+  // top-F candidates per draft row and wave: nseg < 0 means -nseg hot lanes dumped their raw
+  // chunks (lane ids in hl), nseg >= 0 that many key entries
+  uint64_t reg[kMaxK][kWaves][kRegW];
+  int nseg[kMaxK][kWaves];
+  int hl[kMaxK][kWaves][8];
+  uint32_t thr[kMaxK][kWaves];  // the dump's threshold key: smaller tokens are no candidates
+  uint32_t fb[kWaves];  // draft rows the wave filters again after phase 1 (bit r)
   uint64_t best[kMaxK][kMaxF];
   uint64_t spare[kWaves][64];  // where the compaction's failing tokens are written
-  int leader;
   // decision (last tile to arrive)
   float L[kMaxR2];
   float zg[2 * kMaxK];      // logits at the draft tokens: draft rows 0..K-1, then target rows
@@ -318,7 +340,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
   };
   uint32_t* ctl = a.ctl + int64_t(b) * 64;
   uint64_t* dec = a.dec + int64_t(b) * 32;
-  const uint32_t tag_ld = ld_agent(ctl + kCtlTag);  // read before this tile arrives (see below)
+  // This call's tag is one past the sequence's last. Every word a tile publishes carries it, so
+  // the load below has returned before the tile publishes anything; the deciding tile stores the
+  // new tag once it has seen every tile's statistics.
+  const uint32_t tag_ld = ld_agent(ctl + kCtlTag);
 
   // per-sequence inputs, loaded before the rows and staged to LDS after phase 1
   const int x_v = (t < K) ? a.x[b * K + t] : -1;
@@ -329,11 +354,15 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
 
   // load mode of this tile (uniform): whole vector chunks everywhere but in a row's last tile
   const int mode = !aligned ? 2 : (c0 + kTileTok <= V ? 0 : 1);
+  const int Fp = a.topfFmax + 1;  // candidates kept per wave: one more than the guesses
+  constexpr int kHot = hot_slots<ET>();
+  if (FM > 0 && lane == 0) sh.fb[w] = (mode == 2) ? (1u << K) - 1u : 0u;
 
-  // ---- phase 1: row statistics of this tile
+  // ---- phase 1: row statistics of this tile, and the top-F candidates of its draft rows
   TRACE(0);
-  // max and sum 2^(z c - max) of one row over the lane's tokens, merged over 16-lane groups
-  auto row_stats = [&](const float (&z)[kE], int r) __attribute__((always_inline)) {
+  // max and sum 2^(z c - max) of one row over the lane's tokens, merged over 16-lane groups;
+  // returns the lane's maximum
+  auto row_stats = [&](const float (&z)[kE], int r) __attribute__((always_inline)) -> float {
     float m = z[0];
 #pragma unroll
     for (int q = 1; q < kE; ++q) m = fmaxf(m, z[q]);
@@ -354,12 +383,83 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     const float Mc = M * cc;
     const float S = row16_sum((s > 0.f) ? s * ex2(mc - Mc) : 0.f);
     if ((t & 15) == 0) sh.g16[r][grp] = make_float2(Mc, S);
+    return m;
+  };
+  // The Fp-th largest lane maximum of the wave, tied lanes counted: take the largest remaining
+  // maximum and every lane that holds it until Fp lanes are taken. n = lanes taken; n < Fp when
+  // fewer lanes hold a finite token. Wave-uniform.
+  auto lane_thr = [&](float m, int& n) __attribute__((always_inline)) -> float {
+    float mm = m, thr = -INFINITY;
+    int taken = 0;
+#pragma unroll 1
+    for (int f = 0; f < Fp; ++f) {
+      const float cur = wave_max(mm);
+      if (!(cur > -INFINITY)) break;
+      thr = cur;
+      taken += __popcll(__ballot(mm == cur));
+      if (taken >= Fp) break;
+      mm = (mm == cur) ? -INFINITY : mm;
+    }
+    n = taken;
+    return thr;
+  };
+  // Draft rows during phase 1, up to four at once (rows g0 + jb + i, i < 4, of the load group).
+  // The threshold of a row is the Fp-th largest of its 16 quad maxima (quad = 4 lanes): lanes
+  // 16 i + q gather quad q's maximum of row i, count the quads of their row with a larger one
+  // (15 DPP row rotations), and the smallest maximum with fewer than Fp larger ones is it. At
+  // least Fp quads, so at least Fp lanes, reach it, so the lanes that reach it ("hot") hold every
+  // top-Fp token of the wave: a token of any other lane has Fp larger ones, the maxima of those
+  // lanes. With fewer than Fp non-empty quads the threshold is 0 and every non-empty lane is hot.
+  // Hot lanes copy their raw chunks into the row's region (chunks past V are dropped at
+  // selection); a row with more hot lanes than slots is filtered again after phase 1.
+  auto draft_batch = [&](const RowRaw<ET>* raw, const uint32_t* mk, int r0, int nb) __attribute__((always_inline)) {
+    if (Fp > kHot) {  // more guesses than slots: every row of the batch is filtered later
+      if (lane == 0)
+        for (int i = 0; i < nb; ++i)
+          if (r0 + i < K) sh.fb[w] |= 1u << (r0 + i);
+      return;
+    }
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < nb) {
+        const uint32_t g = uint32_t(__builtin_amdgcn_ds_bpermute((lane & 15) << 4, int(quad_max_u(mk[i]))));
+        v = ((lane >> 4) == i && r0 + i < K) ? g : v;
+      }
+    }
+    const uint32_t th = row16_min_u(row16_count_larger(v) < Fp ? v : 0xFFFFFFFFu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < nb && r0 + i < K) {
+        const int r = r0 + i;
+        const uint32_t thr = uint32_t(__builtin_amdgcn_readlane(int(th), 16 * i));
+        const bool hot = mk[i] >= thr && mk[i] != 0u;
+        const uint64_t hm = __ballot(hot);
+        const int n = __popcll(hm);
+        if (n <= kHot) {
+          if (hot) {
+            const int sl = __builtin_amdgcn_mbcnt_hi(uint32_t(hm >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(hm), 0u));
+            uint4* dst = reinterpret_cast<uint4*>(&sh.reg[r][w][0]) + sl * LY::NV;
+#pragma unroll
+            for (int j = 0; j < LY::NV; ++j) dst[j] = raw[i].w[j];
+            sh.hl[r][w][sl] = lane;
+          }
+          if (lane == 0) {
+            sh.nseg[r][w] = -n;
+            sh.thr[r][w] = thr;
+          }
+        } else if (lane == 0) {
+          sh.fb[w] |= 1u << r;
+        }
+      }
+    }
   };
   if (mode != 2) {
     // aligned rows: every row of a group in flight at once, consumed in load order; chunks past V
     // (a row's last tile) are loaded from a clamped address and masked
     for (int g0 = 0; g0 < R2; g0 += G) {
       RowRaw<ET> raw[G];
+      uint32_t mk[G];  // order keys of the lane maxima (0: no finite token)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         row_load_clamped<ET>(row_ptr(min(g0 + j, R2 - 1)), bl, V, raw[j]);
@@ -370,12 +470,27 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
         float z[kE];
         row_unpack<ET>(raw[j], z);
         if (mode == 1) mask_tail<ET>(z, bl, V);
-        if (g0 + j < R2) row_stats(z, g0 + j);
+        mk[j] = 0u;
+        if (g0 + j < R2) {
+          const float m = row_stats(z, g0 + j);
+          mk[j] = (m > -INFINITY) ? ordered_key(m) : 0u;
+        }
         if (j == 0 && g0 == 0) TRACE(8);
+        if (j == 5 && g0 == 0) TRACE(22);
+        // after every fourth row (and the group's last), the draft rows among the last four
+        constexpr int kB = 4;
+        if (FM > 0 && ((j % kB) == kB - 1 || j == G - 1)) {
+          const int jb = j - (j % kB);
+          if (g0 + jb < K) {
+            if (g0 == 0 && jb == 0) TRACE(20);
+            draft_batch(raw + jb, mk + jb, g0 + jb, j - jb + 1);
+            if (g0 == 0 && jb == 0) TRACE(21);
+          }
+        }
       }
     }
   } else {
-    // rows not 16-byte aligned: one row at a time
+    // rows not 16-byte aligned: one row at a time (their top-F filter runs after phase 1)
 #pragma unroll 1
     for (int r = 0; r < R2; ++r) {
       float z[kE];
@@ -390,9 +505,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
   }
   if (t <= K) sh.u[t] = u_v;
   if (t < K * sF) sh.sv[t] = sv_v;
+  const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
   __syncthreads();
 
-  // ---- publish the tile's partials; once they have completed, count the tile in
+  // ---- publish the tile's partials: max and sum of each row, one tagged word each
   if (t < R2) {
     float M = -INFINITY;
 #pragma unroll
@@ -403,372 +519,373 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
       const float2 v = sh.g16[t][q];
       if (v.y > 0.f) S += v.y * ex2(v.x - M);
     }
-    st_agent(a.stats + (int64_t(b) * R2 + t) * nT + tile, pack2(M, S));
+    uint64_t* st = a.stats + ((int64_t(b) * R2 + t) * nT + tile) * 2;
+    st_agent(st, tagged(tag, __float_as_uint(M)));
+    st_agent(st + 1, tagged(tag, __float_as_uint(S)));
   }
-  wait_vmem();
-  __syncthreads();
-  if (t == 0) sh.leader = (atomicAdd(ctl + kCtlArrive, 1u) == unsigned(nT - 1));
-  // Every tile read the last tag before its arrival (its loads completed before the atomic), so
-  // the leader may advance it now.
-  const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
-  __syncthreads();
   TRACE(1);
 
-  // ---- top-F guesses, per tile: each draft row's candidates are filtered into per-wave LDS regions,
-  // the tile's best F per row go to the workspace, then a word tagged with the call says they are
-  // in. Run while the tile would otherwise wait (non-leaders before the decision record, the
-  // leader after publishing its residual mass), re-reading the draft rows from cache.
-  const int Fp = a.topfFmax + 1;  // candidates kept per wave: one more than the guesses
-  // Top-F candidates of draft row r of this tile into this wave's LDS region.
+  // ---- top-F guesses, per tile: the tile's best F per draft row go to the workspace, then a word
+  // tagged with the call says they are in. Runs while the tile waits for the decision.
+  // Draft row r of a row that phase 1 could not filter: compaction of the tokens at or above the
+  // threshold into the wave's region (exact top Fp from registers if too many pass).
   auto row_filter = [&](const float (&z)[kE], int r) __attribute__((always_inline)) {
     float m = z[0];
 #pragma unroll
     for (int q = 1; q < kE; ++q) m = fmaxf(m, z[q]);
-    const float m2 = fmaxf(m, dpp_f<kDppXor1>(m));
-    const float m4 = fmaxf(m2, dpp_f<kDppXor2>(m2));
-    const float m8 = fmaxf(m4, dpp_f<kDppHalfMirror>(m4));
-    const float M = fmaxf(m8, dpp_f<kDppMirror>(m8));
-    // Top-F candidates of a draft row into this wave's region. The sampled token is dropped
-      // only at selection, so the filter keeps the wave's top Fp = F_max + 1 tokens. Threshold:
-      // the smallest maximum over the non-empty groups of the coarsest grouping (16, 8, 4 or 1
-      // lanes) that has at least Fp non-empty groups; Fp groups then each hold a token at least
-      // that large, so every top-Fp token of the wave passes. Positions past V read as -inf and
-      // never pass. With fewer than Fp non-empty lanes everything finite passes.
-      constexpr float kInf = __builtin_inff();
-      int lvl = (Fp <= 4) ? 0 : (Fp <= 8) ? 1 : (Fp <= 16) ? 2 : 3;
-      if (lvl == 0 && __popcll(__ballot(M > -kInf) & 0x0001000100010001ull) < Fp) lvl = 1;
-      if (lvl == 1 && __popcll(__ballot(m8 > -kInf) & 0x0101010101010101ull) < Fp) lvl = 2;
-      if (lvl == 2 && __popcll(__ballot(m4 > -kInf) & 0x1111111111111111ull) < Fp) lvl = 3;
-      float g;
-      if (lvl == 0) {
-        g = (M > -kInf) ? M : kInf;
-      } else if (lvl == 1) {
-        const float h = (m8 > -kInf) ? m8 : kInf;
-        g = fminf(h, dpp_f<kDppMirror>(h));
-      } else if (lvl == 2) {
-        const float q4 = (m4 > -kInf) ? m4 : kInf;
-        g = fminf(q4, dpp_f<kDppHalfMirror>(q4));
-        g = fminf(g, dpp_f<kDppMirror>(g));
-      } else {
-        g = (m > -kInf) ? m : kInf;
-        g = fminf(g, dpp_f<kDppXor1>(g));
-        g = fminf(g, dpp_f<kDppXor2>(g));
-        g = fminf(g, dpp_f<kDppHalfMirror>(g));
-        g = fminf(g, dpp_f<kDppMirror>(g));
-      }
-      const bool few = lvl == 3 && __popcll(__ballot(m > -kInf)) < Fp;
-      const float thr = few ? -__FLT_MAX__ : rows_min(g);
-      // Compaction without a scalar round trip per token: per-lane counts, a DPP scan for each
-      // lane's first slot, then one LDS write per token, the tokens that fail going to a
-      // per-lane spare slot. An entry holds the raw float bits and ~token.
-      int cnt = 0;
+    int n;
+    const float thr0 = lane_thr(m, n);
+    const float thr = (n < Fp) ? -__FLT_MAX__ : thr0;  // fewer than Fp finite lanes: all finite pass
+    // Compaction without a scalar round trip per token: per-lane counts, a DPP scan for each
+    // lane's first slot, then one LDS write per token, the tokens that fail going to a per-lane
+    // spare slot. An entry holds the raw float bits and ~token.
+    int cnt = 0;
 #pragma unroll
-      for (int q = 0; q < kE; ++q) cnt += (z[q] >= thr) ? 1 : 0;
-      const int incl = wave_incl_scan_i(cnt);
-      int total = __builtin_amdgcn_readlane(incl, 63);
-      uint64_t* region = sh.cand[r][w];
-      if (total <= kCandW) {
-        int slot = incl - cnt;
-        uint64_t* spare = &sh.spare[w][lane];
+    for (int q = 0; q < kE; ++q) cnt += (z[q] >= thr) ? 1 : 0;
+    const int incl = wave_incl_scan_i(cnt);
+    int total = __builtin_amdgcn_readlane(incl, 63);
+    uint64_t* region = sh.reg[r][w];
+    if (total <= kRegW) {
+      int slot = incl - cnt;
+      uint64_t* spare = &sh.spare[w][lane];
+#pragma unroll
+      for (int q = 0; q < kE; ++q) {
+        const bool pass = z[q] >= thr;
+        uint64_t* dst = pass ? region + slot : spare;
+        *dst = (uint64_t(__float_as_uint(z[q])) << 32) | uint64_t(~uint32_t(LY::tok(bl, q)));
+        slot += pass ? 1 : 0;
+      }
+    } else {  // too many pass (ties): the wave's exact top Fp from registers
+      uint64_t prev = ~0ull;
+#pragma unroll 1
+      for (int f = 0; f < Fp; ++f) {
+        uint64_t best = 0;
 #pragma unroll
         for (int q = 0; q < kE; ++q) {
-          const bool pass = z[q] >= thr;
-          uint64_t* dst = pass ? region + slot : spare;
-          *dst = (uint64_t(__float_as_uint(z[q])) << 32) | uint64_t(~uint32_t(LY::tok(bl, q)));
-          slot += pass ? 1 : 0;
+          const uint64_t kq = (z[q] > -INFINITY)
+                                  ? (uint64_t(ordered_key(z[q])) << 32) | uint64_t(~uint32_t(LY::tok(bl, q)))
+                                  : 0ull;
+          best = (kq < prev && kq > best) ? kq : best;
         }
-      } else {  // too many pass (ties, a short last tile): the wave's exact top Fp from registers
-        uint32_t ph = 0xFFFFFFFFu, pl = 0xFFFFFFFFu;
-#pragma unroll 1
-        for (int f = 0; f < Fp; ++f) {
-          uint32_t bh = 0, blo = 0;
-#pragma unroll
-          for (int q = 0; q < kE; ++q) {
-            const bool ok = z[q] > -INFINITY;
-            const uint32_t kh = ok ? ordered_key(z[q]) : 0u;
-            const uint32_t kl = ok ? ~uint32_t(LY::tok(bl, q)) : 0u;
-            if (key_gt(ph, pl, kh, kl) && key_gt(kh, kl, bh, blo)) {
-              bh = kh;
-              blo = kl;
-            }
-          }
-          wave_max_key(bh, blo);
-          if (lane == 0)  // raw float bits, as the compaction writes them (0 = none)
-            region[f] = bh ? (uint64_t(__float_as_uint(key_to_float(bh))) << 32) | blo : 0ull;
-          ph = bh;
-          pl = blo;
-        }
-        total = Fp;
+        best = wave_max_u64(best);
+        const uint32_t bh = uint32_t(best >> 32);
+        if (lane == 0)  // raw float bits, as the compaction writes them (0 = none)
+          region[f] = bh ? (uint64_t(__float_as_uint(key_to_float(bh))) << 32) | uint32_t(best) : 0ull;
+        prev = best;
       }
-      if (lane == 0) sh.ncw[r][w] = total;
+      total = Fp;
+    }
+    if (lane == 0) sh.nseg[r][w] = total;
   };
   auto topf_tile = [&]() __attribute__((always_inline)) {
-    if (mode != 2) {
-      // four draft rows in flight at once, then filtered one after another
-      constexpr int kQ = 4;
-#pragma unroll 1
-      for (int r0 = 0; r0 < K; r0 += kQ) {
-        RowRaw<ET> raw[kQ];
+    TRACEV(23, 1000000000ull + (sh.fb[0] | sh.fb[1] | sh.fb[2] | sh.fb[3]));
+    uint32_t fbm = __builtin_amdgcn_readfirstlane(sh.fb[w]);
+    while (fbm) {  // rows the hot-lane copy could not take: re-read from cache
+      const int r = __builtin_ctz(fbm);
+      fbm &= fbm - 1u;
+      float z[kE];
+      row_fetch<ET>(row_ptr(r), bl, V, mode, z);
+      row_filter(z, r);
+    }
+    TRACE(16);
+    __syncthreads();
+    TRACE(17);
+    // wave w selects the F best candidates (value desc, index asc) of rows w, w + 4, ...
+    if (w == 0) TRACE(26);
+    // Dumped slots are numbered across the four regions; lane l takes element l % 16 of slots
+    // l / 16 + 4 i. Key-list regions (rows filtered after phase 1) give one entry per lane.
+    for (int r = w; r < K; r += kWaves) {
+      const int F = sh.F[r];
+      const int xs = sh.xe[r];
+      int nw[kWaves], S[kWaves + 1];
+      uint32_t tw[kWaves];
+      S[0] = 0;
 #pragma unroll
-        for (int j = 0; j < kQ; ++j) {
-          row_load_clamped<ET>(row_ptr(min(r0 + j, K - 1)), bl, V, raw[j]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int ww = 0; ww < kWaves; ++ww) {
+        nw[ww] = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
+        tw[ww] = __builtin_amdgcn_readfirstlane(sh.thr[r][ww]);
+        S[ww + 1] = S[ww] + (nw[ww] < 0 ? -nw[ww] : 0);
+      }
+      const int e = lane & 15;
+      uint64_t key[kSel + kWaves];
 #pragma unroll
-        for (int j = 0; j < kQ; ++j) {
-          if (r0 + j >= K) continue;
-          float z[kE];
-          row_unpack<ET>(raw[j], z);
-          if (mode == 1) mask_tail<ET>(z, bl, V);
-          if (r0 + j == 0) TRACE(16);
-          row_filter(z, r0 + j);
-          if (r0 + j == 0) TRACE(17);
+      for (int i = 0; i < kSel; ++i) {
+        key[i] = 0;
+        if (4 * i >= S[kWaves]) continue;  // uniform: no slot of this round is filled
+        const int g = (lane >> 4) + 4 * i;
+        const int ww = int(g >= S[1]) + int(g >= S[2]) + int(g >= S[3]);
+        const int s0 = (ww == 0) ? 0 : (ww == 1) ? S[1] : (ww == 2) ? S[2] : S[3];
+        const uint32_t th = (ww == 0) ? tw[0] : (ww == 1) ? tw[1] : (ww == 2) ? tw[2] : tw[3];
+        const int sl = min(g - s0, kHot - 1);
+        const T* slot = reinterpret_cast<const T*>(&sh.reg[r][ww][0]) + sl * kE;
+        const float v = ET::one(slot, e);
+        const int tok = c0 + ww * LY::WTOK + sh.hl[r][ww][sl] * LY::VEC + LY::tok(0, e);
+        const uint32_t kv = ordered_key(v);
+        key[i] = (g < S[kWaves] && v > -INFINITY && kv >= th && tok < V && tok != xs)
+                     ? (uint64_t(kv) << 32) | uint64_t(~uint32_t(tok))
+                     : 0ull;  // the sampled token is never a guess
+      }
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        key[kSel + ww] = 0;
+        if (nw[ww] > 0) {
+          const uint64_t ent = sh.reg[r][ww][min(lane, kRegW - 1)];
+          const float v = __uint_as_float(uint32_t(ent >> 32));
+          const int tok = int(~uint32_t(ent));
+          if (lane < nw[ww] && uint32_t(ent) != 0u && tok != xs)  // entry lo 0 = none
+            key[kSel + ww] = (uint64_t(ordered_key(v)) << 32) | uint32_t(ent);
         }
       }
-    } else {
-#pragma unroll 1
-      for (int r = 0; r < K; ++r) {
-        float z[kE];
-        row_fetch<ET>(row_ptr(r), bl, V, mode, z);
-        row_filter(z, r);
+      if (r == 0) TRACE(24);
+      for (int f = 0; f < F; ++f) {
+        uint64_t mine = key[0];
+#pragma unroll
+        for (int i = 1; i < kSel + kWaves; ++i) mine = max_u64(mine, key[i]);
+        const uint64_t win = wave_max_u64(mine);
+        if (lane == 0) sh.best[r][f] = win;
+#pragma unroll
+        for (int i = 0; i < kSel + kWaves; ++i)
+          key[i] = (key[i] == win) ? 0ull : key[i];  // keys are unique: only the winner is cleared
       }
     }
+    TRACE(18);
     __syncthreads();
-    if (FM > 0) {  // wave w selects the F best candidates (value desc, index asc) of rows w, w+4, ...
-      for (int r = w; r < K; r += kWaves) {
-        const int F = sh.F[r];
-        const int xs = sh.xe[r];
-        uint64_t key[kCandSel];  // candidate q = lane + 64 i is entry q % kCandW of wave q / kCandW
+    TRACE(19);
+    // the tile's guesses: two words per key (high and low half), each tagged with the call
+    if (t < K * a.topfFmax) {
+      const int r = t / a.topfFmax, f = t - r * a.topfFmax;
+      if (f < sh.F[r]) {
+        uint64_t* cw = a.cand + (((int64_t(b) * K + r) * nT + tile) * a.topfFmax + f) * 2;
+        const uint64_t kv = sh.best[r][f];
+        st_agent(cw, tagged(tag, uint32_t(kv >> 32)));
+        st_agent(cw + 1, tagged(tag, uint32_t(kv)));
+      }
+    }
+    };
+  TRACE(10);
+
+  // ---- decide: the row's last tile waits for every tile's statistics, merges them, takes the
+  // decisions and publishes them in a record of tagged words, which the other tiles poll
+  // The top-F pass runs first everywhere: the other tiles would wait for the record anyway, and
+  // the deciding tile is the row's last (often short) tile, which tends to finish phase 1 early.
+  if (FM > 0) topf_tile();
+  TRACE(10);
+  const bool leader = tile == nT - 1;
+  float rv[kE], pre[kE];
+  {
+    if (leader) {
+      // logits at the draft tokens (draft and target rows 0..K-1) and at the Saguaro-set tokens,
+      // gathered from the rows; issued first, so they overlap the top-F pass and the statistics loads
+      float zg_v = 0.f, zs_v = 0.f;
+      int set_v = -1;
+      if (t < 2 * K) {
+        const int xr = sh.xe[t < K ? t : t - K];
+        if (unsigned(xr) < unsigned(V)) zg_v = ET::one(row_ptr(t), xr);
+      }
+      if (t < K * sF) {
+        set_v = (unsigned(sh.sv[t]) < unsigned(V)) ? sh.sv[t] : -1;
+        if (set_v >= 0) zs_v = ET::one(row_ptr(t / sF), set_v);
+      }
+      // 16-lane group g merges rows g, g + 16, g + 32: lane l takes tiles l, l + 16, ..., then the
+      // group combines its lanes with DPP (a fixed order, the same bits on every run)
+      for (int r = grp; r < R2; r += kGroupsPerBlock) {
+        const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * nT * 2;
+        float M = -INFINITY, S = 0.f;
+        constexpr int kAhead = 4;  // tiles per lane per polling round
+        for (int q0 = (t & 15); q0 < nT; q0 += kAhead * 16) {
+          uint64_t mv[kAhead], sv[kAhead];
+          for (int spins = 0;; ++spins) {  // until both words of each tile carry this call's tag
+            bool ok = true;
 #pragma unroll
-        for (int i = 0; i < kCandSel; ++i) {
-          const int q = lane + 64 * i, ww = q / kCandW, sl = q - ww * kCandW;
-          const uint64_t e = (ww < kWaves && sl < sh.ncw[r][ww]) ? sh.cand[r][ww][sl] : 0ull;
-          key[i] = uint32_t(e) ? (uint64_t(ordered_key(__uint_as_float(uint32_t(e >> 32)))) << 32) |
-                                     uint32_t(e)
-                               : 0ull;
-          if (uint32_t(key[i]) == ~uint32_t(xs)) key[i] = 0;  // the sampled token is never a guess
+            for (int i = 0; i < kAhead; ++i) {
+              const int q = q0 + i * 16;
+              mv[i] = (q < nT) ? ld_agent(st + 2 * q) : tagged(tag, 0xFF800000u);
+              sv[i] = (q < nT) ? ld_agent(st + 2 * q + 1) : tagged(tag, 0u);
+              ok = ok && uint32_t(mv[i] >> 32) == tag && uint32_t(sv[i] >> 32) == tag;
+            }
+            if (__all(ok)) break;
+            if (spins > a.spin_limit) {
+              if (!ok) atomicOr(a.flags, kFlagTimeout);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+#pragma unroll
+          for (int i = 0; i < kAhead; ++i) {
+            const float m = lo_f(mv[i]), s = lo_f(sv[i]);
+            if (s > 0.f) {
+              if (m > M) {
+                S = S * ex2(M - m) + s;
+                M = m;
+              } else {
+                S += s * ex2(m - M);
+              }
+            }
+          }
         }
-        for (int f = 0; f < F; ++f) {
-          uint64_t mine = key[0];
-#pragma unroll
-          for (int i = 1; i < kCandSel; ++i) mine = (key[i] > mine) ? key[i] : mine;
-          uint32_t hi = uint32_t(mine >> 32), lo = uint32_t(mine);
-          wave_max_key(hi, lo);
-          const uint64_t win = (uint64_t(hi) << 32) | lo;
-          if (lane == 0) sh.best[r][f] = win;
-#pragma unroll
-          for (int i = 0; i < kCandSel; ++i)
-            if (key[i] == win) key[i] = 0;  // keys are unique: only the winner is cleared
+        const float Mr = row16_max(M);
+        const float Sr = row16_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
+        if ((t & 15) == 0) sh.L[r] = Mr + lg2(Sr);
+      }
+      // thread 0 has seen row 0 of every tile with this call's tag, so every tile has read the
+      // previous tag: the next call may start from this one
+      if (t == 0) st_agent(ctl + kCtlTag, tag);
+      TRACE(11);
+      if (t < 2 * K) sh.zg[t] = zg_v;
+      if (t < K * sF) {
+        const int i = t / sF, f = t - i * sF;
+        for (int g = 0; g < f && set_v >= 0; ++g)  // the first occurrence of a token counts
+          if (sh.sv[i * sF + g] == set_v) set_v = -1;
+        sh.set[t] = set_v;
+        sh.zs[t] = zs_v;
+      }
+      __syncthreads();
+      TRACE(12);
+      if (t < 64) {  // wave 0: lane i takes the accept test of position i
+        const float C = a.C;
+        const int i = min(lane, K - 1);
+        const float Lq = sh.L[i], Lp = sh.L[K + i];
+        const int xi = sh.xe[i];
+        const bool xok = unsigned(xi) < unsigned(V);
+        if (lane < K && !xok) atomicOr(a.flags, kFlagBadToken);
+        float Nn = 1.f;
+        bool xin = false;
+        if (sF > 0) {  // Saguaro: N = 1 - (1 - C) sigma, sigma = q mass of the set
+          float sig = 0.f;
+          for (int f = 0; f < sF; ++f) {
+            const int sv = sh.set[i * sF + f];
+            if (sv < 0) continue;
+            sig += ex2(fmaf(sh.zs[i * sF + f], cc, -Lq));
+            if (sv == xi) xin = true;
+          }
+          Nn = 1.f - (1.f - C) * sig;
+          if (lane < K && !(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+        }
+        bool accept;
+        float ai;
+        if (!xok) {
+          accept = false;
+          ai = 0.f;
+        } else {
+          const float wx = xin ? C : 1.f;
+          const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
+          const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
+          if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
+            accept = dp > -INFINITY;
+            ai = accept ? 1.f : 0.f;
+          } else {
+            const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
+            accept = sh.u[i] < ratio;
+            ai = fminf(1.f, ratio);
+          }
+        }
+        if (a.aprob_out && lane < K) a.aprob_out[b * K + lane] = ai;
+        const uint64_t rej = __ballot(lane < K && !accept);
+        const int k = rej ? __builtin_ctzll(rej) : K;  // first rejection
+        const float Nk = (k < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), k)) : 1.f;
+        if (lane == 0) {
+          a.k_out[b] = k;
+          int n = 0;
+          if (k < K)
+            for (int f = 0; f < sF; ++f) {
+              const int sv = sh.set[k * sF + f];
+              if (sv >= 0) sh.myset[n++] = sv;
+            }
+          for (int f = n; f < kMaxF; ++f) sh.myset[f] = -1;
+          sh.k = k;
+          sh.nset = n;
+          sh.Lp = sh.L[K + k];
+          sh.Lq = (k < K) ? sh.L[k] : 0.f;
+          sh.w_out = 1.f / Nk;
+          sh.w_in = C / Nk;
         }
       }
       __syncthreads();
+      if (t < kDecWords) {  // publish the record, one tagged word per thread
+        uint32_t v;
+        if (t == kDecK) v = uint32_t(sh.k);
+        else if (t == kDecLp) v = __float_as_uint(sh.Lp);
+        else if (t == kDecLq) v = __float_as_uint(sh.Lq);
+        else if (t == kDecWout) v = __float_as_uint(sh.w_out);
+        else if (t == kDecWin) v = __float_as_uint(sh.w_in);
+        else if (t == kDecNset) v = uint32_t(sh.nset);
+        else v = uint32_t(sh.myset[t - kDecSet]);
+        st_agent(dec + t, tagged(tag, v));
+      }
+      TRACE(13);
+    } else if (t < 64) {
+      // wave 0 polls the record until every word carries this call's tag
+      uint64_t v = 0;
+      for (int spins = 0;; ++spins) {
+        v = (lane < kDecWords) ? ld_agent(dec + lane) : tagged(tag, 0u);
+        if (__all(uint32_t(v >> 32) == tag)) break;
+        if (spins > a.spin_limit) {
+          if (lane == 0) atomicOr(a.flags, kFlagTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      const uint32_t x = uint32_t(v);
+      if (lane == kDecK) sh.k = int(x);
+      if (lane == kDecLp) sh.Lp = __uint_as_float(x);
+      if (lane == kDecLq) sh.Lq = __uint_as_float(x);
+      if (lane == kDecWout) sh.w_out = __uint_as_float(x);
+      if (lane == kDecWin) sh.w_in = __uint_as_float(x);
+      if (lane == kDecNset) sh.nset = int(x);
+      if (lane >= kDecSet && lane < kDecWords) sh.myset[lane - kDecSet] = int(x);
     }
-    TRACE(19);
-    if (t < K * a.topfFmax) {
-      const int r = t / a.topfFmax, f = t - r * a.topfFmax;
-      if (f < sh.F[r])
-        st_agent(a.cand + ((int64_t(b) * K + r) * nT + tile) * a.topfFmax + f, sh.best[r][f]);
-    }
-    wait_vmem();
+    TRACE(2);
     __syncthreads();
-    if (t == 0) st_agent(a.cready + int64_t(b) * nT + tile, tagged(tag, 1u));
-  };
-  if (FM > 0 && !sh.leader) topf_tile();
-  TRACE(10);
+    TRACE(3);
+    const int k = min(max(sh.k, 0), K);
+    const bool resid = k < K;
+    const T* prow = target + int64_t(k) * V;
+    const T* qrow = resid ? draft + int64_t(k) * V : nullptr;
+    const float Lp = sh.Lp, Lq = sh.Lq, w_out = sh.w_out, w_in = sh.w_in;
+    const int nset = resid ? min(max(sh.nset, 0), kMaxF) : 0;
 
-  // ---- decide: the last tile to arrive merges the statistics and publishes the decision
-  if (sh.leader) {
-    if (t == 0) {  // every tile has arrived: ready for the next call
-      st_agent(ctl + kCtlArrive, 0u);
-      st_agent(ctl + kCtlTag, tag);
-    }
-    // logits at the draft tokens (draft and target rows 0..K-1) and at the Saguaro-set tokens,
-    // gathered from the rows; issued first, so they overlap the statistics loads
-    float zg_v = 0.f, zs_v = 0.f;
-    int set_v = -1;
-    if (t < 2 * K) {
-      const int xr = sh.xe[t < K ? t : t - K];
-      if (unsigned(xr) < unsigned(V)) zg_v = ET::one(row_ptr(t), xr);
-    }
-    if (t < K * sF) {
-      set_v = (unsigned(sh.sv[t]) < unsigned(V)) ? sh.sv[t] : -1;
-      if (set_v >= 0) zs_v = ET::one(row_ptr(t / sF), set_v);
-    }
-    // 16-lane group g merges rows g, g + 16, g + 32: lane l takes tiles l, l + 16, ..., then the
-    // group combines its lanes with DPP (a fixed order, the same bits on every run)
-    for (int r = grp; r < R2; r += kGroupsPerBlock) {
-      const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * nT;
-      float M = -INFINITY, S = 0.f;
-      constexpr int kAhead = 8;  // loads in flight per lane
-      for (int q0 = (t & 15); q0 < nT; q0 += kAhead * 16) {
-        uint64_t vals[kAhead];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) {
-          const int q = q0 + i * 16;
-          vals[i] = (q < nT) ? ld_agent(st + q) : 0ull;
-        }
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) {
-          const float m = lo_f(vals[i]), s = hi_f(vals[i]);
-          if (s > 0.f) {
-            if (m > M) {
-              S = S * ex2(M - m) + s;
-              M = m;
-            } else {
-              S += s * ex2(m - M);
-            }
-          }
-        }
-      }
-      const float Mr = row16_max(M);
-      const float Sr = row16_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
-      if ((t & 15) == 0) sh.L[r] = Mr + lg2(Sr);
-    }
-    TRACE(11);
-    if (t < 2 * K) sh.zg[t] = zg_v;
-    if (t < K * sF) {
-      const int i = t / sF, f = t - i * sF;
-      for (int g = 0; g < f && set_v >= 0; ++g)  // the first occurrence of a token counts
-        if (sh.sv[i * sF + g] == set_v) set_v = -1;
-      sh.set[t] = set_v;
-      sh.zs[t] = zs_v;
-    }
-    __syncthreads();
-    TRACE(12);
-    if (t < 64) {  // wave 0: lane i takes the accept test of position i
-      const float C = a.C;
-      const int i = min(lane, K - 1);
-      const float Lq = sh.L[i], Lp = sh.L[K + i];
-      const int xi = sh.xe[i];
-      const bool xok = unsigned(xi) < unsigned(V);
-      if (lane < K && !xok) atomicOr(a.flags, kFlagBadToken);
-      float Nn = 1.f;
-      bool xin = false;
-      if (sF > 0) {  // Saguaro: N = 1 - (1 - C) sigma, sigma = q mass of the set
-        float sig = 0.f;
-        for (int f = 0; f < sF; ++f) {
-          const int sv = sh.set[i * sF + f];
-          if (sv < 0) continue;
-          sig += ex2(fmaf(sh.zs[i * sF + f], cc, -Lq));
-          if (sv == xi) xin = true;
-        }
-        Nn = 1.f - (1.f - C) * sig;
-        if (lane < K && !(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
-      }
-      bool accept;
-      float ai;
-      if (!xok) {
-        accept = false;
-        ai = 0.f;
-      } else {
-        const float wx = xin ? C : 1.f;
-        const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
-        const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
-        if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
-          accept = dp > -INFINITY;
-          ai = accept ? 1.f : 0.f;
-        } else {
-          const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
-          accept = sh.u[i] < ratio;
-          ai = fminf(1.f, ratio);
-        }
-      }
-      if (a.aprob_out && lane < K) a.aprob_out[b * K + lane] = ai;
-      const uint64_t rej = __ballot(lane < K && !accept);
-      const int k = rej ? __builtin_ctzll(rej) : K;  // first rejection
-      const float Nk = (k < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), k)) : 1.f;
-      if (lane == 0) {
-        a.k_out[b] = k;
-        int n = 0;
-        if (k < K)
-          for (int f = 0; f < sF; ++f) {
-            const int sv = sh.set[k * sF + f];
-            if (sv >= 0) sh.myset[n++] = sv;
-          }
-        for (int f = n; f < kMaxF; ++f) sh.myset[f] = -1;
-        sh.k = k;
-        sh.nset = n;
-        sh.Lp = sh.L[K + k];
-        sh.Lq = (k < K) ? sh.L[k] : 0.f;
-        sh.w_out = 1.f / Nk;
-        sh.w_in = C / Nk;
-      }
-    }
-    __syncthreads();
-    if (t < kDecWords) {  // publish the record, one tagged word per thread
-      uint32_t v;
-      if (t == kDecK) v = uint32_t(sh.k);
-      else if (t == kDecLp) v = __float_as_uint(sh.Lp);
-      else if (t == kDecLq) v = __float_as_uint(sh.Lq);
-      else if (t == kDecWout) v = __float_as_uint(sh.w_out);
-      else if (t == kDecWin) v = __float_as_uint(sh.w_in);
-      else if (t == kDecNset) v = uint32_t(sh.nset);
-      else v = uint32_t(sh.myset[t - kDecSet]);
-      st_agent(dec + t, tagged(tag, v));
-    }
-    TRACE(13);
-  } else if (t < 64) {
-    // wave 0 polls the record until every word carries this call's tag
-    uint64_t v = 0;
-    for (int spins = 0;; ++spins) {
-      v = (lane < kDecWords) ? ld_agent(dec + lane) : tagged(tag, 0u);
-      if (__all(uint32_t(v >> 32) == tag)) break;
-      if (spins > a.spin_limit) {
-        if (lane == 0) atomicOr(a.flags, kFlagTimeout);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    const uint32_t x = uint32_t(v);
-    if (lane == kDecK) sh.k = int(x);
-    if (lane == kDecLp) sh.Lp = __uint_as_float(x);
-    if (lane == kDecLq) sh.Lq = __uint_as_float(x);
-    if (lane == kDecWout) sh.w_out = __uint_as_float(x);
-    if (lane == kDecWin) sh.w_in = __uint_as_float(x);
-    if (lane == kDecNset) sh.nset = int(x);
-    if (lane >= kDecSet && lane < kDecWords) sh.myset[lane - kDecSet] = int(x);
+    // ---- residual mass of this tile (values and prefix sums stay in registers), published
+    const float total = tile_residual<ET>(prow, qrow, bl, V, mode, cc, Lp, Lq, w_out, w_in, sh.myset,
+                                          nset, sh.wt, rv, pre);
+    if (t == 0) st_agent(a.res + int64_t(b) * nT + tile, tagged(tag, __float_as_uint(total)));
+    TRACE(4);
   }
-  TRACE(2);
-  __syncthreads();
-  TRACE(3);
-  const int k = min(max(sh.k, 0), K);  // in range even if a timed-out wait read a stale record
+  const int k = min(max(sh.k, 0), K);
   const bool resid = k < K;
   const T* prow = target + int64_t(k) * V;
-  const T* qrow = resid ? draft + int64_t(k) * V : nullptr;
-  const float Lp = sh.Lp, Lq = sh.Lq, w_out = sh.w_out, w_in = sh.w_in;
-  const int nset = resid ? min(max(sh.nset, 0), kMaxF) : 0;
-
-  // ---- residual mass of this tile (values and prefix sums stay in registers), published
-  float rv[kE], pre[kE];
-  const float total = tile_residual<ET>(prow, qrow, bl, V, mode, cc, Lp, Lq, w_out, w_in, sh.myset,
-                                        nset, sh.wt, rv, pre);
-  if (t == 0) st_agent(a.res + int64_t(b) * nT + tile, tagged(tag, __float_as_uint(total)));
-  TRACE(4);
-  if (FM > 0 && sh.leader) topf_tile();
+  const float Lp = sh.Lp;
 
   // ---- top-F guesses of draft rows tile, tile + T, ... while the other tiles finish: each
   // wave takes its own top F of the tiles' candidates, then wave 0 merges the four lists. Keys
   // are unique (a token lives in one tile), so round f picks the largest key below round f-1's.
-  if (FM > 0 && tile < K) {  // every tile's candidates must be in
-    const int per = (nT + kThreads - 1) / kThreads;
-    const int q0 = min(t * per, nT), q1 = min(nT, q0 + per);
-    const uint64_t* cr = a.cready + int64_t(b) * nT;
-    for (int spins = 0;; ++spins) {
-      bool ok = true;
-      for (int q = q0; q < q1; ++q) ok = ok && uint32_t(ld_agent(cr + q) >> 32) == tag;
-      if (__all(ok)) break;
-      if (spins > a.spin_limit) {
-        if (lane == 0) atomicOr(a.flags, kFlagTimeout);
-        break;
+  if (FM > 0 && tile < K) {  // every tile's candidate words for these rows must carry the tag
+    for (int r = tile; r < K; r += nT) {
+      const int F = sh.F[r];
+      const uint64_t* cd = a.cand + (int64_t(b) * K + r) * nT * a.topfFmax * 2;
+      for (int q = t; q < nT * F; q += kThreads) {
+        const int tl = q / F, ff = q - tl * F;
+        const uint64_t* cw = cd + (int64_t(tl) * a.topfFmax + ff) * 2;
+        for (int spins = 0;; ++spins) {
+          if (uint32_t(ld_agent(cw) >> 32) == tag && uint32_t(ld_agent(cw + 1) >> 32) == tag) break;
+          if (spins > a.spin_limit) {
+            atomicOr(a.flags, kFlagTimeout);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
       }
-      __builtin_amdgcn_s_sleep(1);
     }
     __syncthreads();
   }
   for (int r = tile; FM > 0 && r < K; r += nT) {
     const int F = sh.F[r];
     int32_t* out = a.topf_out + (int64_t(b) * K + r) * a.topfFmax;
-    const uint64_t* cd = a.cand + (int64_t(b) * K + r) * nT * a.topfFmax;
+    const uint64_t* cd = a.cand + (int64_t(b) * K + r) * nT * a.topfFmax * 2;
+    auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F) from its two words
+      const int tl = q / F, ff = q - tl * F;
+      const uint64_t* cw = cd + (int64_t(tl) * a.topfFmax + ff) * 2;
+      return (uint64_t(uint32_t(ld_agent(cw))) << 32) | uint32_t(ld_agent(cw + 1));
+    };
     const int n = nT * F;
     constexpr int kKeep = 4;
     uint64_t keys[kKeep];
@@ -776,10 +893,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     for (int i = 0; i < kKeep; ++i) {
       const int q = t + i * kThreads;
       keys[i] = 0;
-      if (q < n) {
-        const int tl = q / F, ff = q - tl * F;
-        keys[i] = ld_agent(cd + int64_t(tl) * a.topfFmax + ff);
-      }
+      if (q < n) keys[i] = cand_at(q);
     }
     uint32_t ph = 0xFFFFFFFFu, pl = 0xFFFFFFFFu;
     for (int f = 0; f < F; ++f) {
@@ -789,8 +903,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
       for (int i = 0; i < kKeep; ++i)
         if (keys[i] < prev && keys[i] > bk) bk = keys[i];
       for (int q = t + kKeep * kThreads; q < n; q += kThreads) {  // beyond what registers hold
-        const int tl = q / F, ff = q - tl * F;
-        const uint64_t v = ld_agent(cd + int64_t(tl) * a.topfFmax + ff);
+        const uint64_t v = cand_at(q);
         if (v < prev && v > bk) bk = v;
       }
       ph = uint32_t(bk >> 32);
