@@ -52,7 +52,7 @@ constexpr int kGroupsPerBlock = kThreads / 16;
 // either the raw chunks of the wave's hot lanes (at most kHot of them, see hot_dump), or a list of
 // (float bits << 32 | ~token) entries from the compaction filter.
 constexpr int kRegW = 48;
-constexpr int kSel = 8;  // dumped elements per lane at selection: up to 32 slots of 16
+constexpr int kSel = 8;  // candidates per lane at selection: two rounds of 64 per wave region
 static_assert(kRegW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
 static_assert(kRegW <= 64, "a key-list region gives at most one entry per lane");
 template <class ET>
@@ -60,7 +60,7 @@ constexpr int hot_slots() {
   return (kRegW * 8 / (kE * int(sizeof(typename ET::T)))) < 8 ? (kRegW * 8 / (kE * int(sizeof(typename ET::T))))
                                                                : 8;
 }
-static_assert(kWaves * 8 * kE <= 64 * kSel, "selection registers must cover the hot-lane dumps");
+static_assert(kSel % kWaves == 0 && 8 * kE <= 64 * (kSel / kWaves), "selection rounds must cover a region's dump");
 
 // Per-sequence control words (64 x uint32): word kCtlTag holds the tag of the sequence's last
 // call. A call's tag is the last tag + 1 (never 0, the value of a zero-filled workspace), so it
@@ -324,7 +324,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
   using LY = Lay<ET>;
   __shared__ Shared sh;
 
-  const int t = threadIdx.x, lane = t & 63, grp = t >> 4, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, in a scalar register
   const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF;
   const float cc = a.c2;
   const bool aligned = a.aligned != 0;
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
           }
           if (lane == 0) {
             sh.nseg[r][w] = -n;
-            sh.thr[r][w] = thr;
+            sh.thr[r][w] = max(thr, 0x00800000u);  // above the key of -inf
           }
         } else if (lane == 0) {
           sh.fb[w] |= 1u << r;
@@ -592,60 +593,68 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     TRACE(17);
     // wave w selects the F best candidates (value desc, index asc) of rows w, w + 4, ...
     if (w == 0) TRACE(26);
-    // Dumped slots are numbered across the four regions; lane l takes element l % 16 of slots
-    // l / 16 + 4 i. Key-list regions (rows filtered after phase 1) give one entry per lane.
+    // Candidate round i reads the region of wave i / 2: a dump gives lane l element l % 16 of slot
+    // l / 16 + 4 (i % 2); a key list (rows filtered after phase 1) gives lane l its entry l.
     for (int r = w; r < K; r += kWaves) {
       const int F = sh.F[r];
       const int xs = sh.xe[r];
-      int nw[kWaves], S[kWaves + 1];
-      uint32_t tw[kWaves];
-      S[0] = 0;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        nw[ww] = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
-        tw[ww] = __builtin_amdgcn_readfirstlane(sh.thr[r][ww]);
-        S[ww + 1] = S[ww] + (nw[ww] < 0 ? -nw[ww] : 0);
-      }
       const int e = lane & 15;
-      uint64_t key[kSel + kWaves];
+      uint64_t key[kSel];
 #pragma unroll
       for (int i = 0; i < kSel; ++i) {
+        constexpr int kParts = kSel / kWaves;
+        const int ww = i / kParts, part = i % kParts;
+        const int n = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
         key[i] = 0;
-        if (4 * i >= S[kWaves]) continue;  // uniform: no slot of this round is filled
-        const int g = (lane >> 4) + 4 * i;
-        const int ww = int(g >= S[1]) + int(g >= S[2]) + int(g >= S[3]);
-        const int s0 = (ww == 0) ? 0 : (ww == 1) ? S[1] : (ww == 2) ? S[2] : S[3];
-        const uint32_t th = (ww == 0) ? tw[0] : (ww == 1) ? tw[1] : (ww == 2) ? tw[2] : tw[3];
-        const int sl = min(g - s0, kHot - 1);
-        const T* slot = reinterpret_cast<const T*>(&sh.reg[r][ww][0]) + sl * kE;
-        const float v = ET::one(slot, e);
-        const int tok = c0 + ww * LY::WTOK + sh.hl[r][ww][sl] * LY::VEC + LY::tok(0, e);
-        const uint32_t kv = ordered_key(v);
-        key[i] = (g < S[kWaves] && v > -INFINITY && kv >= th && tok < V && tok != xs)
-                     ? (uint64_t(kv) << 32) | uint64_t(~uint32_t(tok))
-                     : 0ull;  // the sampled token is never a guess
-      }
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        key[kSel + ww] = 0;
-        if (nw[ww] > 0) {
-          const uint64_t ent = sh.reg[r][ww][min(lane, kRegW - 1)];
+        if (n < 0 && 4 * part < -n) {  // uniform: some slot of this quarter holds a dump
+          const uint32_t th = __builtin_amdgcn_readfirstlane(sh.thr[r][ww]);
+          const int sl = (lane >> 4) + 4 * part;
+          const int slc = min(sl, kHot - 1);
+          const float v = ET::one(reinterpret_cast<const T*>(&sh.reg[r][ww][0]) + slc * kE, e);
+          const int tok = c0 + ww * LY::WTOK + sh.hl[r][ww][slc] * LY::VEC + LY::tok(0, e);
+          const uint32_t kv = ordered_key(v);
+          // th is above the key of -inf; the sampled token is never a guess
+          const bool ok = (sl < -n) & (kv >= th) & (tok < V) & (tok != xs);
+          key[i] = ok ? (uint64_t(kv) << 32) | uint64_t(~uint32_t(tok)) : 0ull;
+        } else if (n > 64 * part) {  // key list
+          const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
           const float v = __uint_as_float(uint32_t(ent >> 32));
           const int tok = int(~uint32_t(ent));
-          if (lane < nw[ww] && uint32_t(ent) != 0u && tok != xs)  // entry lo 0 = none
-            key[kSel + ww] = (uint64_t(ordered_key(v)) << 32) | uint32_t(ent);
+          if (lane + 64 * part < n && uint32_t(ent) != 0u && tok != xs)  // entry lo 0 = none
+            key[i] = (uint64_t(ordered_key(v)) << 32) | uint32_t(ent);
         }
       }
       if (r == 0) TRACE(24);
-      for (int f = 0; f < F; ++f) {
-        uint64_t mine = key[0];
+      // the nonzero keys (a few per wave region) into one list, one per lane: the F rounds then
+      // take a single key per lane (more than 64: rounds over all of them)
+      uint64_t* lst = sh.spare[w];
+      int N = 0;
 #pragma unroll
-        for (int i = 1; i < kSel + kWaves; ++i) mine = max_u64(mine, key[i]);
-        const uint64_t win = wave_max_u64(mine);
-        if (lane == 0) sh.best[r][f] = win;
+      for (int i = 0; i < kSel; ++i) {
+        const uint64_t m = __ballot(key[i] != 0ull);
+        if (m) {
+          const int at = N + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+          if (key[i] != 0ull && at < 64) lst[at] = key[i];
+          N += __popcll(m);
+        }
+      }
+      if (N <= 64) {
+        uint64_t mine = (lane < N) ? lst[lane] : 0ull;
+        for (int f = 0; f < F; ++f) {
+          const uint64_t win = wave_max_u64(mine);
+          if (lane == 0) sh.best[r][f] = win;
+          mine = (mine == win) ? 0ull : mine;  // keys are unique: only the winner is cleared
+        }
+      } else {
+        for (int f = 0; f < F; ++f) {
+          uint64_t mine = key[0];
 #pragma unroll
-        for (int i = 0; i < kSel + kWaves; ++i)
-          key[i] = (key[i] == win) ? 0ull : key[i];  // keys are unique: only the winner is cleared
+          for (int i = 1; i < kSel; ++i) mine = max_u64(mine, key[i]);
+          const uint64_t win = wave_max_u64(mine);
+          if (lane == 0) sh.best[r][f] = win;
+#pragma unroll
+          for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
+        }
       }
     }
     TRACE(18);
