@@ -205,7 +205,14 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # per-launch duration of the kernel: an event pair on the launch stream around each step
+    # per-launch duration of the kernel over the timed region: every step issues the same number of
+    # launches of it (rounds of resident sequences), back to back on this stream
+    n_launch = ssd.ssd_verify_launches(B, K, V, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32, topf)
+    if n_launch < 1:
+        sys.exit(f"ssd_verify_launches returned {n_launch}")
+    launch_ms = ms_per_step / n_launch
+
+    # the same launch alone between an event pair (includes the event and dispatch overhead)
     n_ev = min(args.steps, 500)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
@@ -216,7 +223,7 @@ def main():
         calls[i % n_rep]()
         e1.record(stream)
     torch.cuda.synchronize()
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    isolated_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -256,7 +263,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "verify_fused_kernel",
-                     "launch_ms": round(launch_ms, 6), "kernel_hash": khash},
+                     "launch_ms": round(launch_ms, 6), "launches_per_step": n_launch,
+                     "isolated_launch_ms": round(isolated_ms, 6), "kernel_hash": khash},
         "accepted_len_hist": k_hist,
     }
     if not args.no_cpu_baseline:

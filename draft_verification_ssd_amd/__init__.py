@@ -28,5 +28,6 @@ from ._lib import (  # noqa: F401
     ssd_topf_guess,
     ssd_topf_workspace_bytes,
     ssd_verify,
+    ssd_verify_launches,
     ssd_verify_workspace_bytes,
 )

@@ -17,7 +17,8 @@ SSD_F32, SSD_BF16 = 0, 1
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 20, 65535
 FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT = 0x1, 0x2, 0x4, 0x8
 
-EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify", "ssd_topf_workspace_bytes", "ssd_topf_guess",
+EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify", "ssd_topf_workspace_bytes",
+           "ssd_topf_guess",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",
            "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string"]
 
@@ -35,6 +36,8 @@ def _declare(L):
     L.ssd_status_string.argtypes = [ctypes.c_int]
     L.ssd_verify_workspace_bytes.restype = SZ
     L.ssd_verify_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    L.ssd_verify_launches.restype = ctypes.c_int
+    L.ssd_verify_launches.argtypes = [I32, I32, I32, ctypes.c_int, I32]
     L.ssd_verify.restype = ctypes.c_int
     L.ssd_verify.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32,
                              P, I32, P, P, P, P, P, P, SZ, P]
@@ -141,6 +144,11 @@ class Workspace:
 
 def ssd_verify_workspace_bytes(B: int, K: int, V: int, topf_F_max: int = 0) -> int:
     return int(lib().ssd_verify_workspace_bytes(B, K, V, topf_F_max))
+
+
+def ssd_verify_launches(B: int, K: int, V: int, dtype: int, topf_F_max: int = 0) -> int:
+    """Kernel launches ssd_verify issues for this shape on the current device (-1 if rejected)."""
+    return int(lib().ssd_verify_launches(B, K, V, dtype, topf_F_max))
 
 
 def ssd_topf_workspace_bytes(R: int, V: int, F_max: int) -> int:

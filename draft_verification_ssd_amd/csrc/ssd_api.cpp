@@ -125,6 +125,21 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   return hip_status(e);
 }
 
+int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max) {
+  using namespace ssd;
+  if (!dtype_ok(dtype)) return -1;
+  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V) return -1;
+  if (topf_F_max < 0 || topf_F_max > SSD_MAX_F) return -1;
+  if (B == 0) return 0;
+  VerifyArgs a{};
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.T = verify_layout(B, K, V, topf_F_max).T;
+  a.topfFmax = topf_F_max;
+  return count_verify_launches(a, dtype == SSD_BF16);
+}
+
 #ifdef SSD_TRACE
 // analysis builds only: device buffer of 8 timestamps per verification workgroup
 void ssd_set_trace_buffer(void* device_buffer) { ssd_trace_buffer = device_buffer; }

@@ -93,6 +93,8 @@ struct CacheLookupArgs {
 };
 
 hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t st);
+// kernel launches launch_verify issues for these arguments on the current device (-1 on error)
+int count_verify_launches(const VerifyArgs& a, bool bf16);
 hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st);

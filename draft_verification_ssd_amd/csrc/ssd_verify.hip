@@ -1080,11 +1080,15 @@ static int capacity_blocks() {
 }
 
 template <class ET, int FM, int G>
-static hipError_t launch_fused(VerifyArgs a, hipStream_t st) {
+static hipError_t launch_fused(VerifyArgs a, hipStream_t st, int* n_launches) {
   const int cap = capacity_blocks<ET, FM, G>();
   if (cap < a.T) return hipErrorInvalidConfiguration;
   const int per_round = cap / a.T;  // whole sequences whose tiles are all resident at once
   const int B = a.B;
+  if (n_launches) {  // count only
+    *n_launches = (B + per_round - 1) / per_round;
+    return hipSuccess;
+  }
   for (int b0 = 0; b0 < B; b0 += per_round) {
     const int nb = (B - b0 < per_round) ? (B - b0) : per_round;
     a.b0 = b0;
@@ -1099,20 +1103,26 @@ static hipError_t launch_fused(VerifyArgs a, hipStream_t st) {
 // (16 VGPRs per row). Larger K runs several groups; a smaller K loads the last row again for the
 // unused slots (cache hits) and skips their arithmetic.
 template <class ET, int FM>
-static hipError_t launch_g(const VerifyArgs& a, hipStream_t st) {
-  return launch_fused<ET, FM, (sizeof(typename ET::T) == 2 ? 9 : 5)>(a, st);
+static hipError_t launch_g(const VerifyArgs& a, hipStream_t st, int* n) {
+  return launch_fused<ET, FM, (sizeof(typename ET::T) == 2 ? 9 : 5)>(a, st, n);
 }
 
 template <class ET>
-static hipError_t launch_verify_e(const VerifyArgs& a, hipStream_t st) {
-  if (a.topfFmax == 0) return launch_g<ET, 0>(a, st);
-  if (a.topfFmax <= 4) return launch_g<ET, 4>(a, st);
-  if (a.topfFmax <= 8) return launch_g<ET, 8>(a, st);
-  return launch_g<ET, 16>(a, st);
+static hipError_t launch_verify_e(const VerifyArgs& a, hipStream_t st, int* n) {
+  if (a.topfFmax == 0) return launch_g<ET, 0>(a, st, n);
+  if (a.topfFmax <= 4) return launch_g<ET, 4>(a, st, n);
+  if (a.topfFmax <= 8) return launch_g<ET, 8>(a, st, n);
+  return launch_g<ET, 16>(a, st, n);
 }
 
 hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t st) {
-  return bf16 ? launch_verify_e<BF16T>(a, st) : launch_verify_e<F32T>(a, st);
+  return bf16 ? launch_verify_e<BF16T>(a, st, nullptr) : launch_verify_e<F32T>(a, st, nullptr);
+}
+
+int count_verify_launches(const VerifyArgs& a, bool bf16) {
+  int n = -1;
+  const hipError_t e = bf16 ? launch_verify_e<BF16T>(a, nullptr, &n) : launch_verify_e<F32T>(a, nullptr, &n);
+  return e == hipSuccess ? n : -1;
 }
 
 }  // namespace ssd

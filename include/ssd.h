@@ -96,14 +96,19 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   accept_prob       device fp32 [B, K] out or NULL: min(1, p_i(x_i) / q'_i(x_i)) at every i.
  *   residual_mass     device fp32 [B] out or NULL: R (1 when k = K).
  *   workspace         device scratch of ssd_verify_workspace_bytes(B, K, V, topf_F_max) bytes.
- * Launch: one kernel per round of sequences, each round as many whole sequences (ceil(V / 2048)
+ * Launch: one kernel per round of sequences, each round as many whole sequences (ceil(V / 4096)
  * workgroups each) as the device keeps resident at once; the workgroups of a sequence wait for
- * each other with bounded spins (SSD_FLAG_TIMEOUT instead of a hang).
+ * each other with bounded spins (SSD_FLAG_TIMEOUT instead of a hang). ssd_verify_launches gives
+ * the number of rounds.
  * Errors: SSD_ERR_INVALID_ARG (null required pointer, bad size/stride/T/C/F), SSD_ERR_UNSUPPORTED
- * (dtype, or a vocabulary whose 2048-token tiles cannot all be resident on the device),
+ * (dtype, or a vocabulary whose 4096-token tiles cannot all be resident on the device),
  * SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
  * ------------------------------------------------------------------------------------------- */
 size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max);
+/* Kernel launches (rounds of resident sequences) that ssd_verify issues for this shape on the
+ * current device; -1 for arguments ssd_verify rejects or an occupancy query that fails. Launches
+ * nothing; the same host-side plan that ssd_verify follows. */
+int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max);
 
 ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
                       const void* target_logits, int64_t target_seq_stride,

@@ -127,6 +127,14 @@ def test_workspace_sizes():
     assert ssd.ssd_saguaro_workspace_bytes(8192, 128256) > 0
 
 
+def test_verify_launch_count_rejects_what_verify_rejects():
+    for args in [(-1, 4, 1000, ssd.SSD_BF16, 3), (1, 0, 1000, ssd.SSD_BF16, 3), (1, 17, 1000, ssd.SSD_F32, 0),
+                 (1, 4, 0, ssd.SSD_F32, 0), (1, 4, (1 << 20) + 1, ssd.SSD_F32, 0), (1, 4, 1000, 7, 0),
+                 (1, 4, 1000, ssd.SSD_BF16, 17), (1, 4, 1000, ssd.SSD_BF16, -1)]:
+        assert ssd.ssd_verify_launches(*args) == -1, args
+    assert ssd.ssd_verify_launches(0, 4, 1000, ssd.SSD_BF16, 3) == 0
+
+
 @pytest.mark.parametrize("K,a,r,budget", [(4, 0.7, 1.0, 12), (4, 0.7, 1.0, 32), (8, 0.55, 0.5, 100),
                                           (2, 0.9, 2.0, 7), (0, 0.5, 1.0, 5), (6, 0.3, 1.5, 0),
                                           (16, 0.8, 1.0, 1000), (3, 0.99, 0.1, 9)])

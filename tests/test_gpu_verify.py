@@ -190,3 +190,12 @@ def test_empty_batch_is_a_no_op():
     st = L.ssd_verify(None, 400, None, 500, 0, 0, 4, 100, 1.0, None, None, None, 0, 1.0, None, 0, None,
                       None, None, None, None, ws.ptr, ws.nbytes, None)
     assert st == ssd.SSD_OK
+
+
+def test_launch_count_on_the_device():
+    # the headline shape fits the device in one round; a batch far beyond residency needs several
+    one = ssd.ssd_verify_launches(16, 4, 128256, ssd.SSD_BF16, 3)
+    many = ssd.ssd_verify_launches(4096, 4, 128256, ssd.SSD_BF16, 3)
+    assert one == 1
+    assert many > 1 and many == ssd.ssd_verify_launches(4096, 4, 128256, ssd.SSD_BF16, 3)
+    assert ssd.ssd_verify_launches(1, 4, 32000, ssd.SSD_F32, 0) == 1
