@@ -48,6 +48,7 @@ static_assert(kTileTok == kPlanTile, "host plan and kernel disagree on the tile 
 constexpr int kMaxVT = (kMaxV + kTileTok - 1) / kTileTok;  // tiles of the longest row
 constexpr int kMaxR2 = 2 * kMaxK + 1;
 constexpr int kGroupsPerBlock = kThreads / 16;
+constexpr int kAhead = 4;  // phase-1 rows in flight per lane
 // Per draft row and wave, the top-F candidates live in an LDS region of kRegW 64-bit words:
 // either the raw chunks of the wave's hot lanes (at most kHot of them, see hot_dump), or a list of
 // (float bits << 32 | ~token) entries from the compaction filter.
@@ -252,7 +253,6 @@ struct Shared {
   float res[kMaxVT];
   int cstar, clamp, fallback, first, lastp;
   float base, target, R;
-  uint64_t wtop[kWaves][kMaxF];
 };
 
 // Residual values of a lane's kE tokens of one tile and their prefix sums in token order, relative
@@ -461,13 +461,17 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     for (int g0 = 0; g0 < R2; g0 += G) {
       RowRaw<ET> raw[G];
       uint32_t mk[G];  // order keys of the lane maxima (0: no finite token)
+      // kAhead rows in flight: the rest of the group is issued one row per row consumed, so the
+      // requests of all workgroups interleave and every workgroup's first rows land early
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < G && j < kAhead; ++j) {
         row_load_clamped<ET>(row_ptr(min(g0 + j, R2 - 1)), bl, V, raw[j]);
         __builtin_amdgcn_sched_barrier(0);  // issue in row order
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
+        if (j + kAhead < G) row_load_clamped<ET>(row_ptr(min(g0 + j + kAhead, R2 - 1)), bl, V, raw[j + kAhead]);
+        __builtin_amdgcn_sched_barrier(0);
         float z[kE];
         row_unpack<ET>(raw[j], z);
         if (mode == 1) mask_tail<ET>(z, bl, V);
@@ -864,78 +868,58 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
   const T* prow = target + int64_t(k) * V;
   const float Lp = sh.Lp;
 
-  // ---- top-F guesses of draft rows tile, tile + T, ... while the other tiles finish: each
-  // wave takes its own top F of the tiles' candidates, then wave 0 merges the four lists. Keys
+  // ---- top-F guesses of draft rows tile, tile + T, ...: wave 0 merges the tiles' candidates. Keys
   // are unique (a token lives in one tile), so round f picks the largest key below round f-1's.
-  if (FM > 0 && tile < K) {  // every tile's candidate words for these rows must carry the tag
-    for (int r = tile; r < K; r += nT) {
-      const int F = sh.F[r];
-      const uint64_t* cd = a.cand + (int64_t(b) * K + r) * nT * a.topfFmax * 2;
-      for (int q = t; q < nT * F; q += kThreads) {
-        const int tl = q / F, ff = q - tl * F;
-        const uint64_t* cw = cd + (int64_t(tl) * a.topfFmax + ff) * 2;
-        for (int spins = 0;; ++spins) {
-          if (uint32_t(ld_agent(cw) >> 32) == tag && uint32_t(ld_agent(cw + 1) >> 32) == tag) break;
-          if (spins > a.spin_limit) {
-            atomicOr(a.flags, kFlagTimeout);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-    }
-    __syncthreads();
-  }
-  for (int r = tile; FM > 0 && r < K; r += nT) {
+  // Each key is two words tagged with the call; a lane polls its own.
+  for (int r = tile; FM > 0 && w == 0 && r < K; r += nT) {
     const int F = sh.F[r];
     int32_t* out = a.topf_out + (int64_t(b) * K + r) * a.topfFmax;
     const uint64_t* cd = a.cand + (int64_t(b) * K + r) * nT * a.topfFmax * 2;
-    auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F) from its two words
+    const int n = nT * F;
+    auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F), once tagged
       const int tl = q / F, ff = q - tl * F;
       const uint64_t* cw = cd + (int64_t(tl) * a.topfFmax + ff) * 2;
-      return (uint64_t(uint32_t(ld_agent(cw))) << 32) | uint32_t(ld_agent(cw + 1));
+      uint64_t hi = 0, lo = 0;
+      for (int spins = 0;; ++spins) {
+        hi = ld_agent(cw);
+        lo = ld_agent(cw + 1);
+        if (uint32_t(hi >> 32) == tag && uint32_t(lo >> 32) == tag) break;
+        if (spins > a.spin_limit) {
+          atomicOr(a.flags, kFlagTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
     };
-    const int n = nT * F;
-    constexpr int kKeep = 4;
-    uint64_t keys[kKeep];
+    constexpr int kM = 4;  // keys per lane held in registers
+    if (n <= 64 * kM) {
+      uint64_t key[kM];
 #pragma unroll
-    for (int i = 0; i < kKeep; ++i) {
-      const int q = t + i * kThreads;
-      keys[i] = 0;
-      if (q < n) keys[i] = cand_at(q);
-    }
-    uint32_t ph = 0xFFFFFFFFu, pl = 0xFFFFFFFFu;
-    for (int f = 0; f < F; ++f) {
-      uint64_t bk = 0;
-      const uint64_t prev = (uint64_t(ph) << 32) | pl;
-#pragma unroll
-      for (int i = 0; i < kKeep; ++i)
-        if (keys[i] < prev && keys[i] > bk) bk = keys[i];
-      for (int q = t + kKeep * kThreads; q < n; q += kThreads) {  // beyond what registers hold
-        const uint64_t v = cand_at(q);
-        if (v < prev && v > bk) bk = v;
-      }
-      ph = uint32_t(bk >> 32);
-      pl = uint32_t(bk);
-      wave_max_key(ph, pl);
-      if (lane == 0) sh.wtop[w][f] = (uint64_t(ph) << 32) | pl;
-    }
-    __syncthreads();
-    if (t < 64) {
-      const uint64_t key = (lane < kWaves * F) ? sh.wtop[lane / F][lane % F] : 0ull;
-      ph = 0xFFFFFFFFu;
-      pl = 0xFFFFFFFFu;
+      for (int i = 0; i < kM; ++i) key[i] = (lane + 64 * i < n) ? cand_at(lane + 64 * i) : 0ull;
       for (int f = 0; f < F; ++f) {
-        const uint64_t prev = (uint64_t(ph) << 32) | pl;
-        const uint64_t bk = (key < prev) ? key : 0ull;
-        ph = uint32_t(bk >> 32);
-        pl = uint32_t(bk);
-        wave_max_key(ph, pl);
-        if (lane == 0) out[f] = (ph | pl) ? int(~pl) : -1;
+        uint64_t mine = key[0];
+#pragma unroll
+        for (int i = 1; i < kM; ++i) mine = max_u64(mine, key[i]);
+        const uint64_t win = wave_max_u64(mine);
+        if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+#pragma unroll
+        for (int i = 0; i < kM; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
       }
-      for (int f = F + lane; f < a.topfFmax; f += 64) out[f] = -1;
+    } else {  // many tiles: every round re-reads the keys, taking the largest below the last
+      uint64_t prev = ~0ull;
+      for (int f = 0; f < F; ++f) {
+        uint64_t best = 0;
+        for (int q = lane; q < n; q += 64) {
+          const uint64_t kq = cand_at(q);
+          best = (kq < prev && kq > best) ? kq : best;
+        }
+        const uint64_t win = wave_max_u64(best);
+        if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+        prev = win;
+      }
     }
-    __syncthreads();
+    for (int f = F + lane; f < a.topfFmax; f += 64) out[f] = -1;
     TRACE(14);
   }
 
