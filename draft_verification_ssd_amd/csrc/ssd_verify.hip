@@ -65,8 +65,9 @@ static_assert(kSel % kWaves == 0 && 8 * kE <= 64 * (kSel / kWaves), "selection r
 
 // Per-sequence control words (64 x uint32): word kCtlTag holds the tag of the sequence's last
 // call. A call's tag is the last tag + 1 (never 0, the value of a zero-filled workspace), so it
-// advances on every launch, graph replays included, with no host state.
-constexpr int kCtlTag = 16;
+// advances on every launch, graph replays included, with no host state. Word kCtlLead holds the
+// tag of the call whose deciding tile has claimed it.
+constexpr int kCtlTag = 16, kCtlLead = 32;
 
 // Per-sequence decision record: 64-bit words (call tag << 32 | value), each written once per
 // call, so a reader knows a word is current when its tag matches the call's.
@@ -239,6 +240,7 @@ struct Shared {
   uint32_t fb[kWaves];  // draft rows the wave filters again after phase 1 (bit r)
   uint64_t best[kMaxK][kMaxF];
   uint64_t spare[kWaves][64];  // where the compaction's failing tokens are written
+  int leader;
   // decision (last tile to arrive)
   float L[kMaxR2];
   float zg[2 * kMaxK];      // logits at the draft tokens: draft rows 0..K-1, then target rows
@@ -677,13 +679,28 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     };
   TRACE(10);
 
-  // ---- decide: the row's last tile waits for every tile's statistics, merges them, takes the
-  // decisions and publishes them in a record of tagged words, which the other tiles poll
-  // The top-F pass runs first everywhere: the other tiles would wait for the record anyway, and
-  // the deciding tile is the row's last (often short) tile, which tends to finish phase 1 early.
+  // ---- claim the decision: the first tile past phase 1 swaps the lead word from the last call's
+  // tag to this call's. It has the most time to spare before the last statistics arrive, so its
+  // own top-F pass costs the decision nothing. The answer is read after the pass.
+  uint32_t seen = tag_ld;
+  bool won = false;
+  if (t == 0)
+    won = __hip_atomic_compare_exchange_strong(ctl + kCtlLead, &seen, tag, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
   if (FM > 0) topf_tile();
   TRACE(10);
-  const bool leader = tile == nT - 1;
+  if (t == 0) {
+    // a word that holds neither the last tag nor this one is left from a call that timed out:
+    // claim from whatever it holds
+    for (int i = 0; i < 8 && !won && seen != tag; ++i)
+      won = __hip_atomic_compare_exchange_strong(ctl + kCtlLead, &seen, tag, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sh.leader = won ? 1 : 0;
+  }
+  __syncthreads();
+  const bool leader = sh.leader != 0;
+  // ---- decide: the claiming tile waits for every tile's statistics, merges them, takes the
+  // decisions and publishes them in a record of tagged words, which the other tiles poll
   float rv[kE], pre[kE];
   {
     if (leader) {
