@@ -169,6 +169,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
   return (uint64_t(hi) << 32) | lo;
 }
+// unsigned 32-bit maximum over the wave, the same way (one DPP operand per step)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x142, 0xA, 0xF, false)));
+  v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x143, 0xC, 0xF, false)));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
 // lexicographic max of (hi, lo) key pairs over the wave
 __device__ __forceinline__ void wave_max_key(uint32_t& hi, uint32_t& lo) {
   const uint64_t m = wave_max_u64((uint64_t(hi) << 32) | lo);

@@ -602,64 +602,131 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     // Candidate round i reads the region of wave i / 2: a dump gives lane l element l % 16 of slot
     // l / 16 + 4 (i % 2); a key list (rows filtered after phase 1) gives lane l its entry l.
     for (int r = w; r < K; r += kWaves) {
-      const int F = sh.F[r];
-      const int xs = sh.xe[r];
-      const int e = lane & 15;
-      uint64_t key[kSel];
+      if constexpr (sizeof(T) == 2) {
+        // bf16: 32-bit keys, the value's 16-bit order key above 0xFFFF - (token - c0), so a larger
+        // key is a larger value, then a smaller token; 0 = none (every real key is above 2^23)
+        const int F = sh.F[r];
+        const uint32_t xs_l = uint32_t(sh.xe[r] - c0);  // the sampled token, relative to the tile
+        const int e = lane & 15;
+        uint32_t key[kSel];
 #pragma unroll
-      for (int i = 0; i < kSel; ++i) {
-        constexpr int kParts = kSel / kWaves;
-        const int ww = i / kParts, part = i % kParts;
-        const int n = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
-        key[i] = 0;
-        if (n < 0 && 4 * part < -n) {  // uniform: some slot of this quarter holds a dump
-          const uint32_t th = __builtin_amdgcn_readfirstlane(sh.thr[r][ww]);
-          const int sl = (lane >> 4) + 4 * part;
-          const int slc = min(sl, kHot - 1);
-          const float v = ET::one(reinterpret_cast<const T*>(&sh.reg[r][ww][0]) + slc * kE, e);
-          const int tok = c0 + ww * LY::WTOK + sh.hl[r][ww][slc] * LY::VEC + LY::tok(0, e);
-          const uint32_t kv = ordered_key(v);
-          // th is above the key of -inf; the sampled token is never a guess
-          const bool ok = (sl < -n) & (kv >= th) & (tok < V) & (tok != xs);
-          key[i] = ok ? (uint64_t(kv) << 32) | uint64_t(~uint32_t(tok)) : 0ull;
-        } else if (n > 64 * part) {  // key list
-          const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
-          const float v = __uint_as_float(uint32_t(ent >> 32));
-          const int tok = int(~uint32_t(ent));
-          if (lane + 64 * part < n && uint32_t(ent) != 0u && tok != xs)  // entry lo 0 = none
-            key[i] = (uint64_t(ordered_key(v)) << 32) | uint32_t(ent);
+        for (int i = 0; i < kSel; ++i) {
+          constexpr int kParts = kSel / kWaves;
+          const int ww = i / kParts, part = i % kParts;
+          const int n = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
+          key[i] = 0;
+          if (n < 0 && 4 * part < -n) {  // uniform: some slot of this quarter holds a dump
+            const uint32_t th = uint32_t(__builtin_amdgcn_readfirstlane(sh.thr[r][ww])) >> 16;
+            const int sl = (lane >> 4) + 4 * part;
+            const int slc = min(sl, kHot - 1);
+            const uint32_t raw = reinterpret_cast<const uint16_t*>(&sh.reg[r][ww][0])[slc * kE + e];
+            const uint32_t ok16 = (raw & 0x8000u) ? (~raw & 0xFFFFu) : (raw | 0x8000u);
+            const uint32_t tl = uint32_t(ww * LY::WTOK + sh.hl[r][ww][slc] * LY::VEC + LY::tok(0, e));
+            // th is above the key of -inf; the sampled token is never a guess
+            const bool ok = (sl < -n) & (ok16 >= th) & (int(tl) < V - c0) & (tl != xs_l);
+            key[i] = ok ? (ok16 << 16) | (0xFFFFu - tl) : 0u;
+          } else if (n > 64 * part) {  // key list (its tokens lie in this tile)
+            const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
+            const uint32_t tl = uint32_t(int(~uint32_t(ent)) - c0);
+            const uint32_t ok16 = ordered_key(__uint_as_float(uint32_t(ent >> 32))) >> 16;
+            if (lane + 64 * part < n && uint32_t(ent) != 0u && tl != xs_l)  // entry lo 0 = none
+              key[i] = (ok16 << 16) | (0xFFFFu - tl);
+          }
         }
-      }
-      if (r == 0) TRACE(24);
-      // the nonzero keys (a few per wave region) into one list, one per lane: the F rounds then
-      // take a single key per lane (more than 64: rounds over all of them)
-      uint64_t* lst = sh.spare[w];
-      int N = 0;
+        // the nonzero keys into one list, one per lane, then F rounds of a wave maximum
+        uint32_t* lst = reinterpret_cast<uint32_t*>(sh.spare[w]);
+        int N = 0;
 #pragma unroll
-      for (int i = 0; i < kSel; ++i) {
-        const uint64_t m = __ballot(key[i] != 0ull);
-        if (m) {
-          const int at = N + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
-          if (key[i] != 0ull && at < 64) lst[at] = key[i];
-          N += __popcll(m);
+        for (int i = 0; i < kSel; ++i) {
+          const uint64_t m = __ballot(key[i] != 0u);
+          if (m) {
+            const int at = N + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+            if (key[i] != 0u && at < 128) lst[at] = key[i];
+            N += __popcll(m);
+          }
         }
-      }
-      if (N <= 64) {
-        uint64_t mine = (lane < N) ? lst[lane] : 0ull;
+        uint32_t k0 = (lane < N) ? lst[lane] : 0u, k1 = (lane + 64 < N) ? lst[lane + 64] : 0u;
         for (int f = 0; f < F; ++f) {
-          const uint64_t win = wave_max_u64(mine);
-          if (lane == 0) sh.best[r][f] = win;
-          mine = (mine == win) ? 0ull : mine;  // keys are unique: only the winner is cleared
+          uint32_t win;
+          if (N <= 128) {
+            win = wave_max_u32(max(k0, k1));
+          } else {  // more than 128 survivors: rounds over all the keys
+            uint32_t mine = key[0];
+#pragma unroll
+            for (int i = 1; i < kSel; ++i) mine = max(mine, key[i]);
+            win = wave_max_u32(mine);
+#pragma unroll
+            for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0u : key[i];
+          }
+          k0 = (k0 == win) ? 0u : k0;  // keys are unique: only the winner is cleared
+          k1 = (k1 == win) ? 0u : k1;
+          if (lane == 0) {  // back to the 64-bit (order key of the float, ~token) form
+            const uint32_t h = win >> 16;
+            const uint32_t okf = (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
+            sh.best[r][f] = win ? (uint64_t(okf) << 32) | uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
+                                : 0ull;
+          }
         }
       } else {
-        for (int f = 0; f < F; ++f) {
-          uint64_t mine = key[0];
+        const int F = sh.F[r];
+        const int xs = sh.xe[r];
+        const int e = lane & 15;
+        uint64_t key[kSel];
 #pragma unroll
-          for (int i = 1; i < kSel; ++i) mine = max_u64(mine, key[i]);
-          const uint64_t win = wave_max_u64(mine);
-          if (lane == 0) sh.best[r][f] = win;
+        for (int i = 0; i < kSel; ++i) {
+          constexpr int kParts = kSel / kWaves;
+          const int ww = i / kParts, part = i % kParts;
+          const int n = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
+          key[i] = 0;
+          if (n < 0 && 4 * part < -n) {  // uniform: some slot of this quarter holds a dump
+            const uint32_t th = __builtin_amdgcn_readfirstlane(sh.thr[r][ww]);
+            const int sl = (lane >> 4) + 4 * part;
+            const int slc = min(sl, kHot - 1);
+            const float v = ET::one(reinterpret_cast<const T*>(&sh.reg[r][ww][0]) + slc * kE, e);
+            const int tok = c0 + ww * LY::WTOK + sh.hl[r][ww][slc] * LY::VEC + LY::tok(0, e);
+            const uint32_t kv = ordered_key(v);
+            // th is above the key of -inf; the sampled token is never a guess
+            const bool ok = (sl < -n) & (kv >= th) & (tok < V) & (tok != xs);
+            key[i] = ok ? (uint64_t(kv) << 32) | uint64_t(~uint32_t(tok)) : 0ull;
+          } else if (n > 64 * part) {  // key list
+            const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
+            const float v = __uint_as_float(uint32_t(ent >> 32));
+            const int tok = int(~uint32_t(ent));
+            if (lane + 64 * part < n && uint32_t(ent) != 0u && tok != xs)  // entry lo 0 = none
+              key[i] = (uint64_t(ordered_key(v)) << 32) | uint32_t(ent);
+          }
+        }
+        if (r == 0) TRACE(24);
+        // the nonzero keys (a few per wave region) into one list, one per lane: the F rounds then
+        // take a single key per lane (more than 64: rounds over all of them)
+        uint64_t* lst = sh.spare[w];
+        int N = 0;
 #pragma unroll
-          for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
+        for (int i = 0; i < kSel; ++i) {
+          const uint64_t m = __ballot(key[i] != 0ull);
+          if (m) {
+            const int at = N + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+            if (key[i] != 0ull && at < 64) lst[at] = key[i];
+            N += __popcll(m);
+          }
+        }
+        if (N <= 64) {
+          uint64_t mine = (lane < N) ? lst[lane] : 0ull;
+          for (int f = 0; f < F; ++f) {
+            const uint64_t win = wave_max_u64(mine);
+            if (lane == 0) sh.best[r][f] = win;
+            mine = (mine == win) ? 0ull : mine;  // keys are unique: only the winner is cleared
+          }
+        } else {
+          for (int f = 0; f < F; ++f) {
+            uint64_t mine = key[0];
+#pragma unroll
+            for (int i = 1; i < kSel; ++i) mine = max_u64(mine, key[i]);
+            const uint64_t win = wave_max_u64(mine);
+            if (lane == 0) sh.best[r][f] = win;
+#pragma unroll
+            for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
+          }
         }
       }
     }
