@@ -238,7 +238,6 @@ struct Shared {
   int hl[kMaxK][kWaves][8];
   uint32_t thr[kMaxK][kWaves];  // the dump's threshold key: smaller tokens are no candidates
   uint32_t fb[kWaves];  // draft rows the wave filters again after phase 1 (bit r)
-  uint64_t best[kMaxK][kMaxF];
   uint64_t spare[kWaves][64];  // where the compaction's failing tokens are written
   int leader;
   // decision (last tile to arrive)
@@ -482,17 +481,11 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
           const float m = row_stats(z, g0 + j);
           mk[j] = (m > -INFINITY) ? ordered_key(m) : 0u;
         }
-        if (j == 0 && g0 == 0) TRACE(8);
-        if (j == 5 && g0 == 0) TRACE(22);
         // after every fourth row (and the group's last), the draft rows among the last four
         constexpr int kB = 4;
         if (FM > 0 && ((j % kB) == kB - 1 || j == G - 1)) {
           const int jb = j - (j % kB);
-          if (g0 + jb < K) {
-            if (g0 == 0 && jb == 0) TRACE(20);
-            draft_batch(raw + jb, mk + jb, g0 + jb, j - jb + 1);
-            if (g0 == 0 && jb == 0) TRACE(21);
-          }
+          if (g0 + jb < K) draft_batch(raw + jb, mk + jb, g0 + jb, j - jb + 1);
         }
       }
     }
@@ -584,91 +577,89 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     }
     if (lane == 0) sh.nseg[r][w] = total;
   };
+  // the tile's guess f of draft row r as two words tagged with the call (high, low half of the key)
+  auto publish_guess = [&](int r, int f, uint64_t kv) __attribute__((always_inline)) {
+    uint64_t* cw = a.cand + (((int64_t(b) * K + r) * nT + tile) * a.topfFmax + f) * 2;
+    st_agent(cw, tagged(tag, uint32_t(kv >> 32)));
+    st_agent(cw + 1, tagged(tag, uint32_t(kv)));
+  };
   auto topf_tile = [&]() __attribute__((always_inline)) {
-    TRACEV(23, 1000000000ull + (sh.fb[0] | sh.fb[1] | sh.fb[2] | sh.fb[3]));
-    uint32_t fbm = __builtin_amdgcn_readfirstlane(sh.fb[w]);
-    while (fbm) {  // rows the hot-lane copy could not take: re-read from cache
-      const int r = __builtin_ctz(fbm);
-      fbm &= fbm - 1u;
-      float z[kE];
-      row_fetch<ET>(row_ptr(r), bl, V, mode, z);
-      row_filter(z, r);
+    // rows the hot-lane copy could not take: re-read from cache and filtered into the regions
+    if ((sh.fb[0] | sh.fb[1] | sh.fb[2] | sh.fb[3]) != 0u) {
+      uint32_t fbm = __builtin_amdgcn_readfirstlane(sh.fb[w]);
+      while (fbm) {
+        const int r = __builtin_ctz(fbm);
+        fbm &= fbm - 1u;
+        float z[kE];
+        row_fetch<ET>(row_ptr(r), bl, V, mode, z);
+        row_filter(z, r);
+      }
+      __syncthreads();
     }
-    TRACE(16);
-    __syncthreads();
-    TRACE(17);
-    // wave w selects the F best candidates (value desc, index asc) of rows w, w + 4, ...
-    if (w == 0) TRACE(26);
-    // Candidate round i reads the region of wave i / 2: a dump gives lane l element l % 16 of slot
-    // l / 16 + 4 (i % 2); a key list (rows filtered after phase 1) gives lane l its entry l.
+    // Wave w selects the F best candidates (value desc, index asc) of rows w, w + 4, ... and
+    // publishes them itself. Candidate round i reads the region of wave i / 2: a dump gives lane
+    // l element l % 16 of slot l / 16 + 4 (i % 2); a key list (rows filtered after phase 1) gives
+    // lane l its entry l + 64 (i % 2).
     for (int r = w; r < K; r += kWaves) {
+      const int F = sh.F[r];
       if constexpr (sizeof(T) == 2) {
         // bf16: 32-bit keys, the value's 16-bit order key above 0xFFFF - (token - c0), so a larger
-        // key is a larger value, then a smaller token; 0 = none (every real key is above 2^23)
-        const int F = sh.F[r];
+        // key is a larger value, then a smaller token; 0 = none (every real key is above 2^23).
+        // Every read is issued first (clamped, in bounds), then the keys are formed.
         const uint32_t xs_l = uint32_t(sh.xe[r] - c0);  // the sampled token, relative to the tile
         const int e = lane & 15;
+        int n[kWaves];
+        uint32_t th[kWaves];
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          n[ww] = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
+          th[ww] = uint32_t(__builtin_amdgcn_readfirstlane(sh.thr[r][ww])) >> 16;
+        }
+        constexpr int kParts = kSel / kWaves;
+        uint32_t rawv[kSel];
+        int hlv[kSel];
+#pragma unroll
+        for (int i = 0; i < kSel; ++i) {
+          const int ww = i / kParts, slc = min((lane >> 4) + 4 * (i % kParts), kHot - 1);
+          rawv[i] = reinterpret_cast<const uint16_t*>(&sh.reg[r][ww][0])[slc * kE + e];
+          hlv[i] = sh.hl[r][ww][slc];
+        }
         uint32_t key[kSel];
 #pragma unroll
         for (int i = 0; i < kSel; ++i) {
-          constexpr int kParts = kSel / kWaves;
           const int ww = i / kParts, part = i % kParts;
-          const int n = __builtin_amdgcn_readfirstlane(sh.nseg[r][ww]);
-          key[i] = 0;
-          if (n < 0 && 4 * part < -n) {  // uniform: some slot of this quarter holds a dump
-            const uint32_t th = uint32_t(__builtin_amdgcn_readfirstlane(sh.thr[r][ww])) >> 16;
-            const int sl = (lane >> 4) + 4 * part;
-            const int slc = min(sl, kHot - 1);
-            const uint32_t raw = reinterpret_cast<const uint16_t*>(&sh.reg[r][ww][0])[slc * kE + e];
-            const uint32_t ok16 = (raw & 0x8000u) ? (~raw & 0xFFFFu) : (raw | 0x8000u);
-            const uint32_t tl = uint32_t(ww * LY::WTOK + sh.hl[r][ww][slc] * LY::VEC + LY::tok(0, e));
-            // th is above the key of -inf; the sampled token is never a guess
-            const bool ok = (sl < -n) & (ok16 >= th) & (int(tl) < V - c0) & (tl != xs_l);
-            key[i] = ok ? (ok16 << 16) | (0xFFFFu - tl) : 0u;
-          } else if (n > 64 * part) {  // key list (its tokens lie in this tile)
+          const int sl = (lane >> 4) + 4 * part;
+          const uint32_t raw = rawv[i];
+          const uint32_t ok16 = (raw & 0x8000u) ? (~raw & 0xFFFFu) : (raw | 0x8000u);
+          const uint32_t tl = uint32_t(ww * LY::WTOK + hlv[i] * LY::VEC + LY::tok(0, e));
+          // th is above the key of -inf; the sampled token is never a guess
+          const bool ok = (sl < -n[ww]) & (ok16 >= th[ww]) & (int(tl) < V - c0) & (tl != xs_l);
+          key[i] = ok ? (ok16 << 16) | (0xFFFFu - tl) : 0u;
+          if (n[ww] > 64 * part) {  // uniform: a key list (its tokens lie in this tile)
             const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
-            const uint32_t tl = uint32_t(int(~uint32_t(ent)) - c0);
-            const uint32_t ok16 = ordered_key(__uint_as_float(uint32_t(ent >> 32))) >> 16;
-            if (lane + 64 * part < n && uint32_t(ent) != 0u && tl != xs_l)  // entry lo 0 = none
-              key[i] = (ok16 << 16) | (0xFFFFu - tl);
+            const uint32_t tk = uint32_t(int(~uint32_t(ent)) - c0);
+            const uint32_t o16 = ordered_key(__uint_as_float(uint32_t(ent >> 32))) >> 16;
+            key[i] = (lane + 64 * part < n[ww] && uint32_t(ent) != 0u && tk != xs_l)  // lo 0 = none
+                         ? (o16 << 16) | (0xFFFFu - tk)
+                         : 0u;
           }
         }
-        // the nonzero keys into one list, one per lane, then F rounds of a wave maximum
-        uint32_t* lst = reinterpret_cast<uint32_t*>(sh.spare[w]);
-        int N = 0;
-#pragma unroll
-        for (int i = 0; i < kSel; ++i) {
-          const uint64_t m = __ballot(key[i] != 0u);
-          if (m) {
-            const int at = N + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
-            if (key[i] != 0u && at < 128) lst[at] = key[i];
-            N += __popcll(m);
-          }
-        }
-        uint32_t k0 = (lane < N) ? lst[lane] : 0u, k1 = (lane + 64 < N) ? lst[lane + 64] : 0u;
         for (int f = 0; f < F; ++f) {
-          uint32_t win;
-          if (N <= 128) {
-            win = wave_max_u32(max(k0, k1));
-          } else {  // more than 128 survivors: rounds over all the keys
-            uint32_t mine = key[0];
+          uint32_t mine = key[0];
 #pragma unroll
-            for (int i = 1; i < kSel; ++i) mine = max(mine, key[i]);
-            win = wave_max_u32(mine);
+          for (int i = 1; i < kSel; ++i) mine = max(mine, key[i]);
+          const uint32_t win = wave_max_u32(mine);
 #pragma unroll
-            for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0u : key[i];
-          }
-          k0 = (k0 == win) ? 0u : k0;  // keys are unique: only the winner is cleared
-          k1 = (k1 == win) ? 0u : k1;
+          for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0u : key[i];  // keys are unique
           if (lane == 0) {  // back to the 64-bit (order key of the float, ~token) form
             const uint32_t h = win >> 16;
             const uint32_t okf = (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
-            sh.best[r][f] = win ? (uint64_t(okf) << 32) | uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
-                                : 0ull;
+            publish_guess(r, f, win ? (uint64_t(okf) << 32) |
+                                         uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
+                                    : 0ull);
           }
         }
       } else {
-        const int F = sh.F[r];
         const int xs = sh.xe[r];
         const int e = lane & 15;
         uint64_t key[kSel];
@@ -696,7 +687,6 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
               key[i] = (uint64_t(ordered_key(v)) << 32) | uint32_t(ent);
           }
         }
-        if (r == 0) TRACE(24);
         // the nonzero keys (a few per wave region) into one list, one per lane: the F rounds then
         // take a single key per lane (more than 64: rounds over all of them)
         uint64_t* lst = sh.spare[w];
@@ -714,7 +704,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
           uint64_t mine = (lane < N) ? lst[lane] : 0ull;
           for (int f = 0; f < F; ++f) {
             const uint64_t win = wave_max_u64(mine);
-            if (lane == 0) sh.best[r][f] = win;
+            if (lane == 0) publish_guess(r, f, win);
             mine = (mine == win) ? 0ull : mine;  // keys are unique: only the winner is cleared
           }
         } else {
@@ -723,28 +713,14 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
 #pragma unroll
             for (int i = 1; i < kSel; ++i) mine = max_u64(mine, key[i]);
             const uint64_t win = wave_max_u64(mine);
-            if (lane == 0) sh.best[r][f] = win;
+            if (lane == 0) publish_guess(r, f, win);
 #pragma unroll
             for (int i = 0; i < kSel; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
           }
         }
       }
     }
-    TRACE(18);
-    __syncthreads();
-    TRACE(19);
-    // the tile's guesses: two words per key (high and low half), each tagged with the call
-    if (t < K * a.topfFmax) {
-      const int r = t / a.topfFmax, f = t - r * a.topfFmax;
-      if (f < sh.F[r]) {
-        uint64_t* cw = a.cand + (((int64_t(b) * K + r) * nT + tile) * a.topfFmax + f) * 2;
-        const uint64_t kv = sh.best[r][f];
-        st_agent(cw, tagged(tag, uint32_t(kv >> 32)));
-        st_agent(cw + 1, tagged(tag, uint32_t(kv)));
-      }
-    }
-    };
-  TRACE(10);
+  };
 
   // ---- claim the decision: the first tile past phase 1 swaps the lead word from the last call's
   // tag to this call's. It has the most time to spare before the last statistics arrive, so its
@@ -837,7 +813,6 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
         sh.zs[t] = zs_v;
       }
       __syncthreads();
-      TRACE(12);
       if (t < 64) {  // wave 0: lane i takes the accept test of position i
         const float C = a.C;
         const int i = min(lane, K - 1);
@@ -933,7 +908,6 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
     }
     TRACE(2);
     __syncthreads();
-    TRACE(3);
     const int k = min(max(sh.k, 0), K);
     const bool resid = k < K;
     const T* prow = target + int64_t(k) * V;
