@@ -193,6 +193,12 @@ __device__ __forceinline__ uint32_t quad_max_u(uint32_t v) {
   v = max(v, dpp_u<kDppXor1>(v));
   return max(v, dpp_u<kDppXor2>(v));
 }
+__device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  return max(v, dpp_u<kDppMirror>(v));
+}
 __device__ __forceinline__ uint32_t row16_min_u(uint32_t v) {
   v = min(v, dpp_u<kDppXor1>(v));
   v = min(v, dpp_u<kDppXor2>(v));

@@ -364,28 +364,28 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
   TRACE(0);
   // max and sum 2^(z c - max) of one row over the lane's tokens, merged over 16-lane groups;
   // returns the lane's maximum
-  auto row_stats = [&](const float (&z)[kE], int r) __attribute__((always_inline)) -> float {
+  // Returns the order key of the lane's maximum (0: no finite token).
+  auto row_stats = [&](const float (&z)[kE], int r) __attribute__((always_inline)) -> uint32_t {
     float m = z[0];
 #pragma unroll
     for (int q = 1; q < kE; ++q) m = fmaxf(m, z[q]);
-    float s = 0.f;
     const float mc = m * cc;
-    if (m > -INFINITY) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    float s0 = ex2(fmaf(z[0], cc, -mc)), s1 = ex2(fmaf(z[1], cc, -mc));
+    float s2 = ex2(fmaf(z[2], cc, -mc)), s3 = ex2(fmaf(z[3], cc, -mc));
 #pragma unroll
-      for (int q = 0; q < kE; q += 4) {
-        s0 += ex2(fmaf(z[q], cc, -mc));
-        s1 += ex2(fmaf(z[q + 1], cc, -mc));
-        s2 += ex2(fmaf(z[q + 2], cc, -mc));
-        s3 += ex2(fmaf(z[q + 3], cc, -mc));
-      }
-      s = (s0 + s1) + (s2 + s3);
+    for (int q = 4; q < kE; q += 4) {
+      s0 += ex2(fmaf(z[q], cc, -mc));
+      s1 += ex2(fmaf(z[q + 1], cc, -mc));
+      s2 += ex2(fmaf(z[q + 2], cc, -mc));
+      s3 += ex2(fmaf(z[q + 3], cc, -mc));
     }
-    const float M = row16_max(m);
-    const float Mc = M * cc;
-    const float S = row16_sum((s > 0.f) ? s * ex2(mc - Mc) : 0.f);
+    const bool fin = m > -INFINITY;  // a lane with no finite token adds nothing (its terms are NaN)
+    const uint32_t mk = fin ? ordered_key(m) : 0u;
+    const uint32_t Mk = row16_max_u(mk);  // the row's maximum through its order key
+    const float Mc = (Mk ? key_to_float(Mk) : -INFINITY) * cc;
+    const float S = row16_sum(fin ? ((s0 + s1) + (s2 + s3)) * ex2(mc - Mc) : 0.f);
     if ((t & 15) == 0) sh.g16[r][grp] = make_float2(Mc, S);
-    return m;
+    return mk;
   };
   // The Fp-th largest lane maximum of the wave, tied lanes counted: take the largest remaining
   // maximum and every lane that holds it until Fp lanes are taken. n = lanes taken; n < Fp when
@@ -477,10 +477,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
         row_unpack<ET>(raw[j], z);
         if (mode == 1) mask_tail<ET>(z, bl, V);
         mk[j] = 0u;
-        if (g0 + j < R2) {
-          const float m = row_stats(z, g0 + j);
-          mk[j] = (m > -INFINITY) ? ordered_key(m) : 0u;
-        }
+        if (g0 + j < R2) mk[j] = row_stats(z, g0 + j);
         // after every fourth row (and the group's last), the draft rows among the last four
         constexpr int kB = 4;
         if (FM > 0 && ((j % kB) == kB - 1 || j == G - 1)) {
