@@ -852,34 +852,31 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
         const uint64_t rej = __ballot(lane < K && !accept);
         const int k = rej ? __builtin_ctzll(rej) : K;  // first rejection
         const float Nk = (k < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), k)) : 1.f;
+        // the record, straight from registers: lane j publishes word j (the set of row k keeps
+        // its -1 holes: duplicates and out-of-range entries, which the residual skips)
+        const int nset = (k < K) ? sF : 0;
+        const float Lpk = sh.L[K + k], Lqk = (k < K) ? sh.L[k] : 0.f;
+        const int f = lane - kDecSet;
+        const int sv = (f >= 0 && f < nset) ? sh.set[k * sF + f] : -1;
+        uint32_t v = uint32_t(sv);
+        if (lane == kDecK) v = uint32_t(k);
+        if (lane == kDecLp) v = __float_as_uint(Lpk);
+        if (lane == kDecLq) v = __float_as_uint(Lqk);
+        if (lane == kDecWout) v = __float_as_uint(1.f / Nk);
+        if (lane == kDecWin) v = __float_as_uint(C / Nk);
+        if (lane == kDecNset) v = uint32_t(nset);
+        if (lane < kDecWords) st_agent(dec + lane, tagged(tag, v));
+        // this tile's own copy, for its residual
         if (lane == 0) {
           a.k_out[b] = k;
-          int n = 0;
-          if (k < K)
-            for (int f = 0; f < sF; ++f) {
-              const int sv = sh.set[k * sF + f];
-              if (sv >= 0) sh.myset[n++] = sv;
-            }
-          for (int f = n; f < kMaxF; ++f) sh.myset[f] = -1;
           sh.k = k;
-          sh.nset = n;
-          sh.Lp = sh.L[K + k];
-          sh.Lq = (k < K) ? sh.L[k] : 0.f;
+          sh.nset = nset;
+          sh.Lp = Lpk;
+          sh.Lq = Lqk;
           sh.w_out = 1.f / Nk;
           sh.w_in = C / Nk;
         }
-      }
-      __syncthreads();
-      if (t < kDecWords) {  // publish the record, one tagged word per thread
-        uint32_t v;
-        if (t == kDecK) v = uint32_t(sh.k);
-        else if (t == kDecLp) v = __float_as_uint(sh.Lp);
-        else if (t == kDecLq) v = __float_as_uint(sh.Lq);
-        else if (t == kDecWout) v = __float_as_uint(sh.w_out);
-        else if (t == kDecWin) v = __float_as_uint(sh.w_in);
-        else if (t == kDecNset) v = uint32_t(sh.nset);
-        else v = uint32_t(sh.myset[t - kDecSet]);
-        st_agent(dec + t, tagged(tag, v));
+        if (f >= 0 && f < kMaxF) sh.myset[f] = sv;
       }
       TRACE(13);
     } else if (t < 64) {
