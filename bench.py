@@ -4,6 +4,7 @@
     python bench.py ... --copy-calibration      (also runs a plain device copy of known size)
     python bench.py --traffic-from FETCH.csv WRITE.csv   (no GPU: turns two rocprofv3 --pmc
                                                           counter files into profiles/traffic_*.json)
+    python bench.py --workload ssd_build_b16x12_k4_v128256_bf16   (an SSD round: every stage of it)
 
 A step is one verification round over one batch: every draft and target logit row of the batch
 is streamed once (temperature softmax statistics, fused top-F guesses), the accept decisions and
@@ -158,6 +159,156 @@ def summarize_traffic(fetch_csv, write_csv, workload):
     print(json.dumps(d))
 
 
+class _Stage:
+    def __init__(self, name, nbytes, fn):
+        self.name, self.nbytes, self.fn = name, nbytes, fn
+
+
+def pipeline_bench(args, spec):
+    """One SSD round per step (the cache build and the full round): verification with Saguaro sets
+    and per-position top-F guesses, the guesses of draft row K, cache keys, lookup of the outcome,
+    and, for the speculation-cache branches, their top-F sets and Saguaro adjustment. Each stage
+    is timed on the GPU with an event pair per step; its algorithmic bytes (every logit it reads,
+    once, plus its small inputs and outputs) over that time give its bandwidth."""
+    import numpy as np
+    import torch
+
+    import draft_verification_ssd_amd as ssd
+    import synth
+
+    B, K, V, dtype, T = spec["B"], spec["K"], spec["V"], spec["dtype"], spec["T"]
+    es = 2 if dtype == "bf16" else 4
+    fan, _ = ssd.ssd_fanout_alloc(K, spec["a"], spec["r"], spec["budget"])
+    budget, Gm = sum(fan), max(fan)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    bt = synth.make_verify_batch(B, K, V, dtype, args.seed, T=T, sag_sizes=fan[:K], C=spec["C"])
+    branch = synth.make_branch_rows(B, budget, K, V, dtype, args.seed)
+    Rb = B * budget * K  # branch rows
+
+    def lg(a):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    b_verify = (2 * K + 1) * B * V * es + B * K * 4 + B * (K + 1) * 4 + B * K * Gm * 4 + 2 * B * 4 + B * K * Gm * 4
+    b_rowk = B * V * es + B * fan[K] * 4
+    b_bsets = Rb * V * es + Rb * 4 + Rb * Gm * 4
+    b_sag = Rb * V * es + Rb * Gm * 4 + 2 * Rb * 4
+    b_keys = B * (K + 1) * Gm * 4 + 2 * B * budget * 4
+    b_lookup = 2 * B * budget * 4 + 2 * B * 4 + B * 4 + 4
+    total_logit_bytes = ((2 * K + 2) * B + Rb) * V * es
+    n_rep = max(1, math.ceil(ROTATE_BYTES / total_logit_bytes))
+
+    reps = []
+    ws_v = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, Gm), dev)
+    ws_k = ssd.Workspace(ssd.ssd_topf_workspace_bytes(B, V, fan[K]), dev)
+    ws_b = ssd.Workspace(ssd.ssd_topf_workspace_bytes(Rb, V, Gm), dev)
+    ws_s = ssd.Workspace(ssd.ssd_saguaro_workspace_bytes(Rb, V), dev)
+    Fr = torch.tensor(fan[:K], dtype=torch.int32, device=dev).repeat(B * budget)
+    for _ in range(n_rep):
+        r = {}
+        r["draft"] = lg(bt.draft)                      # [B, K+1, V]
+        r["target"] = lg(bt.target)
+        r["bd"] = lg(branch).view(Rb, V)
+        r["topf"] = torch.empty((B, K, Gm), dtype=torch.int32, device=dev)
+        r["guesses"] = torch.full((B, K + 1, Gm), -1, dtype=torch.int32, device=dev)
+        r["gk"] = torch.empty((B, fan[K]), dtype=torch.int32, device=dev)
+        r["bsets"] = torch.empty((Rb, Gm), dtype=torch.int32, device=dev)
+        r["sig"] = torch.empty(Rb, dtype=torch.float32, device=dev)
+        r["N"] = torch.empty(Rb, dtype=torch.float32, device=dev)
+        r["ck"] = torch.empty((B, budget), dtype=torch.int32, device=dev)
+        r["ct"] = torch.empty((B, budget), dtype=torch.int32, device=dev)
+        r["slot"] = torch.empty(B, dtype=torch.int32, device=dev)
+        r["miss"] = torch.empty(1, dtype=torch.int32, device=dev)
+        r["verify"] = ssd.VerifyCall(r["draft"], r["target"], torch.from_numpy(bt.x).to(dev),
+                                     torch.from_numpy(bt.u).to(dev), T,
+                                     sag_set=torch.from_numpy(bt.sets).to(dev), sag_C=bt.C, topf_F=fan[:K],
+                                     topf_F_max=Gm, topf_out=r["topf"], workspace=ws_v)
+        reps.append(r)
+
+    def stages(r):
+        out = r["verify"].outputs
+
+        def keys():
+            r["guesses"][:, :K].copy_(r["topf"])
+            r["guesses"][:, K, : fan[K]].copy_(r["gk"])
+            ssd.ssd_cache_keys(r["guesses"], fan, cache_k=r["ck"], cache_tok=r["ct"])
+
+        return [
+            _Stage("verify (ssd_verify, fused top-F and Saguaro)", b_verify, r["verify"]),
+            _Stage("row-K guesses (ssd_topf_guess)", b_rowk,
+                   lambda: ssd.ssd_topf_guess(r["draft"][:, K, :], fan[K], out=r["gk"], workspace=ws_k)),
+            _Stage("cache keys (ssd_cache_keys)", b_keys, keys),
+            _Stage("lookup (ssd_cache_lookup)", b_lookup,
+                   lambda: ssd.ssd_cache_lookup(r["ck"], r["ct"], out["accepted_len"], out["bonus_token"],
+                                                out_slot=r["slot"], out_miss_count=r["miss"])),
+            _Stage("branch sets (ssd_topf_guess)", b_bsets,
+                   lambda: ssd.ssd_topf_guess(r["bd"], Gm, F_per_row=Fr, out=r["bsets"], workspace=ws_b)),
+            _Stage("branch Saguaro (ssd_saguaro_adjust)", b_sag,
+                   lambda: ssd.ssd_saguaro_adjust(r["bd"], T, r["bsets"], bt.C, out_set_mass=r["sig"],
+                                                  out_norm=r["N"], workspace=ws_s)),
+        ]
+
+    plans = [stages(r) for r in reps]
+    for i in range(args.warmup):
+        for st in plans[i % n_rep]:
+            st.fn()
+    torch.cuda.synchronize()
+    nst = len(plans[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        for j, st in enumerate(plans[i % n_rep]):
+            st.fn()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = [float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j in range(nst)]
+    step_ms = float(np.median([ev[i][0].elapsed_time(ev[i][nst]) for i in range(args.steps)]))
+    flags = ssd.ssd_read_flags(ws_v) | ssd.ssd_read_flags(ws_k) | ssd.ssd_read_flags(ws_b) | ssd.ssd_read_flags(ws_s)
+    if flags:
+        print(f"device flags {flags:#x}", file=sys.stderr)
+        sys.exit(3)
+    rows = (2 * K + 2) * B + Rb
+    algo = b_verify + b_rowk + b_keys + b_lookup + b_bsets + b_sag
+    miss = int(reps[0]["miss"].item())
+    st_out = {}
+    for st, ms in zip(plans[0], stage_ms):
+        st_out[st.name] = {"ms": round(ms, 5), "algorithmic_bytes": st.nbytes,
+                           "GB/s": round(st.nbytes / (ms * 1e-3) / 1e9, 1)}
+    dom = max(range(nst), key=lambda j: stage_ms[j])
+    line = {
+        "metric": METRIC,
+        "value": round(rows / (step_ms * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "K": K, "V": V, "T": T, "fanout": fan,
+                   "C": spec["C"], "branch_rows": Rb, "rows_per_step": rows,
+                   "algorithmic_bytes_per_step": algo, "input_replicas": n_rep},
+        "roofline": {"bound": "hbm", "achieved": st_out[plans[0][dom].name]["GB/s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(st_out[plans[0][dom].name]["GB/s"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": plans[0][dom].name,
+                     "note": "median stage time per step from HIP event pairs on the launch stream"},
+        "stages": st_out,
+        "step_GB/s": round(algo / (step_ms * 1e-3) / 1e9, 1),
+        "cache": {"misses": miss, "hits": B - miss, "path": "zero-wait" if miss == 0 else "fallback"},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -174,6 +325,9 @@ def main():
     import synth
 
     spec = synth.workload(args.workload)
+    if "budget" in spec:  # an SSD round (cache build, full round)
+        pipeline_bench(args, spec)
+        return
     B, K, V, dtype = spec["B"], spec["K"], spec["V"], spec["dtype"]
     topf = spec.get("topf", 0)
     esize = 2 if dtype == "bf16" else 4

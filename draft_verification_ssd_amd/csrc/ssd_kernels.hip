@@ -154,20 +154,127 @@ __device__ void merge_lists(const Cand* __restrict__ cands, int n_lists, int str
 // =============================================================================================
 // Standalone top-F guesses
 // =============================================================================================
+// Each wave keeps a lower bound tau of the F-th best (value desc, index asc) among the tokens it
+// has read, and a buffer of candidate keys (ordered value key << 32 | ~index; larger is better)
+// in LDS. A batch of 32 tokens per lane whose lane maxima all fall below tau is skipped after one
+// ballot; otherwise its tokens at or above tau are appended, and a buffer past kTReduce keys is
+// cut to its top F, whose F-th key raises tau. The first batch sets tau to the (F+1)-th largest
+// lane maximum: F + 1 tokens of distinct lanes reach it, so F of them are not the excluded one.
+constexpr int kTBuf = 256;     // candidate keys per wave
+constexpr int kTReduce = 128;  // cut the buffer to its top F beyond this many keys
+constexpr int kTBatch = 32;    // tokens per lane per batch
+
+__device__ __forceinline__ uint64_t cand_key64(float v, int idx) {
+  return (uint64_t(ordered_key(v)) << 32) | uint64_t(~uint32_t(idx));
+}
+
+// The top F of the n keys in buf (keys unique), in order, to buf[0 .. m); returns m <= F.
+__device__ __forceinline__ int wave_cut_keys(uint64_t* buf, int n, int F) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kPer = kTBuf / 64;
+  uint64_t k[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) k[i] = (lane + 64 * i < n) ? buf[lane + 64 * i] : 0ull;
+  uint64_t mine_out = 0;
+  int m = 0;
+  for (int f = 0; f < F; ++f) {
+    uint64_t mine = k[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) mine = max_u64(mine, k[i]);
+    const uint64_t win = wave_max_u64(mine);
+    if (win == 0ull) break;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) k[i] = (k[i] == win) ? 0ull : k[i];
+    if (lane == f) mine_out = win;
+    ++m;
+  }
+  if (lane < m) buf[lane] = mine_out;
+  return m;
+}
+
+template <class ET>
+struct TopfWave {
+  uint64_t* buf;  // this wave's kTBuf keys
+  int n;          // keys in buf (wave-uniform)
+  float tau;      // lower bound of the F-th best so far (wave-uniform); -inf: none yet
+  int F, exclude;
+
+  // one batch: lane tokens z[0..NB) (-inf for a place past the chunk), token index of place e
+  // from idx_of(e) (evaluated only for batches that reach tau)
+  template <int NB, class Idx>
+  __device__ __forceinline__ void batch(const float (&z)[NB], Idx idx_of) {
+    const int lane = threadIdx.x & 63;
+    float bm = z[0];
+#pragma unroll
+    for (int e = 1; e < NB; ++e) bm = fmaxf(bm, z[e]);
+    if (tau == -INFINITY && n == 0) {  // first batch: tau from the lane maxima
+      const int Fp = F + 1;
+      float mm = bm, thr = -INFINITY;
+      int taken = 0;
+      for (int f = 0; f < Fp; ++f) {
+        const float cur = wave_max(mm);
+        if (!(cur > -INFINITY)) break;
+        thr = cur;
+        taken += __popcll(__ballot(mm == cur));
+        if (taken >= Fp) break;
+        mm = (mm == cur) ? -INFINITY : mm;
+      }
+      if (taken >= Fp) tau = thr;
+    }
+    if (__ballot(bm >= tau && bm > -INFINITY) == 0ull) return;  // nothing here reaches tau
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < NB; ++e) cnt += (z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude) ? 1 : 0;
+    const int incl = wave_incl_scan_i(cnt);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (n + total <= kTBuf) {
+      int pos = n + incl - cnt;
+#pragma unroll
+      for (int e = 0; e < NB; ++e)
+        if (z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude) buf[pos++] = cand_key64(z[e], idx_of(e));
+      n += total;
+    } else {
+      // too many to append at once (ties): one place of every lane at a time, cutting the buffer
+      // (and raising tau) whenever the next place would not fit
+      for (int e = 0; e < NB; ++e) {
+        bool c = z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude;
+        uint64_t m = __ballot(c);
+        if (m == 0ull) continue;
+        if (n + __popcll(m) > kTBuf) {
+          n = wave_cut_keys(buf, n, F);
+          if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
+          c = c && z[e] >= tau;
+          m = __ballot(c);
+        }
+        if (c) buf[n + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)))] =
+            cand_key64(z[e], idx_of(e));
+        n += __popcll(m);
+      }
+    }
+    if (n > kTReduce) {
+      n = wave_cut_keys(buf, n, F);
+      if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
+    }
+  }
+};
+
 template <class ET, int FM>
 __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   using T = typename ET::T;
-  __shared__ uint32_t shk[2 * kWaves];
-  __shared__ float wv[kMaxF];
-  __shared__ int wi[kMaxF];
+  constexpr int N = ET::kVec;
+  constexpr int U = kTBatch / N;  // vectors per lane per batch
+  __shared__ uint64_t sbuf[kWaves][kTBuf];
+  __shared__ uint64_t stop[kWaves][kMaxF];
+  __shared__ int sn[kWaves];
   const int item = blockIdx.x;
   const int row = item / a.n1;
   const int chunk = item - row * a.n1;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int F = a.Fmax;
   if (a.F_per_row) {
     F = a.F_per_row[row];
     if (F < 0 || F > a.Fmax) {
-      if (chunk == 0 && threadIdx.x == 0) atomicOr(a.flags, kFlagBadF);
+      if (chunk == 0 && t == 0) atomicOr(a.flags, kFlagBadF);
       F = F < 0 ? 0 : a.Fmax;
     }
   }
@@ -175,18 +282,75 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   const T* p = reinterpret_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
   const int c0 = chunk * a.chunk1;
   const int c1 = min(a.V, c0 + a.chunk1);
-  float mx = -INFINITY, s = 0.f;
-  TopList<FM> tl;
-  tl.init(F);
-  chunk_pass<ET, false, FM>(p, c0, c1, a.aligned != 0, 1.f, ex, mx, s, tl);
-  block_merge_top<FM>(tl, F, shk, wv, wi);
-  if (threadIdx.x == 0) {
+  TopfWave<ET> tw;
+  tw.buf = sbuf[w];
+  tw.n = 0;
+  tw.tau = -INFINITY;
+  tw.F = F;
+  tw.exclude = ex;
+  if (F > 0) {
+    int tail0 = c0;
+    if (a.aligned) {
+      // thread t reads vectors t, t + 256, ... of the chunk, U per batch
+      const uint4* rv = reinterpret_cast<const uint4*>(p);
+      const int v0 = c0 / N, v1 = v0 + (c1 - c0) / N;
+      tail0 = v1 * N;
+      auto load_batch = [&](int vb, uint4 (&raw)[U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int vi = vb + u * kThreads;
+          raw[u] = (vi < v1) ? load16(rv + vi)
+                             : make_uint4(ET::kNegInfWord, ET::kNegInfWord, ET::kNegInfWord, ET::kNegInfWord);
+        }
+      };
+      auto run_batch = [&](int vb, const uint4 (&raw)[U]) __attribute__((always_inline)) {
+        float z[kTBatch];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ET::unpack(raw[u], z + u * N);
+        tw.batch(z, [&](int e) { return (vb + (e / N) * kThreads) * N + (e % N); });
+      };
+      // two batches in flight: the next one loads while this one is examined (the trip count is
+      // the same for every lane)
+      constexpr int kStep = kThreads * U;
+      uint4 ra[U], rb[U];
+      int vb = v0 + t;
+      if (vb - t < v1) load_batch(vb, ra);
+      for (; vb - t < v1; vb += 2 * kStep) {
+        if (vb + kStep - t < v1) load_batch(vb + kStep, rb);
+        run_batch(vb, ra);
+        if (vb + kStep - t >= v1) break;
+        if (vb + 2 * kStep - t < v1) load_batch(vb + 2 * kStep, ra);
+        run_batch(vb + kStep, rb);
+      }
+    }
+    // elements after the last whole vector, or every element of an unaligned row, one per lane
+    for (int e0 = tail0; e0 < c1; e0 += kThreads) {
+      const int e = e0 + t;
+      float z[1];
+      z[0] = (e < c1) ? ET::one(p, e) : -INFINITY;
+      tw.batch(z, [&](int) { return e; });
+    }
+    tw.n = wave_cut_keys(tw.buf, tw.n, F);  // the wave's top F, in order
+  }
+  if (lane == 0) sn[w] = tw.n;
+  if (lane < kMaxF) stop[w][lane] = (lane < tw.n) ? tw.buf[lane] : 0ull;
+  __syncthreads();
+  if (w == 0) {  // the chunk's top F from the waves' lists
+    uint64_t k = 0ull;
+    if (F > 0 && lane < kWaves * F) k = stop[lane / F][lane % F];
+    uint64_t win_out = 0ull;
+    for (int f = 0; f < F; ++f) {
+      const uint64_t win = wave_max_u64(k);
+      k = (k == win) ? 0ull : k;
+      if (lane == f) win_out = win;
+    }
     if (a.n1 == 1) {
       int32_t* out = a.out + int64_t(row) * a.Fmax;
-      for (int r = 0; r < a.Fmax; ++r) out[r] = (r < F) ? wi[r] : -1;
-    } else {
+      for (int r = lane; r < a.Fmax; r += 64) out[r] = (r < F && win_out) ? int(~uint32_t(win_out)) : -1;
+    } else if (lane < F) {
       Cand* cd = reinterpret_cast<Cand*>(a.cand) + (int64_t(row) * a.n1 + chunk) * a.Fmax;
-      for (int r = 0; r < F; ++r) cd[r] = Cand{wv[r], wi[r]};
+      cd[lane] = win_out ? Cand{key_to_float(uint32_t(win_out >> 32)), int(~uint32_t(win_out))}
+                         : Cand{-INFINITY, -1};
     }
   }
 }

@@ -72,9 +72,22 @@ struct TopfLayout {
   size_t off_cand, total;
 };
 
+// Top-F chunks are longer than the statistics chunks: each wave's candidate search has a fixed
+// cost (its first threshold, the final cut, the merge of the chunks), so whole rows are kept
+// whenever the rows alone give the device a few workgroups per CU.
+constexpr int kTopfTargetGroups = 768;
+constexpr int kTopfMinChunk = 16384;
+
 inline TopfLayout topf_layout(int R, int V, int F_max) {
   TopfLayout L;
-  L.rp = plan_rows(R, V);
+  int64_t n1 = ceil_div(kTopfTargetGroups, R > 0 ? R : 1);
+  int64_t cap = ceil_div(V, kTopfMinChunk);
+  if (cap > kPlanMaxChunks) cap = kPlanMaxChunks;
+  if (n1 > cap) n1 = cap;
+  if (n1 < 1) n1 = 1;
+  const int64_t chunk = ceil_div(ceil_div(V, n1), 8) * 8;
+  L.rp.chunk1 = int(chunk);
+  L.rp.n1 = int(ceil_div(V, chunk));
   L.off_cand = kAlign;
   L.total = align_up(L.off_cand + size_t(R) * L.rp.n1 * F_max * 8);
   return L;
