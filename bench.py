@@ -110,6 +110,29 @@ def cpu_baseline(bt, topf, seconds):
                        f"float64 NumPy oracle verify + top-{topf} guesses, {el:.1f} s on 1 thread")
 
 
+def cpu_baseline_round(bt, branch, fan, seconds):
+    """The float64 oracle on a bounded sample of an SSD round (single thread): whole sequences,
+    each with its verification, guesses, keys, lookup and its branch rows' sets and Saguaro."""
+    import oracle as O
+
+    t0 = time.perf_counter()
+    seqs = 0
+    B, K = bt.B, bt.K
+    nbr = branch.shape[1]
+    while True:
+        b = seqs % B
+        O.ssd_round(bt.draft[b:b + 1], bt.target[b:b + 1], bt.dtype, bt.x[b:b + 1], bt.u[b:b + 1], bt.T,
+                    bt.sets[b:b + 1], bt.C, fan, branch=branch[b:b + 1])
+        seqs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    rows = seqs * ((2 * K + 2) + nbr * K)
+    return dict(value=rows / el, unit="rows/s", cores=1, kind="oracle",
+                sample=f"{seqs} whole sequences of the round (seed 0) with their {nbr} branches, {rows} logit "
+                       f"rows, float64 NumPy oracle, {el:.1f} s on 1 thread")
+
+
 def load_traffic(workload, khash):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -282,6 +305,7 @@ def pipeline_bench(args, spec):
         st_out[st.name] = {"ms": round(ms, 5), "algorithmic_bytes": st.nbytes,
                            "GB/s": round(st.nbytes / (ms * 1e-3) / 1e9, 1)}
     dom = max(range(nst), key=lambda j: stage_ms[j])
+    cpu = None if args.no_cpu_baseline else cpu_baseline_round(bt, branch, fan, args.cpu_seconds)
     line = {
         "metric": METRIC,
         "value": round(rows / (step_ms * 1e-3), 1),
@@ -306,6 +330,8 @@ def pipeline_bench(args, spec):
         "step_GB/s": round(algo / (step_ms * 1e-3) / 1e9, 1),
         "cache": {"misses": miss, "hits": B - miss, "path": "zero-wait" if miss == 0 else "fallback"},
     }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
