@@ -190,7 +190,8 @@ class _Stage:
 def pipeline_bench(args, spec):
     """One SSD round per step (the cache build and the full round): verification with Saguaro sets
     and per-position top-F guesses, the guesses of draft row K, cache keys, lookup of the outcome,
-    and, for the speculation-cache branches, their top-F sets and Saguaro adjustment. Each stage
+    and, for the speculation-cache branches, their top-F sets with Saguaro mass and normaliser in
+    one pass over each branch row (ssd_saguaro_topf). Each stage
     is timed on the GPU with an event pair per step; its algorithmic bytes (every logit it reads,
     once, plus its small inputs and outputs) over that time give its bandwidth."""
     import numpy as np
@@ -218,8 +219,7 @@ def pipeline_bench(args, spec):
 
     b_verify = (2 * K + 1) * B * V * es + B * K * 4 + B * (K + 1) * 4 + B * K * Gm * 4 + 2 * B * 4 + B * K * Gm * 4
     b_rowk = B * V * es + B * fan[K] * 4
-    b_bsets = Rb * V * es + Rb * 4 + Rb * Gm * 4
-    b_sag = Rb * V * es + Rb * Gm * 4 + 2 * Rb * 4
+    b_branch = Rb * V * es + Rb * 4 + Rb * Gm * 4 + 2 * Rb * 4  # one read of every branch row
     b_keys = B * (K + 1) * Gm * 4 + 2 * B * budget * 4
     b_lookup = 2 * B * budget * 4 + 2 * B * 4 + B * 4 + 4
     total_logit_bytes = ((2 * K + 2) * B + Rb) * V * es
@@ -228,8 +228,7 @@ def pipeline_bench(args, spec):
     reps = []
     ws_v = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, Gm), dev)
     ws_k = ssd.Workspace(ssd.ssd_topf_workspace_bytes(B, V, fan[K]), dev)
-    ws_b = ssd.Workspace(ssd.ssd_topf_workspace_bytes(Rb, V, Gm), dev)
-    ws_s = ssd.Workspace(ssd.ssd_saguaro_workspace_bytes(Rb, V), dev)
+    ws_b = ssd.Workspace(ssd.ssd_saguaro_topf_workspace_bytes(Rb, V, Gm), dev)
     Fr = torch.tensor(fan[:K], dtype=torch.int32, device=dev).repeat(B * budget)
     for _ in range(n_rep):
         r = {}
@@ -268,11 +267,9 @@ def pipeline_bench(args, spec):
             _Stage("lookup (ssd_cache_lookup)", b_lookup,
                    lambda: ssd.ssd_cache_lookup(r["ck"], r["ct"], out["accepted_len"], out["bonus_token"],
                                                 out_slot=r["slot"], out_miss_count=r["miss"])),
-            _Stage("branch sets (ssd_topf_guess)", b_bsets,
-                   lambda: ssd.ssd_topf_guess(r["bd"], Gm, F_per_row=Fr, out=r["bsets"], workspace=ws_b)),
-            _Stage("branch Saguaro (ssd_saguaro_adjust)", b_sag,
-                   lambda: ssd.ssd_saguaro_adjust(r["bd"], T, r["bsets"], bt.C, out_set_mass=r["sig"],
-                                                  out_norm=r["N"], workspace=ws_s)),
+            _Stage("branch sets + Saguaro (ssd_saguaro_topf)", b_branch,
+                   lambda: ssd.ssd_saguaro_topf(r["bd"], T, Gm, bt.C, F_per_row=Fr, out_set=r["bsets"],
+                                                out_set_mass=r["sig"], out_norm=r["N"], workspace=ws_b)),
         ]
 
     plans = [stages(r) for r in reps]
@@ -293,12 +290,12 @@ def pipeline_bench(args, spec):
     stage_ms = [float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j in range(nst)]
     step_ms = float(np.median([ev[i][0].elapsed_time(ev[i][nst]) for i in range(args.steps)]))
-    flags = ssd.ssd_read_flags(ws_v) | ssd.ssd_read_flags(ws_k) | ssd.ssd_read_flags(ws_b) | ssd.ssd_read_flags(ws_s)
+    flags = ssd.ssd_read_flags(ws_v) | ssd.ssd_read_flags(ws_k) | ssd.ssd_read_flags(ws_b)
     if flags:
         print(f"device flags {flags:#x}", file=sys.stderr)
         sys.exit(3)
     rows = (2 * K + 2) * B + Rb
-    algo = b_verify + b_rowk + b_keys + b_lookup + b_bsets + b_sag
+    algo = b_verify + b_rowk + b_keys + b_lookup + b_branch
     miss = int(reps[0]["miss"].item())
     st_out = {}
     for st, ms in zip(plans[0], stage_ms):

@@ -24,6 +24,8 @@ from ._lib import (  # noqa: F401
     ssd_fanout_alloc,
     ssd_read_flags,
     ssd_saguaro_adjust,
+    ssd_saguaro_topf,
+    ssd_saguaro_topf_workspace_bytes,
     ssd_saguaro_workspace_bytes,
     ssd_topf_guess,
     ssd_topf_workspace_bytes,

@@ -18,7 +18,7 @@ SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 20, 65535
 FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT = 0x1, 0x2, 0x4, 0x8
 
 EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify", "ssd_topf_workspace_bytes",
-           "ssd_topf_guess",
+           "ssd_topf_guess", "ssd_saguaro_topf_workspace_bytes", "ssd_saguaro_topf",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",
            "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string"]
 
@@ -45,6 +45,10 @@ def _declare(L):
     L.ssd_topf_workspace_bytes.argtypes = [I32, I32, I32]
     L.ssd_topf_guess.restype = ctypes.c_int
     L.ssd_topf_guess.argtypes = [P, I64, ctypes.c_int, I32, I32, P, P, I32, P, P, SZ, P]
+    L.ssd_saguaro_topf_workspace_bytes.restype = SZ
+    L.ssd_saguaro_topf_workspace_bytes.argtypes = [I32, I32, I32]
+    L.ssd_saguaro_topf.restype = ctypes.c_int
+    L.ssd_saguaro_topf.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, SZ, P]
     L.ssd_saguaro_workspace_bytes.restype = SZ
     L.ssd_saguaro_workspace_bytes.argtypes = [I32, I32]
     L.ssd_saguaro_adjust.restype = ctypes.c_int
@@ -153,6 +157,10 @@ def ssd_verify_launches(B: int, K: int, V: int, dtype: int, topf_F_max: int = 0)
 
 def ssd_topf_workspace_bytes(R: int, V: int, F_max: int) -> int:
     return int(lib().ssd_topf_workspace_bytes(R, V, F_max))
+
+
+def ssd_saguaro_topf_workspace_bytes(R: int, V: int, F_max: int) -> int:
+    return int(lib().ssd_saguaro_topf_workspace_bytes(R, V, F_max))
 
 
 def ssd_saguaro_workspace_bytes(R: int, V: int) -> int:
@@ -291,6 +299,35 @@ def ssd_saguaro_adjust(logits, temperature: float, set_, C: float, *, materialis
                                    out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr,
                                    workspace.nbytes, _stream(stream, dev)), "ssd_saguaro_adjust")
     return out_probs, out_set_mass, out_norm
+
+
+def ssd_saguaro_topf(logits, temperature: float, F_max: int, C: float, *, F_per_row=None, out_set=None,
+                     out_set_mass=None, out_norm=None, workspace: Optional[Workspace] = None, stream=None):
+    """Each row's top-F set with its Saguaro mass and normaliser in one pass; returns (set, sigma, N)."""
+    torch = _torch()
+    if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
+        raise ValueError("logits must be a [R, V] device view with unit element stride")
+    R, V = logits.shape
+    dev = logits.device
+    if F_per_row is not None:
+        _need(F_per_row, torch.int32, (R,), "F_per_row")
+    if out_set is None:
+        out_set = torch.empty((R, F_max), dtype=torch.int32, device=dev)
+    if out_set_mass is None:
+        out_set_mass = torch.empty(R, dtype=torch.float32, device=dev)
+    if out_norm is None:
+        out_norm = torch.empty(R, dtype=torch.float32, device=dev)
+    _need(out_set, torch.int32, (R, F_max), "out_set")
+    _need(out_set_mass, torch.float32, (R,), "out_set_mass")
+    _need(out_norm, torch.float32, (R,), "out_norm")
+    if workspace is None:
+        workspace = Workspace(ssd_saguaro_topf_workspace_bytes(R, V, F_max), dev)
+    stride = logits.stride(0) if R > 1 else V
+    check(lib().ssd_saguaro_topf(logits.data_ptr(), stride, _dtype_code(logits), R, V, float(temperature),
+                                 _ptr(F_per_row), int(F_max), float(C), out_set.data_ptr(),
+                                 out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr, workspace.nbytes,
+                                 _stream(stream, dev)), "ssd_saguaro_topf")
+    return out_set, out_set_mass, out_norm
 
 
 def ssd_fanout_alloc(K: int, a: float, r: float, budget: int):

@@ -25,9 +25,9 @@ __device__ __forceinline__ void chunk_pass(const typename ET::T* __restrict__ ro
   const bool topf = (FM > 0) && (tl.F > 0);
 
   auto consume1 = [&](float z, int idx) {
-    if (STATS) {
+    if (STATS && z > -INFINITY) {  // a -inf token adds nothing (also before the first finite one)
       if (z > mx) {
-        s = s * ex2((mx - z) * c);
+        s = (mx > -INFINITY) ? s * ex2((mx - z) * c) : 0.f;
         mx = z;
       }
       s += ex2(fmaf(z, c, -(mx * c)));
@@ -58,9 +58,9 @@ __device__ __forceinline__ void chunk_pass(const typename ET::T* __restrict__ ro
       float bm = z[0];
 #pragma unroll
       for (int m = 1; m < U * N; ++m) bm = fmaxf(bm, z[m]);
-      if (STATS) {
+      if (STATS && bm > -INFINITY) {  // a batch of -inf adds nothing (also before the first finite one)
         if (bm > mx) {
-          s = s * ex2((mx - bm) * c);
+          s = (mx > -INFINITY) ? s * ex2((mx - bm) * c) : 0.f;
           mx = bm;
         }
         const float mc = mx * c;
@@ -203,10 +203,15 @@ struct TopfWave {
   // from idx_of(e) (evaluated only for batches that reach tau)
   template <int NB, class Idx>
   __device__ __forceinline__ void batch(const float (&z)[NB], Idx idx_of) {
-    const int lane = threadIdx.x & 63;
     float bm = z[0];
 #pragma unroll
     for (int e = 1; e < NB; ++e) bm = fmaxf(bm, z[e]);
+    batch_bm(z, bm, idx_of);
+  }
+  // the same with the lane maximum bm of z already formed
+  template <int NB, class Idx>
+  __device__ __forceinline__ void batch_bm(const float (&z)[NB], float bm, Idx idx_of) {
+    const int lane = threadIdx.x & 63;
     if (tau == -INFINITY && n == 0) {  // first batch: tau from the lane maxima
       const int Fp = F + 1;
       float mm = bm, thr = -INFINITY;
@@ -258,7 +263,29 @@ struct TopfWave {
   }
 };
 
-template <class ET, int FM>
+// Running softmax statistics of a lane's tokens: mx = largest logit so far, s = sum of
+// 2^(z c - mx c). A place at -inf adds nothing (also before the first finite token).
+struct LaneStats {
+  float mx = -INFINITY, s = 0.f;
+  template <int NB>
+  __device__ __forceinline__ void add(const float (&z)[NB], float bm, float c) {
+    if (!(bm > -INFINITY)) return;
+    if (bm > mx) {
+      s = (mx > -INFINITY) ? s * ex2((mx - bm) * c) : 0.f;
+      mx = bm;
+    }
+    const float mc = mx * c;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < NB; ++e) acc[e % 4] += ex2(fmaf(z[e], c, -mc));
+    s += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+};
+
+// SAG: ssd_saguaro_topf — the row's statistics in the same pass, and sigma = q mass of the top F
+// with N = 1 - (1 - C) sigma once the row is complete (here when a row is one chunk, else in the
+// merge kernel).
+template <class ET, int FM, bool SAG>
 __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   using T = typename ET::T;
   constexpr int N = ET::kVec;
@@ -266,6 +293,9 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   __shared__ uint64_t sbuf[kWaves][kTBuf];
   __shared__ uint64_t stop[kWaves][kMaxF];
   __shared__ int sn[kWaves];
+  __shared__ float shf[2 * kWaves];
+  LaneStats ls;
+  const float cc = a.c2;
   const int item = blockIdx.x;
   const int row = item / a.n1;
   const int chunk = item - row * a.n1;
@@ -307,7 +337,11 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
         float z[kTBatch];
 #pragma unroll
         for (int u = 0; u < U; ++u) ET::unpack(raw[u], z + u * N);
-        tw.batch(z, [&](int e) { return (vb + (e / N) * kThreads) * N + (e % N); });
+        float bm = z[0];
+#pragma unroll
+        for (int e = 1; e < kTBatch; ++e) bm = fmaxf(bm, z[e]);
+        if (SAG) ls.add(z, bm, cc);
+        tw.batch_bm(z, bm, [&](int e) { return (vb + (e / N) * kThreads) * N + (e % N); });
       };
       // two batches in flight: the next one loads while this one is examined (the trip count is
       // the same for every lane)
@@ -328,12 +362,19 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
       const int e = e0 + t;
       float z[1];
       z[0] = (e < c1) ? ET::one(p, e) : -INFINITY;
-      tw.batch(z, [&](int) { return e; });
+      if (SAG) ls.add(z, z[0], cc);
+      tw.batch_bm(z, z[0], [&](int) { return e; });
     }
     tw.n = wave_cut_keys(tw.buf, tw.n, F);  // the wave's top F, in order
   }
   if (lane == 0) sn[w] = tw.n;
   if (lane < kMaxF) stop[w][lane] = (lane < tw.n) ? tw.buf[lane] : 0ull;
+  float MXc = -INFINITY, S = 0.f;  // the chunk's (max c, sum 2^(z c - max c))
+  if (SAG && F > 0) {
+    const float MX = block_max(ls.mx, shf);
+    MXc = MX * cc;
+    S = block_sum((ls.s > 0.f) ? ls.s * ex2(ls.mx * cc - MXc) : 0.f, shf + kWaves);
+  }
   __syncthreads();
   if (w == 0) {  // the chunk's top F from the waves' lists
     uint64_t k = 0ull;
@@ -347,14 +388,29 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
     if (a.n1 == 1) {
       int32_t* out = a.out + int64_t(row) * a.Fmax;
       for (int r = lane; r < a.Fmax; r += 64) out[r] = (r < F && win_out) ? int(~uint32_t(win_out)) : -1;
-    } else if (lane < F) {
-      Cand* cd = reinterpret_cast<Cand*>(a.cand) + (int64_t(row) * a.n1 + chunk) * a.Fmax;
-      cd[lane] = win_out ? Cand{key_to_float(uint32_t(win_out >> 32)), int(~uint32_t(win_out))}
-                         : Cand{-INFINITY, -1};
+      if (SAG) {  // sigma over the set, from the logits its keys carry
+        const float L = MXc + lg2(S);
+        const float term = (lane < F && win_out) ? ex2(fmaf(key_to_float(uint32_t(win_out >> 32)), cc, -L)) : 0.f;
+        const float sig = (F > 0) ? wave_sum(term) : 0.f;
+        const float Nn = 1.f - (1.f - a.C) * sig;
+        if (lane == 0) {
+          if (a.out_set_mass) a.out_set_mass[row] = sig;
+          if (a.out_norm) a.out_norm[row] = Nn;
+          if (!(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+        }
+      }
+    } else {
+      if (lane < F) {
+        Cand* cd = reinterpret_cast<Cand*>(a.cand) + (int64_t(row) * a.n1 + chunk) * a.Fmax;
+        cd[lane] = win_out ? Cand{key_to_float(uint32_t(win_out >> 32)), int(~uint32_t(win_out))}
+                           : Cand{-INFINITY, -1};
+      }
+      if (SAG && lane == 0) a.stats[int64_t(row) * a.n1 + chunk] = make_float2(MXc, S);
     }
   }
 }
 
+template <class ET, bool SAG>
 __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
   __shared__ uint32_t shk[2 * kWaves];
   const int row = blockIdx.x;
@@ -364,7 +420,27 @@ __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
     F = F < 0 ? 0 : (F > a.Fmax ? a.Fmax : F);
   }
   const Cand* cd = reinterpret_cast<const Cand*>(a.cand) + int64_t(row) * a.n1 * a.Fmax;
-  merge_lists(cd, F > 0 ? a.n1 : 0, a.Fmax, F, a.out + int64_t(row) * a.Fmax, a.Fmax, shk);
+  int32_t* out = a.out + int64_t(row) * a.Fmax;
+  merge_lists(cd, F > 0 ? a.n1 : 0, a.Fmax, F, out, a.Fmax, shk);
+  if (SAG && threadIdx.x == 0) {  // thread 0 wrote the set; its logits give sigma
+    float sig = 0.f;
+    if (F > 0) {
+      const float2* st = a.stats + int64_t(row) * a.n1;
+      float M = -INFINITY;
+      for (int q = 0; q < a.n1; ++q) M = fmaxf(M, st[q].x);
+      float S = 0.f;
+      for (int q = 0; q < a.n1; ++q)
+        if (st[q].y > 0.f) S += st[q].y * ex2(st[q].x - M);
+      const float L = M + lg2(S);
+      const typename ET::T* p = reinterpret_cast<const typename ET::T*>(a.logits) + int64_t(row) * a.row_stride;
+      for (int f = 0; f < F; ++f)
+        if (out[f] >= 0) sig += ex2(fmaf(ET::one(p, out[f]), a.c2, -L));
+    }
+    const float Nn = 1.f - (1.f - a.C) * sig;
+    if (a.out_set_mass) a.out_set_mass[row] = sig;
+    if (a.out_norm) a.out_norm[row] = Nn;
+    if (!(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+  }
 }
 
 // =============================================================================================
@@ -517,14 +593,18 @@ __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
 // =============================================================================================
 static hipError_t last_error() { return hipGetLastError(); }
 
-template <class ET, int FM>
-static hipError_t launch_topf_t(const TopfArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((topf_rows_kernel<ET, FM>), dim3(unsigned(int64_t(a.R) * a.n1)), dim3(kThreads),
+template <class ET, int FM, bool SAG>
+static hipError_t launch_topf_s(const TopfArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((topf_rows_kernel<ET, FM, SAG>), dim3(unsigned(int64_t(a.R) * a.n1)), dim3(kThreads),
                      0, st, a);
   hipError_t e = last_error();
   if (e != hipSuccess || a.n1 == 1) return e;
-  hipLaunchKernelGGL(topf_merge_kernel, dim3(a.R), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((topf_merge_kernel<ET, SAG>), dim3(a.R), dim3(kThreads), 0, st, a);
   return last_error();
+}
+template <class ET, int FM>
+static hipError_t launch_topf_t(const TopfArgs& a, hipStream_t st) {
+  return a.sag ? launch_topf_s<ET, FM, true>(a, st) : launch_topf_s<ET, FM, false>(a, st);
 }
 
 template <class ET>

@@ -53,6 +53,12 @@ struct TopfArgs {
   void* cand;
   int n1, chunk1;
   int aligned;
+  // Saguaro over the row's own top-F set (ssd_saguaro_topf): row statistics in the same pass
+  int sag;           // 0: top-F only
+  float c2, C;       // log2(e) / T, Saguaro scale
+  float2* stats;     // [R][n1] (max c, sum 2^(z c - max c)) per chunk (when n1 > 1)
+  float* out_set_mass;
+  float* out_norm;
 };
 
 struct SagArgs {
@@ -95,7 +101,7 @@ struct CacheLookupArgs {
 hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t st);
 // kernel launches launch_verify issues for these arguments on the current device (-1 on error)
 int count_verify_launches(const VerifyArgs& a, bool bf16);
-hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);  // also ssd_saguaro_topf (a.sag)
 hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st);
 hipError_t launch_cache_lookup(const CacheLookupArgs& a, hipStream_t st);

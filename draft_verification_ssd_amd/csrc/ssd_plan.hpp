@@ -69,7 +69,7 @@ inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
 
 struct TopfLayout {
   RowPlan rp;
-  size_t off_cand, total;
+  size_t off_cand, off_stats, total;
 };
 
 // Top-F chunks are longer than the statistics chunks: each wave's candidate search has a fixed
@@ -89,7 +89,9 @@ inline TopfLayout topf_layout(int R, int V, int F_max) {
   L.rp.chunk1 = int(chunk);
   L.rp.n1 = int(ceil_div(V, chunk));
   L.off_cand = kAlign;
-  L.total = align_up(L.off_cand + size_t(R) * L.rp.n1 * F_max * 8);
+  L.off_stats = align_up(L.off_cand + size_t(R) * L.rp.n1 * F_max * 8);
+  // chunk statistics (ssd_saguaro_topf) only when a row has several chunks
+  L.total = align_up(L.off_stats + (L.rp.n1 > 1 ? size_t(R) * L.rp.n1 * 8 : 0));
   return L;
 }
 

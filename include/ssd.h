@@ -159,6 +159,28 @@ ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype 
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ssd_saguaro_topf — the speculation cache's branch rows in one pass each ([SSD] "Saguaro 优化二",
+ * "怎么猜奖励 token"): the set S of a row is its F_r largest logits (the tokens the cache holds;
+ * ties to the smaller index, never a -inf logit, -1 pads), q = softmax(row / T),
+ * sigma = sum_{s in S} q(s) and N = 1 - (1 - C) sigma, the normaliser of the down-weighted q'.
+ * Gives what ssd_topf_guess (no exclusion) followed by ssd_saguaro_adjust with that set gives,
+ * reading each row once.
+ *   logits        device [R rows, V]; row r at element r * row_stride (>= V).
+ *   F_per_row     device int32 [R] (0..F_max; out of range flagged SSD_FLAG_BAD_F) or NULL (F_max).
+ *   F_max         1..SSD_MAX_F.  C in [0, 1].  temperature > 0 and finite.
+ *   out_set       device int32 [R, F_max] out.
+ *   out_set_mass  device fp32 [R] sigma, or NULL.
+ *   out_norm      device fp32 [R] N, or NULL. N <= 0 is flagged (SSD_FLAG_SAGUARO_NORM).
+ *   workspace     ssd_saguaro_topf_workspace_bytes(R, V, F_max) bytes.
+ * ------------------------------------------------------------------------------------------- */
+size_t ssd_saguaro_topf_workspace_bytes(int R, int V, int F_max);
+
+ssd_status ssd_saguaro_topf(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                            float temperature, const int32_t* F_per_row, int F_max, float C,
+                            int32_t* out_set, float* out_set_mass, float* out_norm, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ssd_fanout_alloc — geometric fan-out of a cache budget ([SSD] "最优扇出度分配"). Host only,
  * synchronous. P(k) = (1-a) a^k for k < K and a^K for k = K; minimising sum_k P(k) F_k^-r under
  * sum_k F_k = budget gives F_k proportional to P(k)^(1/(1+r)). Integers: floor, then the leftover

@@ -103,6 +103,25 @@ def test_topf_and_saguaro_validation():
     assert sag(FAKE, 100, 0, 0, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == OK
 
 
+def test_saguaro_topf_validation():
+    st = ssd.lib().ssd_saguaro_topf
+    # (logits, stride, dtype, R, V, T, F_per_row, F_max, C, out_set, sigma, N, ws, bytes, stream)
+    assert st(FAKE, 100, 9, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == UNS
+    assert st(FAKE, 99, 0, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 0.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, float("inf"), None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 0, 0.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 17, 0.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 1.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, float("nan"), FAKE, None, None, None, 0, None) == INV
+    assert st(None, 100, 0, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 0.5, None, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == WS
+    assert st(FAKE, 100, 0, 0, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == OK
+    assert ssd.ssd_saguaro_topf_workspace_bytes(768, 128256, 3) > 0
+    assert ssd.ssd_saguaro_topf_workspace_bytes(4, 100, 0) == 0
+
+
 def test_cache_validation():
     L = ssd.lib()
     F = (ctypes.c_int32 * 5)(3, 2, 2, 2, 3)

@@ -111,6 +111,86 @@ def test_saguaro_degenerate_normaliser_is_flagged():
     assert ssd.ssd_read_flags(ws) & ssd.FLAG_SAGUARO_NORM
 
 
+@pytest.mark.parametrize("R,V,F,C,T,dtype", [(1, 1, 1, 0.5, 1.0, "f32"), (3, 5, 7, 0.0, 1.0, "bf16"),
+                                             (17, 2049, 4, 0.3, 0.7, "bf16"), (4, 40000, 16, 0.5, 1.0, "f32"),
+                                             (300, 9000, 8, 1.0, 1.0, "bf16"), (2, 128256, 3, 0.5, 1.0, "bf16"),
+                                             (800, 20000, 3, 0.5, 1.0, "f32"), (3, 77777, 5, 0.3, 2.0, "f32")])
+def test_saguaro_topf_matches_topf_then_saguaro(R, V, F, C, T, dtype):
+    """One pass (set = the row's top F, then sigma and N) against the oracle's top-F and Saguaro;
+    the shapes cover rows cut into several chunks (few rows) and whole-row chunks (many rows)."""
+    print(f"[case] saguaro_topf R{R} V{V} F{F} C{C} T{T} {dtype}", flush=True)
+    rng = np.random.default_rng(R * 31 + V)
+    if R % 2:
+        z = tie_heavy_rows(R, V, dtype, seed=R + V)
+    else:
+        z = rng.normal(0, 2, size=(R, V)).astype(np.float32)
+        z[rng.random((R, V)) < 0.02] = -np.inf
+        if dtype == "bf16":
+            z = synth.f32_to_bf16_bits(z)
+    Fr = rng.integers(0, F + 1, size=R).astype(np.int32)
+    ws = ssd.Workspace(ssd.ssd_saguaro_topf_workspace_bytes(R, V, F))
+    S, sig, N = ssd.ssd_saguaro_topf(logits_to_device(z, dtype), T, F, C, F_per_row=torch.from_numpy(Fr).to(DEV),
+                                     workspace=ws)
+    S, sig, N = S.cpu().numpy(), sig.cpu().numpy(), N.cpu().numpy()
+    z64 = O.logits_f64(z, dtype)
+    for r in range(R):
+        want = O.topf(z64[r], int(Fr[r]))
+        assert list(S[r]) == list(want) + [-1] * (F - len(want)), f"set of row {r}"
+        if not np.isfinite(z64[r]).any():
+            continue
+        q = O.softmax_t(z64[r], T)
+        if C == 0.0 and abs(q[list(want)].sum() - 1.0) < 1e-12:  # the set holds all the mass: N = 0
+            assert abs(N[r]) < PROB_ATOL, f"row {r}"
+            assert ssd.ssd_read_flags(ws, clear=False) & ssd.FLAG_SAGUARO_NORM
+            continue
+        _, s_ref, n_ref = O.saguaro(q, want, C)
+        assert abs(sig[r] - s_ref) < PROB_ATOL and abs(N[r] - n_ref) < PROB_ATOL, f"row {r}"
+    flags = ssd.ssd_read_flags(ws)
+    assert flags & ~ssd.FLAG_SAGUARO_NORM == 0
+
+
+def test_saguaro_topf_on_a_strided_row_view_and_degenerate_norm():
+    bt = synth.make_verify_batch(6, 4, 20000, synth.BF16, 3)
+    view = logits_to_device(bt.draft, bt.dtype)[:, bt.K, :]   # row K of every sequence
+    print("[case] saguaro_topf strided view", flush=True)
+    S, sig, N = ssd.ssd_saguaro_topf(view, 1.0, 4, 0.5)
+    z64 = O.logits_f64(bt.draft[:, bt.K], bt.dtype)
+    for r in range(6):
+        want = O.topf(z64[r], 4)
+        assert list(S[r].cpu().numpy()) == list(want)
+        _, s_ref, n_ref = O.saguaro(O.softmax_t(z64[r], 1.0), want, 0.5)
+        assert abs(sig[r].item() - s_ref) < PROB_ATOL and abs(N[r].item() - n_ref) < PROB_ATOL
+    z = np.full((1, 4), -np.inf, dtype=np.float32)
+    z[0, :2] = 0.0                                            # the set holds all the mass; C = 0
+    ws = ssd.Workspace(ssd.ssd_saguaro_topf_workspace_bytes(1, 4, 2))
+    ssd.ssd_saguaro_topf(logits_to_device(z, "f32"), 1.0, 2, 0.0, workspace=ws)
+    assert ssd.ssd_read_flags(ws) & ssd.FLAG_SAGUARO_NORM
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_saguaro_statistics_with_a_long_masked_prefix(dtype):
+    """Rows whose first tens of thousands of tokens are -inf: every lane's first batches hold no
+    finite token, which the running statistics must skip (regression: they turned the lane's sum
+    into NaN and lost its tokens)."""
+    R, V = 4, 60000
+    rng = np.random.default_rng(11)
+    z = rng.normal(0, 2, size=(R, V)).astype(np.float32)
+    for r in range(R):
+        z[r, : 20000 + 9000 * r] = -np.inf
+    zz = synth.f32_to_bf16_bits(z) if dtype == "bf16" else z
+    z64 = O.logits_f64(zz, dtype)
+    zd = logits_to_device(zz, dtype)
+    print(f"[case] masked prefix {dtype}", flush=True)
+    sets = np.stack([O.topf(z64[r], 3) for r in range(R)]).astype(np.int32)
+    _, sig_a, N_a = ssd.ssd_saguaro_adjust(zd, 1.0, torch.from_numpy(sets).to(DEV), 0.5)
+    S, sig_b, N_b = ssd.ssd_saguaro_topf(zd, 1.0, 3, 0.5)
+    assert np.array_equal(S.cpu().numpy(), sets)
+    for r in range(R):
+        _, s_ref, n_ref = O.saguaro(O.softmax_t(z64[r], 1.0), sets[r], 0.5)
+        for sig, N in ((sig_a, N_a), (sig_b, N_b)):
+            assert abs(sig[r].item() - s_ref) < PROB_ATOL and abs(N[r].item() - n_ref) < PROB_ATOL, f"row {r}"
+
+
 @pytest.mark.parametrize("B,K,G,fan", [(3, 4, 3, [3, 2, 2, 2, 3]), (5, 4, 8, [8, 7, 5, 5, 7]),
                                        (2, 2, 2, [0, 2, 1]), (1, 1, 1, [1, 0])])
 def test_cache_keys_and_lookup_match_oracle(B, K, G, fan):
