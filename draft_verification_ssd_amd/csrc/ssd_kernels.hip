@@ -157,11 +157,12 @@ __device__ void merge_lists(const Cand* __restrict__ cands, int n_lists, int str
 // Each wave keeps a lower bound tau of the F-th best (value desc, index asc) among the tokens it
 // has read, and a buffer of candidate keys (ordered value key << 32 | ~index; larger is better)
 // in LDS. A batch of 32 tokens per lane whose lane maxima all fall below tau is skipped after one
-// ballot; otherwise its tokens at or above tau are appended, and a buffer past kTReduce keys is
-// cut to its top F, whose F-th key raises tau. The first batch sets tau to the (F+1)-th largest
+// ballot; otherwise its tokens at or above tau are appended, and a buffer past max(2F, kTReduce)
+// keys is cut to its top F, whose F-th key raises tau (early cuts keep tau near the running F-th
+// best, so later batches rarely hold a candidate). The first batch sets tau to the (F+1)-th largest
 // lane maximum: F + 1 tokens of distinct lanes reach it, so F of them are not the excluded one.
 constexpr int kTBuf = 256;     // candidate keys per wave
-constexpr int kTReduce = 128;  // cut the buffer to its top F beyond this many keys
+constexpr int kTReduce = 16;   // cut the buffer to its top F beyond max(2F, this) keys
 constexpr int kTBatch = 32;    // tokens per lane per batch
 
 __device__ __forceinline__ uint64_t cand_key64(float v, int idx) {
@@ -256,7 +257,7 @@ struct TopfWave {
         n += __popcll(m);
       }
     }
-    if (n > kTReduce) {
+    if (n > max(2 * F, kTReduce)) {
       n = wave_cut_keys(buf, n, F);
       if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
     }
