@@ -5,6 +5,7 @@ ctypes binding over it plus the build step. See ``_lib`` for the entry points.
 """
 from ._lib import (  # noqa: F401
     EXPORTS,
+    FLAG_BAD_C,
     FLAG_BAD_F,
     FLAG_BAD_TOKEN,
     FLAG_SAGUARO_NORM,

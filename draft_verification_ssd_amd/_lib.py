@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_F32, SSD_BF16 = 0, 1
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 20, 65535
-FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT = 0x1, 0x2, 0x4, 0x8
+FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT, FLAG_BAD_C = 0x1, 0x2, 0x4, 0x8, 0x10
 
 EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify", "ssd_topf_workspace_bytes",
            "ssd_topf_guess", "ssd_saguaro_topf_workspace_bytes", "ssd_saguaro_topf",
@@ -39,7 +39,7 @@ def _declare(L):
     L.ssd_verify_launches.restype = ctypes.c_int
     L.ssd_verify_launches.argtypes = [I32, I32, I32, ctypes.c_int, I32]
     L.ssd_verify.restype = ctypes.c_int
-    L.ssd_verify.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32,
+    L.ssd_verify.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32, P,
                              P, I32, P, P, P, P, P, P, SZ, P]
     L.ssd_topf_workspace_bytes.restype = SZ
     L.ssd_topf_workspace_bytes.argtypes = [I32, I32, I32]
@@ -48,11 +48,11 @@ def _declare(L):
     L.ssd_saguaro_topf_workspace_bytes.restype = SZ
     L.ssd_saguaro_topf_workspace_bytes.argtypes = [I32, I32, I32]
     L.ssd_saguaro_topf.restype = ctypes.c_int
-    L.ssd_saguaro_topf.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, SZ, P]
+    L.ssd_saguaro_topf.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, P, SZ, P]
     L.ssd_saguaro_workspace_bytes.restype = SZ
     L.ssd_saguaro_workspace_bytes.argtypes = [I32, I32]
     L.ssd_saguaro_adjust.restype = ctypes.c_int
-    L.ssd_saguaro_adjust.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P,
+    L.ssd_saguaro_adjust.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, P,
                                      SZ, P]
     L.ssd_fanout_alloc.restype = ctypes.c_int
     L.ssd_fanout_alloc.argtypes = [I32, F64, F64, I32, P, P]
@@ -180,7 +180,7 @@ class VerifyCall:
     foreign call with the stored arguments (the launch path used for timing)."""
 
     def __init__(self, draft, target, draft_tokens, uniforms, temperature: float, *,
-                 sag_set=None, sag_C: float = 1.0, topf_F: Optional[Sequence[int]] = None,
+                 sag_set=None, sag_C=1.0, topf_F: Optional[Sequence[int]] = None,
                  topf_F_max: int = 0, topf_out=None, accepted_len=None, bonus_token=None,
                  accept_prob=None, residual_mass=None, workspace: Optional[Workspace] = None,
                  stream=None):
@@ -203,6 +203,15 @@ class VerifyCall:
             if topf_out is None:
                 topf_out = torch.empty((B, K, topf_F_max), dtype=torch.int32, device=dev)
             _need(topf_out, torch.int32, (B, K, topf_F_max), "topf_out")
+        self.sag_C_arr = None  # per-position C, host [K]
+        if sag_set is not None and not isinstance(sag_C, (int, float)):
+            cs = [float(c) for c in sag_C]
+            if len(cs) != K:
+                raise ValueError("sag_C needs one value or one per draft position")
+            self.sag_C_arr = (ctypes.c_float * K)(*cs)
+            sag_C = cs[0]
+        elif not isinstance(sag_C, (int, float)):
+            sag_C = float(list(sag_C)[0])
         self.topf_F_arr = None
         if topf_F is not None:
             if len(topf_F) != K:
@@ -228,7 +237,7 @@ class VerifyCall:
         self.args = (
             draft.data_ptr(), dstride, target.data_ptr(), tstride, _dtype_code(draft), B, K, V,
             float(temperature), draft_tokens.data_ptr(), uniforms.data_ptr(), _ptr(sag_set), sag_F,
-            float(sag_C),
+            float(sag_C), None if self.sag_C_arr is None else ctypes.addressof(self.sag_C_arr),
             None if self.topf_F_arr is None else ctypes.addressof(self.topf_F_arr), int(topf_F_max),
             _ptr(topf_out), accepted_len.data_ptr(), bonus_token.data_ptr(), _ptr(accept_prob),
             _ptr(residual_mass), workspace.ptr, workspace.nbytes, _stream(stream, dev))
@@ -268,10 +277,11 @@ def ssd_topf_guess(logits, F_max: int, *, exclude=None, F_per_row=None, out=None
     return out
 
 
-def ssd_saguaro_adjust(logits, temperature: float, set_, C: float, *, materialise: bool = False,
-                       out_probs=None, out_set_mass=None, out_norm=None,
+def ssd_saguaro_adjust(logits, temperature: float, set_, C: float, *, C_per_row=None,
+                       materialise: bool = False, out_probs=None, out_set_mass=None, out_norm=None,
                        workspace: Optional[Workspace] = None, stream=None):
-    """Saguaro down-weighting of every row of a [R, V] logits view; returns (q' or None, sigma, N)."""
+    """Saguaro down-weighting of every row of a [R, V] logits view; returns (q' or None, sigma, N).
+    C_per_row: optional device fp32 [R] factor per row."""
     torch = _torch()
     if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
         raise ValueError("logits must be a [R, V] device view with unit element stride")
@@ -294,16 +304,20 @@ def ssd_saguaro_adjust(logits, temperature: float, set_, C: float, *, materialis
     if workspace is None:
         workspace = Workspace(ssd_saguaro_workspace_bytes(R, V), dev)
     stride = logits.stride(0) if R > 1 else V
+    if C_per_row is not None:
+        _need(C_per_row, torch.float32, (R,), "C_per_row")
     check(lib().ssd_saguaro_adjust(logits.data_ptr(), stride, _dtype_code(logits), R, V,
-                                   float(temperature), _ptr(set_), F, float(C), _ptr(out_probs),
+                                   float(temperature), _ptr(set_), F, float(C), _ptr(C_per_row), _ptr(out_probs),
                                    out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr,
                                    workspace.nbytes, _stream(stream, dev)), "ssd_saguaro_adjust")
     return out_probs, out_set_mass, out_norm
 
 
-def ssd_saguaro_topf(logits, temperature: float, F_max: int, C: float, *, F_per_row=None, out_set=None,
-                     out_set_mass=None, out_norm=None, workspace: Optional[Workspace] = None, stream=None):
-    """Each row's top-F set with its Saguaro mass and normaliser in one pass; returns (set, sigma, N)."""
+def ssd_saguaro_topf(logits, temperature: float, F_max: int, C: float, *, F_per_row=None, C_per_row=None,
+                     out_set=None, out_set_mass=None, out_norm=None, workspace: Optional[Workspace] = None,
+                     stream=None):
+    """Each row's top-F set with its Saguaro mass and normaliser in one pass; returns (set, sigma, N).
+    C_per_row: optional device fp32 [R] factor per row."""
     torch = _torch()
     if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
         raise ValueError("logits must be a [R, V] device view with unit element stride")
@@ -323,8 +337,10 @@ def ssd_saguaro_topf(logits, temperature: float, F_max: int, C: float, *, F_per_
     if workspace is None:
         workspace = Workspace(ssd_saguaro_topf_workspace_bytes(R, V, F_max), dev)
     stride = logits.stride(0) if R > 1 else V
+    if C_per_row is not None:
+        _need(C_per_row, torch.float32, (R,), "C_per_row")
     check(lib().ssd_saguaro_topf(logits.data_ptr(), stride, _dtype_code(logits), R, V, float(temperature),
-                                 _ptr(F_per_row), int(F_max), float(C), out_set.data_ptr(),
+                                 _ptr(F_per_row), int(F_max), float(C), _ptr(C_per_row), out_set.data_ptr(),
                                  out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr, workspace.nbytes,
                                  _stream(stream, dev)), "ssd_saguaro_topf")
     return out_set, out_set_mass, out_norm

@@ -60,7 +60,8 @@ size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max) {
 ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
                       int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
                       float temperature, const int32_t* draft_tokens, const float* uniforms,
-                      const int32_t* sag_set, int sag_F, float sag_C, const int32_t* topf_F,
+                      const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                      const int32_t* topf_F,
                       int topf_F_max, int32_t* topf_out, int32_t* accepted_len,
                       int32_t* bonus_token, float* accept_prob, float* residual_mass,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -70,6 +71,9 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   if (!temp_ok(temperature)) return SSD_ERR_INVALID_ARG;
   if (sag_F < 0 || sag_F > SSD_MAX_F || (sag_F > 0 && (!sag_set || !c_ok(sag_C))))
     return SSD_ERR_INVALID_ARG;
+  if (sag_F > 0 && sag_C_pos)
+    for (int i = 0; i < K; ++i)
+      if (!c_ok(sag_C_pos[i])) return SSD_ERR_INVALID_ARG;
   if (topf_F_max < 0 || topf_F_max > SSD_MAX_F || (topf_F_max > 0 && !topf_out))
     return SSD_ERR_INVALID_ARG;
   if (topf_F)
@@ -100,7 +104,7 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.u = uniforms;
   a.sset = sag_F > 0 ? sag_set : nullptr;
   a.sF = sag_F;
-  a.C = sag_F > 0 ? sag_C : 1.f;
+  for (int i = 0; i < K; ++i) a.Cpos[i] = sag_F > 0 ? (sag_C_pos ? sag_C_pos[i] : sag_C) : 1.f;
   for (int i = 0; i < K; ++i) a.topfF[i] = topf_F ? topf_F[i] : topf_F_max;
   a.topfFmax = topf_F_max;
   a.topf_out = topf_out;
@@ -190,7 +194,8 @@ size_t ssd_saguaro_topf_workspace_bytes(int R, int V, int F_max) {
 
 ssd_status ssd_saguaro_topf(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
                             float temperature, const int32_t* F_per_row, int F_max, float C,
-                            int32_t* out_set, float* out_set_mass, float* out_norm, void* workspace,
+                            const float* C_per_row, int32_t* out_set, float* out_set_mass,
+                            float* out_norm, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
   if (R < 0 || R > (1 << 24) || V < 1 || V > SSD_MAX_V || F_max < 1 || F_max > SSD_MAX_F ||
@@ -219,6 +224,7 @@ ssd_status ssd_saguaro_topf(const void* logits, int64_t row_stride, ssd_dtype dt
   a.sag = 1;
   a.c2 = float(kLog2e / double(temperature));
   a.C = C;
+  a.C_per_row = C_per_row;
   a.stats = at<float2>(workspace, L.off_stats);
   a.out_set_mass = out_set_mass;
   a.out_norm = out_norm;
@@ -233,8 +239,9 @@ size_t ssd_saguaro_workspace_bytes(int R, int V) {
 
 ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
                               float temperature, const int32_t* set, int F, float C,
-                              float* out_probs, float* out_set_mass, float* out_norm,
-                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                              const float* C_per_row, float* out_probs, float* out_set_mass,
+                              float* out_norm, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
   if (R < 0 || R > 65535 || V < 1 || V > SSD_MAX_V || row_stride < V || !temp_ok(temperature) ||
       F < 0 || F > SSD_MAX_F || (F > 0 && !set) || !c_ok(C))
@@ -254,6 +261,7 @@ ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype 
   a.set = set;
   a.F = F;
   a.C = C;
+  a.C_per_row = C_per_row;
   a.out_probs = out_probs;
   a.out_set_mass = out_set_mass;
   a.out_norm = out_norm;

@@ -24,6 +24,18 @@ constexpr uint32_t kFlagBadToken = 0x1u;
 constexpr uint32_t kFlagSaguaroNorm = 0x2u;
 constexpr uint32_t kFlagBadF = 0x4u;
 constexpr uint32_t kFlagTimeout = 0x8u;
+constexpr uint32_t kFlagBadC = 0x10u;
+
+// Saguaro factor of a row: the per-row array's entry (a value outside [0, 1] is clamped to it, NaN
+// taken as 1, and flagged when `flag` is set), else the call's single factor.
+__device__ __forceinline__ float row_saguaro_c(const float* C_per_row, float C, int64_t row, uint32_t* flags,
+                                               bool flag) {
+  if (!C_per_row) return C;
+  const float c = C_per_row[row];
+  if (c >= 0.f && c <= 1.f) return c;
+  if (flag) atomicOr(flags, kFlagBadC);
+  return (c < 0.f) ? 0.f : 1.f;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

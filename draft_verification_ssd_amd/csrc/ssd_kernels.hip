@@ -393,7 +393,8 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
         const float L = MXc + lg2(S);
         const float term = (lane < F && win_out) ? ex2(fmaf(key_to_float(uint32_t(win_out >> 32)), cc, -L)) : 0.f;
         const float sig = (F > 0) ? wave_sum(term) : 0.f;
-        const float Nn = 1.f - (1.f - a.C) * sig;
+        const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, lane == 0);
+        const float Nn = 1.f - (1.f - Cr) * sig;
         if (lane == 0) {
           if (a.out_set_mass) a.out_set_mass[row] = sig;
           if (a.out_norm) a.out_norm[row] = Nn;
@@ -437,7 +438,8 @@ __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
       for (int f = 0; f < F; ++f)
         if (out[f] >= 0) sig += ex2(fmaf(ET::one(p, out[f]), a.c2, -L));
     }
-    const float Nn = 1.f - (1.f - a.C) * sig;
+    const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, true);
+    const float Nn = 1.f - (1.f - Cr) * sig;
     if (a.out_set_mass) a.out_set_mass[row] = sig;
     if (a.out_norm) a.out_norm[row] = Nn;
     if (!(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void sag_finalize_kernel(SagArgs a) {
   __shared__ float2 s_part[kMaxChunks];
   __shared__ int s_set[kMaxF];
   __shared__ float s_zs[kMaxF];
-  __shared__ float s_L, s_N;
+  __shared__ float s_L, s_N, s_C;
   const int chunk = blockIdx.x, row = blockIdx.y, t = threadIdx.x;
   const int F = a.F, V = a.V;
   const T* p = reinterpret_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
@@ -502,9 +504,11 @@ __global__ __launch_bounds__(kThreads) void sag_finalize_kernel(SagArgs a) {
     float sig = 0.f;
     for (int f = 0; f < F; ++f)
       if (s_set[f] >= 0) sig += ex2(fmaf(s_zs[f], a.c2, -L));
-    const float N = 1.f - (1.f - a.C) * sig;
+    const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, chunk == 0);
+    const float N = 1.f - (1.f - Cr) * sig;
     s_L = L;
     s_N = N;
+    s_C = Cr;
     if (chunk == 0) {
       if (a.out_set_mass) a.out_set_mass[row] = sig;
       if (a.out_norm) a.out_norm[row] = N;
@@ -513,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void sag_finalize_kernel(SagArgs a) {
   }
   __syncthreads();
   if (!a.out_probs) return;
-  const float L = s_L, w_out = 1.f / s_N, w_in = a.C / s_N;
+  const float L = s_L, w_out = 1.f / s_N, w_in = s_C / s_N;
   const int c0 = chunk * a.chunk_out;
   const int c1 = min(V, c0 + a.chunk_out);
   int nin = 0;

@@ -21,7 +21,7 @@ struct VerifyArgs {
   const float* u;
   const int32_t* sset;
   int sF;
-  float C;
+  float Cpos[16];  // Saguaro factor per draft position
   int topfF[16];
   int topfFmax;
   int32_t* topf_out;
@@ -56,6 +56,7 @@ struct TopfArgs {
   // Saguaro over the row's own top-F set (ssd_saguaro_topf): row statistics in the same pass
   int sag;           // 0: top-F only
   float c2, C;       // log2(e) / T, Saguaro scale
+  const float* C_per_row;  // device [R] Saguaro scale per row, or null (C)
   float2* stats;     // [R][n1] (max c, sum 2^(z c - max c)) per chunk (when n1 > 1)
   float* out_set_mass;
   float* out_norm;
@@ -69,6 +70,7 @@ struct SagArgs {
   const int32_t* set;
   int F;
   float C;
+  const float* C_per_row;  // device [R] Saguaro scale per row, or null (C)
   float* out_probs;
   float* out_set_mass;
   float* out_norm;

@@ -811,8 +811,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
       }
       __syncthreads();
       if (t < 64) {  // wave 0: lane i takes the accept test of position i
-        const float C = a.C;
         const int i = min(lane, K - 1);
+        const float C = a.Cpos[i];  // Saguaro factor of position i
         const float Lq = sh.L[i], Lp = sh.L[K + i];
         const int xi = sh.xe[i];
         const bool xok = unsigned(xi) < unsigned(V);
@@ -852,6 +852,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
         const uint64_t rej = __ballot(lane < K && !accept);
         const int k = rej ? __builtin_ctzll(rej) : K;  // first rejection
         const float Nk = (k < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), k)) : 1.f;
+        const float Ck = (k < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(C), k)) : 1.f;
         // the record, straight from registers: lane j publishes word j (the set of row k keeps
         // its -1 holes: duplicates and out-of-range entries, which the residual skips)
         const int nset = (k < K) ? sF : 0;
@@ -863,7 +864,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
         if (lane == kDecLp) v = __float_as_uint(Lpk);
         if (lane == kDecLq) v = __float_as_uint(Lqk);
         if (lane == kDecWout) v = __float_as_uint(1.f / Nk);
-        if (lane == kDecWin) v = __float_as_uint(C / Nk);
+        if (lane == kDecWin) v = __float_as_uint(Ck / Nk);
         if (lane == kDecNset) v = uint32_t(nset);
         if (lane < kDecWords) st_agent(dec + lane, tagged(tag, v));
         // this tile's own copy, for its residual
@@ -874,7 +875,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
           sh.Lp = Lpk;
           sh.Lq = Lqk;
           sh.w_out = 1.f / Nk;
-          sh.w_in = C / Nk;
+          sh.w_in = Ck / Nk;
         }
         if (f >= 0 && f < kMaxF) sh.myset[f] = sv;
       }

@@ -61,6 +61,7 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 #define SSD_FLAG_SAGUARO_NORM 0x2u  /* Saguaro normaliser N <= 0 (C = 0 with S holding all mass) */
 #define SSD_FLAG_BAD_F 0x4u         /* a per-row F outside [0, F_max] (clamped) */
 #define SSD_FLAG_TIMEOUT 0x8u       /* a wait between workgroups gave up (workspace needs re-zeroing) */
+#define SSD_FLAG_BAD_C 0x10u        /* a per-row Saguaro C outside [0, 1] (clamped; NaN as 1) */
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_verify — one round of verification for B sequences.
@@ -87,6 +88,10 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   sag_set, sag_F    device int32 [B, K, sag_F] Saguaro sets (entries < 0, >= V or repeated are
  *                     ignored), or NULL with sag_F = 0. 0 <= sag_F <= SSD_MAX_F.
  *   sag_C             C in [0, 1]; ignored when sag_F = 0.
+ *   sag_C_pos         host fp32 [K]: position i down-weights its set by sag_C_pos[i] in [0, 1]
+ *                     instead of sag_C (a per-position C, the direction [SSD] "关于逐位置 的思考"
+ *                     names; the pages' own C is one value), or NULL (sag_C everywhere). Copied
+ *                     at the call. A uniform array gives the bits of the single-value call.
  *   topf_F            host int32 [K]: guesses wanted per draft position (0..topf_F_max), or NULL
  *                     (= topf_F_max everywhere).
  *   topf_F_max        0..SSD_MAX_F; 0 disables the guesses.
@@ -114,7 +119,7 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
                       const void* target_logits, int64_t target_seq_stride,
                       ssd_dtype dtype, int B, int K, int V, float temperature,
                       const int32_t* draft_tokens, const float* uniforms,
-                      const int32_t* sag_set, int sag_F, float sag_C,
+                      const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
                       const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
                       int32_t* accepted_len, int32_t* bonus_token,
                       float* accept_prob, float* residual_mass,
@@ -146,6 +151,8 @@ ssd_status ssd_topf_guess(const void* logits, int64_t row_stride, ssd_dtype dtyp
  *   set, F        device int32 [R, F] (-1 pads; out-of-range and repeated entries ignored), F in
  *                 0..SSD_MAX_F (set may be NULL iff F = 0).
  *   C             in [0, 1].
+ *   C_per_row     device fp32 [R] (row r uses C_per_row[r]; a value outside [0, 1] is clamped,
+ *                 NaN taken as 1, and flagged SSD_FLAG_BAD_C) or NULL (C for every row).
  *   out_probs     device fp32 [R, V] q' or NULL (then nothing of size V is written).
  *   out_set_mass  device fp32 [R] sigma, or NULL.
  *   out_norm      device fp32 [R] N, or NULL. N <= 0 is flagged (SSD_FLAG_SAGUARO_NORM).
@@ -155,8 +162,9 @@ size_t ssd_saguaro_workspace_bytes(int R, int V);
 
 ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
                               float temperature, const int32_t* set, int F, float C,
-                              float* out_probs, float* out_set_mass, float* out_norm,
-                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+                              const float* C_per_row, float* out_probs, float* out_set_mass,
+                              float* out_norm, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_saguaro_topf — the speculation cache's branch rows in one pass each ([SSD] "Saguaro 优化二",
@@ -168,6 +176,7 @@ ssd_status ssd_saguaro_adjust(const void* logits, int64_t row_stride, ssd_dtype 
  *   logits        device [R rows, V]; row r at element r * row_stride (>= V).
  *   F_per_row     device int32 [R] (0..F_max; out of range flagged SSD_FLAG_BAD_F) or NULL (F_max).
  *   F_max         1..SSD_MAX_F.  C in [0, 1].  temperature > 0 and finite.
+ *   C_per_row     device fp32 [R] per-row C (as for ssd_saguaro_adjust) or NULL (C everywhere).
  *   out_set       device int32 [R, F_max] out.
  *   out_set_mass  device fp32 [R] sigma, or NULL.
  *   out_norm      device fp32 [R] N, or NULL. N <= 0 is flagged (SSD_FLAG_SAGUARO_NORM).
@@ -177,8 +186,9 @@ size_t ssd_saguaro_topf_workspace_bytes(int R, int V, int F_max);
 
 ssd_status ssd_saguaro_topf(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
                             float temperature, const int32_t* F_per_row, int F_max, float C,
-                            int32_t* out_set, float* out_set_mass, float* out_norm, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream);
+                            const float* C_per_row, int32_t* out_set, float* out_set_mass,
+                            float* out_norm, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_fanout_alloc — geometric fan-out of a cache budget ([SSD] "最优扇出度分配"). Host only,

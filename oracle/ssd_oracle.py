@@ -101,13 +101,15 @@ class VerifyResult:
 
 
 def verify_sequence(zq: np.ndarray, zp: np.ndarray, x: Sequence[int], u: Sequence[float], T: float,
-                    sets: Optional[Sequence[Sequence[int]]] = None, C: float = 1.0) -> VerifyResult:
+                    sets: Optional[Sequence[Sequence[int]]] = None, C=1.0) -> VerifyResult:
     """Verify K draft tokens of one sequence.
 
     zq [K, V]   draft logits of the K drafted positions (float64 values)
     zp [K+1, V] target logits; row K scores the position after the last draft token
     x  [K]      draft tokens;  u [K+1] uniforms, u[K] samples the bonus token
-    sets        per-position Saguaro sets (or None), C the Saguaro factor
+    sets        per-position Saguaro sets (or None), C the Saguaro factor: one value for every
+                position, or K values, position i down-weighting its set by C[i] ([SSD] "关于逐位置
+                的思考": the pages' C is global and a per-position C is the direction they name)
 
     Steps ([SD7.3] 7.3.2 steps 3-4 and 7.3.3; [HW] "三、接受概率为什么是对的"; [SSD] "接受-拒绝机制"):
     accept x_i with probability min(1, p(x_i)/q(x_i)); stop at the first rejection and discard the
@@ -118,11 +120,13 @@ def verify_sequence(zq: np.ndarray, zp: np.ndarray, x: Sequence[int], u: Sequenc
     V = zq.shape[1]
     assert zq.shape[0] >= K and zp.shape == (K + 1, V) and len(u) == K + 1
     p = [softmax_t(zp[i], T) for i in range(K + 1)]
+    Cs = [float(C)] * K if np.ndim(C) == 0 else [float(c) for c in C]
+    assert len(Cs) == K
     qd = []
     for i in range(K):
         q = softmax_t(zq[i], T)
         if sets is not None:
-            q, _, _ = saguaro(q, sets[i], C)
+            q, _, _ = saguaro(q, sets[i], Cs[i])
         qd.append(q)
 
     a = np.empty(K)
@@ -159,8 +163,9 @@ def verify_sequence(zq: np.ndarray, zp: np.ndarray, x: Sequence[int], u: Sequenc
 
 
 def verify_batch(draft: np.ndarray, target: np.ndarray, dtype: str, x: np.ndarray, u: np.ndarray,
-                 T: float, sets: Optional[np.ndarray] = None, C: float = 1.0, seqs=None):
-    """verify_sequence over sequences of stored logits; draft [B, >=K, V], target [B, K+1, V]."""
+                 T: float, sets: Optional[np.ndarray] = None, C=1.0, seqs=None):
+    """verify_sequence over sequences of stored logits; draft [B, >=K, V], target [B, K+1, V];
+    C one value or K per-position values."""
     B, K = x.shape
     seqs = range(B) if seqs is None else seqs
     out = {}

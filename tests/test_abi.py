@@ -48,8 +48,8 @@ def test_status_strings():
 def _verify(**over):
     B, K, V = 2, 4, 1000
     a = dict(draft=FAKE, dstride=K * V, target=FAKE, tstride=(K + 1) * V, dtype=ssd.SSD_F32, B=B, K=K,
-             V=V, T=1.0, x=FAKE, u=FAKE, sset=None, sF=0, C=1.0, topfF=None, topfFmax=0, topf_out=None,
-             k=FAKE, bonus=FAKE, aprob=None, rmass=None, ws=None, wsb=0, stream=None)
+             V=V, T=1.0, x=FAKE, u=FAKE, sset=None, sF=0, C=1.0, Cpos=None, topfF=None, topfFmax=0,
+             topf_out=None, k=FAKE, bonus=FAKE, aprob=None, rmass=None, ws=None, wsb=0, stream=None)
     a.update(over)
     return ssd.lib().ssd_verify(*a.values())
 
@@ -75,6 +75,15 @@ def test_verify_argument_validation(over, want):
     assert _verify(**over) == want
 
 
+def test_verify_per_position_c_is_checked():
+    good = (ctypes.c_float * 4)(0.5, 0.3, 1.0, 0.0)
+    bad = (ctypes.c_float * 4)(0.5, 1.2, 1.0, 0.0)
+    nan = (ctypes.c_float * 4)(0.5, float("nan"), 1.0, 0.0)
+    assert _verify(sset=FAKE, sF=2, Cpos=ctypes.addressof(bad)) == INV
+    assert _verify(sset=FAKE, sF=2, Cpos=ctypes.addressof(nan)) == INV
+    assert _verify(sset=FAKE, sF=2, Cpos=ctypes.addressof(good)) == WS   # valid: fails at the workspace
+
+
 def test_verify_topf_per_position_range_is_checked():
     F = (ctypes.c_int32 * 4)(1, 2, 4, 1)                  # 4 > topf_F_max = 3
     assert _verify(topfF=ctypes.addressof(F), topfFmax=3, topf_out=FAKE) == INV
@@ -93,31 +102,31 @@ def test_topf_and_saguaro_validation():
     assert L.ssd_topf_guess(FAKE, 100, 0, 4, 100, None, None, 3, FAKE, None, 0, None) == WS
     assert L.ssd_topf_guess(FAKE, 100, 0, 0, 100, None, None, 3, FAKE, None, 0, None) == OK
     sag = L.ssd_saguaro_adjust
-    assert sag(FAKE, 100, 0, 4, 100, 0.0, None, 0, 0.5, None, None, None, None, 0, None) == INV
-    assert sag(FAKE, 100, 0, 4, 100, 1.0, None, 2, 0.5, None, None, None, None, 0, None) == INV
-    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 2, -0.1, None, None, None, None, 0, None) == INV
-    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 17, 0.5, None, None, None, None, 0, None) == INV
-    assert sag(FAKE, 99, 0, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == INV
-    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == WS
-    assert sag(FAKE, 100, 5, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == UNS
-    assert sag(FAKE, 100, 0, 0, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, 0, None) == OK
+    assert sag(FAKE, 100, 0, 4, 100, 0.0, None, 0, 0.5, None, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, None, 2, 0.5, None, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 2, -0.1, None, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 17, 0.5, None, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 99, 0, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, None, 0, None) == INV
+    assert sag(FAKE, 100, 0, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, None, 0, None) == WS
+    assert sag(FAKE, 100, 5, 4, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, None, 0, None) == UNS
+    assert sag(FAKE, 100, 0, 0, 100, 1.0, FAKE, 2, 0.5, None, None, None, None, None, 0, None) == OK
 
 
 def test_saguaro_topf_validation():
     st = ssd.lib().ssd_saguaro_topf
     # (logits, stride, dtype, R, V, T, F_per_row, F_max, C, out_set, sigma, N, ws, bytes, stream)
-    assert st(FAKE, 100, 9, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == UNS
-    assert st(FAKE, 99, 0, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 0.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, float("inf"), None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 0, 0.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 17, 0.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 1.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, float("nan"), FAKE, None, None, None, 0, None) == INV
-    assert st(None, 100, 0, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 0.5, None, None, None, None, 0, None) == INV
-    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == WS
-    assert st(FAKE, 100, 0, 0, 100, 1.0, None, 3, 0.5, FAKE, None, None, None, 0, None) == OK
+    assert st(FAKE, 100, 9, 4, 100, 1.0, None, 3, 0.5, None, FAKE, None, None, None, 0, None) == UNS
+    assert st(FAKE, 99, 0, 4, 100, 1.0, None, 3, 0.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 0.0, None, 3, 0.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, float("inf"), None, 3, 0.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 0, 0.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 17, 0.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 1.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, float("nan"), None, FAKE, None, None, None, 0, None) == INV
+    assert st(None, 100, 0, 4, 100, 1.0, None, 3, 0.5, None, FAKE, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 0.5, None, None, None, None, None, 0, None) == INV
+    assert st(FAKE, 100, 0, 4, 100, 1.0, None, 3, 0.5, None, FAKE, None, None, None, 0, None) == WS
+    assert st(FAKE, 100, 0, 0, 100, 1.0, None, 3, 0.5, None, FAKE, None, None, None, 0, None) == OK
     assert ssd.ssd_saguaro_topf_workspace_bytes(768, 128256, 3) > 0
     assert ssd.ssd_saguaro_topf_workspace_bytes(4, 100, 0) == 0
 

@@ -191,6 +191,38 @@ def test_saguaro_statistics_with_a_long_masked_prefix(dtype):
             assert abs(sig[r].item() - s_ref) < PROB_ATOL and abs(N[r].item() - n_ref) < PROB_ATOL, f"row {r}"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_per_row_saguaro_c_in_both_saguaro_calls(dtype):
+    """A Saguaro factor per row (the branch rows of different draft positions): both entry points
+    against the oracle; an out-of-range factor is clamped (NaN taken as 1) and flagged."""
+    R, V, F = 40, 5000, 3
+    rng = np.random.default_rng(21)
+    z = rng.normal(0, 2, size=(R, V)).astype(np.float32)
+    zz = synth.f32_to_bf16_bits(z) if dtype == "bf16" else z
+    z64 = O.logits_f64(zz, dtype)
+    Cr = rng.uniform(0.0, 1.0, size=R).astype(np.float32)
+    Cr[0], Cr[1], Cr[5], Cr[9] = 0.0, 1.0, 1.5, np.nan
+    C_eff = np.where(np.isnan(Cr), 1.0, np.clip(Cr, 0.0, 1.0))
+    sets = np.stack([O.topf(z64[r], F) for r in range(R)]).astype(np.int32)
+    zd = logits_to_device(zz, dtype)
+    Cd = torch.from_numpy(Cr).to(DEV)
+    print(f"[case] per-row C {dtype}", flush=True)
+    ws_a = ssd.Workspace(ssd.ssd_saguaro_workspace_bytes(R, V))
+    qp, sig_a, N_a = ssd.ssd_saguaro_adjust(zd, 1.0, torch.from_numpy(sets).to(DEV), 0.5, C_per_row=Cd,
+                                            materialise=True, workspace=ws_a)
+    ws_b = ssd.Workspace(ssd.ssd_saguaro_topf_workspace_bytes(R, V, F))
+    S, sig_b, N_b = ssd.ssd_saguaro_topf(zd, 1.0, F, 0.5, C_per_row=Cd, workspace=ws_b)
+    assert ssd.ssd_read_flags(ws_a) == ssd.FLAG_BAD_C
+    assert ssd.ssd_read_flags(ws_b) == ssd.FLAG_BAD_C
+    assert np.array_equal(S.cpu().numpy(), sets)
+    qp = qp.cpu().numpy()
+    for r in range(R):
+        want, s_ref, n_ref = O.saguaro(O.softmax_t(z64[r], 1.0), sets[r], float(C_eff[r]))
+        for sig, N in ((sig_a, N_a), (sig_b, N_b)):
+            assert abs(sig[r].item() - s_ref) < PROB_ATOL and abs(N[r].item() - n_ref) < PROB_ATOL, f"row {r}"
+        np.testing.assert_allclose(qp[r], want, atol=PROB_ATOL, rtol=0)
+
+
 @pytest.mark.parametrize("B,K,G,fan", [(3, 4, 3, [3, 2, 2, 2, 3]), (5, 4, 8, [8, 7, 5, 5, 7]),
                                        (2, 2, 2, [0, 2, 1]), (1, 1, 1, [1, 0])])
 def test_cache_keys_and_lookup_match_oracle(B, K, G, fan):

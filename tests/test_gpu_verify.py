@@ -187,7 +187,7 @@ def test_output_marginal_is_the_target_distribution():
 def test_empty_batch_is_a_no_op():
     L = ssd.lib()
     ws = ssd.Workspace(256)
-    st = L.ssd_verify(None, 400, None, 500, 0, 0, 4, 100, 1.0, None, None, None, 0, 1.0, None, 0, None,
+    st = L.ssd_verify(None, 400, None, 500, 0, 0, 4, 100, 1.0, None, None, None, 0, 1.0, None, None, 0, None,
                       None, None, None, None, ws.ptr, ws.nbytes, None)
     assert st == ssd.SSD_OK
 
@@ -199,3 +199,41 @@ def test_launch_count_on_the_device():
     assert one == 1
     assert many > 1 and many == ssd.ssd_verify_launches(4096, 4, 128256, ssd.SSD_BF16, 3)
     assert ssd.ssd_verify_launches(1, 4, 32000, ssd.SSD_F32, 0) == 1
+
+
+# --- per-position Saguaro factor ---------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_per_position_saguaro_c_matches_oracle(dtype):
+    B, K, V = 8, 4, 30000
+    bt = synth.make_verify_batch(B, K, V, dtype, 5, sag_sizes=[3, 2, 2, 2], C=0.5)
+    Cs = [0.2, 0.5, 0.0, 1.0]
+    d = batch_to_device(bt)
+    aprob = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    rmass = torch.empty(B, dtype=torch.float32, device=DEV)
+    print(f"[case] per-position C {dtype}", flush=True)
+    call = ssd.VerifyCall(d["draft"], d["target"], d["x"], d["u"], bt.T, sag_set=d["sets"], sag_C=Cs,
+                          topf_F_max=3, accept_prob=aprob, residual_mass=rmass)
+    out = call()
+    torch.cuda.synchronize()
+    assert ssd.ssd_read_flags(call.workspace) == 0
+    ref = O.verify_batch(bt.draft, bt.target, bt.dtype, bt.x, bt.u, bt.T, bt.sets, Cs)
+    report(f"per-position C {dtype}", compare_verify(bt, out, ref, aprob, rmass))
+
+
+def test_uniform_per_position_c_gives_the_single_value_bits():
+    B, K, V = 8, 4, 50000
+    bt = synth.make_verify_batch(B, K, V, synth.BF16, 6, sag_sizes=[3, 2, 2, 2], C=0.3)
+    d = batch_to_device(bt)
+    print("[case] uniform per-position C", flush=True)
+    res = []
+    for C in (0.3, [0.3] * K):
+        aprob = torch.empty((B, K), dtype=torch.float32, device=DEV)
+        rmass = torch.empty(B, dtype=torch.float32, device=DEV)
+        out = ssd.ssd_verify(d["draft"], d["target"], d["x"], d["u"], bt.T, sag_set=d["sets"], sag_C=C,
+                             topf_F_max=3, accept_prob=aprob, residual_mass=rmass)
+        torch.cuda.synchronize()
+        res.append([out["accepted_len"].cpu().numpy(), out["bonus_token"].cpu().numpy(),
+                    aprob.cpu().numpy().view(np.int32), rmass.cpu().numpy().view(np.int32),
+                    out["topf"].cpu().numpy()])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)

@@ -203,6 +203,36 @@ def test_lossless_two_positions_and_bonus_after_full_acceptance():
     np.testing.assert_allclose(third / p_k2, _norm(P3), atol=1e-12)
 
 
+def test_lossless_two_positions_with_per_position_saguaro():
+    """Drafts from per-position q'_i (C_1 = 1/3 and C_2 = 1/2 on token 0), verified against them:
+    every emitted token keeps the target marginal. q'_1 = [1,1,2,2]/6 and q'_2 = [2,2,1,1]/6 are
+    worked by hand; every decision boundary falls on the 1/12 grid, so the integral is exact."""
+    zq = _logits([Q1, Q2])
+    zp = _logits([P1, P2, P3])
+    q1, q2 = np.array([1, 1, 2, 2]) / 6.0, np.array([2, 2, 1, 1]) / 6.0
+    G = 12
+    first, second, third = np.zeros(4), np.zeros(4), np.zeros(4)
+    p_k1 = p_k2 = 0.0
+    g = _grid(G)
+    for x1, x2 in itertools.product(range(4), range(4)):
+        w = q1[x1] * q2[x2] / G ** 3
+        for u1, u2, u3 in itertools.product(g, g, g):
+            r = O.verify_sequence(zq, zp, [x1, x2], [u1, u2, u3], 1.0, [[0], [0]], [1.0 / 3.0, 0.5])
+            first[x1 if r.k >= 1 else r.bonus] += w
+            if r.k >= 1:
+                p_k1 += w
+                second[x2 if r.k == 2 else r.bonus] += w
+            if r.k == 2:
+                p_k2 += w
+                third[r.bonus] += w
+    np.testing.assert_allclose(first, _norm(P1), atol=1e-12)
+    np.testing.assert_allclose(second / p_k1, _norm(P2), atol=1e-12)
+    np.testing.assert_allclose(third / p_k2, _norm(P3), atol=1e-12)
+    # the accept probabilities of the first position against the hand-worked q'_1
+    r = O.verify_sequence(zq, zp, [0, 0], [0.5, 0.5, 0.5], 1.0, [[0], [0]], [1.0 / 3.0, 0.5])
+    assert r.a[0] == pytest.approx(0.75, abs=1e-15)
+
+
 def test_accepted_length_is_geometric_with_identical_rows():
     """[SSD] 最优扇出度分配: with the same acceptance rate a at every position the accepted
     length is geometric, P(k) = (1-a) a^k (k < K), a^K (k = K)."""
