@@ -6,6 +6,7 @@ Every function is pinned by ``tests/test_oracle_pins.py`` against facts the page
 (closed forms, library routines, exact enumeration, brute force); none is "parity unpinned".
 """
 from .ssd_oracle import (  # noqa: F401
+    SampleResult,
     VerifyResult,
     all_hit_probability,
     branch_layout,
@@ -15,6 +16,7 @@ from .ssd_oracle import (  # noqa: F401
     geometric_pk,
     logits_f64,
     saguaro,
+    saguaro_sample,
     softmax_t,
     ssd_round,
     topf,

@@ -193,6 +193,37 @@ def topf(z: np.ndarray, F: int, exclude: int = -1) -> np.ndarray:
     return out
 
 
+@dataclass
+class SampleResult:
+    S: np.ndarray     # the Saguaro set: top-F of the row (-1 pads)
+    sigma: float      # q mass of S
+    N: float          # normaliser 1 - (1 - C) sigma
+    x: int            # sampled draft token, -1 when q' has no mass
+    qx: float         # q'(x)
+    c_lo: float       # cumulative q' before x; the draw is x exactly when c_lo <= u < c_hi
+    c_hi: float       # cumulative q' through x
+
+
+def saguaro_sample(z: np.ndarray, T: float, F: int, C: float, u: float) -> SampleResult:
+    """Draft-side Saguaro sampling of one row ([SSD] "Saguaro 优化二：Saguaro 采样",
+    "解法：操纵草稿分布"): the down-weighted set is the row's own top F (raw logits, nothing
+    excluded), the draft distribution is q' = saguaro(softmax_t(z, T), S, C), and the draft token
+    is drawn from q' with the uniform u by the inverse CDF in ascending token order, the reading
+    used for the bonus token: the first token whose cumulative q' exceeds u, or the last token of
+    positive mass when u is not below the total."""
+    z = np.asarray(z, dtype=np.float64)
+    S = topf(z, F)
+    q = softmax_t(z, T)
+    qs, sigma, N = saguaro(q, [int(v) for v in S if v >= 0], C)
+    cum = np.cumsum(qs)
+    x = int(np.searchsorted(cum, float(u), side="right"))  # first index with cum > u
+    if x >= len(qs):
+        x = int(np.nonzero(qs > 0.0)[0][-1])
+    c_lo = float(cum[x - 1]) if x > 0 else 0.0
+    return SampleResult(S=S, sigma=float(sigma), N=float(N), x=x, qx=float(qs[x]), c_lo=c_lo,
+                        c_hi=float(cum[x]))
+
+
 def geometric_pk(K: int, a: float) -> np.ndarray:
     """Geometric acceptance law ([SSD] "最优扇出度分配"): P(k) = (1-a) a^k for k < K, a^K for k = K."""
     P = np.array([(1.0 - a) * a ** k for k in range(K)] + [a ** K], dtype=np.float64)

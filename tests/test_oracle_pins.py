@@ -324,6 +324,54 @@ def test_topf_distinct_values_is_argsort():
 
 
 # ------------------------------------------------------------------------------------------
+# draft-side Saguaro sampling
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("F,C,T", [(0, 1.0, 1.0), (3, 0.2, 0.8), (7, 0.0, 1.3), (5, 1.0, 0.5)])
+def test_saguaro_sample_is_the_library_inverse_cdf(F, C, T):
+    """x is scipy's discrete quantile function of q' (the pinned saguaro() over the pinned top-F
+    set), for random u; the reported set, mass and normaliser are those of the same q'."""
+    from scipy.stats import rv_discrete
+    rng = np.random.default_rng(11 + F)
+    V = 300
+    z = rng.normal(0, 2, size=V)
+    z[rng.random(V) < 0.05] = -np.inf
+    S = O.topf(z, F)
+    qs, sig, N = O.saguaro(O.softmax_t(z, T), [int(v) for v in S if v >= 0], C)
+    dist = rv_discrete(values=(np.arange(V), qs / qs.sum()))
+    for u in rng.random(200):
+        r = O.saguaro_sample(z, T, F, C, float(u))
+        assert r.x == int(dist.ppf(u))
+        assert list(r.S) == list(S) and r.sigma == sig and r.N == N
+        assert r.qx == qs[r.x] and r.c_lo <= u < r.c_hi
+
+
+def test_saguaro_sample_grid_frequencies_are_q_prime():
+    """Uniforms on a midpoint grid of G points land on token v about G q'(v) times (within one
+    point per boundary): the inverse CDF carries the uniform onto q'."""
+    w = np.array([3, 1, 4, 1, 5, 9, 2, 6, 5, 3, 5, 8], dtype=np.float64)
+    z = _logits(w)
+    G = 20000
+    xs = np.array([O.saguaro_sample(z, 1.0, 3, 0.25, u).x for u in _grid(G)])
+    top3 = {5, 11, 7}  # weights 9, 8, 6
+    ww = np.array([wi * (0.25 if v in top3 else 1.0) for v, wi in enumerate(w)])
+    want = G * ww / ww.sum()
+    assert np.abs(np.bincount(xs, minlength=len(w)) - want).max() <= 1.0
+
+
+def test_saguaro_sample_edges():
+    """u = 0 gives the first token of positive mass; u at or past 1 the last; C = 0 never draws a
+    set member; a masked token is never drawn."""
+    z = np.array([-np.inf, 0.5, 2.0, -np.inf, 1.0, 3.0, -1.0, -np.inf])
+    assert O.saguaro_sample(z, 1.0, 2, 0.5, 0.0).x == 1
+    assert O.saguaro_sample(z, 1.0, 2, 0.5, 1.0).x == 6
+    assert O.saguaro_sample(z, 1.0, 2, 0.5, 1.0 - 1e-15).x == 6
+    xs = {O.saguaro_sample(z, 0.7, 2, 0.0, u).x for u in _grid(5000)}
+    assert xs == {1, 4, 6}  # every unmasked token outside the top two {5, 2}
+    xs = {O.saguaro_sample(z, 0.7, 0, 0.0, u).x for u in _grid(5000)}
+    assert xs == {1, 2, 4, 5, 6}
+
+
+# ------------------------------------------------------------------------------------------
 # fan-out
 # ------------------------------------------------------------------------------------------
 def _objective(P, F, r):
