@@ -110,9 +110,10 @@ def cpu_baseline(bt, topf, seconds):
                        f"float64 NumPy oracle verify + top-{topf} guesses, {el:.1f} s on 1 thread")
 
 
-def cpu_baseline_round(bt, branch, fan, seconds):
+def cpu_baseline_round(bt, branch, branch_u, fan, seconds):
     """The float64 oracle on a bounded sample of an SSD round (single thread): whole sequences,
-    each with its verification, guesses, keys, lookup and its branch rows' sets and Saguaro."""
+    each with its verification, guesses, keys, lookup and its branch rows' draft step (set,
+    Saguaro mass and normaliser, sampled token)."""
     import oracle as O
 
     t0 = time.perf_counter()
@@ -122,7 +123,7 @@ def cpu_baseline_round(bt, branch, fan, seconds):
     while True:
         b = seqs % B
         O.ssd_round(bt.draft[b:b + 1], bt.target[b:b + 1], bt.dtype, bt.x[b:b + 1], bt.u[b:b + 1], bt.T,
-                    bt.sets[b:b + 1], bt.C, fan, branch=branch[b:b + 1])
+                    bt.sets[b:b + 1], bt.C, fan, branch=branch[b:b + 1], branch_u=branch_u[b:b + 1])
         seqs += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -190,8 +191,8 @@ class _Stage:
 def pipeline_bench(args, spec):
     """One SSD round per step (the cache build and the full round): verification with Saguaro sets
     and per-position top-F guesses, the guesses of draft row K, cache keys, lookup of the outcome,
-    and, for the speculation-cache branches, their top-F sets with Saguaro mass and normaliser in
-    one pass over each branch row (ssd_saguaro_topf). Each stage
+    and, for the speculation-cache branches, the draft step of every branch row in one pass: its
+    top-F set, Saguaro mass and normaliser, and a token drawn from q' (ssd_saguaro_sample). Each stage
     is timed on the GPU with an event pair per step; its algorithmic bytes (every logit it reads,
     once, plus its small inputs and outputs) over that time give its bandwidth."""
     import numpy as np
@@ -209,6 +210,7 @@ def pipeline_bench(args, spec):
     stream = torch.cuda.current_stream(dev)
     bt = synth.make_verify_batch(B, K, V, dtype, args.seed, T=T, sag_sizes=fan[:K], C=spec["C"])
     branch = synth.make_branch_rows(B, budget, K, V, dtype, args.seed)
+    branch_u = synth.make_branch_uniforms(B, budget, K, args.seed)
     Rb = B * budget * K  # branch rows
 
     def lg(a):
@@ -219,7 +221,8 @@ def pipeline_bench(args, spec):
 
     b_verify = (2 * K + 1) * B * V * es + B * K * 4 + B * (K + 1) * 4 + B * K * Gm * 4 + 2 * B * 4 + B * K * Gm * 4
     b_rowk = B * V * es + B * fan[K] * 4
-    b_branch = Rb * V * es + Rb * 4 + Rb * Gm * 4 + 2 * Rb * 4  # one read of every branch row
+    # one read of every branch row; F and u in; set, sigma, N, token and q'(token) out
+    b_branch = Rb * V * es + 2 * Rb * 4 + Rb * Gm * 4 + 4 * Rb * 4
     b_keys = B * (K + 1) * Gm * 4 + 2 * B * budget * 4
     b_lookup = 2 * B * budget * 4 + 2 * B * 4 + B * 4 + 4
     total_logit_bytes = ((2 * K + 2) * B + Rb) * V * es
@@ -228,7 +231,8 @@ def pipeline_bench(args, spec):
     reps = []
     ws_v = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, Gm), dev)
     ws_k = ssd.Workspace(ssd.ssd_topf_workspace_bytes(B, V, fan[K]), dev)
-    ws_b = ssd.Workspace(ssd.ssd_saguaro_topf_workspace_bytes(Rb, V, Gm), dev)
+    ws_b = ssd.Workspace(ssd.ssd_saguaro_sample_workspace_bytes(Rb, V, Gm), dev)
+    ub = torch.from_numpy(branch_u.reshape(-1)).to(dev)
     Fr = torch.tensor(fan[:K], dtype=torch.int32, device=dev).repeat(B * budget)
     for _ in range(n_rep):
         r = {}
@@ -241,6 +245,8 @@ def pipeline_bench(args, spec):
         r["bsets"] = torch.empty((Rb, Gm), dtype=torch.int32, device=dev)
         r["sig"] = torch.empty(Rb, dtype=torch.float32, device=dev)
         r["N"] = torch.empty(Rb, dtype=torch.float32, device=dev)
+        r["btok"] = torch.empty(Rb, dtype=torch.int32, device=dev)
+        r["bprob"] = torch.empty(Rb, dtype=torch.float32, device=dev)
         r["ck"] = torch.empty((B, budget), dtype=torch.int32, device=dev)
         r["ct"] = torch.empty((B, budget), dtype=torch.int32, device=dev)
         r["slot"] = torch.empty(B, dtype=torch.int32, device=dev)
@@ -267,9 +273,10 @@ def pipeline_bench(args, spec):
             _Stage("lookup (ssd_cache_lookup)", b_lookup,
                    lambda: ssd.ssd_cache_lookup(r["ck"], r["ct"], out["accepted_len"], out["bonus_token"],
                                                 out_slot=r["slot"], out_miss_count=r["miss"])),
-            _Stage("branch sets + Saguaro (ssd_saguaro_topf)", b_branch,
-                   lambda: ssd.ssd_saguaro_topf(r["bd"], T, Gm, bt.C, F_per_row=Fr, out_set=r["bsets"],
-                                                out_set_mass=r["sig"], out_norm=r["N"], workspace=ws_b)),
+            _Stage("branch draft step (ssd_saguaro_sample)", b_branch,
+                   lambda: ssd.ssd_saguaro_sample(r["bd"], T, Gm, bt.C, ub, F_per_row=Fr, out_token=r["btok"],
+                                                  out_prob=r["bprob"], out_set=r["bsets"], out_set_mass=r["sig"],
+                                                  out_norm=r["N"], workspace=ws_b)),
         ]
 
     plans = [stages(r) for r in reps]
@@ -302,7 +309,7 @@ def pipeline_bench(args, spec):
         st_out[st.name] = {"ms": round(ms, 5), "algorithmic_bytes": st.nbytes,
                            "GB/s": round(st.nbytes / (ms * 1e-3) / 1e9, 1)}
     dom = max(range(nst), key=lambda j: stage_ms[j])
-    cpu = None if args.no_cpu_baseline else cpu_baseline_round(bt, branch, fan, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_round(bt, branch, branch_u, fan, args.cpu_seconds)
     line = {
         "metric": METRIC,
         "value": round(rows / (step_ms * 1e-3), 1),

@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     ssd_fanout_alloc,
     ssd_read_flags,
     ssd_saguaro_adjust,
+    ssd_saguaro_sample,
+    ssd_saguaro_sample_workspace_bytes,
     ssd_saguaro_topf,
     ssd_saguaro_topf_workspace_bytes,
     ssd_saguaro_workspace_bytes,

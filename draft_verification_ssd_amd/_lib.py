@@ -19,6 +19,7 @@ FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT, FLAG_BAD_C = 0x1, 0
 
 EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify", "ssd_topf_workspace_bytes",
            "ssd_topf_guess", "ssd_saguaro_topf_workspace_bytes", "ssd_saguaro_topf",
+           "ssd_saguaro_sample_workspace_bytes", "ssd_saguaro_sample",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",
            "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string"]
 
@@ -49,6 +50,11 @@ def _declare(L):
     L.ssd_saguaro_topf_workspace_bytes.argtypes = [I32, I32, I32]
     L.ssd_saguaro_topf.restype = ctypes.c_int
     L.ssd_saguaro_topf.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, P, SZ, P]
+    L.ssd_saguaro_sample_workspace_bytes.restype = SZ
+    L.ssd_saguaro_sample_workspace_bytes.argtypes = [I32, I32, I32]
+    L.ssd_saguaro_sample.restype = ctypes.c_int
+    L.ssd_saguaro_sample.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, P, P, P,
+                                     P, SZ, P]
     L.ssd_saguaro_workspace_bytes.restype = SZ
     L.ssd_saguaro_workspace_bytes.argtypes = [I32, I32]
     L.ssd_saguaro_adjust.restype = ctypes.c_int
@@ -161,6 +167,10 @@ def ssd_topf_workspace_bytes(R: int, V: int, F_max: int) -> int:
 
 def ssd_saguaro_topf_workspace_bytes(R: int, V: int, F_max: int) -> int:
     return int(lib().ssd_saguaro_topf_workspace_bytes(R, V, F_max))
+
+
+def ssd_saguaro_sample_workspace_bytes(R: int, V: int, F_max: int) -> int:
+    return int(lib().ssd_saguaro_sample_workspace_bytes(R, V, F_max))
 
 
 def ssd_saguaro_workspace_bytes(R: int, V: int) -> int:
@@ -344,6 +354,48 @@ def ssd_saguaro_topf(logits, temperature: float, F_max: int, C: float, *, F_per_
                                  out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr, workspace.nbytes,
                                  _stream(stream, dev)), "ssd_saguaro_topf")
     return out_set, out_set_mass, out_norm
+
+
+def ssd_saguaro_sample(logits, temperature: float, F_max: int, C: float, u, *, F_per_row=None,
+                       C_per_row=None, out_token=None, out_prob=None, out_set=None, out_set_mass=None,
+                       out_norm=None, workspace: Optional[Workspace] = None, stream=None):
+    """The draft's sampling step with Saguaro: each row's top-F set, its mass and normaliser, and a
+    token drawn from the down-weighted distribution with the row's uniform u (device fp32 [R]) in
+    one pass; returns (token, q' of it, set, sigma, N)."""
+    torch = _torch()
+    if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
+        raise ValueError("logits must be a [R, V] device view with unit element stride")
+    R, V = logits.shape
+    dev = logits.device
+    _need(u, torch.float32, (R,), "u")
+    if F_per_row is not None:
+        _need(F_per_row, torch.int32, (R,), "F_per_row")
+    if C_per_row is not None:
+        _need(C_per_row, torch.float32, (R,), "C_per_row")
+    if out_token is None:
+        out_token = torch.empty(R, dtype=torch.int32, device=dev)
+    if out_prob is None:
+        out_prob = torch.empty(R, dtype=torch.float32, device=dev)
+    if out_set is None:
+        out_set = torch.empty((R, F_max), dtype=torch.int32, device=dev)
+    if out_set_mass is None:
+        out_set_mass = torch.empty(R, dtype=torch.float32, device=dev)
+    if out_norm is None:
+        out_norm = torch.empty(R, dtype=torch.float32, device=dev)
+    _need(out_token, torch.int32, (R,), "out_token")
+    _need(out_prob, torch.float32, (R,), "out_prob")
+    _need(out_set, torch.int32, (R, F_max), "out_set")
+    _need(out_set_mass, torch.float32, (R,), "out_set_mass")
+    _need(out_norm, torch.float32, (R,), "out_norm")
+    if workspace is None:
+        workspace = Workspace(ssd_saguaro_sample_workspace_bytes(R, V, F_max), dev)
+    stride = logits.stride(0) if R > 1 else V
+    check(lib().ssd_saguaro_sample(logits.data_ptr(), stride, _dtype_code(logits), R, V, float(temperature),
+                                   _ptr(F_per_row), int(F_max), float(C), _ptr(C_per_row), u.data_ptr(),
+                                   out_token.data_ptr(), out_prob.data_ptr(), _ptr(out_set if F_max > 0 else None),
+                                   out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr, workspace.nbytes,
+                                   _stream(stream, dev)), "ssd_saguaro_sample")
+    return out_token, out_prob, out_set, out_set_mass, out_norm
 
 
 def ssd_fanout_alloc(K: int, a: float, r: float, budget: int):

@@ -232,6 +232,58 @@ ssd_status ssd_saguaro_topf(const void* logits, int64_t row_stride, ssd_dtype dt
 }
 
 // ------------------------------------------------------------------------------------------------
+size_t ssd_saguaro_sample_workspace_bytes(int R, int V, int F_max) {
+  if (R < 0 || V < 1 || V > SSD_MAX_V || F_max < 0 || F_max > SSD_MAX_F) return 0;
+  return sample_layout(R, V, F_max).total;
+}
+
+ssd_status ssd_saguaro_sample(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                              float temperature, const int32_t* F_per_row, int F_max, float C,
+                              const float* C_per_row, const float* u, int32_t* out_token,
+                              float* out_prob, int32_t* out_set, float* out_set_mass, float* out_norm,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
+  if (R < 0 || R > (1 << 24) || V < 1 || V > SSD_MAX_V || F_max < 0 || F_max > SSD_MAX_F ||
+      row_stride < V || !temp_ok(temperature) || !c_ok(C))
+    return SSD_ERR_INVALID_ARG;
+  if (R == 0) return SSD_OK;
+  if (!logits || !u || !out_token || (F_max > 0 && !out_set)) return SSD_ERR_INVALID_ARG;
+  const SampleLayout L = sample_layout(R, V, F_max);
+  if ((V + int64_t(L.seg_len) - 1) / L.seg_len > 256) return SSD_ERR_INVALID_ARG;  // not reached for V <= SSD_MAX_V
+  if (!ws_ok(workspace, workspace_bytes, L.total)) return SSD_ERR_WORKSPACE;
+  const int es = elem_size(dtype);
+  TopfArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.R = R;
+  a.V = V;
+  a.exclude = nullptr;
+  a.F_per_row = F_max > 0 ? F_per_row : nullptr;
+  a.Fmax = F_max;
+  a.out = out_set;
+  a.flags = at<uint32_t>(workspace, 0);
+  a.cand = at<void>(workspace, L.t.off_cand);
+  a.n1 = L.t.rp.n1;
+  a.chunk1 = L.t.rp.chunk1;
+  a.aligned = aligned16(logits) && (row_stride * es) % 16 == 0;
+  a.sag = 1;
+  a.c2 = float(kLog2e / double(temperature));
+  a.C = C;
+  a.C_per_row = C_per_row;
+  a.stats = at<float2>(workspace, L.t.off_stats);
+  a.out_set_mass = out_set_mass;
+  a.out_norm = out_norm;
+  a.u = u;
+  a.out_token = out_token;
+  a.out_prob = out_prob;
+  a.seg_len = L.seg_len;
+  a.nseg = L.nseg;
+  a.seg = at<float2>(workspace, L.off_seg);
+  return hip_status(launch_topf(a, dtype == SSD_BF16, stream));
+}
+
+// ------------------------------------------------------------------------------------------------
 size_t ssd_saguaro_workspace_bytes(int R, int V) {
   if (R < 0 || V < 1 || V > SSD_MAX_V) return 0;
   return saguaro_layout(R, V).total;

@@ -96,7 +96,8 @@ __device__ __forceinline__ void chunk_pass(const typename ET::T* __restrict__ ro
 // Merge candidate lists: n_lists lists of `stride` entries, of which the first F count. The top F
 // (value desc, index asc) go to out[0..F), -1 to out[F..Fmax). Runs on the whole block.
 __device__ void merge_lists(const Cand* __restrict__ cands, int n_lists, int stride, int F,
-                            int32_t* __restrict__ out, int Fmax, uint32_t* shk) {
+                            int32_t* __restrict__ out, int Fmax, uint32_t* shk,
+                            int* sh_set = nullptr) {
   constexpr int kPer = (kMaxChunks * kMaxF + kThreads - 1) / kThreads;
   const int n = n_lists * F;
   uint32_t kh[kPer], kl[kPer];
@@ -146,7 +147,10 @@ __device__ void merge_lists(const Cand* __restrict__ cands, int n_lists, int str
           kl[q] = 0;
         }
     }
-    if (threadIdx.x == 0) out[r] = (gh != 0) ? int(~gl) : -1;
+    if (threadIdx.x == 0) {
+      out[r] = (gh != 0) ? int(~gl) : -1;
+      if (sh_set) sh_set[r] = (gh != 0) ? int(~gl) : -1;
+    }
   }
   for (int r = F + threadIdx.x; r < Fmax; r += kThreads) out[r] = -1;
 }
@@ -283,18 +287,142 @@ struct LaneStats {
   }
 };
 
+// =============================================================================================
+// Draft-side Saguaro sampling: the inverse CDF of q' in ascending token order
+// =============================================================================================
+// The streaming pass leaves every segment of seg_len tokens its q mass as a (max c, sum) pair. The
+// segment where the cumulative q' mass first exceeds u times the total is found from those pairs
+// (one segment per thread; the set members' share of a segment is scaled by C), then only that
+// segment is read again, each thread owning seg_len / 256 consecutive tokens: a block scan of the
+// runs' masses names the run, whose thread walks it token by token. When rounding leaves the
+// target past the last crossing, the last token of positive mass is taken (segment, then run).
+constexpr float kSegEps = 9.5367431640625e-07f;  // 2^-20: a segment's q' mass below this share of
+                                                 // its q mass is cancellation left over, not mass
+static_assert(kPlanSampleSpan == kThreads * kTBatch, "a sampling segment is whole top-F batches");
+static_assert(kPlanMaxSeg * kWaves <= 64, "one wave holds every per-wave segment pair");
+
+// tokens [b0, b1) of row p in ascending order, 16-byte loads when aligned (b0 % kVec == 0)
+template <class ET, class Fn>
+__device__ __forceinline__ void for_run(const typename ET::T* __restrict__ p, int b0, int b1, bool aligned,
+                                        Fn fn) {
+  constexpr int N = ET::kVec;
+  int e = b0;
+  if (aligned) {
+    for (; e + N <= b1; e += N) {
+      float z[N];
+      ET::unpack(load16(p + e), z);
+#pragma unroll
+      for (int j = 0; j < N; ++j) fn(z[j], e + j);
+    }
+  }
+  for (; e < b1; ++e) fn(ET::one(p, e), e);
+}
+
+// Whole block. segm: ns <= 256 segment pairs (LDS); set / zs: the F set members and their logits
+// (LDS, -1 for an empty place); L = log2 of the row's normaliser in the units of z c. Writes the
+// token (-1 when q' has no mass) and q' of it. shf >= kWaves + 2 floats, shi >= kWaves ints.
+template <class ET>
+__device__ void block_sample(const typename ET::T* __restrict__ p, int V, bool aligned, const float2* segm,
+                             int ns, int seg_len, float L, float cc, float Cr, float Nn, const int* set,
+                             const float* zs, int F, float u, float* shf, int* shi, int32_t* out_token,
+                             float* out_prob, uint32_t* flags) {
+  const int t = threadIdx.x;
+  float m = 0.f;
+  if (t < ns) {
+    const float2 r = segm[t];
+    const float mq = (r.y > 0.f) ? r.y * ex2(r.x - L) : 0.f;
+    float in_set = 0.f;
+    for (int f = 0; f < F; ++f)
+      if (set[f] >= 0 && set[f] / seg_len == t) in_set += ex2(fmaf(zs[f], cc, -L));
+    const float mp = mq - (1.f - Cr) * in_set;
+    m = (mp > kSegEps * mq) ? mp : 0.f;
+  }
+  float Z;
+  const float excl = block_excl_scan(m, shf, Z);
+  const float tau = u * Z;
+  int sg = block_min_i((m > 0.f && excl + m > tau) ? t : INT_MAX, shi);
+  float rem = INFINITY;  // tau less the mass before the segment; +inf: its last token of mass
+  if (sg == INT_MAX) {
+    sg = block_max_i(m > 0.f ? t : -1, shi);
+  } else {
+    if (t == sg) shf[kWaves + 1] = tau - excl;
+    __syncthreads();
+    rem = shf[kWaves + 1];
+  }
+  if (sg < 0 || !(Nn > 0.f)) {  // no mass: a masked row, or C = 0 with the set holding it all
+    if (t == 0) {
+      *out_token = -1;
+      if (out_prob) *out_prob = 0.f;
+      if (L > -INFINITY) atomicOr(flags, kFlagSaguaroNorm);  // N = 0 up to rounding
+    }
+    return;
+  }
+  float zmin = INFINITY;  // smallest logit of the set: cheaper membership test
+  for (int f = 0; f < F; ++f)
+    if (set[f] >= 0) zmin = fminf(zmin, zs[f]);
+  auto mass = [&](float z, int e) {
+    float wgt = 1.f;
+    if (z >= zmin)
+      for (int f = 0; f < F; ++f)
+        if (set[f] == e) wgt = Cr;
+    return wgt * ex2(fmaf(z, cc, -L));
+  };
+  const int a0 = sg * seg_len, a1 = min(V, a0 + seg_len);
+  const int run = seg_len / kThreads;
+  const int b0 = min(a1, a0 + t * run), b1 = min(a1, b0 + run);
+  float sum = 0.f;
+  int lp = -1;
+  for_run<ET>(p, b0, b1, aligned, [&](float z, int e) {
+    const float q = mass(z, e);
+    sum += q;
+    if (q > 0.f) lp = e;
+  });
+  float Ts;
+  const float ex = block_excl_scan(sum, shf, Ts);
+  const int owner = block_min_i((sum > 0.f && ex + sum > rem) ? t : INT_MAX, shi);
+  int x = -1;
+  bool writer = false;
+  if (owner == INT_MAX) {
+    x = block_max_i(lp, shi);
+    writer = (t == 0);
+  } else if (t == owner) {
+    float c = ex;
+    for_run<ET>(p, b0, b1, aligned, [&](float z, int e) {
+      if (x < 0) {
+        c += mass(z, e);
+        if (c > rem) x = e;
+      }
+    });
+    if (x < 0) x = lp;
+    writer = true;
+  }
+  if (writer) {
+    *out_token = x;
+    if (out_prob) *out_prob = (x >= 0) ? mass(ET::one(p, x), x) / Nn : 0.f;
+  }
+}
+
 // SAG: ssd_saguaro_topf — the row's statistics in the same pass, and sigma = q mass of the top F
 // with N = 1 - (1 - C) sigma once the row is complete (here when a row is one chunk, else in the
-// merge kernel).
-template <class ET, int FM, bool SAG>
+// merge kernel). SMP (with SAG): ssd_saguaro_sample — the statistics are kept per segment and a
+// token is drawn from q' once the row is complete.
+template <class ET, int FM, bool SAG, bool SMP>
 __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
+  static_assert(SAG || !SMP, "sampling needs the row statistics");
   using T = typename ET::T;
   constexpr int N = ET::kVec;
   constexpr int U = kTBatch / N;  // vectors per lane per batch
+  constexpr int NS = SMP ? kPlanMaxSeg : 1;
   __shared__ uint64_t sbuf[kWaves][kTBuf];
   __shared__ uint64_t stop[kWaves][kMaxF];
   __shared__ int sn[kWaves];
   __shared__ float shf[2 * kWaves];
+  __shared__ float2 srec[NS][kWaves];  // per wave and segment: (max c, sum)
+  __shared__ float2 segm[NS];          // per segment, over the block
+  __shared__ int s_set[SMP ? kMaxF : 1];
+  __shared__ float s_zs[SMP ? kMaxF : 1];
+  __shared__ float s_lnc[3];
+  __shared__ int shi[kWaves];
   LaneStats ls;
   const float cc = a.c2;
   const int item = blockIdx.x;
@@ -319,7 +447,19 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   tw.tau = -INFINITY;
   tw.F = F;
   tw.exclude = ex;
-  if (F > 0) {
+  // SMP: a lane's statistics cover the current segment only; at a segment's end the wave's pair
+  // goes to srec and the lane starts again
+  int cur_seg = 0, seg_batches = 0;
+  const int G = SMP ? a.seg_len / kPlanSampleSpan : 1;
+  if (SMP && lane < NS) srec[lane][w] = make_float2(-INFINITY, 0.f);
+  auto seg_flush = [&]() __attribute__((always_inline)) {
+    const float Mw = wave_max(ls.mx);
+    const float Sw = wave_sum((ls.s > 0.f) ? ls.s * ex2(ls.mx * cc - Mw * cc) : 0.f);
+    if (lane == 0) srec[cur_seg][w] = make_float2(Mw * cc, Sw);
+    ls.mx = -INFINITY;
+    ls.s = 0.f;
+  };
+  if (F > 0 || SMP) {
     int tail0 = c0;
     if (a.aligned) {
       // thread t reads vectors t, t + 256, ... of the chunk, U per batch
@@ -341,8 +481,16 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
         float bm = z[0];
 #pragma unroll
         for (int e = 1; e < kTBatch; ++e) bm = fmaxf(bm, z[e]);
+        if (SMP) {  // batches come in order, G to a segment
+          if (seg_batches == G) {
+            seg_flush();
+            ++cur_seg;
+            seg_batches = 0;
+          }
+          ++seg_batches;
+        }
         if (SAG) ls.add(z, bm, cc);
-        tw.batch_bm(z, bm, [&](int e) { return (vb + (e / N) * kThreads) * N + (e % N); });
+        if (F > 0) tw.batch_bm(z, bm, [&](int e) { return (vb + (e / N) * kThreads) * N + (e % N); });
       };
       // two batches in flight: the next one loads while this one is examined (the trip count is
       // the same for every lane)
@@ -363,20 +511,47 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
       const int e = e0 + t;
       float z[1];
       z[0] = (e < c1) ? ET::one(p, e) : -INFINITY;
+      if (SMP) {
+        const int sg = (e0 - c0) / a.seg_len;
+        if (sg != cur_seg) {
+          seg_flush();
+          cur_seg = sg;
+        }
+      }
       if (SAG) ls.add(z, z[0], cc);
-      tw.batch_bm(z, z[0], [&](int) { return e; });
+      if (F > 0) tw.batch_bm(z, z[0], [&](int) { return e; });
     }
+    if (SMP) seg_flush();
     tw.n = wave_cut_keys(tw.buf, tw.n, F);  // the wave's top F, in order
   }
   if (lane == 0) sn[w] = tw.n;
   if (lane < kMaxF) stop[w][lane] = (lane < tw.n) ? tw.buf[lane] : 0ull;
   float MXc = -INFINITY, S = 0.f;  // the chunk's (max c, sum 2^(z c - max c))
-  if (SAG && F > 0) {
+  if (SAG && !SMP && F > 0) {
     const float MX = block_max(ls.mx, shf);
     MXc = MX * cc;
     S = block_sum((ls.s > 0.f) ? ls.s * ex2(ls.mx * cc - MXc) : 0.f, shf + kWaves);
   }
   __syncthreads();
+  if (SMP) {  // segment pairs over the block, then the chunk's pair from them
+    if (t < NS) {
+      float M = srec[t][0].x;
+#pragma unroll
+      for (int q = 1; q < kWaves; ++q) M = fmaxf(M, srec[t][q].x);
+      float Ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q)
+        if (srec[t][q].y > 0.f) Ss += srec[t][q].y * ex2(srec[t][q].x - M);
+      segm[t] = make_float2(M, Ss);
+      if (a.n1 > 1 && t < a.nseg) a.seg[(int64_t(row) * a.n1 + chunk) * a.nseg + t] = make_float2(M, Ss);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NS; ++q) MXc = fmaxf(MXc, segm[q].x);
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+      if (segm[q].y > 0.f) S += segm[q].y * ex2(segm[q].x - MXc);
+  }
   if (w == 0) {  // the chunk's top F from the waves' lists
     uint64_t k = 0ull;
     if (F > 0 && lane < kWaves * F) k = stop[lane / F][lane % F];
@@ -391,7 +566,8 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
       for (int r = lane; r < a.Fmax; r += 64) out[r] = (r < F && win_out) ? int(~uint32_t(win_out)) : -1;
       if (SAG) {  // sigma over the set, from the logits its keys carry
         const float L = MXc + lg2(S);
-        const float term = (lane < F && win_out) ? ex2(fmaf(key_to_float(uint32_t(win_out >> 32)), cc, -L)) : 0.f;
+        const float zk = key_to_float(uint32_t(win_out >> 32));
+        const float term = (lane < F && win_out) ? ex2(fmaf(zk, cc, -L)) : 0.f;
         const float sig = (F > 0) ? wave_sum(term) : 0.f;
         const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, lane == 0);
         const float Nn = 1.f - (1.f - Cr) * sig;
@@ -399,6 +575,17 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
           if (a.out_set_mass) a.out_set_mass[row] = sig;
           if (a.out_norm) a.out_norm[row] = Nn;
           if (!(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+        }
+        if (SMP) {
+          if (lane < F) {
+            s_set[lane] = win_out ? int(~uint32_t(win_out)) : -1;
+            s_zs[lane] = zk;
+          }
+          if (lane == 0) {
+            s_lnc[0] = L;
+            s_lnc[1] = Nn;
+            s_lnc[2] = Cr;
+          }
         }
       }
     } else {
@@ -410,39 +597,68 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
       if (SAG && lane == 0) a.stats[int64_t(row) * a.n1 + chunk] = make_float2(MXc, S);
     }
   }
+  if (SMP && a.n1 == 1) {
+    __syncthreads();
+    const int ns = (a.V + a.seg_len - 1) / a.seg_len;
+    block_sample<ET>(p, a.V, a.aligned != 0, segm, ns, a.seg_len, s_lnc[0], cc, s_lnc[2], s_lnc[1], s_set, s_zs,
+                     F, a.u[row], shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
+                     a.flags);
+  }
 }
 
-template <class ET, bool SAG>
+template <class ET, bool SAG, bool SMP>
 __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
   __shared__ uint32_t shk[2 * kWaves];
+  __shared__ int s_set[kMaxF];
+  __shared__ float s_zs[kMaxF];
+  __shared__ float2 s_segm[SMP ? kThreads : 1];
+  __shared__ float shf[2 * kWaves];
+  __shared__ int shi[kWaves];
+  __shared__ float s_lnc[3];
   const int row = blockIdx.x;
   int F = a.Fmax;
   if (a.F_per_row) {
     F = a.F_per_row[row];
     F = F < 0 ? 0 : (F > a.Fmax ? a.Fmax : F);
   }
+  const typename ET::T* p = reinterpret_cast<const typename ET::T*>(a.logits) + int64_t(row) * a.row_stride;
   const Cand* cd = reinterpret_cast<const Cand*>(a.cand) + int64_t(row) * a.n1 * a.Fmax;
   int32_t* out = a.out + int64_t(row) * a.Fmax;
-  merge_lists(cd, F > 0 ? a.n1 : 0, a.Fmax, F, out, a.Fmax, shk);
+  merge_lists(cd, F > 0 ? a.n1 : 0, a.Fmax, F, out, a.Fmax, shk, s_set);
   if (SAG && threadIdx.x == 0) {  // thread 0 wrote the set; its logits give sigma
     float sig = 0.f;
-    if (F > 0) {
+    float L = -INFINITY;
+    {
       const float2* st = a.stats + int64_t(row) * a.n1;
       float M = -INFINITY;
       for (int q = 0; q < a.n1; ++q) M = fmaxf(M, st[q].x);
       float S = 0.f;
       for (int q = 0; q < a.n1; ++q)
         if (st[q].y > 0.f) S += st[q].y * ex2(st[q].x - M);
-      const float L = M + lg2(S);
-      const typename ET::T* p = reinterpret_cast<const typename ET::T*>(a.logits) + int64_t(row) * a.row_stride;
-      for (int f = 0; f < F; ++f)
-        if (out[f] >= 0) sig += ex2(fmaf(ET::one(p, out[f]), a.c2, -L));
+      L = M + lg2(S);
+      for (int f = 0; f < F; ++f) {
+        const int v = s_set[f];
+        const float z = (v >= 0) ? ET::one(p, v) : 0.f;
+        s_zs[f] = z;
+        if (v >= 0) sig += ex2(fmaf(z, a.c2, -L));
+      }
     }
     const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, true);
     const float Nn = 1.f - (1.f - Cr) * sig;
     if (a.out_set_mass) a.out_set_mass[row] = sig;
     if (a.out_norm) a.out_norm[row] = Nn;
     if (!(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+    s_lnc[0] = L;
+    s_lnc[1] = Nn;
+    s_lnc[2] = Cr;
+  }
+  if (SMP) {
+    const int ns = (a.V + a.seg_len - 1) / a.seg_len;
+    if (int(threadIdx.x) < ns) s_segm[threadIdx.x] = a.seg[int64_t(row) * a.n1 * a.nseg + threadIdx.x];
+    __syncthreads();
+    block_sample<ET>(p, a.V, a.aligned != 0, s_segm, ns, a.seg_len, s_lnc[0], a.c2, s_lnc[2], s_lnc[1], s_set,
+                     s_zs, F, a.u[row], shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
+                     a.flags);
   }
 }
 
@@ -598,18 +814,19 @@ __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
 // =============================================================================================
 static hipError_t last_error() { return hipGetLastError(); }
 
-template <class ET, int FM, bool SAG>
+template <class ET, int FM, bool SAG, bool SMP>
 static hipError_t launch_topf_s(const TopfArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((topf_rows_kernel<ET, FM, SAG>), dim3(unsigned(int64_t(a.R) * a.n1)), dim3(kThreads),
-                     0, st, a);
+  hipLaunchKernelGGL((topf_rows_kernel<ET, FM, SAG, SMP>), dim3(unsigned(int64_t(a.R) * a.n1)),
+                     dim3(kThreads), 0, st, a);
   hipError_t e = last_error();
   if (e != hipSuccess || a.n1 == 1) return e;
-  hipLaunchKernelGGL((topf_merge_kernel<ET, SAG>), dim3(a.R), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((topf_merge_kernel<ET, SAG, SMP>), dim3(a.R), dim3(kThreads), 0, st, a);
   return last_error();
 }
 template <class ET, int FM>
 static hipError_t launch_topf_t(const TopfArgs& a, hipStream_t st) {
-  return a.sag ? launch_topf_s<ET, FM, true>(a, st) : launch_topf_s<ET, FM, false>(a, st);
+  if (a.u) return launch_topf_s<ET, FM, true, true>(a, st);
+  return a.sag ? launch_topf_s<ET, FM, true, false>(a, st) : launch_topf_s<ET, FM, false, false>(a, st);
 }
 
 template <class ET>

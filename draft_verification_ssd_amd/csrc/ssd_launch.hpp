@@ -60,6 +60,12 @@ struct TopfArgs {
   float2* stats;     // [R][n1] (max c, sum 2^(z c - max c)) per chunk (when n1 > 1)
   float* out_set_mass;
   float* out_norm;
+  // draft-side sampling from q' (ssd_saguaro_sample): one uniform per row
+  const float* u;      // device [R], or null: no sampling
+  int32_t* out_token;  // [R]
+  float* out_prob;     // [R] q' of the sampled token, or null
+  int seg_len, nseg;   // tokens per segment (a whole number of 8192-token batches), segments per chunk
+  float2* seg;         // [R][n1 * nseg] (max c, sum) per segment (when n1 > 1)
 };
 
 struct SagArgs {

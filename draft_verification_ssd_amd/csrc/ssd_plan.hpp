@@ -78,13 +78,18 @@ struct TopfLayout {
 constexpr int kTopfTargetGroups = 768;
 constexpr int kTopfMinChunk = 16384;
 
-inline TopfLayout topf_layout(int R, int V, int F_max) {
-  TopfLayout L;
+inline int64_t topf_chunks(int R, int V) {
   int64_t n1 = ceil_div(kTopfTargetGroups, R > 0 ? R : 1);
   int64_t cap = ceil_div(V, kTopfMinChunk);
   if (cap > kPlanMaxChunks) cap = kPlanMaxChunks;
   if (n1 > cap) n1 = cap;
   if (n1 < 1) n1 = 1;
+  return n1;
+}
+
+inline TopfLayout topf_layout(int R, int V, int F_max) {
+  TopfLayout L;
+  const int64_t n1 = topf_chunks(R, V);
   const int64_t chunk = ceil_div(ceil_div(V, n1), 8) * 8;
   L.rp.chunk1 = int(chunk);
   L.rp.n1 = int(ceil_div(V, chunk));
@@ -92,6 +97,41 @@ inline TopfLayout topf_layout(int R, int V, int F_max) {
   L.off_stats = align_up(L.off_cand + size_t(R) * L.rp.n1 * F_max * 8);
   // chunk statistics (ssd_saguaro_topf) only when a row has several chunks
   L.total = align_up(L.off_stats + (L.rp.n1 > 1 ? size_t(R) * L.rp.n1 * 8 : 0));
+  return L;
+}
+
+// Draft-side sampling (ssd_saguaro_sample) runs the top-F pass with the row cut into segments of
+// seg_len tokens, a whole number of the pass's 8192-token batches, at most kPlanMaxSeg per chunk;
+// chunks are a whole number of segments, so segment g of a row covers tokens
+// [g seg_len, (g + 1) seg_len) whatever the chunking. Each segment's (max c, sum) pair locates the
+// sampled token's segment; only that segment is read again.
+constexpr int kPlanSampleSpan = 8192;  // tokens of one top-F batch of a workgroup (256 lanes x 32)
+constexpr int kPlanMaxSeg = 16;
+
+struct SampleLayout {
+  TopfLayout t;
+  int seg_len, nseg;  // tokens per segment, segments per chunk
+  size_t off_seg;     // [R][n1 * nseg] float2 segment pairs (when n1 > 1)
+  size_t total;
+};
+
+inline SampleLayout sample_layout(int R, int V, int F_max) {
+  SampleLayout L;
+  const int64_t n1 = topf_chunks(R, V);
+  const int64_t len0 = ceil_div(V, n1);
+  const int64_t G = ceil_div(ceil_div(len0, kPlanSampleSpan), kPlanMaxSeg);
+  const int64_t seg = G * kPlanSampleSpan;
+  const int64_t chunk = ceil_div(len0, seg) * seg;
+  L.seg_len = int(seg);
+  L.nseg = int(chunk / seg);
+  L.t.rp.chunk1 = int(chunk);
+  L.t.rp.n1 = int(ceil_div(V, chunk));
+  const size_t n1s = size_t(L.t.rp.n1);
+  L.t.off_cand = kAlign;
+  L.t.off_stats = align_up(L.t.off_cand + size_t(R) * n1s * size_t(F_max) * 8);
+  L.off_seg = align_up(L.t.off_stats + (n1s > 1 ? size_t(R) * n1s * 8 : 0));
+  L.total = align_up(L.off_seg + (n1s > 1 ? size_t(R) * n1s * L.nseg * 8 : 0));
+  L.t.total = L.total;
   return L;
 }
 

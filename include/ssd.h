@@ -191,6 +191,34 @@ ssd_status ssd_saguaro_topf(const void* logits, int64_t row_stride, ssd_dtype dt
                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ssd_saguaro_sample — the draft's sampling step with Saguaro, one pass over each row ([SSD]
+ * "Saguaro 优化二：Saguaro 采样", "解法：操纵草稿分布"): what ssd_saguaro_topf computes (the set S =
+ * the row's F_r largest logits, sigma, N), and a draft token drawn from q' = q (C on S, 1 elsewhere)
+ * / N with the row's uniform u by the inverse CDF in ascending token order: the first token whose
+ * cumulative q' exceeds u, or the last token of positive mass when rounding leaves u past the total
+ * (the reading used for the bonus token). q' itself is never written.
+ *   logits, row_stride, dtype, R, V, temperature, F_per_row, C, C_per_row, out_set, out_set_mass,
+ *                 out_norm: as for ssd_saguaro_topf, except F_max may be 0 (plain sampling from q;
+ *                 out_set may then be NULL).
+ *   u             device fp32 [R] uniforms in [0, 1) (not checked: u >= 1 gives the last token of
+ *                 positive mass, u < 0 the first).
+ *   out_token     device int32 [R] the sampled token; -1 when q' has no mass: every logit -inf, or
+ *                 the set holding all of q's mass with C = 0 (N = 0 up to rounding), which is also
+ *                 flagged SSD_FLAG_SAGUARO_NORM.
+ *   out_prob      device fp32 [R] q' of the sampled token (0 with -1), or NULL.
+ *   workspace     ssd_saguaro_sample_workspace_bytes(R, V, F_max) bytes.
+ * Logits must be finite or -inf. Rows are cut into segments of a whole number of 8192-token spans;
+ * after the pass only the segment holding the drawn token is read again.
+ * ------------------------------------------------------------------------------------------- */
+size_t ssd_saguaro_sample_workspace_bytes(int R, int V, int F_max);
+
+ssd_status ssd_saguaro_sample(const void* logits, int64_t row_stride, ssd_dtype dtype, int R, int V,
+                              float temperature, const int32_t* F_per_row, int F_max, float C,
+                              const float* C_per_row, const float* u, int32_t* out_token,
+                              float* out_prob, int32_t* out_set, float* out_set_mass, float* out_norm,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ssd_fanout_alloc — geometric fan-out of a cache budget ([SSD] "最优扇出度分配"). Host only,
  * synchronous. P(k) = (1-a) a^k for k < K and a^K for k = K; minimising sum_k P(k) F_k^-r under
  * sum_k F_k = budget gives F_k proportional to P(k)^(1/(1+r)). Integers: floor, then the leftover

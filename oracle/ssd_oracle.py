@@ -289,13 +289,15 @@ def branch_layout(budget: int, K: int) -> dict:
                 batch_size=budget, branch_rows=budget * K)
 
 
-def ssd_round(draft, target, dtype, x, u, T, sets, C, F, branch=None, seqs=None):
+def ssd_round(draft, target, dtype, x, u, T, sets, C, F, branch=None, seqs=None, branch_u=None):
     """One SSD round for the sampled sequences:
     guesses (top-F_k of draft row k excluding x_k for k < K, of the extra row K without exclusion),
     cache keys, Saguaro verification, cache lookup; and, for the branch rows, the Saguaro set
-    (top-F of the row) with its mass and normaliser.
+    (top-F of the row) with its mass and normaliser, and with branch_u ([B, budget, K] uniforms)
+    the draft token each branch row draws from its q' (saguaro_sample).
 
-    Returns {b: dict(k, bonus, guesses, keys_k, keys_t, slot, branch_sigma, branch_N)}.
+    Returns {b: dict(k, bonus, guesses, keys_k, keys_t, slot, branch_sigma, branch_N
+    [, branch_sample])}.
     """
     B, K = x.shape
     seqs = range(B) if seqs is None else seqs
@@ -314,13 +316,21 @@ def ssd_round(draft, target, dtype, x, u, T, sets, C, F, branch=None, seqs=None)
             sig = np.empty((nbr, K))
             nrm = np.empty((nbr, K))
             sets_b = np.empty((nbr, K, max(1, int(max(F[:K])))), dtype=np.int64)
+            samples = {}
             for j in range(nbr):
                 for i in range(K):
                     zb = logits_f64(branch[b, j, i], dtype)
-                    S = topf(zb, int(F[i]))
+                    if branch_u is None:
+                        S = topf(zb, int(F[i]))
+                        _, sig[j, i], nrm[j, i] = saguaro(softmax_t(zb, T), S, C)
+                    else:
+                        smp = saguaro_sample(zb, T, int(F[i]), C, float(branch_u[b, j, i]))
+                        S, sig[j, i], nrm[j, i] = smp.S, smp.sigma, smp.N
+                        samples[(j, i)] = smp
                     sets_b[j, i, :] = -1
                     sets_b[j, i, : len(S)] = S
-                    _, sig[j, i], nrm[j, i] = saguaro(softmax_t(zb, T), S, C)
             d.update(branch_sets=sets_b, branch_sigma=sig, branch_N=nrm)
+            if branch_u is not None:
+                d["branch_sample"] = samples
         out[b] = d
     return out

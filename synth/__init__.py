@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_branch_rows,
+    make_branch_uniforms,
     make_verify_batch,
     workload,
     WORKLOADS,

@@ -10,9 +10,11 @@ generators stand in for them:
   Saguaro set S_i is given, from the draft distribution with the weight of S_i scaled by C;
 * verification uniforms u in [0, 1), fp32, one per draft position plus one for the bonus token.
 
-Random streams: ``SeedSequence(seed).spawn(5)`` gives, in order, draft logits, target noise,
-draft-token sampling, verification uniforms and speculation-branch rows.  bf16 values are made by
-round-to-nearest-even from fp32 and are carried as their uint16 bit patterns.
+Random streams: ``SeedSequence(seed).spawn(6)`` gives, in order, draft logits, target noise,
+draft-token sampling, verification uniforms, speculation-branch rows and the branch rows' sampling
+uniforms (a child stream depends only on its index, so adding the sixth left the others as they
+were).  bf16 values are made by round-to-nearest-even from fp32 and are carried as their uint16
+bit patterns.
 
 Nothing here computes a softmax, an acceptance test, a residual or a sampler inverse CDF.
 """
@@ -43,7 +45,7 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def _streams(seed: int, n: int = 5):
+def _streams(seed: int, n: int = 6):
     return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
 
 
@@ -121,7 +123,7 @@ def make_verify_batch(
     ``sag_sizes[i]`` largest raw logits, and x_i is drawn with those tokens' weight scaled by C.
     """
     assert dtype in (BF16, F32)
-    r_logit, r_noise, r_draw, r_unif, _ = _streams(seed)
+    r_logit, r_noise, r_draw, r_unif = _streams(seed)[:4]
     rows = B * (K + 1)
     zq = _draft_logits(r_logit, rows, V, draft_sigma, zipf_s)
     zp = zq + np.float32(noise_sigma) * r_noise.standard_normal((rows, V), dtype=np.float32)
@@ -168,6 +170,11 @@ def make_branch_rows(B: int, budget: int, K: int, V: int, dtype: str, seed: int,
     if dtype == BF16:
         return f32_to_bf16_bits(z).reshape(B, budget, K, V)
     return z.reshape(B, budget, K, V)
+
+
+def make_branch_uniforms(B: int, budget: int, K: int, seed: int) -> np.ndarray:
+    """Uniforms in [0, 1), fp32, [B, budget, K]: one per branch row, for drawing its draft token."""
+    return _streams(seed)[5].random((B, budget, K), dtype=np.float32)
 
 
 # The five workloads: verification at several scales, and two SSD rounds (cache build and full round).

@@ -131,6 +131,35 @@ def test_saguaro_topf_validation():
     assert ssd.ssd_saguaro_topf_workspace_bytes(4, 100, 0) == 0
 
 
+def test_saguaro_sample_validation():
+    st = ssd.lib().ssd_saguaro_sample
+    # (logits, stride, dtype, R, V, T, F_per_row, F_max, C, C_per_row, u, token, prob, set, sigma, N,
+    #  ws, bytes, stream)
+    def call(**kw):
+        a = dict(logits=FAKE, stride=100, dtype=0, R=4, V=100, T=1.0, Fr=None, Fmax=3, C=0.5, Cr=None,
+                 u=FAKE, tok=FAKE, prob=None, set_=FAKE, sig=None, N=None, ws=None, nb=0, stream=None)
+        a.update(kw)
+        return st(*a.values())
+    assert call(dtype=9) == UNS
+    assert call(stride=99) == INV
+    assert call(T=0.0) == INV
+    assert call(Fmax=17) == INV
+    assert call(Fmax=-1) == INV
+    assert call(C=-0.1) == INV
+    assert call(logits=None) == INV
+    assert call(u=None) == INV
+    assert call(tok=None) == INV
+    assert call(set_=None) == INV
+    assert call(set_=None, Fmax=0) == WS        # plain sampling needs no set buffer
+    assert call() == WS
+    assert call(R=0, u=None, tok=None) == OK
+    assert ssd.ssd_saguaro_sample_workspace_bytes(2048, 128256, 3) > 0
+    assert ssd.ssd_saguaro_sample_workspace_bytes(4, 100, 0) > 0
+    assert ssd.ssd_saguaro_sample_workspace_bytes(4, 100, 17) == 0
+    # few rows are cut into chunks, which then keep per-segment pairs in the workspace
+    assert ssd.ssd_saguaro_sample_workspace_bytes(4, 128256, 3) > ssd.ssd_saguaro_topf_workspace_bytes(4, 128256, 3)
+
+
 def test_cache_validation():
     L = ssd.lib()
     F = (ctypes.c_int32 * 5)(3, 2, 2, 2, 3)

@@ -1,11 +1,12 @@
 """Full-size workloads on the GPU against the oracle on sampled sequences / rows:
 
   * SSD cache build: B=16 outer x 12 branches, K=4, V=128256 bf16, fan-out budget 12 (a=0.7, r=1),
-    Saguaro C=0.5 — guesses, keys, Saguaro verification, branch-row Saguaro, lookup and hit rate;
+    Saguaro C=0.5 — guesses, keys, Saguaro verification, the branch rows' draft step (top-F set,
+    Saguaro mass and normaliser, sampled token), lookup and hit rate;
   * large batch: B=128, K=8, V=152064 fp32 Zipf-shaped rows, T=0.7, top-4 guesses (several launch
     rounds of the verification kernel);
   * full SSD round: B=64 x budget 32 = 2048 branches (8192 branch rows) plus the outer rows,
-    V=128256 fp32, C=0.3 — Saguaro adjust on every branch row, verification, lookup, miss count.
+    V=128256 fp32, C=0.3 — the draft step on every branch row, verification, lookup, miss count.
 """
 import numpy as np
 import pytest
@@ -14,15 +15,16 @@ import torch
 import draft_verification_ssd_amd as ssd
 import oracle as O
 import synth
-from gpu_helpers import DEV, PROB_ATOL, compare_verify, logits_to_device, report
+from gpu_helpers import BOUNDARY, DEV, PROB_ATOL, compare_verify, logits_to_device, report
 
 pytestmark = pytest.mark.gpu
 
 
-def ssd_round_gpu(bt, fan, branch=None, branch_sample=None):
+def ssd_round_gpu(bt, fan, branch=None, branch_u=None):
     """One SSD round through the library: guesses of the outer draft rows (verify-fused for rows
-    0..K-1, standalone for row K), cache keys, Saguaro verification, lookup; and Saguaro adjust of
-    the branch rows with sets = their top-F_j guesses."""
+    0..K-1, standalone for row K), cache keys, Saguaro verification, lookup; and the branch rows'
+    draft step in one pass each (ssd_saguaro_sample: set = the row's top F_j, its mass and
+    normaliser, and the token drawn from q' with the row's uniform)."""
     B, K, V = bt.B, bt.K, bt.V
     draft = logits_to_device(bt.draft, bt.dtype)          # [B, K+1, V]
     target = logits_to_device(bt.target, bt.dtype)
@@ -46,15 +48,15 @@ def ssd_round_gpu(bt, fan, branch=None, branch_sample=None):
         nb = branch.shape[1]
         bd = logits_to_device(branch, bt.dtype).view(B * nb * K, V)
         Fr = torch.tensor(fan[:K], dtype=torch.int32, device=DEV).repeat(B * nb)
-        bsets = ssd.ssd_topf_guess(bd, Gm, F_per_row=Fr)
-        _, sig, N = ssd.ssd_saguaro_adjust(bd, bt.T, bsets, bt.C)
+        ub = torch.from_numpy(np.ascontiguousarray(branch_u).reshape(-1)).to(DEV)
+        tok, prob, bsets, sig, N = ssd.ssd_saguaro_sample(bd, bt.T, Gm, bt.C, ub, F_per_row=Fr)
         res.update(branch_sets=bsets.view(B, nb, K, Gm), branch_sigma=sig.view(B, nb, K),
-                   branch_N=N.view(B, nb, K))
+                   branch_N=N.view(B, nb, K), branch_token=tok.view(B, nb, K), branch_prob=prob.view(B, nb, K))
     torch.cuda.synchronize()
     return res
 
 
-def check_round(bt, fan, res, seqs, branch=None, branch_seqs=(), name=""):
+def check_round(bt, fan, res, seqs, branch=None, branch_seqs=(), name="", branch_u=None):
     ref = O.ssd_round(bt.draft, bt.target, bt.dtype, bt.x, bt.u, bt.T, bt.sets, bt.C, fan,
                       branch=None, seqs=seqs)
     st = compare_verify(bt, res["out"], {b: ref[b]["verify"] for b in seqs},
@@ -75,13 +77,22 @@ def check_round(bt, fan, res, seqs, branch=None, branch_seqs=(), name=""):
         bs = res["branch_sets"].cpu().numpy()
         sig = res["branch_sigma"].cpu().numpy()
         nrm = res["branch_N"].cpu().numpy()
+        tok = res["branch_token"].cpu().numpy()
+        prob = res["branch_prob"].cpu().numpy()
+        st["branch_rows"] = st["branch_token_near_boundary"] = 0
         for b, j in branch_seqs:
             for i in range(bt.K):
                 zb = O.logits_f64(branch[b, j, i], bt.dtype)
-                S = O.topf(zb, fan[i])
-                assert list(bs[b, j, i, : fan[i]]) == list(S), f"branch set {b},{j},{i}"
-                _, s_ref, n_ref = O.saguaro(O.softmax_t(zb, bt.T), S, bt.C)
-                assert abs(sig[b, j, i] - s_ref) < PROB_ATOL and abs(nrm[b, j, i] - n_ref) < PROB_ATOL
+                smp = O.saguaro_sample(zb, bt.T, fan[i], bt.C, float(branch_u[b, j, i]))
+                assert list(bs[b, j, i, : fan[i]]) == list(smp.S), f"branch set {b},{j},{i}"
+                assert abs(sig[b, j, i] - smp.sigma) < PROB_ATOL and abs(nrm[b, j, i] - smp.N) < PROB_ATOL
+                st["branch_rows"] += 1
+                if int(tok[b, j, i]) != smp.x:
+                    uu = float(branch_u[b, j, i])
+                    assert min(abs(uu - smp.c_lo), abs(uu - smp.c_hi)) < BOUNDARY, f"branch token {b},{j},{i}"
+                    st["branch_token_near_boundary"] += 1
+                qs, _, _ = O.saguaro(O.softmax_t(zb, bt.T), [int(v) for v in smp.S if v >= 0], bt.C)
+                assert abs(prob[b, j, i] - qs[int(tok[b, j, i])]) < PROB_ATOL, f"branch q' {b},{j},{i}"
     st["hits"] = int((slot >= 0).sum())
     st["miss_count"] = miss
     report(name, st)
@@ -97,9 +108,11 @@ def test_ssd_cache_build_b16x12_k4_v128256_bf16(seed):
     bt = synth.make_verify_batch(w["B"], w["K"], w["V"], w["dtype"], seed, T=w["T"], sag_sizes=fan[: w["K"]],
                                  C=w["C"])
     branch = synth.make_branch_rows(w["B"], w["budget"], w["K"], w["V"], w["dtype"], seed)
+    bu = synth.make_branch_uniforms(w["B"], w["budget"], w["K"], seed)
     print(f"[case] ssd cache build seed {seed}", flush=True)
-    res = ssd_round_gpu(bt, fan, branch)
+    res = ssd_round_gpu(bt, fan, branch, bu)
     check_round(bt, fan, res, range(w["B"]), branch, [(b, j) for b in (0, 7, 15) for j in (0, 5, 11)],
+                branch_u=bu,
                 name=f"ssd_build seed{seed}")
 
 
@@ -139,10 +152,11 @@ def test_full_ssd_round_b64x32_k4_v128256_f32():
     bt = synth.make_verify_batch(w["B"], w["K"], w["V"], w["dtype"], 0, T=w["T"], sag_sizes=fan[: w["K"]],
                                  C=w["C"])
     branch = synth.make_branch_rows(w["B"], w["budget"], w["K"], w["V"], w["dtype"], 0)
+    bu = synth.make_branch_uniforms(w["B"], w["budget"], w["K"], 0)
     print("[case] full ssd round b64x32", flush=True)
-    res = ssd_round_gpu(bt, fan, branch)
+    res = ssd_round_gpu(bt, fan, branch, bu)
     seqs = list(range(0, w["B"], 9)) + [w["B"] - 1]
-    st = check_round(bt, fan, res, seqs, branch, [(0, 0), (13, 31), (40, 17), (63, 5)],
+    st = check_round(bt, fan, res, seqs, branch, [(0, 0), (13, 31), (40, 17), (63, 5)], branch_u=bu,
                      name="ssd_round b64x32")
     # host-side choice of the path from the miss count ([SSD] Saguaro 优化三): zero-wait only if
     # every sequence hit
