@@ -166,6 +166,7 @@ __device__ void merge_lists(const Cand* __restrict__ cands, int n_lists, int str
 // best, so later batches rarely hold a candidate). The first batch sets tau to the (F+1)-th largest
 // lane maximum: F + 1 tokens of distinct lanes reach it, so F of them are not the excluded one.
 constexpr int kTBuf = 256;     // candidate keys per wave
+constexpr int kTBufSample = 192;  // with the sampling pass's per-lane segment pairs in LDS too
 constexpr int kTReduce = 16;   // cut the buffer to its top F beyond max(2F, this) keys
 constexpr int kTBatch = 32;    // tokens per lane per batch
 
@@ -173,10 +174,12 @@ __device__ __forceinline__ uint64_t cand_key64(float v, int idx) {
   return (uint64_t(ordered_key(v)) << 32) | uint64_t(~uint32_t(idx));
 }
 
-// The top F of the n keys in buf (keys unique), in order, to buf[0 .. m); returns m <= F.
+// The top F of the n keys in buf (keys unique, n <= BUF), in order, to buf[0 .. m); returns m <= F.
+template <int BUF>
 __device__ __forceinline__ int wave_cut_keys(uint64_t* buf, int n, int F) {
+  static_assert(BUF % 64 == 0, "whole keys per lane");
   const int lane = threadIdx.x & 63;
-  constexpr int kPer = kTBuf / 64;
+  constexpr int kPer = BUF / 64;
   uint64_t k[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) k[i] = (lane + 64 * i < n) ? buf[lane + 64 * i] : 0ull;
@@ -197,9 +200,9 @@ __device__ __forceinline__ int wave_cut_keys(uint64_t* buf, int n, int F) {
   return m;
 }
 
-template <class ET>
+template <class ET, int BUF>
 struct TopfWave {
-  uint64_t* buf;  // this wave's kTBuf keys
+  uint64_t* buf;  // this wave's BUF keys
   int n;          // keys in buf (wave-uniform)
   float tau;      // lower bound of the F-th best so far (wave-uniform); -inf: none yet
   int F, exclude;
@@ -237,7 +240,7 @@ struct TopfWave {
     for (int e = 0; e < NB; ++e) cnt += (z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude) ? 1 : 0;
     const int incl = wave_incl_scan_i(cnt);
     const int total = __builtin_amdgcn_readlane(incl, 63);
-    if (n + total <= kTBuf) {
+    if (n + total <= BUF) {
       int pos = n + incl - cnt;
 #pragma unroll
       for (int e = 0; e < NB; ++e)
@@ -250,8 +253,8 @@ struct TopfWave {
         bool c = z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude;
         uint64_t m = __ballot(c);
         if (m == 0ull) continue;
-        if (n + __popcll(m) > kTBuf) {
-          n = wave_cut_keys(buf, n, F);
+        if (n + __popcll(m) > BUF) {
+          n = wave_cut_keys<BUF>(buf, n, F);
           if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
           c = c && z[e] >= tau;
           m = __ballot(c);
@@ -262,7 +265,7 @@ struct TopfWave {
       }
     }
     if (n > max(2 * F, kTReduce)) {
-      n = wave_cut_keys(buf, n, F);
+      n = wave_cut_keys<BUF>(buf, n, F);
       if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
     }
   }
@@ -413,12 +416,12 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   constexpr int N = ET::kVec;
   constexpr int U = kTBatch / N;  // vectors per lane per batch
   constexpr int NS = SMP ? kPlanMaxSeg : 1;
-  __shared__ uint64_t sbuf[kWaves][kTBuf];
+  constexpr int BUF = SMP ? kTBufSample : kTBuf;
+  __shared__ uint64_t sbuf[kWaves][BUF];
   __shared__ uint64_t stop[kWaves][kMaxF];
-  __shared__ int sn[kWaves];
   __shared__ float shf[2 * kWaves];
-  __shared__ float2 srec[NS][kWaves];  // per wave and segment: (max c, sum)
-  __shared__ float2 segm[NS];          // per segment, over the block
+  __shared__ float2 lrec[NS][SMP ? kThreads : 1];  // per segment and lane: (max, sum 2^(z c - max c))
+  __shared__ float2 segm[NS];                      // per segment, over the block: (max c, sum)
   __shared__ int s_set[SMP ? kMaxF : 1];
   __shared__ float s_zs[SMP ? kMaxF : 1];
   __shared__ float s_lnc[3];
@@ -438,24 +441,26 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
     }
   }
   const int ex = a.exclude ? a.exclude[row] : -1;
+  // the row's Saguaro factor and uniform are read now, so they are here when the row is complete
+  const bool whole_row = a.n1 == 1;
+  const float Cr = (SAG && whole_row) ? row_saguaro_c(a.C_per_row, a.C, row, a.flags, t == 0) : 1.f;
+  const float u_row = (SMP && whole_row) ? a.u[row] : 0.f;
   const T* p = reinterpret_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
   const int c0 = chunk * a.chunk1;
   const int c1 = min(a.V, c0 + a.chunk1);
-  TopfWave<ET> tw;
+  TopfWave<ET, BUF> tw;
   tw.buf = sbuf[w];
   tw.n = 0;
   tw.tau = -INFINITY;
   tw.F = F;
   tw.exclude = ex;
-  // SMP: a lane's statistics cover the current segment only; at a segment's end the wave's pair
-  // goes to srec and the lane starts again
+  // SMP: a lane's statistics cover the current segment only; at a segment's end the lane's pair
+  // goes to LDS (every lane takes part in every batch, so each segment of the chunk gets all 256)
+  // and the lane starts again; the pairs are merged once, after the pass
   int cur_seg = 0, seg_batches = 0;
   const int G = SMP ? a.seg_len / kPlanSampleSpan : 1;
-  if (SMP && lane < NS) srec[lane][w] = make_float2(-INFINITY, 0.f);
   auto seg_flush = [&]() __attribute__((always_inline)) {
-    const float Mw = wave_max(ls.mx);
-    const float Sw = wave_sum((ls.s > 0.f) ? ls.s * ex2(ls.mx * cc - Mw * cc) : 0.f);
-    if (lane == 0) srec[cur_seg][w] = make_float2(Mw * cc, Sw);
+    if constexpr (SMP) lrec[cur_seg][t] = make_float2(ls.mx, ls.s);
     ls.mx = -INFINITY;
     ls.s = 0.f;
   };
@@ -522,9 +527,8 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
       if (F > 0) tw.batch_bm(z, z[0], [&](int) { return e; });
     }
     if (SMP) seg_flush();
-    tw.n = wave_cut_keys(tw.buf, tw.n, F);  // the wave's top F, in order
+    tw.n = wave_cut_keys<BUF>(tw.buf, tw.n, F);  // the wave's top F, in order
   }
-  if (lane == 0) sn[w] = tw.n;
   if (lane < kMaxF) stop[w][lane] = (lane < tw.n) ? tw.buf[lane] : 0ull;
   float MXc = -INFINITY, S = 0.f;  // the chunk's (max c, sum 2^(z c - max c))
   if (SAG && !SMP && F > 0) {
@@ -533,17 +537,26 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
     S = block_sum((ls.s > 0.f) ? ls.s * ex2(ls.mx * cc - MXc) : 0.f, shf + kWaves);
   }
   __syncthreads();
-  if (SMP) {  // segment pairs over the block, then the chunk's pair from them
-    if (t < NS) {
-      float M = srec[t][0].x;
+  if constexpr (SMP) {  // segment pairs over the block (16 threads a segment, each 16 lanes), then the chunk's
+    static_assert(NS * 16 == kThreads, "16 threads merge each segment's lane pairs");
+    const int nseg_c = (c1 - c0 + a.seg_len - 1) / a.seg_len;  // segments this chunk has
+    const int sgi = t >> 4, j = t & 15;
+    float M = -INFINITY, Ss = 0.f;
+    if (sgi < nseg_c) {
+      float2 r[16];
 #pragma unroll
-      for (int q = 1; q < kWaves; ++q) M = fmaxf(M, srec[t][q].x);
-      float Ss = 0.f;
+      for (int q = 0; q < 16; ++q) r[q] = lrec[sgi][q * 16 + j];
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q)
-        if (srec[t][q].y > 0.f) Ss += srec[t][q].y * ex2(srec[t][q].x - M);
-      segm[t] = make_float2(M, Ss);
-      if (a.n1 > 1 && t < a.nseg) a.seg[(int64_t(row) * a.n1 + chunk) * a.nseg + t] = make_float2(M, Ss);
+      for (int q = 0; q < 16; ++q) M = fmaxf(M, r[q].x);
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (r[q].y > 0.f) Ss += r[q].y * ex2(r[q].x * cc - M * cc);
+    }
+    const float Mr = row16_max(M);
+    const float Sr = row16_sum((Ss > 0.f) ? Ss * ex2(M * cc - Mr * cc) : 0.f);
+    if (j == 0) {
+      segm[sgi] = make_float2(Mr * cc, Sr);
+      if (a.n1 > 1 && sgi < nseg_c) a.seg[(int64_t(row) * a.n1 + chunk) * a.nseg + sgi] = make_float2(Mr * cc, Sr);
     }
     __syncthreads();
 #pragma unroll
@@ -569,7 +582,6 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
         const float zk = key_to_float(uint32_t(win_out >> 32));
         const float term = (lane < F && win_out) ? ex2(fmaf(zk, cc, -L)) : 0.f;
         const float sig = (F > 0) ? wave_sum(term) : 0.f;
-        const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, lane == 0);
         const float Nn = 1.f - (1.f - Cr) * sig;
         if (lane == 0) {
           if (a.out_set_mass) a.out_set_mass[row] = sig;
@@ -601,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
     __syncthreads();
     const int ns = (a.V + a.seg_len - 1) / a.seg_len;
     block_sample<ET>(p, a.V, a.aligned != 0, segm, ns, a.seg_len, s_lnc[0], cc, s_lnc[2], s_lnc[1], s_set, s_zs,
-                     F, a.u[row], shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
+                     F, u_row, shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
                      a.flags);
   }
 }
@@ -612,6 +624,7 @@ __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
   __shared__ int s_set[kMaxF];
   __shared__ float s_zs[kMaxF];
   __shared__ float2 s_segm[SMP ? kThreads : 1];
+  __shared__ float2 s_chunk[SAG ? kMaxChunks : 1];
   __shared__ float shf[2 * kWaves];
   __shared__ int shi[kWaves];
   __shared__ float s_lnc[3];
@@ -624,26 +637,35 @@ __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
   const typename ET::T* p = reinterpret_cast<const typename ET::T*>(a.logits) + int64_t(row) * a.row_stride;
   const Cand* cd = reinterpret_cast<const Cand*>(a.cand) + int64_t(row) * a.n1 * a.Fmax;
   int32_t* out = a.out + int64_t(row) * a.Fmax;
+  const int t = threadIdx.x;
+  // the chunk (and, sampling, segment) pairs are loaded first so that they arrive during the merge
+  float2 chunk_pair = make_float2(-INFINITY, 0.f), seg_pair = make_float2(-INFINITY, 0.f);
+  const int ns = SMP ? (a.V + a.seg_len - 1) / a.seg_len : 0;
+  if (SAG && t < a.n1) chunk_pair = a.stats[int64_t(row) * a.n1 + t];
+  if (SMP && t < ns) seg_pair = a.seg[int64_t(row) * a.n1 * a.nseg + t];
+  const float u_row = SMP ? a.u[row] : 0.f;
+  const float Cr = SAG ? row_saguaro_c(a.C_per_row, a.C, row, a.flags, t == 0) : 1.f;
   merge_lists(cd, F > 0 ? a.n1 : 0, a.Fmax, F, out, a.Fmax, shk, s_set);
-  if (SAG && threadIdx.x == 0) {  // thread 0 wrote the set; its logits give sigma
+  if (SAG) {
+    if (t < a.n1) s_chunk[t] = chunk_pair;
+    if (SMP && t < ns) s_segm[t] = seg_pair;
+    __syncthreads();  // the set (thread 0 wrote it) and the pairs
+    if (t < F) s_zs[t] = (s_set[t] >= 0) ? ET::one(p, s_set[t]) : 0.f;
+    __syncthreads();
+  }
+  if (SAG && t == 0) {  // the row's normaliser, then sigma from the set's logits
     float sig = 0.f;
     float L = -INFINITY;
     {
-      const float2* st = a.stats + int64_t(row) * a.n1;
       float M = -INFINITY;
-      for (int q = 0; q < a.n1; ++q) M = fmaxf(M, st[q].x);
+      for (int q = 0; q < a.n1; ++q) M = fmaxf(M, s_chunk[q].x);
       float S = 0.f;
       for (int q = 0; q < a.n1; ++q)
-        if (st[q].y > 0.f) S += st[q].y * ex2(st[q].x - M);
+        if (s_chunk[q].y > 0.f) S += s_chunk[q].y * ex2(s_chunk[q].x - M);
       L = M + lg2(S);
-      for (int f = 0; f < F; ++f) {
-        const int v = s_set[f];
-        const float z = (v >= 0) ? ET::one(p, v) : 0.f;
-        s_zs[f] = z;
-        if (v >= 0) sig += ex2(fmaf(z, a.c2, -L));
-      }
+      for (int f = 0; f < F; ++f)
+        if (s_set[f] >= 0) sig += ex2(fmaf(s_zs[f], a.c2, -L));
     }
-    const float Cr = row_saguaro_c(a.C_per_row, a.C, row, a.flags, true);
     const float Nn = 1.f - (1.f - Cr) * sig;
     if (a.out_set_mass) a.out_set_mass[row] = sig;
     if (a.out_norm) a.out_norm[row] = Nn;
@@ -653,11 +675,9 @@ __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
     s_lnc[2] = Cr;
   }
   if (SMP) {
-    const int ns = (a.V + a.seg_len - 1) / a.seg_len;
-    if (int(threadIdx.x) < ns) s_segm[threadIdx.x] = a.seg[int64_t(row) * a.n1 * a.nseg + threadIdx.x];
     __syncthreads();
     block_sample<ET>(p, a.V, a.aligned != 0, s_segm, ns, a.seg_len, s_lnc[0], a.c2, s_lnc[2], s_lnc[1], s_set,
-                     s_zs, F, a.u[row], shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
+                     s_zs, F, u_row, shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
                      a.flags);
   }
 }
