@@ -9,6 +9,8 @@ from .ssd_oracle import (  # noqa: F401
     SampleResult,
     VerifyResult,
     all_hit_probability,
+    backup_crossover,
+    batch_speedup,
     branch_layout,
     cache_keys,
     cache_lookup,

@@ -253,6 +253,45 @@ def fanout(K: int, a: float, r: float, budget: int):
     return Fi, Fc
 
 
+def batch_speedup(h: float, E_hit: float, E_miss: float, T_p: float, T_b: float, b: float) -> float:
+    """Expected speedup over autoregressive decoding for a batch of b sequences ([SSD] "SSD 的核心思想"
+    speedup formula; "解法：根据 batch 大小切换备用推测器"). The page's formulas are lost; this reading
+    keeps every quantity its text names: h the cache hit rate of one sequence, E_hit / E_miss the
+    expected tokens a round yields on a hit / a miss, T_p / T_b the primary / backup speculator
+    latencies in units of one target verification. A round costs the verification (or the primary
+    speculator when it is the slower), and the whole batch waits for the backup whenever any of its b
+    sequences misses, with probability 1 - h^b:
+        S(b) = (h E_hit + (1 - h) E_miss) / (max(1, T_p) + (1 - h^b) T_b).
+    As b grows the miss term tends to T_b: the backup's latency bounds the speedup."""
+    if not (0.0 <= h <= 1.0) or min(E_hit, E_miss, T_p, T_b) < 0.0 or not (b > 0):
+        raise ValueError("bad speedup arguments")
+    A = h * E_hit + (1.0 - h) * E_miss
+    return A / (max(1.0, T_p) + (1.0 - h ** b) * T_b)
+
+
+def backup_crossover(h: float, E_hit: float, E_miss_neural: float, T_neural: float, E_miss_fast: float,
+                     T_fast: float, T_p: float):
+    """Where a fast backup speculator overtakes a neural one as the batch grows ([SSD] "解法：根据
+    batch 大小切换备用推测器"; "消融实验": the fast backup wins from the critical size on). Writing
+    x = 1 - h^b and A = h E_hit + (1 - h) E_miss, batch_speedup equal for the two backups means
+    A_n (D + x T_fast) = A_f (D + x T_neural), D = max(1, T_p), so x* = D (A_n - A_f) / (A_f T_neural -
+    A_n T_fast) and b* = ln(1 - x*) / ln h.
+    Returns (b_star, fast_wins_large): b_star the real batch size where the two speedups are equal
+    (nan when they do not cross at any b > 0), fast_wins_large whether the fast backup is at least
+    as good in the limit of large batches."""
+    D = max(1.0, T_p)
+    A_n = h * E_hit + (1.0 - h) * E_miss_neural
+    A_f = h * E_hit + (1.0 - h) * E_miss_fast
+    fast_large = A_f * (D + T_neural) >= A_n * (D + T_fast)
+    den = A_f * T_neural - A_n * T_fast
+    if den == 0.0 or not (0.0 < h < 1.0):
+        return math.nan, bool(fast_large)
+    xs = D * (A_n - A_f) / den
+    if not (0.0 < xs < 1.0):
+        return math.nan, bool(fast_large)
+    return math.log(1.0 - xs) / math.log(h), bool(fast_large)
+
+
 def cache_keys(guesses: Sequence[Sequence[int]], F: Sequence[int]):
     """Keys of one sequence's speculation cache ([SSD] "SSD 的核心思想": an outcome is (k, t), k
     drafts accepted and t the bonus token). For each k the F_k guesses of draft position k

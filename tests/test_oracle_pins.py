@@ -484,3 +484,57 @@ def test_ninety_two_percent_example():
     g = json.load(open(os.path.join(GOLDEN, "all_hit_92.json")))
     miss = 1.0 - O.all_hit_probability(g["h"], g["B"])
     assert abs(miss - g["fraction_rounds_with_miss"]) < g["abs_tol"]
+
+
+# ------------------------------------------------------------------------------------------
+# batch speedup and the backup speculator's crossover
+# ------------------------------------------------------------------------------------------
+def test_batch_speedup_hand_values_and_limits():
+    # h = 0.9, E_hit = 4, E_miss = 2, T_p = 0.5, T_b = 1: tokens 3.6 + 0.2 = 3.8 per round;
+    # b = 1 waits 0.1, b = 2 waits 1 - 0.81 = 0.19 of a verification for the backup
+    assert abs(O.batch_speedup(0.9, 4, 2, 0.5, 1.0, 1) - 3.8 / 1.1) < 1e-12
+    assert abs(O.batch_speedup(0.9, 4, 2, 0.5, 1.0, 2) - 3.8 / 1.19) < 1e-12
+    # a primary speculator slower than the verification sets the round: 3.8 / (1.5 + 0.1)
+    assert abs(O.batch_speedup(0.9, 4, 2, 1.5, 1.0, 1) - 3.8 / 1.6) < 1e-12
+    # every sequence hits: no wait at any batch size; every one misses: always the backup
+    for b in (1, 7, 1000):
+        assert O.batch_speedup(1.0, 5, 1, 0.2, 3.0, b) == 5.0
+        assert abs(O.batch_speedup(0.0, 5, 1.5, 0.2, 0.5, b) - 1.5 / 1.5) < 1e-12
+    # large batches: the backup's latency alone bounds it (the page's limit)
+    assert abs(O.batch_speedup(0.9, 4, 2, 0.5, 1.0, 10 ** 4) - 3.8 / 2.0) < 1e-12
+
+
+def test_batch_speedup_falls_with_the_batch_as_all_hit_probability_does():
+    S = [O.batch_speedup(0.93, 4.5, 2.0, 0.8, 0.7, b) for b in range(1, 200)]
+    assert all(a >= c for a, c in zip(S, S[1:]))
+    # the wait term is exactly the probability that not all sequences hit (the 92 % example)
+    s24 = O.batch_speedup(0.9, 1.0, 1.0, 0.0, 1.0, 24)
+    assert abs((1.0 / s24 - 1.0) - (1.0 - O.all_hit_probability(0.9, 24))) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_backup_crossover_is_the_first_batch_where_the_fast_backup_wins(seed):
+    """Brute force over integer batch sizes against the analytic crossover."""
+    rng = np.random.default_rng(seed)
+    found = 0
+    while found < 20:
+        h = rng.uniform(0.5, 0.99)
+        E_hit = rng.uniform(2, 6)
+        En, Ef = rng.uniform(1.5, 4), rng.uniform(1.0, 1.5)   # the neural backup drafts better
+        Tn, Tf = rng.uniform(0.3, 2.0), rng.uniform(0.0, 0.1)  # and takes longer
+        Tp = rng.uniform(0.1, 1.5)
+        bs, fast_large = O.backup_crossover(h, E_hit, En, Tn, Ef, Tf, Tp)
+        wins = [O.batch_speedup(h, E_hit, Ef, Tp, Tf, b) >= O.batch_speedup(h, E_hit, En, Tp, Tn, b)
+                for b in range(1, 3001)]
+        assert fast_large == (O.batch_speedup(h, E_hit, Ef, Tp, Tf, 10 ** 6)
+                              >= O.batch_speedup(h, E_hit, En, Tp, Tn, 10 ** 6))
+        if math.isnan(bs) or bs > 2500:
+            assert all(w == wins[0] for w in wins) or bs > 2500
+            continue
+        found += 1
+        first = wins.index(True) + 1 if fast_large else None
+        if fast_large:
+            assert first == max(1, math.ceil(bs)), (bs, first)
+            assert all(wins[first - 1:])
+        # the two speedups agree at the real crossing
+        assert abs(O.batch_speedup(h, E_hit, Ef, Tp, Tf, bs) - O.batch_speedup(h, E_hit, En, Tp, Tn, bs)) < 1e-9
