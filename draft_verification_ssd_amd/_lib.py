@@ -19,7 +19,8 @@ FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT, FLAG_BAD_C = 0x1, 0
 
 EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify", "ssd_topf_workspace_bytes",
            "ssd_topf_guess", "ssd_saguaro_topf_workspace_bytes", "ssd_saguaro_topf",
-           "ssd_saguaro_sample_workspace_bytes", "ssd_saguaro_sample",
+           "ssd_saguaro_sample_workspace_bytes", "ssd_saguaro_sample", "ssd_batch_speedup",
+           "ssd_backup_crossover",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",
            "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string"]
 
@@ -50,6 +51,11 @@ def _declare(L):
     L.ssd_saguaro_topf_workspace_bytes.argtypes = [I32, I32, I32]
     L.ssd_saguaro_topf.restype = ctypes.c_int
     L.ssd_saguaro_topf.argtypes = [P, I64, ctypes.c_int, I32, I32, F32, P, I32, F32, P, P, P, P, P, SZ, P]
+    D = ctypes.c_double
+    L.ssd_batch_speedup.restype = ctypes.c_int
+    L.ssd_batch_speedup.argtypes = [D, D, D, D, D, I32, P]
+    L.ssd_backup_crossover.restype = ctypes.c_int
+    L.ssd_backup_crossover.argtypes = [D, D, D, D, D, D, D, P, P]
     L.ssd_saguaro_sample_workspace_bytes.restype = SZ
     L.ssd_saguaro_sample_workspace_bytes.argtypes = [I32, I32, I32]
     L.ssd_saguaro_sample.restype = ctypes.c_int
@@ -396,6 +402,23 @@ def ssd_saguaro_sample(logits, temperature: float, F_max: int, C: float, u, *, F
                                    out_set_mass.data_ptr(), out_norm.data_ptr(), workspace.ptr, workspace.nbytes,
                                    _stream(stream, dev)), "ssd_saguaro_sample")
     return out_token, out_prob, out_set, out_set_mass, out_norm
+
+
+def ssd_batch_speedup(h: float, E_hit: float, E_miss: float, T_p: float, T_b: float, b: int) -> float:
+    """Host-only expected speedup of a batch of b sequences under cache misses."""
+    out = ctypes.c_double()
+    check(lib().ssd_batch_speedup(h, E_hit, E_miss, T_p, T_b, int(b), ctypes.byref(out)), "ssd_batch_speedup")
+    return out.value
+
+
+def ssd_backup_crossover(h: float, E_hit: float, E_miss_neural: float, T_neural: float, E_miss_fast: float,
+                         T_fast: float, T_p: float):
+    """Host-only batch size where the fast and neural backups tie; returns (b_star, fast_wins_large)."""
+    b = ctypes.c_double()
+    f = ctypes.c_int32()
+    check(lib().ssd_backup_crossover(h, E_hit, E_miss_neural, T_neural, E_miss_fast, T_fast, T_p, ctypes.byref(b),
+                                     ctypes.byref(f)), "ssd_backup_crossover")
+    return b.value, bool(f.value)
 
 
 def ssd_fanout_alloc(K: int, a: float, r: float, budget: int):

@@ -1,6 +1,7 @@
 // extern "C" entry points: argument validation (before any HIP call), workspace carving, launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -363,6 +364,43 @@ ssd_status ssd_fanout_alloc(int K, double a, double r, int budget, int32_t* out_
     out_F[best] += 1;
     frac[best] = -1.0;
   }
+  return SSD_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+namespace {
+bool speed_args_ok(double h, double E_hit, double E_miss, double T_p, double T_b) {
+  return h >= 0.0 && h <= 1.0 && E_hit >= 0.0 && E_miss >= 0.0 && T_p >= 0.0 && T_b >= 0.0 &&
+         std::isfinite(E_hit) && std::isfinite(E_miss) && std::isfinite(T_p) && std::isfinite(T_b);
+}
+// tokens per round (A) and the round's time (D + miss wait) of one backup choice
+double round_tokens(double h, double E_hit, double E_miss) { return h * E_hit + (1.0 - h) * E_miss; }
+}  // namespace
+
+ssd_status ssd_batch_speedup(double h, double E_hit, double E_miss, double T_p, double T_b, int b,
+                             double* out_speedup) {
+  if (!speed_args_ok(h, E_hit, E_miss, T_p, T_b) || b < 1 || !out_speedup) return SSD_ERR_INVALID_ARG;
+  const double wait = (1.0 - std::pow(h, double(b))) * T_b;  // the batch waits unless all b hit
+  *out_speedup = round_tokens(h, E_hit, E_miss) / (std::max(1.0, T_p) + wait);
+  return SSD_OK;
+}
+
+ssd_status ssd_backup_crossover(double h, double E_hit, double E_miss_neural, double T_neural,
+                                double E_miss_fast, double T_fast, double T_p, double* out_b_star,
+                                int32_t* out_fast_wins_large) {
+  if (!speed_args_ok(h, E_hit, E_miss_neural, T_p, T_neural) ||
+      !speed_args_ok(h, E_hit, E_miss_fast, T_p, T_fast) || !out_b_star)
+    return SSD_ERR_INVALID_ARG;
+  const double D = std::max(1.0, T_p);
+  const double An = round_tokens(h, E_hit, E_miss_neural), Af = round_tokens(h, E_hit, E_miss_fast);
+  // the speedups are An / (D + x T_neural) and Af / (D + x T_fast) with x = 1 - h^b in (0, 1): one
+  // linear equation in x
+  if (out_fast_wins_large) *out_fast_wins_large = (Af * (D + T_neural) >= An * (D + T_fast)) ? 1 : 0;
+  const double slope = Af * T_neural - An * T_fast;
+  *out_b_star = std::nan("");
+  if (slope == 0.0 || !(h > 0.0 && h < 1.0)) return SSD_OK;
+  const double x = D * (An - Af) / slope;
+  if (x > 0.0 && x < 1.0) *out_b_star = std::log1p(-x) / std::log(h);
   return SSD_OK;
 }
 

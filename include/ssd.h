@@ -231,6 +231,36 @@ ssd_status ssd_fanout_alloc(int K, double a, double r, int budget, int32_t* out_
                             double* out_F_cont);
 
 /* ---------------------------------------------------------------------------------------------
+ * ssd_batch_speedup — expected speedup over autoregressive decoding of a batch of b sequences
+ * ([SSD] "SSD 的核心思想" speedup formula; "解法：根据 batch 大小切换备用推测器"). The page's formulas
+ * are lost; this reading keeps every quantity its text names, with times in units of one target
+ * verification: a round costs max(1, T_p) (the verification, or the primary speculator when it is
+ * slower), and the whole batch waits T_b for the backup speculator whenever any of its b sequences
+ * misses (probability 1 - h^b):  S(b) = (h E_hit + (1 - h) E_miss) / (max(1, T_p) + (1 - h^b) T_b).
+ * Host only, synchronous.
+ *   h in [0, 1] the hit rate of one sequence; E_hit, E_miss >= 0 expected tokens a round yields on a
+ *   hit / a miss; T_p, T_b >= 0 finite; b >= 1.  out_speedup  host double.
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_batch_speedup(double h, double E_hit, double E_miss, double T_p, double T_b, int b,
+                             double* out_speedup);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_backup_crossover — the batch size at which a fast backup speculator (E_miss_fast, T_fast)
+ * and a neural one (E_miss_neural, T_neural) give the same ssd_batch_speedup ([SSD] "解法：根据
+ * batch 大小切换备用推测器": small batches take the better drafts, large ones the shorter wait).
+ * With x = 1 - h^b and A = h E_hit + (1 - h) E_miss, equality is one linear equation in x; its root
+ * x* in (0, 1) gives b* = ln(1 - x*) / ln h. Host only, synchronous.
+ *   Arguments as for ssd_batch_speedup.
+ *   out_b_star           host double: b* (real), NaN when the two never cross at any b > 0.
+ *   out_fast_wins_large  host int32 (or NULL): 1 if the fast backup is at least as good as b grows
+ *                        without bound. The caller picks the fast backup for batches past b* when
+ *                        this is 1 (or compares ssd_batch_speedup of the two at its batch size).
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_backup_crossover(double h, double E_hit, double E_miss_neural, double T_neural,
+                                double E_miss_fast, double T_fast, double T_p, double* out_b_star,
+                                int32_t* out_fast_wins_large);
+
+/* ---------------------------------------------------------------------------------------------
  * ssd_cache_keys — keys of each sequence's speculation cache ([SSD] "SSD 的核心思想": an outcome
  * (k, t) is k accepted drafts and bonus t; "怎么猜奖励 token"). For k = 0..K the F_k guesses of
  * draft position k occupy consecutive slots (position K is the draft row after the last drafted

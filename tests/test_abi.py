@@ -5,6 +5,7 @@ argument, and the workspace pointer is NULL wherever the expected error comes ea
 validation slip surfaces as a wrong status code rather than a launch.
 """
 import ctypes
+import math
 import os
 import re
 
@@ -208,3 +209,47 @@ def test_fanout_validation():
     for args in [(4, 1.0, 1.0, 3), (4, 0.0, 1.0, 3), (4, 0.5, 0.0, 3), (4, 0.5, 1.0, -1), (-1, 0.5, 1.0, 3)]:
         assert L.ssd_fanout_alloc(*args, ctypes.addressof(out), None) == INV
     assert L.ssd_fanout_alloc(4, 0.5, 1.0, 3, None, None) == INV
+
+
+# ------------------------------------------------------------------------------------------
+# host-only speedup model against the oracle
+# ------------------------------------------------------------------------------------------
+def test_batch_speedup_matches_the_oracle():
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        h, Eh, Em = rng.uniform(0, 1), rng.uniform(0, 8), rng.uniform(0, 4)
+        Tp, Tb, b = rng.uniform(0, 2), rng.uniform(0, 3), int(rng.integers(1, 500))
+        got = ssd.ssd_batch_speedup(h, Eh, Em, Tp, Tb, b)
+        assert abs(got - O.batch_speedup(h, Eh, Em, Tp, Tb, b)) <= 1e-12 * max(1.0, got)
+    assert ssd.ssd_batch_speedup(1.0, 5.0, 1.0, 0.2, 3.0, 64) == 5.0
+
+
+def test_backup_crossover_matches_the_oracle():
+    rng = np.random.default_rng(4)
+    crossed = 0
+    for _ in range(500):
+        args = (rng.uniform(0.3, 0.999), rng.uniform(1, 6), rng.uniform(1, 4), rng.uniform(0, 2),
+                rng.uniform(0.5, 2), rng.uniform(0, 0.5), rng.uniform(0, 1.5))
+        b, fl = ssd.ssd_backup_crossover(*args)
+        b_ref, fl_ref = O.backup_crossover(*args)
+        assert fl == fl_ref
+        if math.isnan(b_ref):
+            assert math.isnan(b)
+        else:
+            crossed += 1
+            assert abs(b - b_ref) <= 1e-9 * max(1.0, b_ref)
+    assert crossed > 50
+    b, fl = ssd.ssd_backup_crossover(1.0, 4, 3, 1, 1, 0, 0.5)      # no misses: never cross
+    assert math.isnan(b)
+
+
+def test_speedup_validation():
+    L = ssd.lib()
+    out = ctypes.c_double()
+    assert L.ssd_batch_speedup(1.5, 1, 1, 0, 0, 1, ctypes.byref(out)) == INV
+    assert L.ssd_batch_speedup(0.5, -1, 1, 0, 0, 1, ctypes.byref(out)) == INV
+    assert L.ssd_batch_speedup(0.5, 1, 1, 0, float("inf"), 1, ctypes.byref(out)) == INV
+    assert L.ssd_batch_speedup(0.5, 1, 1, 0, 0, 0, ctypes.byref(out)) == INV
+    assert L.ssd_batch_speedup(0.5, 1, 1, 0, 0, 1, None) == INV
+    assert L.ssd_backup_crossover(0.5, 1, 1, 0, 1, 0, float("nan"), ctypes.byref(out), None) == INV
+    assert L.ssd_backup_crossover(0.5, 1, 1, 0, 1, 0, 0, None, None) == INV
