@@ -5,6 +5,8 @@
     python bench.py --traffic-from FETCH.csv WRITE.csv   (no GPU: turns two rocprofv3 --pmc
                                                           counter files into profiles/traffic_*.json)
     python bench.py --workload ssd_build_b16x12_k4_v128256_bf16   (an SSD round: every stage of it)
+    python bench.py --ablation fanout   (cache hit rate of geometric against uniform fan-out over
+                                         temperatures; one JSON object)
 
 A step is one verification round over one batch: every draft and target logit row of the batch
 is streamed once (temperature softmax statistics, fused top-F guesses), the accept decisions and
@@ -57,7 +59,71 @@ def parse():
                     help="after the timed loop, copy COPY_BYTES device-to-device a few times so a "
                          "counter run sees the copy kernel beside the verification kernel")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--ablation", choices=["fanout"])
+    ap.add_argument("--temps", default="0.5,0.75,1.0,1.5,2.0")
+    ap.add_argument("--ablation-batch", type=int, default=128)
+    ap.add_argument("--ablation-seeds", type=int, default=4)
+    ap.add_argument("--ablation-rows", default="zipf,gauss",
+                    help="row shapes: zipf (rank^-1.1 profile, noise 0.8, as the large-batch workload) "
+                         "and/or gauss (N(0, 2^2), noise 0.5, as the cache-build workload)")
     return ap.parse_args()
+
+
+def uniform_fanout(K, budget):
+    """The budget split evenly over the K+1 outcomes' positions, the remainder to the smallest k."""
+    base, left = divmod(budget, K + 1)
+    return [base + (1 if k < left else 0) for k in range(K + 1)]
+
+
+def fanout_ablation(args):
+    """Geometric against uniform fan-out ([SSD] "消融实验": geometric fan-out keeps a higher cache hit
+    rate, the more so at high temperature). For each temperature, seeded synthetic batches of the
+    cache-build shape (K=4, V=128256 bf16, budget 12, C=1 so that only the fan-out differs), with
+    Zipf-shaped or Gaussian rows, are
+    verified on the GPU with top-F_max guesses at every position; the geometric fan-out uses the
+    acceptance rate measured in that batch (mean accept probability of the drafted tokens) and r=1;
+    each fan-out's cache keys are built from the same guesses and the batch's outcomes looked up."""
+    import numpy as np
+    import torch
+
+    import draft_verification_ssd_amd as ssd
+    import synth
+
+    B, K, V, dtype, budget, r = args.ablation_batch, 4, 128256, "bf16", 12, 1.0
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = {"zipf": dict(zipf_s=1.1, noise_sigma=0.8), "gauss": dict(draft_sigma=2.0, noise_sigma=0.5)}
+    rows = []
+    for shape, T in [(sh, float(t)) for sh in args.ablation_rows.split(",") for t in args.temps.split(",")]:
+        hits = {"geometric": 0, "uniform": 0}
+        a_sum, n_seq, fans = 0.0, 0, {}
+        for seed in range(args.ablation_seeds):
+            bt = synth.make_verify_batch(B, K, V, dtype, args.seed * 1000 + seed, T=T, **shapes[shape])
+            lg = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+            draft, target = lg(bt.draft), lg(bt.target)
+            ap = torch.empty((B, K), device=dev)
+            Gm = 8
+            out = ssd.ssd_verify(draft[:, :K], target, torch.from_numpy(bt.x).to(dev), torch.from_numpy(bt.u).to(dev),
+                                 T, topf_F_max=Gm, accept_prob=ap)
+            guesses = torch.cat([out["topf"], ssd.ssd_topf_guess(draft[:, K, :], Gm)[:, None, :]], dim=1).contiguous()
+            a_hat = float(ap.mean().item())
+            fans = {"geometric": ssd.ssd_fanout_alloc(K, min(max(a_hat, 1e-3), 1 - 1e-3), r, budget)[0],
+                    "uniform": uniform_fanout(K, budget)}
+            for name, fan in fans.items():
+                assert max(fan) <= Gm
+                ck, ct = ssd.ssd_cache_keys(guesses, fan)
+                _, miss = ssd.ssd_cache_lookup(ck, ct, out["accepted_len"], out["bonus_token"])
+                hits[name] += B - int(miss.item())
+            a_sum += a_hat * B
+            n_seq += B
+        rows.append({"rows": shape, "T": T, "acceptance_rate": round(a_sum / n_seq, 4), "sequences": n_seq,
+                     "fanout_geometric_last_batch": fans["geometric"], "fanout_uniform": fans["uniform"],
+                     "hit_rate_geometric": round(hits["geometric"] / n_seq, 4),
+                     "hit_rate_uniform": round(hits["uniform"] / n_seq, 4)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"ablation": "fanout", "K": K, "V": V, "dtype": dtype, "budget": budget, "r": r, "C": 1.0,
+                      "data": "synthetic: zipf = -1.1 ln(rank) + N(0,1) draft, target + N(0, 0.8^2); "
+                              "gauss = N(0, 2^2) draft, target + N(0, 0.5^2)", "results": rows}))
 
 
 def algorithmic_bytes(B, K, V, esize, topf):
@@ -348,6 +414,9 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
               f"sequence across GPUs, see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.ablation == "fanout":
+        fanout_ablation(args)
+        return
     import numpy as np
     import torch
 

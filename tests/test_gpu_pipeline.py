@@ -163,3 +163,33 @@ def test_full_ssd_round_b64x32_k4_v128256_f32():
     miss = st["miss_count"]
     path = "zero-wait" if miss == 0 else "fallback"
     print(f"[ssd round] misses {miss}/{w['B']} -> {path} path", flush=True)
+
+
+@pytest.mark.parametrize("T", [0.5, 2.0])
+def test_fanout_ablation_lookups_match_oracle(T):
+    """The fan-out ablation's pieces: both fan-outs' caches built from one set of top-8 guesses and
+    the batch's outcomes looked up, slot for slot against the oracle's guesses and lookup."""
+    import bench
+    B, K, V, budget = 24, 4, 32000, 12
+    bt = synth.make_verify_batch(B, K, V, synth.BF16, 5, T=T)
+    draft = logits_to_device(bt.draft, bt.dtype)
+    target = logits_to_device(bt.target, bt.dtype)
+    ap = torch.empty((B, K), device=DEV)
+    print(f"[case] fan-out ablation T{T}", flush=True)
+    out = ssd.ssd_verify(draft[:, :K], target, torch.from_numpy(bt.x).to(DEV), torch.from_numpy(bt.u).to(DEV), T,
+                         topf_F_max=8, accept_prob=ap, residual_mass=torch.empty(B, device=DEV))
+    guesses = torch.cat([out["topf"], ssd.ssd_topf_guess(draft[:, K, :], 8)[:, None, :]], dim=1).contiguous()
+    ref = O.verify_batch(bt.draft, bt.target, bt.dtype, bt.x, bt.u, T)
+    compare_verify(bt, out, ref, ap, out["residual_mass"])
+    a_hat = float(ap.mean().item())
+    k_gpu, t_gpu = out["accepted_len"].cpu().numpy(), out["bonus_token"].cpu().numpy()
+    for fan in (ssd.ssd_fanout_alloc(K, a_hat, 1.0, budget)[0], bench.uniform_fanout(K, budget)):
+        ck, ct = ssd.ssd_cache_keys(guesses, fan)
+        slot, miss = ssd.ssd_cache_lookup(ck, ct, out["accepted_len"], out["bonus_token"])
+        slot = slot.cpu().numpy()
+        for b in range(B):
+            z = O.logits_f64(bt.draft[b], bt.dtype)
+            g = [O.topf(z[i], fan[i], int(bt.x[b, i])) for i in range(K)] + [O.topf(z[K], fan[K])]
+            kk, tt = O.cache_keys(g, fan)
+            assert slot[b] == O.cache_lookup(kk, tt, int(k_gpu[b]), int(t_gpu[b])), f"T {T} fan {fan} seq {b}"
+        assert int(miss.item()) == int((slot < 0).sum())
