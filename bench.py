@@ -476,7 +476,8 @@ def main():
         calls[i % n_rep]()
         e1.record(stream)
     torch.cuda.synchronize()
-    isolated_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # a whole step alone, per launch
+    isolated_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / n_launch
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -492,7 +493,10 @@ def main():
 
     rows = (2 * K + 1) * B
     value = rows / (ms_per_step * 1e-3)
-    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    # algorithmic bytes of one launch (a step's bytes over its launches, which run back to back) over
+    # the per-launch time: the step's bytes over the step's time
+    launch_bytes = step_bytes / n_launch
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
     khash = kernel_hash()
     traffic = load_traffic(args.workload, khash)
 
