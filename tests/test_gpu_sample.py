@@ -55,7 +55,8 @@ def _check(z64, T, F, Fr, C_eff, u, out, rows):
                                              (17, 2049, 4, 0.3, 0.7, "bf16"), (4, 40000, 16, 0.5, 1.0, "f32"),
                                              (300, 9000, 8, 1.0, 1.0, "bf16"), (2, 128256, 3, 0.5, 1.0, "bf16"),
                                              (800, 20000, 0, 1.0, 1.0, "f32"), (3, 77777, 5, 0.0, 2.0, "f32"),
-                                             (64, 128256, 3, 0.5, 1.0, "f32")])
+                                             (64, 128256, 3, 0.5, 1.0, "f32"), (3, 100000, 0, 1.0, 1.0, "bf16"),
+                                             (2, 1 << 20, 4, 0.5, 1.0, "f32")])
 def test_sample_matches_oracle(R, V, F, C, T, dtype):
     """Rows cut into several chunks (few rows) and whole-row chunks (many rows), tie-heavy rows,
     F = 0 (plain sampling), C = 0 and C = 1, per-row F, u = 0 and u just below 1."""
@@ -103,6 +104,18 @@ def test_sample_on_unaligned_strided_rows():
     out = ssd.ssd_saguaro_sample(view, 1.0, F, 0.4, torch.from_numpy(u).to(DEV))
     z64 = O.logits_f64(np.ascontiguousarray(z[:, :V]), "f32")
     _check(z64, 1.0, F, np.full(R, F), np.full(R, 0.4), u, out, range(R))
+
+
+def test_sample_on_unaligned_rows_cut_into_chunks():
+    """Few unaligned rows: several chunks a row, element-wise loads, the draw in the merge kernel."""
+    R, V, F = 2, 50001, 5
+    z = _rows(R, V + 1, "f32", seed=19)
+    view = logits_to_device(z, "f32")[:, :V]
+    u = np.array([0.37, 0.91], dtype=np.float32)
+    print("[case] sample unaligned chunked rows", flush=True)
+    out = ssd.ssd_saguaro_sample(view, 0.8, F, 0.2, torch.from_numpy(u).to(DEV))
+    z64 = O.logits_f64(np.ascontiguousarray(z[:, :V]), "f32")
+    _check(z64, 0.8, F, np.full(R, F), np.full(R, 0.2), u, out, range(R))
 
 
 def test_sample_grid_frequencies_are_q_prime():
