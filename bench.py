@@ -479,6 +479,24 @@ def main():
     # a whole step alone, per launch
     isolated_ms = float(np.mean([a.elapsed_time(b) for a, b in evs])) / n_launch
 
+    # context: what a plain device-to-device copy reaches on this GPU (outside the timed region),
+    # read + write bytes over its event-pair time, best of a few 512 MiB copies (not in counter
+    # runs, whose calibration copy must be the only large copy)
+    copy_gbs = None
+    if not args.copy_calibration:
+        csrc = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        copy_ms = []
+        for _ in range(6):
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            cdst.copy_(csrc)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            copy_ms.append(c0.elapsed_time(c1))
+        copy_gbs = round(2 * csrc.numel() / (min(copy_ms[1:]) * 1e-3) / 1e9, 1)
+        del csrc, cdst
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -521,7 +539,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "verify_fused_kernel",
                      "launch_ms": round(launch_ms, 6), "launches_per_step": n_launch,
-                     "isolated_launch_ms": round(isolated_ms, 6), "kernel_hash": khash},
+                     "isolated_launch_ms": round(isolated_ms, 6), "kernel_hash": khash,
+                     "device_copy_GBps": copy_gbs},
         "accepted_len_hist": k_hist,
     }
     if not args.no_cpu_baseline:
