@@ -319,8 +319,11 @@ __device__ __forceinline__ float tile_residual(const typename ET::T* prow, const
   return total;
 }
 
-template <class ET, int FM, int G>
-__global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a) {
+// MB: workgroups per CU the register allocation is sized for. 2 fits the whole kernel in registers;
+// 4 holds twice the sequences per launch at the cost of a few spilled registers, and is taken
+// only when it needs fewer launches (rounds of resident sequences) than 2.
+template <class ET, int FM, int G, int MB>
+__global__ __launch_bounds__(kThreads, MB) void verify_fused_kernel(VerifyArgs a) {
   using T = typename ET::T;
   using LY = Lay<ET>;
   __shared__ Shared sh;
@@ -1098,7 +1101,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_fused_kernel(VerifyArgs a)
 // ---------------------------------------------------------------------------------------------
 // launch: grids of whole sequences whose tiles all fit the device at once
 // ---------------------------------------------------------------------------------------------
-template <class ET, int FM, int G>
+template <class ET, int FM, int G, int MB>
 static int capacity_blocks() {
   static std::mutex mu;
   static int cache[64] = {0};
@@ -1108,7 +1111,7 @@ static int capacity_blocks() {
   if (cache[dev] == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(verify_fused_kernel<ET, FM, G>), kThreads, 0) != hipSuccess)
+            &per_cu, reinterpret_cast<const void*>(verify_fused_kernel<ET, FM, G, MB>), kThreads, 0) != hipSuccess)
       return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     cache[dev] = per_cu * cus;
@@ -1116,9 +1119,18 @@ static int capacity_blocks() {
   return cache[dev];
 }
 
-template <class ET, int FM, int G>
+// launches of the MB variant for a.B sequences (0: the device cannot hold one sequence's tiles)
+template <class ET, int FM, int G, int MB>
+static int rounds_needed(const VerifyArgs& a) {
+  const int cap = capacity_blocks<ET, FM, G, MB>();
+  if (cap < a.T) return 0;
+  const int per_round = cap / a.T;
+  return (a.B + per_round - 1) / per_round;
+}
+
+template <class ET, int FM, int G, int MB>
 static hipError_t launch_fused(VerifyArgs a, hipStream_t st, int* n_launches) {
-  const int cap = capacity_blocks<ET, FM, G>();
+  const int cap = capacity_blocks<ET, FM, G, MB>();
   if (cap < a.T) return hipErrorInvalidConfiguration;
   const int per_round = cap / a.T;  // whole sequences whose tiles are all resident at once
   const int B = a.B;
@@ -1129,7 +1141,7 @@ static hipError_t launch_fused(VerifyArgs a, hipStream_t st, int* n_launches) {
   for (int b0 = 0; b0 < B; b0 += per_round) {
     const int nb = (B - b0 < per_round) ? (B - b0) : per_round;
     a.b0 = b0;
-    hipLaunchKernelGGL((verify_fused_kernel<ET, FM, G>), dim3(unsigned(nb * a.T)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_fused_kernel<ET, FM, G, MB>), dim3(unsigned(nb * a.T)), dim3(kThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1141,7 +1153,13 @@ static hipError_t launch_fused(VerifyArgs a, hipStream_t st, int* n_launches) {
 // unused slots (cache hits) and skips their arithmetic.
 template <class ET, int FM>
 static hipError_t launch_g(const VerifyArgs& a, hipStream_t st, int* n) {
-  return launch_fused<ET, FM, (sizeof(typename ET::T) == 2 ? 9 : 5)>(a, st, n);
+  constexpr int G = (sizeof(typename ET::T) == 2 ? 9 : 5);
+  // four workgroups per CU only when that saves launches (measured: 7 -> 5 launches for 128
+  // sequences of 152064 fp32 logits, 373 -> 352 us a step; one launch of 16 sequences is ~4 %
+  // slower with the spills, so it keeps two)
+  const int r2 = rounds_needed<ET, FM, G, 2>(a), r4 = rounds_needed<ET, FM, G, 4>(a);
+  if (r4 > 0 && (r2 == 0 || r4 < r2)) return launch_fused<ET, FM, G, 4>(a, st, n);
+  return launch_fused<ET, FM, G, 2>(a, st, n);
 }
 
 template <class ET>
