@@ -1,7 +1,9 @@
 // gfx950 kernels for the standalone SSD / Saguaro pieces: top-F bonus-token guesses, Saguaro
-// down-weighting, and the speculation-cache keys and lookup. (Verification itself lives in
-// ssd_verify.hip.) Rows are cut into chunks; one 256-thread workgroup streams one chunk with
-// 16-byte loads (chunk_pass), then a second launch merges the chunks' partial results per row.
+// down-weighting (alone, with the row's own top-F set, and with the draft token drawn from the
+// down-weighted distribution), and the speculation-cache keys and lookup. (Verification itself
+// lives in ssd_verify.hip.) Rows are cut into chunks; one 256-thread workgroup streams one chunk
+// with 16-byte loads, then, when a row has several chunks, a second launch merges the chunks'
+// partial results per row.
 #include <hip/hip_runtime.h>
 
 #include "ssd_device.hpp"
