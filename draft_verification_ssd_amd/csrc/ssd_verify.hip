@@ -9,15 +9,16 @@
 //
 //  phase 1   Each lane loads its chunks of every row of a load group at once, forms max and
 //            sum 2^(z c - max) per row with c = log2(e)/T, and merges them over 16-lane groups with
-//            DPP. Partials go out with write-through (agent-coherent) stores; once they have
-//            completed, one atomic per tile counts the tile in.
-//  top-F     While it waits for the decision, a tile re-reads its draft rows from cache and keeps
-//            the candidates of each wave that pass a threshold every top-F token of the wave
-//            passes (from the same DPP maxima), selects the tile's best F per row and publishes them.
-//  decide    The tile that arrives last merges the row statistics in one fixed order, gathers the
-//            logits at the draft tokens, takes the accept decisions and k, writes k and the accept
-//            probabilities, and publishes a small decision record of words tagged with the call,
-//            which the other tiles poll.
+//            DPP; the draft rows' lanes that can hold a top-F token copy their chunks to LDS. The
+//            tile's (max, sum) per row goes out as words tagged with the call, written through
+//            to memory (agent-coherent stores).
+//  top-F     While it waits for the decision, a tile selects its best F per draft row from those
+//            copies (rows with too many candidate lanes are re-read from cache and filtered) and
+//            publishes them as tagged words.
+//  decide    The first tile past phase 1 claims the decision; it polls every tile's statistics,
+//            merges them in one fixed order, gathers the logits at the draft tokens, takes the
+//            accept decisions and k, writes k and the accept probabilities, and publishes a small
+//            decision record of tagged words, which the other tiles poll.
 //  residual  Every tile sums r = max(p_k - q'_k, 0) (or p_K when all drafts pass) over its token
 //            range, re-reading the two rows from cache, keeps r and its prefix sums in registers
 //            and publishes the tagged sum.
