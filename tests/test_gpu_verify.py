@@ -201,6 +201,14 @@ def test_launch_count_on_the_device():
     assert ssd.ssd_verify_launches(1, 4, 32000, ssd.SSD_F32, 0) == 1
 
 
+def test_bf16_batch_in_two_launches_of_four_workgroups_per_cu():
+    """64 sequences of bf16 rows: registers sized for four workgroups per CU need two launches
+    where two per CU would need three, so this runs that variant (a few registers spilled)."""
+    assert ssd.ssd_verify_launches(64, 4, 128256, ssd.SSD_BF16, 3) == 2
+    bt = synth.make_verify_batch(64, 4, 128256, synth.BF16, 7)
+    check_batch(bt, "b64_k4_v128256_bf16_top3 (two launches)", topf_F_max=3)
+
+
 # --- per-position Saguaro factor ---------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_per_position_saguaro_c_matches_oracle(dtype):
