@@ -806,21 +806,47 @@ __global__ __launch_bounds__(kThreads) void cache_keys_kernel(CacheKeysArgs a) {
   a.cache_tok[g] = (tok >= 0) ? tok : -1;
 }
 
+// One workgroup. Wave w takes sequences w, w + 4, ..., four at a time: lane j reads slot j of each
+// (64 slots a round), so the reads of four sequences are in flight together, and a ballot names
+// the first matching slot. The miss count is summed in a fixed order.
 __global__ __launch_bounds__(kThreads) void cache_lookup_kernel(CacheLookupArgs a) {
   __shared__ int shi[8];
-  int miss = 0;
-  for (int b = threadIdx.x; b < a.B; b += kThreads) {
-    const int k = a.k[b], tok = a.tok[b];
-    int slot = -1;
-    const int32_t* ck = a.cache_k + int64_t(b) * a.budget;
-    const int32_t* ct = a.cache_tok + int64_t(b) * a.budget;
-    for (int j = 0; j < a.budget; ++j)
-      if (ck[j] == k && ct[j] == tok) {
-        slot = j;
-        break;
+  constexpr int kSeq = 4;  // sequences per wave per round
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int miss = 0;  // lane 0 of each wave
+  for (int b0 = w * kSeq; b0 < a.B; b0 += kWaves * kSeq) {
+    int kq[kSeq], tq[kSeq], slot[kSeq];
+#pragma unroll
+    for (int i = 0; i < kSeq; ++i) {
+      const int b = min(b0 + i, a.B - 1);  // clamped: every read in bounds
+      kq[i] = a.k[b];
+      tq[i] = a.tok[b];
+      slot[i] = -1;
+    }
+    for (int j0 = 0; j0 < a.budget; j0 += 64) {
+      const int j = j0 + lane;
+      const int jc = min(j, a.budget - 1);
+      int ckv[kSeq], ctv[kSeq];
+#pragma unroll
+      for (int i = 0; i < kSeq; ++i) {
+        const int64_t base = int64_t(min(b0 + i, a.B - 1)) * a.budget + jc;
+        ckv[i] = a.cache_k[base];
+        ctv[i] = a.cache_tok[base];
       }
-    a.out_slot[b] = slot;
-    miss += (slot < 0);
+#pragma unroll
+      for (int i = 0; i < kSeq; ++i) {
+        const uint64_t hit = __ballot(j < a.budget && ckv[i] == kq[i] && ctv[i] == tq[i]);
+        if (slot[i] < 0 && hit) slot[i] = j0 + __builtin_ctzll(hit);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kSeq; ++i)
+        if (b0 + i < a.B) {
+          a.out_slot[b0 + i] = slot[i];
+          miss += (slot[i] < 0);
+        }
+    }
   }
   // block sum of integers
   for (int o = 32; o >= 1; o >>= 1) miss += __shfl_xor(miss, o, 64);
