@@ -289,7 +289,7 @@ def pipeline_bench(args, spec):
     b_rowk = B * V * es + B * fan[K] * 4
     # one read of every branch row; F and u in; set, sigma, N, token and q'(token) out
     b_branch = Rb * V * es + 2 * Rb * 4 + Rb * Gm * 4 + 4 * Rb * 4
-    b_keys = B * (K + 1) * Gm * 4 + 2 * B * budget * 4
+    b_keys = B * K * Gm * 4 + B * fan[K] * 4 + 2 * B * budget * 4
     b_lookup = 2 * B * budget * 4 + 2 * B * 4 + B * 4 + 4
     total_logit_bytes = ((2 * K + 2) * B + Rb) * V * es
     n_rep = max(1, math.ceil(ROTATE_BYTES / total_logit_bytes))
@@ -306,7 +306,6 @@ def pipeline_bench(args, spec):
         r["target"] = lg(bt.target)
         r["bd"] = lg(branch).view(Rb, V)
         r["topf"] = torch.empty((B, K, Gm), dtype=torch.int32, device=dev)
-        r["guesses"] = torch.full((B, K + 1, Gm), -1, dtype=torch.int32, device=dev)
         r["gk"] = torch.empty((B, fan[K]), dtype=torch.int32, device=dev)
         r["bsets"] = torch.empty((Rb, Gm), dtype=torch.int32, device=dev)
         r["sig"] = torch.empty(Rb, dtype=torch.float32, device=dev)
@@ -326,10 +325,8 @@ def pipeline_bench(args, spec):
     def stages(r):
         out = r["verify"].outputs
 
-        def keys():
-            r["guesses"][:, :K].copy_(r["topf"])
-            r["guesses"][:, K, : fan[K]].copy_(r["gk"])
-            ssd.ssd_cache_keys(r["guesses"], fan, cache_k=r["ck"], cache_tok=r["ct"])
+        def keys():  # straight from ssd_verify's top-F output and the row-K guesses
+            ssd.ssd_cache_keys(r["topf"], fan, guesses_last=r["gk"], cache_k=r["ck"], cache_tok=r["ct"])
 
         return [
             _Stage("verify (ssd_verify, fused top-F and Saguaro)", b_verify, r["verify"]),

@@ -69,7 +69,7 @@ def _declare(L):
     L.ssd_fanout_alloc.restype = ctypes.c_int
     L.ssd_fanout_alloc.argtypes = [I32, F64, F64, I32, P, P]
     L.ssd_cache_keys.restype = ctypes.c_int
-    L.ssd_cache_keys.argtypes = [I32, I32, I32, P, P, I32, P, P, P]
+    L.ssd_cache_keys.argtypes = [I32, I32, I32, P, P, I32, P, I32, P, P, P]
     L.ssd_cache_lookup.restype = ctypes.c_int
     L.ssd_cache_lookup.argtypes = [I32, I32, P, P, P, P, P, P, P]
     L.ssd_read_flags.restype = ctypes.c_int
@@ -430,12 +430,19 @@ def ssd_fanout_alloc(K: int, a: float, r: float, budget: int):
     return list(F), list(Fc)
 
 
-def ssd_cache_keys(guesses, fanout: Sequence[int], *, cache_k=None, cache_tok=None, stream=None):
-    """guesses [B, K+1, G_max] int32 device -> (cache_k, cache_tok) [B, budget]."""
+def ssd_cache_keys(guesses, fanout: Sequence[int], *, guesses_last=None, cache_k=None, cache_tok=None,
+                   stream=None):
+    """guesses [B, K+1, G_max] int32 device, or [B, K, G_max] (ssd_verify's top-F output) with
+    guesses_last [B, G_last] (position K's, ssd_topf_guess's output) -> (cache_k, cache_tok) [B, budget]."""
     torch = _torch()
-    B, K1, G = guesses.shape
-    K = K1 - 1
-    _need(guesses, torch.int32, (B, K1, G), "guesses")
+    B, Kg, G = guesses.shape
+    _need(guesses, torch.int32, (B, Kg, G), "guesses")
+    K = Kg if guesses_last is not None else Kg - 1
+    K1 = K + 1
+    G_last = 0
+    if guesses_last is not None:
+        G_last = guesses_last.shape[1]
+        _need(guesses_last, torch.int32, (B, G_last), "guesses_last")
     budget = int(sum(int(f) for f in fanout))
     dev = guesses.device
     if cache_k is None:
@@ -443,7 +450,7 @@ def ssd_cache_keys(guesses, fanout: Sequence[int], *, cache_k=None, cache_tok=No
     if cache_tok is None:
         cache_tok = torch.empty((B, budget), dtype=torch.int32, device=dev)
     F = (ctypes.c_int32 * K1)(*[int(f) for f in fanout])
-    check(lib().ssd_cache_keys(B, K, G, guesses.data_ptr(), ctypes.addressof(F), budget,
+    check(lib().ssd_cache_keys(B, K, G, guesses.data_ptr(), _ptr(guesses_last), G_last, ctypes.addressof(F), budget,
                                cache_k.data_ptr(), cache_tok.data_ptr(), _stream(stream, dev)),
           "ssd_cache_keys")
     return cache_k, cache_tok

@@ -405,16 +405,18 @@ ssd_status ssd_backup_crossover(double h, double E_hit, double E_miss_neural, do
 }
 
 // ------------------------------------------------------------------------------------------------
-ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* fanout,
-                          int budget, int32_t* cache_k, int32_t* cache_tok, hipStream_t stream) {
+ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
+                          int G_last, const int32_t* fanout, int budget, int32_t* cache_k,
+                          int32_t* cache_tok, hipStream_t stream) {
   if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || G_max < 1 || G_max > SSD_MAX_F ||
-      budget < 0 || !fanout)
+      budget < 0 || !fanout || (guesses_last && (G_last < 1 || G_last > SSD_MAX_F)))
     return SSD_ERR_INVALID_ARG;
   CacheKeysArgs a;
   std::memset(&a, 0, sizeof(a));
   int64_t off = 0;
   for (int k = 0; k <= K; ++k) {
-    if (fanout[k] < 0 || fanout[k] > G_max) return SSD_ERR_INVALID_ARG;
+    const int width = (guesses_last && k == K) ? G_last : G_max;
+    if (fanout[k] < 0 || fanout[k] > width) return SSD_ERR_INVALID_ARG;
     a.off[k] = int(off);
     off += fanout[k];
   }
@@ -427,6 +429,8 @@ ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const
   a.Gmax = G_max;
   a.budget = budget;
   a.guesses = guesses;
+  a.last = guesses_last;
+  a.Glast = G_last;
   a.cache_k = cache_k;
   a.cache_tok = cache_tok;
   return hip_status(launch_cache_keys(a, stream));

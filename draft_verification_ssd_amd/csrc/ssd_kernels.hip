@@ -801,7 +801,8 @@ __global__ __launch_bounds__(kThreads) void cache_keys_kernel(CacheKeysArgs a) {
   int k = 0;
   while (k < a.K && slot >= a.off[k + 1]) ++k;
   const int rank = slot - a.off[k];
-  const int tok = a.guesses[(int64_t(b) * (a.K + 1) + k) * a.Gmax + rank];
+  const int tok = (a.last && k == a.K) ? a.last[int64_t(b) * a.Glast + rank]
+                                       : a.guesses[(int64_t(b) * (a.last ? a.K : a.K + 1) + k) * a.Gmax + rank];
   a.cache_k[g] = (tok >= 0) ? k : -1;
   a.cache_tok[g] = (tok >= 0) ? tok : -1;
 }

@@ -90,7 +90,9 @@ struct SagArgs {
 
 struct CacheKeysArgs {
   int B, K, Gmax, budget;
-  const int32_t* guesses;
+  const int32_t* guesses;  // [B, K+1, Gmax], or [B, K, Gmax] with last
+  const int32_t* last;     // [B, Glast] position K's guesses, or null
+  int Glast;
   int off[18];  // slot offset of each position k (prefix sums of the fan-out), off[K+1] = budget
   int32_t* cache_k;
   int32_t* cache_tok;

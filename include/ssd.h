@@ -265,12 +265,17 @@ ssd_status ssd_backup_crossover(double h, double E_hit, double E_miss_neural, do
  * (k, t) is k accepted drafts and bonus t; "怎么猜奖励 token"). For k = 0..K the F_k guesses of
  * draft position k occupy consecutive slots (position K is the draft row after the last drafted
  * token); a guess of -1 leaves an empty slot (-1, -1).
- *   guesses     device int32 [B, K+1, G_max] (-1 padded), F_k <= G_max.
- *   fanout      host int32 [K+1], sum = budget.
+ *   guesses       device int32 [B, K+1, G_max] (-1 padded), F_k <= G_max; or, with guesses_last,
+ *                 [B, K, G_max] for positions 0..K-1 (the layout of ssd_verify's topf_out).
+ *   guesses_last  device int32 [B, G_last] position K's guesses (the layout of ssd_topf_guess's
+ *                 out), F_K <= G_last; or NULL (position K in guesses). Lets the cache be keyed
+ *                 straight from the two calls' outputs, with no copy into one buffer.
+ *   fanout        host int32 [K+1], sum = budget.
  *   cache_k, cache_tok  device int32 [B, budget] out.
  * ------------------------------------------------------------------------------------------- */
-ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* fanout,
-                          int budget, int32_t* cache_k, int32_t* cache_tok, hipStream_t stream);
+ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
+                          int G_last, const int32_t* fanout, int budget, int32_t* cache_k,
+                          int32_t* cache_tok, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_cache_lookup — look the verification outcome up in each sequence's cache ([SSD]

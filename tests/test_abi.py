@@ -165,11 +165,15 @@ def test_cache_validation():
     L = ssd.lib()
     F = (ctypes.c_int32 * 5)(3, 2, 2, 2, 3)
     # fan-out must sum to the budget and fit the guess width
-    assert L.ssd_cache_keys(2, 4, 3, FAKE, ctypes.addressof(F), 11, FAKE, FAKE, None) == INV
-    assert L.ssd_cache_keys(2, 4, 2, FAKE, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
-    assert L.ssd_cache_keys(2, 4, 3, FAKE, None, 12, FAKE, FAKE, None) == INV
-    assert L.ssd_cache_keys(2, 4, 3, None, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
-    assert L.ssd_cache_keys(0, 4, 3, FAKE, ctypes.addressof(F), 12, FAKE, FAKE, None) == OK
+    assert L.ssd_cache_keys(2, 4, 3, FAKE, None, 0, ctypes.addressof(F), 11, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 2, FAKE, None, 0, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 3, FAKE, None, 0, None, 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 3, None, None, 0, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(0, 4, 3, FAKE, None, 0, ctypes.addressof(F), 12, FAKE, FAKE, None) == OK
+    # position K's guesses apart: their width bounds F_K (3 here), not G_max
+    assert L.ssd_cache_keys(2, 4, 3, FAKE, FAKE, 2, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(2, 4, 3, FAKE, FAKE, 0, ctypes.addressof(F), 12, FAKE, FAKE, None) == INV
+    assert L.ssd_cache_keys(0, 4, 2, FAKE, FAKE, 3, ctypes.addressof((ctypes.c_int32 * 5)(2, 2, 2, 2, 3)), 11, FAKE, FAKE, None) == OK
     assert L.ssd_cache_lookup(2, 12, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == INV
     assert L.ssd_cache_lookup(2, 12, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INV
     assert L.ssd_cache_lookup(-1, 12, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INV

@@ -38,9 +38,11 @@ def ssd_round_gpu(bt, fan, branch=None, branch_u=None):
                          topf_F_max=Gm, topf_out=topf,
                          accept_prob=torch.empty((B, K), device=DEV), residual_mass=torch.empty(B, device=DEV))
     guesses[:, :K] = topf
+    last = ssd.ssd_topf_guess(draft[:, K, :], max(1, fan[K]))
     if fan[K] > 0:
-        guesses[:, K, : fan[K]] = ssd.ssd_topf_guess(draft[:, K, :], fan[K])
-    ck, ct = ssd.ssd_cache_keys(guesses.contiguous(), fan)
+        guesses[:, K, : fan[K]] = last[:, : fan[K]]
+    # keys straight from the two calls' outputs (no copy into one buffer)
+    ck, ct = ssd.ssd_cache_keys(topf, fan, guesses_last=last)
     slot, miss = ssd.ssd_cache_lookup(ck, ct, out["accepted_len"], out["bonus_token"])
     res = dict(k=out["accepted_len"], bonus=out["bonus_token"], guesses=guesses, ck=ck, ct=ct,
                slot=slot, miss=miss, out=out)

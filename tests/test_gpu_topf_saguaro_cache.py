@@ -233,7 +233,11 @@ def test_cache_keys_and_lookup_match_oracle(B, K, G, fan):
         for k in range(K + 1):
             n = rng.integers(0, G + 1)
             guesses[b, k, :n] = rng.permutation(50)[:n]
-    ck, ct = ssd.ssd_cache_keys(torch.from_numpy(guesses).to(DEV), fan)
+    gd = torch.from_numpy(guesses).to(DEV)
+    ck, ct = ssd.ssd_cache_keys(gd, fan)
+    # the same keys from position K's guesses held apart (a narrower array, as ssd_topf_guess gives)
+    ck2, ct2 = ssd.ssd_cache_keys(gd[:, :K].contiguous(), fan, guesses_last=gd[:, K, : max(1, fan[K])].contiguous())
+    assert torch.equal(ck, ck2) and torch.equal(ct, ct2)
     ck, ct = ck.cpu().numpy(), ct.cpu().numpy()
     kk_all, tt_all = [], []
     for b in range(B):
