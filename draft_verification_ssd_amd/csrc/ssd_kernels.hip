@@ -304,7 +304,6 @@ struct LaneStats {
 constexpr float kSegEps = 9.5367431640625e-07f;  // 2^-20: a segment's q' mass below this share of
                                                  // its q mass is cancellation left over, not mass
 static_assert(kPlanSampleSpan == kThreads * kTBatch, "a sampling segment is whole top-F batches");
-static_assert(kPlanMaxSeg * kWaves <= 64, "one wave holds every per-wave segment pair");
 
 // tokens [b0, b1) of row p in ascending order, 16-byte loads when aligned (b0 % kVec == 0)
 template <class ET, class Fn>
