@@ -102,6 +102,35 @@ __device__ void merge_lists(const Cand* __restrict__ cands, int n_lists, int str
                             int* sh_set = nullptr) {
   constexpr int kPer = (kMaxChunks * kMaxF + kThreads - 1) / kThreads;
   const int n = n_lists * F;
+  if (n <= 4 * 64) {  // up to four keys a lane: wave 0 alone, F rounds of a wave maximum, no barrier
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    uint64_t k[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      k[q] = 0ull;
+      if (e < n) {
+        const int list = e / F, r = e - list * F;
+        const Cand cd = cands[list * stride + r];
+        if (cd.i >= 0) k[q] = (uint64_t(ordered_key(cd.v)) << 32) | uint64_t(~uint32_t(cd.i));
+      }
+    }
+    int mine = -1;  // lane f: the f-th best token
+    for (int r = 0; r < F; ++r) {
+      const uint64_t win = wave_max_u64(max_u64(max_u64(k[0], k[1]), max_u64(k[2], k[3])));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) k[q] = (k[q] == win) ? 0ull : k[q];  // keys are unique
+      if (lane == r) mine = win ? int(~uint32_t(win)) : -1;
+    }
+    static_assert(kMaxF <= 64, "lane f holds the f-th best");
+    if (lane < Fmax) {
+      const int v = (lane < F) ? mine : -1;
+      out[lane] = v;
+      if (sh_set && lane < F) sh_set[lane] = v;
+    }
+    return;
+  }
   uint32_t kh[kPer], kl[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {

@@ -56,7 +56,7 @@ def _check(z64, T, F, Fr, C_eff, u, out, rows):
                                              (300, 9000, 8, 1.0, 1.0, "bf16"), (2, 128256, 3, 0.5, 1.0, "bf16"),
                                              (800, 20000, 0, 1.0, 1.0, "f32"), (3, 77777, 5, 0.0, 2.0, "f32"),
                                              (64, 128256, 3, 0.5, 1.0, "f32"), (3, 100000, 0, 1.0, 1.0, "bf16"),
-                                             (2, 1 << 20, 4, 0.5, 1.0, "f32")])
+                                             (2, 1 << 20, 4, 0.5, 1.0, "f32"), (2, 300000, 16, 0.4, 1.0, "f32")])
 def test_sample_matches_oracle(R, V, F, C, T, dtype):
     """Rows cut into several chunks (few rows) and whole-row chunks (many rows), tie-heavy rows,
     F = 0 (plain sampling), C = 0 and C = 1, per-row F, u = 0 and u just below 1."""

@@ -21,7 +21,7 @@ def tie_heavy_rows(R, V, dtype, seed):
 @pytest.mark.parametrize("R,V,F,dtype", [(1, 1, 1, "f32"), (3, 5, 7, "bf16"), (5, 300, 3, "f32"),
                                          (17, 2049, 4, "bf16"), (4, 40000, 16, "f32"),
                                          (300, 9000, 8, "bf16"), (2, 128256, 3, "bf16"),
-                                         (3, 77777, 5, "f32")])
+                                         (3, 77777, 5, "f32"), (2, 300000, 16, "f32")])
 def test_topf_matches_oracle_with_ties_masks_and_exclusion(R, V, F, dtype):
     print(f"[case] topf R{R} V{V} F{F} {dtype}", flush=True)
     z = tie_heavy_rows(R, V, dtype, seed=R * 7 + V)
@@ -114,7 +114,8 @@ def test_saguaro_degenerate_normaliser_is_flagged():
 @pytest.mark.parametrize("R,V,F,C,T,dtype", [(1, 1, 1, 0.5, 1.0, "f32"), (3, 5, 7, 0.0, 1.0, "bf16"),
                                              (17, 2049, 4, 0.3, 0.7, "bf16"), (4, 40000, 16, 0.5, 1.0, "f32"),
                                              (300, 9000, 8, 1.0, 1.0, "bf16"), (2, 128256, 3, 0.5, 1.0, "bf16"),
-                                             (800, 20000, 3, 0.5, 1.0, "f32"), (3, 77777, 5, 0.3, 2.0, "f32")])
+                                             (800, 20000, 3, 0.5, 1.0, "f32"), (3, 77777, 5, 0.3, 2.0, "f32"),
+                                             (2, 300000, 16, 0.5, 1.0, "bf16")])
 def test_saguaro_topf_matches_topf_then_saguaro(R, V, F, C, T, dtype):
     """One pass (set = the row's top F, then sigma and N) against the oracle's top-F and Saguaro;
     the shapes cover rows cut into several chunks (few rows) and whole-row chunks (many rows)."""
