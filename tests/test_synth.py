@@ -50,3 +50,19 @@ def test_draft_tokens_follow_the_draft_distribution():
     hits = p[np.arange(B), bt.x[:, 0]].mean()
     expect = (p ** 2).sum(1).mean()   # E[p(x)] when x ~ p
     assert abs(hits - expect) < 0.02
+
+
+def test_branch_uniforms_are_seeded_and_leave_the_other_streams_alone():
+    """The branch rows' sampling uniforms come from a sixth child stream: deterministic, in [0, 1),
+    and adding that stream left the five earlier ones (and so every earlier input) unchanged."""
+    import numpy as np
+    a = synth.make_branch_uniforms(3, 4, 2, seed=5)
+    b = synth.make_branch_uniforms(3, 4, 2, seed=5)
+    assert a.shape == (3, 4, 2) and a.dtype == np.float32
+    assert np.array_equal(a, b) and (a >= 0).all() and (a < 1).all()
+    assert not np.array_equal(a, synth.make_branch_uniforms(3, 4, 2, seed=6))
+    five = np.random.SeedSequence(5).spawn(5)
+    six = np.random.SeedSequence(5).spawn(6)
+    for x, y in zip(five, six[:5]):
+        assert np.array_equal(np.random.Generator(np.random.PCG64(x)).random(8),
+                              np.random.Generator(np.random.PCG64(y)).random(8))
