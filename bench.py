@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--temps", default="0.5,0.75,1.0,1.5,2.0")
     ap.add_argument("--ablation-batch", type=int, default=128)
     ap.add_argument("--ablation-seeds", type=int, default=4)
+    ap.add_argument("--ablation-budget", type=int, default=12)
+    ap.add_argument("--ablation-C", type=float, default=1.0,
+                    help="Saguaro factor of the verification (the sets are the top-F_max of each draft row)")
     ap.add_argument("--ablation-rows", default="zipf,gauss",
                     help="row shapes: zipf (rank^-1.1 profile, noise 0.8, as the large-batch workload) "
                          "and/or gauss (N(0, 2^2), noise 0.5, as the cache-build workload)")
@@ -78,7 +81,8 @@ def uniform_fanout(K, budget):
 def fanout_ablation(args):
     """Geometric against uniform fan-out ([SSD] "消融实验": geometric fan-out keeps a higher cache hit
     rate, the more so at high temperature). For each temperature, seeded synthetic batches of the
-    cache-build shape (K=4, V=128256 bf16, budget 12, C=1 so that only the fan-out differs), with
+    cache-build shape (K=4, V=128256 bf16, budget 12 unless given, C=1 unless given: only the fan-out
+    differs between the two caches), with
     Zipf-shaped or Gaussian rows, are
     verified on the GPU with top-F_max guesses at every position; the geometric fan-out uses the
     acceptance rate measured in that batch (mean accept probability of the drafted tokens) and r=1;
@@ -89,7 +93,8 @@ def fanout_ablation(args):
     import draft_verification_ssd_amd as ssd
     import synth
 
-    B, K, V, dtype, budget, r = args.ablation_batch, 4, 128256, "bf16", 12, 1.0
+    B, K, V, dtype, budget, r = args.ablation_batch, 4, 128256, "bf16", args.ablation_budget, 1.0
+    C = args.ablation_C
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shapes = {"zipf": dict(zipf_s=1.1, noise_sigma=0.8), "gauss": dict(draft_sigma=2.0, noise_sigma=0.5)}
@@ -98,20 +103,32 @@ def fanout_ablation(args):
         hits = {"geometric": 0, "uniform": 0}
         a_sum, n_seq, fans = 0.0, 0, {}
         for seed in range(args.ablation_seeds):
-            bt = synth.make_verify_batch(B, K, V, dtype, args.seed * 1000 + seed, T=T, **shapes[shape])
             lg = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-            draft, target = lg(bt.draft), lg(bt.target)
-            ap = torch.empty((B, K), device=dev)
-            Gm = 8
-            out = ssd.ssd_verify(draft[:, :K], target, torch.from_numpy(bt.x).to(dev), torch.from_numpy(bt.u).to(dev),
-                                 T, topf_F_max=Gm, accept_prob=ap)
-            guesses = torch.cat([out["topf"], ssd.ssd_topf_guess(draft[:, K, :], Gm)[:, None, :]], dim=1).contiguous()
-            a_hat = float(ap.mean().item())
+            Gm = 16
+
+            def outcome(bt, C_run):
+                """verify the batch (Saguaro sets = its own, when C < 1); the guesses of every position"""
+                draft, target = lg(bt.draft), lg(bt.target)
+                ap = torch.empty((B, K), device=dev)
+                sets = torch.from_numpy(bt.sets).to(dev) if bt.sets is not None else None
+                out = ssd.ssd_verify(draft[:, :K], target, torch.from_numpy(bt.x).to(dev),
+                                     torch.from_numpy(bt.u).to(dev), T, sag_set=sets, sag_C=C_run,
+                                     topf_F_max=Gm, accept_prob=ap)
+                return out, ssd.ssd_topf_guess(draft[:, K, :], Gm), float(ap.mean().item())
+
+            bt0 = synth.make_verify_batch(B, K, V, dtype, args.seed * 1000 + seed, T=T, **shapes[shape])
+            out0, last0, a_hat = outcome(bt0, 1.0)  # the acceptance rate the geometric fan-out uses
             fans = {"geometric": ssd.ssd_fanout_alloc(K, min(max(a_hat, 1e-3), 1 - 1e-3), r, budget)[0],
                     "uniform": uniform_fanout(K, budget)}
             for name, fan in fans.items():
                 assert max(fan) <= Gm
-                ck, ct = ssd.ssd_cache_keys(guesses, fan)
+                if C < 1.0:  # each cache's own guesses are the Saguaro sets its drafts were drawn with
+                    bt = synth.make_verify_batch(B, K, V, dtype, args.seed * 1000 + seed, T=T, **shapes[shape],
+                                                 sag_sizes=fan[:K], C=C)
+                    out, last, _ = outcome(bt, C)
+                else:
+                    out, last = out0, last0
+                ck, ct = ssd.ssd_cache_keys(out["topf"], fan, guesses_last=last)
                 _, miss = ssd.ssd_cache_lookup(ck, ct, out["accepted_len"], out["bonus_token"])
                 hits[name] += B - int(miss.item())
             a_sum += a_hat * B
@@ -121,7 +138,7 @@ def fanout_ablation(args):
                      "hit_rate_geometric": round(hits["geometric"] / n_seq, 4),
                      "hit_rate_uniform": round(hits["uniform"] / n_seq, 4)})
         print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
-    print(json.dumps({"ablation": "fanout", "K": K, "V": V, "dtype": dtype, "budget": budget, "r": r, "C": 1.0,
+    print(json.dumps({"ablation": "fanout", "K": K, "V": V, "dtype": dtype, "budget": budget, "r": r, "C": C,
                       "data": "synthetic: zipf = -1.1 ln(rank) + N(0,1) draft, target + N(0, 0.8^2); "
                               "gauss = N(0, 2^2) draft, target + N(0, 0.5^2)", "results": rows}))
 
