@@ -7,6 +7,8 @@
     python bench.py --workload ssd_build_b16x12_k4_v128256_bf16   (an SSD round: every stage of it)
     python bench.py --ablation fanout   (cache hit rate of geometric against uniform fan-out over
                                          temperatures; one JSON object)
+    python bench.py --trace-timeline [--workload NAME]   (needs libssd_trace.so: per-phase times
+                                         of every verification workgroup, summarised)
 
 A step is one verification round over one batch: every draft and target logit row of the batch
 is streamed once (temperature softmax statistics, fused top-F guesses), the accept decisions and
@@ -32,7 +34,7 @@ METRIC = "verified logit rows/sec and achieved HBM GB/s (B=16,K=4,V=128256)"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes exactly this many bytes per launch
-VERIFY_KERNEL = "verify_fused_kernel"
+VERIFY_KERNEL = "verify_kernel"
 KERNEL_SOURCES = ["draft_verification_ssd_amd/csrc/ssd_verify.hip",
                   "draft_verification_ssd_amd/csrc/ssd_device.hpp",
                   "draft_verification_ssd_amd/csrc/ssd_plan.hpp"]
@@ -60,6 +62,10 @@ def parse():
                          "counter run sees the copy kernel beside the verification kernel")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--ablation", choices=["fanout"])
+    ap.add_argument("--trace-timeline", action="store_true")
+    ap.add_argument("--trace-out", default=None, help="with --trace-timeline: save the raw timestamps (.npy)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes for cpu_baseline (0: the usable cores, at most 16)")
     ap.add_argument("--temps", default="0.5,0.75,1.0,1.5,2.0")
     ap.add_argument("--ablation-batch", type=int, default=128)
     ap.add_argument("--ablation-seeds", type=int, default=4)
@@ -141,6 +147,85 @@ def fanout_ablation(args):
     print(json.dumps({"ablation": "fanout", "K": K, "V": V, "dtype": dtype, "budget": budget, "r": r, "C": C,
                       "data": "synthetic: zipf = -1.1 ln(rank) + N(0,1) draft, target + N(0, 0.8^2); "
                               "gauss = N(0, 2^2) draft, target + N(0, 0.5^2)", "results": rows}))
+
+
+TRACE_SLOTS = 16
+TRACE_PHASES = [  # slot: what the workgroup has just finished
+    (1, "statistics of every row computed"),
+    (2, "statistics published, arrived (role known)"),
+    (3, "closer: every tile's statistics merged"),
+    (4, "decision published (closer) / guesses out and decision read (others)"),
+    (5, "residual mass published"),
+    (6, "others: every residual mass seen"),
+    (7, "closer: every residual mass in"),
+    (8, "bonus token drawn (the tile that drew it)"),
+    (9, "end"),
+]
+
+
+def trace_timeline(args):
+    """Per-phase timestamps of every verification workgroup (libssd_trace.so), relative to the
+    earliest start of the launch, over several launches: percentiles per phase, for all tiles and
+    for the closers (the last tile of each sequence)."""
+    import numpy as np
+    import torch
+
+    import draft_verification_ssd_amd as ssd
+    import synth
+
+    ssd._lib.use_trace_library()
+    spec = synth.workload(args.workload)
+    B, K, V, dtype = spec["B"], spec["K"], spec["V"], spec["dtype"]
+    topf = spec.get("topf", 0)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bt = synth.make_verify_batch(B, K, V, dtype, args.seed, T=spec["T"],
+                                 noise_sigma=spec.get("noise_sigma", 0.5), zipf_s=spec.get("zipf_s"))
+    esize = 2 if dtype == "bf16" else 4
+    n_rep = max(1, math.ceil(ROTATE_BYTES / ((2 * K + 1) * B * V * esize)))
+    ws = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, topf), dev)
+    calls = [make_replica(bt, dev, topf, ws) for _ in range(n_rep)]
+    T = ssd.ssd_verify_tiles(B, K, V, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32)
+    nwg = B * T
+    buf = torch.zeros(nwg * TRACE_SLOTS, dtype=torch.int64, device=dev)
+    ssd.lib().ssd_set_trace_buffer(buf.data_ptr())
+    for i in range(args.warmup):
+        calls[i % n_rep]()
+    torch.cuda.synchronize()
+    rows = []
+    for i in range(args.steps):
+        buf.zero_()
+        calls[i % n_rep]()
+        torch.cuda.synchronize()
+        rows.append(buf.view(nwg, TRACE_SLOTS).cpu().numpy().copy())
+    ssd.lib().ssd_set_trace_buffer(None)
+    if args.trace_out:
+        np.save(args.trace_out, np.stack(rows))
+    out = {"workload": args.workload, "launches": args.steps, "workgroups": nwg, "tiles_per_row": T,
+           "clock": "s_memrealtime, 100 MHz (10 ns)", "phases": []}
+    rel_all = {slot: [] for slot, _ in TRACE_PHASES}
+    rel_cl = {slot: [] for slot, _ in TRACE_PHASES}
+    ends, gave_up = [], 0
+    for r in rows:
+        t0 = r[:, 0].min()
+        role = r[:, 12]
+        closer = (role & 1) != 0
+        gave_up += int(((role >> 8) & 1 == 0).sum())
+        ends.append((r[:, 9].max() - t0) * 10)
+        for slot, _ in TRACE_PHASES:
+            v = r[:, slot]
+            ok = v > 0
+            rel_all[slot].extend(((v[ok] - t0) * 10).tolist())
+            rel_cl[slot].extend(((v[ok & closer] - t0) * 10).tolist())
+    pct = lambda a, q: float(np.percentile(a, q)) if len(a) else None
+    for slot, name in TRACE_PHASES:
+        a, c = rel_all[slot], rel_cl[slot]
+        out["phases"].append({"slot": slot, "phase": name, "ns_p10": pct(a, 10), "ns_p50": pct(a, 50),
+                              "ns_p90": pct(a, 90), "ns_max": pct(a, 100), "closer_ns_p50": pct(c, 50),
+                              "closer_ns_max": pct(c, 100)})
+    out["launch_ns_p50"] = pct(ends, 50)
+    out["tiles_that_gave_up_waiting"] = gave_up
+    print(json.dumps(out), flush=True)
 
 
 def algorithmic_bytes(B, K, V, esize, topf):
@@ -430,6 +515,9 @@ def main():
         sys.exit(2)
     if args.ablation == "fanout":
         fanout_ablation(args)
+        return
+    if args.trace_timeline:
+        trace_timeline(args)
         return
     import numpy as np
     import torch

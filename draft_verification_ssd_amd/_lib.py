@@ -11,13 +11,21 @@ import os
 from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
+TRACE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd_trace.so")
 
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_F32, SSD_BF16 = 0, 1
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 20, 65535
+SSD_DEFAULT_WAIT_POLLS = 2048
+
+
+class VerifyOpts(ctypes.Structure):
+    """ssd_verify_opts of include/ssd.h."""
+    _fields_ = [("wait_polls", ctypes.c_int32), ("topf_last_F", ctypes.c_int32), ("topf_last_out", ctypes.c_void_p)]
 FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT, FLAG_BAD_C = 0x1, 0x2, 0x4, 0x8, 0x10
 
-EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify", "ssd_topf_workspace_bytes",
+EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify_tiles", "ssd_verify", "ssd_verify_ex",
+           "ssd_stream_read", "ssd_topf_workspace_bytes",
            "ssd_topf_guess", "ssd_saguaro_topf_workspace_bytes", "ssd_saguaro_topf",
            "ssd_saguaro_sample_workspace_bytes", "ssd_saguaro_sample", "ssd_batch_speedup",
            "ssd_backup_crossover",
@@ -40,9 +48,16 @@ def _declare(L):
     L.ssd_verify_workspace_bytes.argtypes = [I32, I32, I32, I32]
     L.ssd_verify_launches.restype = ctypes.c_int
     L.ssd_verify_launches.argtypes = [I32, I32, I32, ctypes.c_int, I32]
+    L.ssd_verify_tiles.restype = ctypes.c_int
+    L.ssd_verify_tiles.argtypes = [I32, I32, I32, ctypes.c_int]
     L.ssd_verify.restype = ctypes.c_int
     L.ssd_verify.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32, P,
                              P, I32, P, P, P, P, P, P, SZ, P]
+    L.ssd_verify_ex.restype = ctypes.c_int
+    L.ssd_verify_ex.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32, P,
+                                P, I32, P, P, P, P, P, P, P, SZ, P]
+    L.ssd_stream_read.restype = ctypes.c_int
+    L.ssd_stream_read.argtypes = [P, SZ, P, P]
     L.ssd_topf_workspace_bytes.restype = SZ
     L.ssd_topf_workspace_bytes.argtypes = [I32, I32, I32]
     L.ssd_topf_guess.restype = ctypes.c_int
@@ -76,14 +91,29 @@ def _declare(L):
     L.ssd_read_flags.argtypes = [P, P, ctypes.c_int, P]
 
 
+_lib_path = LIB_PATH
+
+
+def use_trace_library() -> None:
+    """Load libssd_trace.so (ssd_verify with per-workgroup phase timestamps) instead of libssd.so.
+    Analysis only; must come before the first call."""
+    global _lib_path
+    if _lib is not None and _lib_path != TRACE_LIB_PATH:
+        raise RuntimeError("the library is already loaded")
+    _lib_path = TRACE_LIB_PATH
+
+
 def lib():
     """The loaded library. Raises if it is missing: there is no CPU or Python fallback."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m draft_verification_ssd_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        if not os.path.exists(_lib_path):
+            raise RuntimeError(f"{_lib_path} is not built; run `python -m draft_verification_ssd_amd.build`")
+        L = ctypes.CDLL(_lib_path)
         _declare(L)
+        if _lib_path == TRACE_LIB_PATH:
+            L.ssd_set_trace_buffer.restype = None
+            L.ssd_set_trace_buffer.argtypes = [P]
         _lib = L
     return _lib
 
@@ -163,8 +193,20 @@ def ssd_verify_workspace_bytes(B: int, K: int, V: int, topf_F_max: int = 0) -> i
 
 
 def ssd_verify_launches(B: int, K: int, V: int, dtype: int, topf_F_max: int = 0) -> int:
-    """Kernel launches ssd_verify issues for this shape on the current device (-1 if rejected)."""
+    """Kernel launches ssd_verify issues for this shape (-1 if rejected)."""
     return int(lib().ssd_verify_launches(B, K, V, dtype, topf_F_max))
+
+
+def ssd_verify_tiles(B: int, K: int, V: int, dtype: int) -> int:
+    """Tiles per logit row (workgroups per sequence) ssd_verify takes for this shape (-1 if rejected)."""
+    return int(lib().ssd_verify_tiles(B, K, V, dtype))
+
+
+def ssd_stream_read(data, sink, stream=None) -> None:
+    """Measurement helper: read every byte of a device tensor once (sink: device int32 [8192])."""
+    nbytes = data.numel() * data.element_size()
+    check(lib().ssd_stream_read(data.data_ptr(), nbytes, sink.data_ptr(), _stream(stream, data.device)),
+          "ssd_stream_read")
 
 
 def ssd_topf_workspace_bytes(R: int, V: int, F_max: int) -> int:
@@ -199,7 +241,7 @@ class VerifyCall:
                  sag_set=None, sag_C=1.0, topf_F: Optional[Sequence[int]] = None,
                  topf_F_max: int = 0, topf_out=None, accepted_len=None, bonus_token=None,
                  accept_prob=None, residual_mass=None, workspace: Optional[Workspace] = None,
-                 stream=None):
+                 stream=None, wait_polls: Optional[int] = None, topf_last_F: int = 0, topf_last_out=None):
         torch = _torch()
         B, Kd, V, dstride = _rows3(draft, "draft", 1)
         Bt, Kt, Vt, tstride = _rows3(target, "target", 2)
@@ -243,12 +285,20 @@ class VerifyCall:
             _need(accept_prob, torch.float32, (B, K), "accept_prob")
         if residual_mass is not None:
             _need(residual_mass, torch.float32, (B,), "residual_mass")
+        if topf_last_F > 0:
+            if topf_last_out is None:
+                topf_last_out = torch.empty((B, topf_last_F), dtype=torch.int32, device=dev)
+            _need(topf_last_out, torch.int32, (B, topf_last_F), "topf_last_out")
+        self.opts = None
+        if wait_polls is not None or topf_last_F > 0:
+            self.opts = VerifyOpts(-1 if wait_polls is None else int(wait_polls), int(topf_last_F),
+                                   _ptr(topf_last_out) if topf_last_F > 0 else None)
         if workspace is None:
-            workspace = Workspace(ssd_verify_workspace_bytes(B, K, V, topf_F_max), dev)
+            workspace = Workspace(ssd_verify_workspace_bytes(B, K, V, max(topf_F_max, topf_last_F)), dev)
         self.B, self.K, self.V = B, K, V
         self.workspace = workspace
         self.outputs = dict(accepted_len=accepted_len, bonus_token=bonus_token, accept_prob=accept_prob,
-                            residual_mass=residual_mass, topf=topf_out)
+                            residual_mass=residual_mass, topf=topf_out, topf_last=topf_last_out)
         self._keep = (draft, target, draft_tokens, uniforms, sag_set)
         self.args = (
             draft.data_ptr(), dstride, target.data_ptr(), tstride, _dtype_code(draft), B, K, V,
@@ -257,11 +307,27 @@ class VerifyCall:
             None if self.topf_F_arr is None else ctypes.addressof(self.topf_F_arr), int(topf_F_max),
             _ptr(topf_out), accepted_len.data_ptr(), bonus_token.data_ptr(), _ptr(accept_prob),
             _ptr(residual_mass), workspace.ptr, workspace.nbytes, _stream(stream, dev))
-        self._fn = lib().ssd_verify
+        if self.opts is not None:
+            self.args = self.args[:22] + (ctypes.addressof(self.opts),) + self.args[22:]
+            self._fn = lib().ssd_verify_ex
+        else:
+            self._fn = lib().ssd_verify
 
     def __call__(self):
         check(self._fn(*self.args), "ssd_verify")
         return self.outputs
+
+    def flags(self, clear: bool = True) -> int:
+        """Device-error flags of this call's workspace (synchronises the stream)."""
+        return ssd_read_flags(self.workspace, clear)
+
+    def checked(self):
+        """Run, synchronise and raise if the device recorded an error (SSD_FLAG_*)."""
+        out = self()
+        f = self.flags()
+        if f:
+            raise RuntimeError(f"ssd_verify: device flags {f:#x}")
+        return out
 
 
 def ssd_verify(draft, target, draft_tokens, uniforms, temperature: float, **kw):

@@ -52,20 +52,20 @@ const char* ssd_status_string(ssd_status s) {
 
 // ------------------------------------------------------------------------------------------------
 size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max) {
-  if (B < 0 || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || topf_F_max < 0 ||
+  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V || topf_F_max < 0 ||
       topf_F_max > SSD_MAX_F)
     return 0;
   return verify_layout(B, K, V, topf_F_max).total;
 }
 
-ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
-                      int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
-                      float temperature, const int32_t* draft_tokens, const float* uniforms,
-                      const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
-                      const int32_t* topf_F,
-                      int topf_F_max, int32_t* topf_out, int32_t* accepted_len,
-                      int32_t* bonus_token, float* accept_prob, float* residual_mass,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
+                         int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
+                         float temperature, const int32_t* draft_tokens, const float* uniforms,
+                         const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                         const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                         int32_t* accepted_len, int32_t* bonus_token, float* accept_prob,
+                         float* residual_mass, const ssd_verify_opts* opts, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
   if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V)
     return SSD_ERR_INVALID_ARG;
@@ -80,16 +80,25 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   if (topf_F)
     for (int i = 0; i < K; ++i)
       if (topf_F[i] < 0 || topf_F[i] > topf_F_max) return SSD_ERR_INVALID_ARG;
+  const int wait_polls = (opts && opts->wait_polls >= 0) ? opts->wait_polls : SSD_DEFAULT_WAIT_POLLS;
+  if (wait_polls > (1 << 20)) return SSD_ERR_INVALID_ARG;
+  const int lastF = opts ? opts->topf_last_F : 0;
+  if (lastF < 0 || lastF > SSD_MAX_F || (lastF > 0 && !opts->topf_last_out)) return SSD_ERR_INVALID_ARG;
+  if (lastF > 0) return SSD_ERR_UNSUPPORTED;
   if (draft_seq_stride < int64_t(K) * V || target_seq_stride < int64_t(K + 1) * V)
     return SSD_ERR_INVALID_ARG;
   if (B == 0) return SSD_OK;
   if (!draft_logits || !target_logits || !draft_tokens || !uniforms || !accepted_len ||
       !bonus_token)
     return SSD_ERR_INVALID_ARG;
-  const VerifyLayout L = verify_layout(B, K, V, topf_F_max);
+  const VerifyLayout L = verify_layout(B, K, V, std::max(topf_F_max, lastF));
   if (!ws_ok(workspace, workspace_bytes, L.total)) return SSD_ERR_WORKSPACE;
 
+  const bool bf16 = dtype == SSD_BF16;
   const int es = elem_size(dtype);
+  const bool aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
+                       (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;
+  const VerifyPlan P = plan_verify(B, K, V, bf16, aligned);
   VerifyArgs a;
   std::memset(&a, 0, sizeof(a));
   a.draft = draft_logits;
@@ -99,7 +108,7 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.B = B;
   a.K = K;
   a.V = V;
-  a.T = L.T;
+  a.T = P.T;
   a.c2 = float(kLog2e / double(temperature));
   a.x = draft_tokens;
   a.u = uniforms;
@@ -107,48 +116,72 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const 
   a.sF = sag_F;
   for (int i = 0; i < K; ++i) a.Cpos[i] = sag_F > 0 ? (sag_C_pos ? sag_C_pos[i] : sag_C) : 1.f;
   for (int i = 0; i < K; ++i) a.topfF[i] = topf_F ? topf_F[i] : topf_F_max;
+  a.topfF[K] = lastF;
   a.topfFmax = topf_F_max;
+  a.lastF = lastF;
+  a.Fcap = L.Fcap;
   a.topf_out = topf_out;
+  a.topf_last_out = lastF > 0 ? opts->topf_last_out : nullptr;
   a.k_out = accepted_len;
   a.bonus_out = bonus_token;
   a.aprob_out = accept_prob;
   a.rmass_out = residual_mass;
   a.flags = at<uint32_t>(workspace, 0);
-  a.ctl = at<uint32_t>(workspace, L.off_ctl);
-  a.dec = at<uint64_t>(workspace, L.off_dec);
+  a.gtag = at<uint32_t>(workspace, 4);
+  a.gdone = at<uint32_t>(workspace, 8);
+  a.seqctl = at<uint32_t>(workspace, L.off_seqctl);
   a.stats = at<uint64_t>(workspace, L.off_stats);
+  a.chunk = at<uint64_t>(workspace, L.off_chunk);
+  a.dec = at<uint64_t>(workspace, L.off_dec);
   a.cand = at<uint64_t>(workspace, L.off_cand);
-  a.res = at<uint64_t>(workspace, L.off_res);
-  a.spin_limit = 1 << 20;
-  a.aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
-              (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;
+  a.Tcap = L.Tcap;
+  a.wait_polls = wait_polls;
+  a.aligned = aligned ? 1 : 0;
 #ifdef SSD_TRACE
   a.trace = static_cast<uint64_t*>(ssd_trace_buffer);
 #endif
-  const hipError_t e = launch_verify(a, dtype == SSD_BF16, stream);
-  if (e == hipErrorInvalidConfiguration) return SSD_ERR_UNSUPPORTED;
-  return hip_status(e);
-}
-
-int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max) {
-  using namespace ssd;
-  if (!dtype_ok(dtype)) return -1;
-  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V) return -1;
-  if (topf_F_max < 0 || topf_F_max > SSD_MAX_F) return -1;
-  if (B == 0) return 0;
-  VerifyArgs a{};
-  a.B = B;
-  a.K = K;
-  a.V = V;
-  a.T = verify_layout(B, K, V, topf_F_max).T;
-  a.topfFmax = topf_F_max;
-  return count_verify_launches(a, dtype == SSD_BF16);
+  return hip_status(launch_verify(a, P, bf16, stream));
 }
 
 #ifdef SSD_TRACE
-// analysis builds only: device buffer of 8 timestamps per verification workgroup
+// analysis builds only: device buffer of 16 timestamps per verification workgroup
 void ssd_set_trace_buffer(void* device_buffer) { ssd_trace_buffer = device_buffer; }
 #endif
+
+ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
+                      int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
+                      float temperature, const int32_t* draft_tokens, const float* uniforms,
+                      const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                      const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                      int32_t* accepted_len, int32_t* bonus_token, float* accept_prob,
+                      float* residual_mass, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return ssd_verify_ex(draft_logits, draft_seq_stride, target_logits, target_seq_stride, dtype, B, K, V,
+                       temperature, draft_tokens, uniforms, sag_set, sag_F, sag_C, sag_C_pos, topf_F,
+                       topf_F_max, topf_out, accepted_len, bonus_token, accept_prob, residual_mass, nullptr,
+                       workspace, workspace_bytes, stream);
+}
+
+int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max) {
+  if (!dtype_ok(dtype)) return -1;
+  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V) return -1;
+  if (topf_F_max < 0 || topf_F_max > SSD_MAX_F) return -1;
+  return B == 0 ? 0 : 1;
+}
+
+int ssd_verify_tiles(int B, int K, int V, ssd_dtype dtype) {
+  if (!dtype_ok(dtype)) return -1;
+  if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V) return -1;
+  return plan_verify(B, K, V, dtype == SSD_BF16, true).T;
+}
+
+// ------------------------------------------------------------------------------------------------
+ssd_status ssd_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!data || !sink || bytes % 16 != 0 || !aligned16(data)) return SSD_ERR_INVALID_ARG;
+  if (bytes == 0) return SSD_OK;
+  return hip_status(launch_stream_read(data, int64_t(bytes / 16), sink, stream));
+}
+
 
 // ------------------------------------------------------------------------------------------------
 size_t ssd_topf_workspace_bytes(int R, int V, int F_max) {

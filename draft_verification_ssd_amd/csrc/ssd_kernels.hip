@@ -886,6 +886,29 @@ __global__ __launch_bounds__(kThreads) void cache_lookup_kernel(CacheLookupArgs 
 
 __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
 
+// Read-only streaming of n16 16-byte words, each read once, four loads in flight per thread: the
+// read bandwidth a kernel reaches on this device for a footprint (a measurement helper). The sink
+// is written only when the words' xor takes one particular value, which keeps the loads live.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ p, int64_t n16,
+                                                               uint32_t* sink) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = load16(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = load16(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+
 // =============================================================================================
 // launchers
 // =============================================================================================
@@ -942,6 +965,13 @@ hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st) {
 
 hipError_t launch_cache_lookup(const CacheLookupArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(cache_lookup_kernel, dim3(1), dim3(kThreads), 0, st, a);
+  return last_error();
+}
+
+hipError_t launch_stream_read(const void* p, int64_t n16, uint32_t* sink, hipStream_t st) {
+  const int64_t g = (n16 + kThreads - 1) / kThreads;
+  const unsigned grid = unsigned(g < 1 ? 1 : (g > kStreamReadGrid ? kStreamReadGrid : g));
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint4*>(p), n16, sink);
   return last_error();
 }
 

@@ -7,6 +7,8 @@
 
 namespace ssd {
 
+constexpr int kStreamReadGrid = 8192;  // workgroups of ssd_stream_read (its sink holds one word each)
+
 
 struct VerifyArgs {
   const void* draft;
@@ -14,31 +16,36 @@ struct VerifyArgs {
   const void* target;
   int64_t tstride;
   int B, K, V;
-  int b0;    // first sequence of this launch
-  int T;     // 4096-token tiles per row
+  int T;     // tiles per row (of 256 * NV * 16 / sizeof(element) tokens)
   float c2;  // log2(e) / T
   const int32_t* x;
   const float* u;
   const int32_t* sset;
   int sF;
   float Cpos[16];  // Saguaro factor per draft position
-  int topfF[16];
-  int topfFmax;
+  int topfF[17];   // guesses per draft row; [K]: the extra draft row K (no exclusion)
+  int topfFmax;    // width of topf_out rows (0: no guesses of rows 0..K-1)
+  int lastF;       // guesses of draft row K (0: none)
+  int Fcap;        // guesses per row and tile the candidate region holds
   int32_t* topf_out;
+  int32_t* topf_last_out;
   int32_t* k_out;
   int32_t* bonus_out;
   float* aprob_out;
   float* rmass_out;
   // workspace views
-  uint32_t* flags;
-  uint32_t* ctl;     // per sequence, 64 words: the last call's tag
-  uint64_t* dec;     // per sequence, 32 tagged words: the decision record (k, log-normalisers, set)
-  uint64_t* stats;   // [B][2K+1][T][2] tagged max c and sum per tile
-  uint64_t* cand;    // [B][K][T][topfFmax][2] candidate keys per tile, two tagged halves each
-  uint64_t* res;     // [B][T] residual mass per tile, tagged with the call
-  int spin_limit;
-  int aligned;  // every logit row starts 16-byte aligned
-  uint64_t* trace;  // per-workgroup phase timestamps (analysis builds only), or null
+  uint32_t* flags;   // sticky device-error flags
+  uint32_t* gtag;    // the last call's tag
+  uint32_t* gdone;   // sequences finished by the running call
+  uint32_t* seqctl;  // [kSeqCtlMax][kPlanSeqCtlWords] arrivals, guess arrivals
+  uint64_t* stats;   // [B][2K+1][Tcap][2]
+  uint64_t* chunk;   // [B][Tcap][2] claim word, mass word
+  uint64_t* dec;     // [B][kPlanDecWords] decision record
+  uint64_t* cand;    // [B][K+1][Tcap][Fcap][2]
+  int Tcap;
+  int wait_polls;    // polls a workgroup spends waiting on the others of its sequence
+  int aligned;       // every logit row starts 16-byte aligned
+  uint64_t* trace;   // per-workgroup phase timestamps (analysis builds only), or null
 };
 
 struct TopfArgs {
@@ -108,9 +115,16 @@ struct CacheLookupArgs {
   int32_t* out_miss;
 };
 
-hipError_t launch_verify(const VerifyArgs& a, bool bf16, hipStream_t st);
-// kernel launches launch_verify issues for these arguments on the current device (-1 on error)
-int count_verify_launches(const VerifyArgs& a, bool bf16);
+// tiles per row and the kernel variant a call takes (the same plan for sizing and launching)
+struct VerifyPlan {
+  int KM;   // register rows per tile: 2 KM + 1 (KM = 4, 8 or 16)
+  int NV;   // 16-byte chunks per lane and row (1 or 2)
+  int T;    // tiles per row
+  bool AL;  // every row 16-byte aligned (vector loads)
+};
+VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned);
+hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, bool bf16, hipStream_t st);
+hipError_t launch_stream_read(const void* p, int64_t n16, uint32_t* out, hipStream_t st);
 hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);  // also ssd_saguaro_topf (a.sag)
 hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st);

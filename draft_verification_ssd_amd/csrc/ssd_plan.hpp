@@ -38,31 +38,48 @@ inline RowPlan plan_rows(int64_t rows, int V) {
   return p;
 }
 
-constexpr int kPlanTile = 4096;  // tokens per verification tile (256 threads x 16)
+// Verification tiles: 256 threads x (NV 16-byte chunks of every row); the host picks NV per call.
+// The smallest tile is 1024 tokens (fp32, one chunk), so a row of V tokens has at most
+// ceil(V / 1024) tiles: the workspace is sized for that many whatever tile the call takes.
+constexpr int kPlanMinTile = 1024;
+constexpr int kSeqCtlMax = 65536;     // per-sequence counter slots: one for every sequence index
+constexpr int kPlanSeqCtlWords = 8;   // 32 bytes per sequence: arrivals, guess arrivals, spare
+constexpr int kPlanDecWords = 32;     // decision record: 256 bytes per sequence
 
 struct VerifyLayout {
-  int T;  // tiles per row
-  size_t off_ctl, off_dec, off_stats, off_cand, off_res, total;
+  int Tcap;     // tiles per row the regions are sized for
+  int Fcap;     // guesses per row the candidate region is sized for
+  size_t off_seqctl, off_stats, off_chunk, off_dec, off_cand, total;
 };
 
-// Workspace: [flags | per-sequence control words (256 B) | per-sequence decision records (256 B) |
-// tile statistics (two tagged words per row and tile) | top-F candidate keys (two tagged words
-// each) | tile residual masses (tagged)]. A zero-filled workspace is a valid start; every call
-// leaves it valid for the next.
+// Workspace of ssd_verify:
+//   [0, 256)      word 0 sticky flags, word 1 the last call's tag, word 2 sequences finished by the
+//                 running call
+//   seqctl        counters per sequence index (arrivals of its tiles, tiles whose guesses are in),
+//                 at a fixed place for every sequence index 0 .. kSeqCtlMax-1, so no call of any
+//                 shape writes data where another call keeps a counter
+//   stats         [B][2K+1][Tcap][2] tagged (max c, sum) per row and tile
+//   chunk         [B][Tcap][2] tagged claim word and residual mass word per tile
+//   dec           [B][kPlanDecWords] tagged decision record per sequence
+//   cand          [B][K+1][Tcap][Fcap][2] tagged halves of each tile's guesses
+// Every data word carries the tag of the call that wrote it (tags grow by one per call), so a word
+// left by an earlier call, of any shape, never passes for the running call's. Counters are back
+// at zero whenever no call runs; a zero-filled workspace is a valid start.
 inline VerifyLayout verify_layout(int B, int K, int V, int topf_F_max) {
   VerifyLayout L;
-  L.T = int(ceil_div(V, kPlanTile));
-  size_t off = kAlign;  // flags word lives at offset 0
-  L.off_ctl = off;
-  off = align_up(off + size_t(B) * 256);
-  L.off_dec = off;
-  off = align_up(off + size_t(B) * 256);
+  L.Tcap = int(ceil_div(V, kPlanMinTile));
+  L.Fcap = topf_F_max > 0 ? topf_F_max : 1;
+  size_t off = kAlign;
+  L.off_seqctl = off;
+  off = align_up(off + size_t(kSeqCtlMax) * kPlanSeqCtlWords * 4);
   L.off_stats = off;
-  off = align_up(off + size_t(B) * (2 * K + 1) * L.T * 16);
+  off = align_up(off + size_t(B) * (2 * K + 1) * L.Tcap * 16);
+  L.off_chunk = off;
+  off = align_up(off + size_t(B) * L.Tcap * 16);
+  L.off_dec = off;
+  off = align_up(off + size_t(B) * kPlanDecWords * 8);
   L.off_cand = off;
-  off = align_up(off + size_t(B) * K * L.T * topf_F_max * 16);
-  L.off_res = off;
-  off = align_up(off + size_t(B) * L.T * 8);
+  off = align_up(off + size_t(B) * (K + 1) * L.Tcap * L.Fcap * 16);
   L.total = off;
   return L;
 }

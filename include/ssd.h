@@ -10,9 +10,8 @@
  *
  * Conventions shared by every entry point
  *   - Every device pointer is caller-owned device memory (e.g. a torch tensor's storage). The
- *     library allocates nothing; its only global state is a per-device cache of how many
- *     verification workgroups fit the device at once. Calls on different streams with different
- *     workspaces are independent.
+ *     library allocates nothing and keeps no state between calls: calls on different streams with
+ *     different workspaces are independent.
  *   - Device calls enqueue work on `stream` and return once it is launched; nothing synchronises.
  *   - Arguments are validated on the host before any launch. Any error code means nothing was
  *     launched, except SSD_ERR_HIP (a launch was rejected by the runtime).
@@ -25,10 +24,11 @@
  *     or sequences is a successful no-op.
  *   - Workspaces: device memory of at least the size the matching *_workspace_bytes helper
  *     returns, 256-byte aligned, zero-filled before its first use. Its first 4 bytes hold the
- *     sticky device-error flags; ssd_verify keeps per-sequence arrival counters in it that each
- *     call returns to zero (re-zero the workspace after an SSD_FLAG_TIMEOUT). The rest is scratch
- *     that each call rewrites before reading. One workspace serves one call at a time: calls that
- *     share a workspace must be ordered on one stream.
+ *     sticky device-error flags. ssd_verify keeps counters in it that every call leaves at zero,
+ *     and tags every other word it writes with a per-call number, so one workspace serves calls of
+ *     any shape (B, K, V, F) in turn, each sized for its own shape, with no re-zeroing. One
+ *     workspace serves one call at a time: calls that share a workspace must be ordered on one
+ *     stream.
  */
 #ifndef SSD_H_
 #define SSD_H_
@@ -60,7 +60,8 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 #define SSD_FLAG_BAD_TOKEN 0x1u     /* a draft token id outside [0, V) */
 #define SSD_FLAG_SAGUARO_NORM 0x2u  /* Saguaro normaliser N <= 0 (C = 0 with S holding all mass) */
 #define SSD_FLAG_BAD_F 0x4u         /* a per-row F outside [0, F_max] (clamped) */
-#define SSD_FLAG_TIMEOUT 0x8u       /* a wait between workgroups gave up (workspace needs re-zeroing) */
+#define SSD_FLAG_TIMEOUT 0x8u       /* a wait on workgroups that had already arrived gave up (never
+                                       expected: it means a device fault; the outputs are not valid) */
 #define SSD_FLAG_BAD_C 0x10u        /* a per-row Saguaro C outside [0, 1] (clamped; NaN as 1) */
 
 /* ---------------------------------------------------------------------------------------------
@@ -99,21 +100,26 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   accepted_len      device int32 [B] out: k in 0..K.
  *   bonus_token       device int32 [B] out.
  *   accept_prob       device fp32 [B, K] out or NULL: min(1, p_i(x_i) / q'_i(x_i)) at every i.
- *   residual_mass     device fp32 [B] out or NULL: R (1 when k = K).
+ *   residual_mass     device fp32 [B] out or NULL: R (1 when k = K; 0 when the residual was all zero
+ *                     and the bonus came from p_k).
  *   workspace         device scratch of ssd_verify_workspace_bytes(B, K, V, topf_F_max) bytes.
- * Launch: one kernel per round of sequences, each round as many whole sequences (ceil(V / 4096)
- * workgroups each) as the device keeps resident at once; the workgroups of a sequence wait for
- * each other with bounded spins (SSD_FLAG_TIMEOUT instead of a hang). ssd_verify_launches gives
- * the number of rounds.
+ * Launch: one kernel of B * T workgroups (T tiles per row, ssd_verify_tiles). The tiles of a
+ * sequence exchange partial results through the workspace, but no workgroup ever needs another to
+ * be resident at the same time: a tile that has polled SSD_DEFAULT_WAIT_POLLS times for the rest of
+ * its sequence hands its remaining work to the sequence's last tile and exits. The outputs are
+ * therefore the same on a device busy with other work; an idle device only gets them sooner.
  * Errors: SSD_ERR_INVALID_ARG (null required pointer, bad size/stride/T/C/F), SSD_ERR_UNSUPPORTED
- * (dtype, or a vocabulary whose 4096-token tiles cannot all be resident on the device),
- * SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
+ * (dtype), SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
  * ------------------------------------------------------------------------------------------- */
+#define SSD_DEFAULT_WAIT_POLLS 2048
+/* Workspace bytes for calls of this shape; topf_F_max is the largest number of guesses per row
+ * the calls make (including ssd_verify_opts.topf_last_F). */
 size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max);
-/* Kernel launches (rounds of resident sequences) that ssd_verify issues for this shape on the
- * current device; -1 for arguments ssd_verify rejects or an occupancy query that fails. Launches
- * nothing; the same host-side plan that ssd_verify follows. */
+/* Kernel launches ssd_verify issues: 1 for B > 0, 0 for B = 0, -1 for arguments it rejects. */
 int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max);
+/* Tiles per logit row (workgroups per sequence) of ssd_verify for this shape with 16-byte aligned
+ * rows (rows that are not take 1024-token fp32 / 2048-token bf16 tiles), -1 if rejected. */
+int ssd_verify_tiles(int B, int K, int V, ssd_dtype dtype);
 
 ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
                       const void* target_logits, int64_t target_seq_stride,
@@ -124,6 +130,32 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
                       int32_t* accepted_len, int32_t* bonus_token,
                       float* accept_prob, float* residual_mass,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Options of ssd_verify_ex (ssd_verify takes the defaults).
+ *   wait_polls     < 0: SSD_DEFAULT_WAIT_POLLS. How many times a tile polls for the rest of its
+ *                  sequence (its statistics, then its residual masses) before it leaves its work to
+ *                  the sequence's last tile; 0 makes every tile but the last hand its work over at
+ *                  once. Any value gives the same outputs; it only moves work between workgroups.
+ *                  At most 1 << 20.
+ *   topf_last_F    0..SSD_MAX_F: also the top guesses of draft row K (the row after the last drafted
+ *                  token, [SSD] "怎么猜奖励 token": the outcome k = K), with no token excluded, read
+ *                  in the same pass. Needs draft_seq_stride >= (K+1) V. 0: none.
+ *   topf_last_out  device int32 [B, topf_last_F] (-1 padded) when topf_last_F > 0. */
+typedef struct ssd_verify_opts {
+  int32_t wait_polls;
+  int32_t topf_last_F;
+  int32_t* topf_last_out;
+} ssd_verify_opts;
+
+ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride,
+                         const void* target_logits, int64_t target_seq_stride,
+                         ssd_dtype dtype, int B, int K, int V, float temperature,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                         const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                         int32_t* accepted_len, int32_t* bonus_token,
+                         float* accept_prob, float* residual_mass, const ssd_verify_opts* opts,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_topf_guess — top-F bonus-token guesses of R rows ([SSD] "怎么猜奖励 token"): per row the
@@ -295,6 +327,16 @@ ssd_status ssd_cache_lookup(int B, int budget, const int32_t* cache_k, const int
  * reset them. Synchronises `stream`.
  * ------------------------------------------------------------------------------------------- */
 ssd_status ssd_read_flags(void* workspace, uint32_t* out_flags, int clear, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_stream_read — measurement helper (not part of the verification path): reads `bytes` bytes of
+ * device memory once, 16 bytes per load, the way a bandwidth-bound kernel streams its input, and
+ * nothing else. Timing it over a footprint gives the read bandwidth the device reaches for it (the
+ * ceiling the verification kernel is compared with).
+ *   data   device, 16-byte aligned; bytes a multiple of 16.
+ *   sink   device uint32 [8192], written only in a case that never arises in practice.
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* ssd_status_string(ssd_status s);

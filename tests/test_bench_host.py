@@ -30,7 +30,7 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path, monkeypatch):
     """A counter that reads half the copy's bytes doubles the kernel's reading; the copy is found
     among the other launches as the one closest to the copy size; medians over dispatches."""
     copy_kib = bench.COPY_BYTES / 1024
-    k = "void ssd::verify_fused_kernel<ssd::BF16T, 4, 9, 2>(ssd::VerifyArgs)"
+    k = "void ssd::verify_kernel<ssd::BF16T, 4, 2, true>(ssd::VerifyArgs)"
     _counter_csv(tmp_path / "fetch.csv", [(k, "FETCH_SIZE", 100.0), (k, "FETCH_SIZE", 102.0),
                                          (k, "FETCH_SIZE", 300.0), ("copy", "FETCH_SIZE", copy_kib / 2),
                                          ("fill", "FETCH_SIZE", 5.0)])
