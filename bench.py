@@ -210,7 +210,7 @@ def trace_timeline(args):
         t0 = r[:, 0].min()
         role = r[:, 12]
         closer = (role & 1) != 0
-        gave_up += int(((role >> 8) & 1 == 0).sum())
+        gave_up += int((((role >> 8) & 1) == 0).sum())
         ends.append((r[:, 9].max() - t0) * 10)
         for slot, _ in TRACE_PHASES:
             v = r[:, slot]
@@ -510,8 +510,8 @@ def main():
         summarize_traffic(args.traffic_from[0], args.traffic_from[1], args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards by "
-              f"sequence across GPUs, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would shard "
+              f"by sequence, each GPU verifying its own sequences with no exchange)", file=sys.stderr)
         sys.exit(2)
     if args.ablation == "fanout":
         fanout_ablation(args)

@@ -55,6 +55,9 @@ constexpr int kDecK = 0, kDecLp = 1, kDecLq = 2, kDecWout = 3, kDecWin = 4, kDec
               kDecWords = kDecSet + kMaxF;
 static_assert(kDecWords <= kPlanDecWords, "decision record exceeds its workspace slot");
 
+#ifndef SSD_VERIFY_PRIO
+#define SSD_VERIFY_PRIO 1  // phase-1 issue priority by progress
+#endif
 #ifndef SSD_VERIFY_AHEAD
 #define SSD_VERIFY_AHEAD 4  // row slots of a tile in flight before the first is consumed
 #endif
@@ -62,9 +65,16 @@ static_assert(kDecWords <= kPlanDecWords, "decision record exceeds its workspace
 #ifdef SSD_TRACE
 // analysis builds only: 100 MHz timestamps per workgroup at each step (slot i of 16), and values
 constexpr int kTraceSlots = 16;
-#define TRACE(i)                                                                                       \
-  do {                                                                                                 \
-    if (threadIdx.x == 0 && a.trace) a.trace[int64_t(blockIdx.x) * kTraceSlots + (i)] = wall_clock64(); \
+// the counter is read through the scalar memory path; waiting right after the read keeps the sample
+// from being taken only at some later wait
+__device__ __forceinline__ uint64_t trace_clock() {
+  uint64_t v;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v));
+  return v;
+}
+#define TRACE(i)                                                                                        \
+  do {                                                                                                  \
+    if (threadIdx.x == 0 && a.trace) a.trace[int64_t(blockIdx.x) * kTraceSlots + (i)] = trace_clock(); \
   } while (0)
 #define TRACEV(i, v)                                                                         \
   do {                                                                                       \
@@ -453,6 +463,17 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
 #pragma unroll
     for (int s = 0; s < RM; ++s) {
       if (s + kAhead < RM) issue(s + kAhead);
+#if SSD_VERIFY_PRIO
+      // A wave's issue priority falls as it gets through its rows, so the waves of the workgroups
+      // that share a CU finish their statistics close together rather than the oldest first.
+      {
+        const int q = (4 * s) / RM;  // a constant once the loop is unrolled
+        if (q == 0) __builtin_amdgcn_s_setprio(3);
+        else if (q == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+#endif
       __builtin_amdgcn_sched_barrier(0);
       if (s < KM) {
         mk[s] = 0u;
@@ -472,9 +493,17 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   }
   // logits at the draft tokens and the Saguaro-set entries (the closer's accept tests): issued now,
   // read once the tile knows it is the closer
-  float zg_v = 0.f, zs_v = 0.f;
-  if (t < 2 * K && unsigned(xg) < unsigned(V)) zg_v = ET::one(row_ptr(t), xg);
-  if (t < K * sF && unsigned(sv_v) < unsigned(V)) zs_v = ET::one(row_ptr(t / sF), sv_v);
+  // Every lane reads (an idle or out-of-range lane the row's first token) and the value is selected
+  // afterwards, so no branch makes the wave wait for the read where it is issued.
+  float zg_v, zs_v;
+  {
+    const bool g_ok = t < 2 * K && unsigned(xg) < unsigned(V);
+    const float g = ET::one(row_ptr(t < 2 * K ? t : 0), g_ok ? xg : 0);
+    const bool s_ok = t < K * sF && unsigned(sv_v) < unsigned(V);
+    const float z2 = ET::one(row_ptr(t < K * sF ? t / sF : 0), s_ok ? sv_v : 0);
+    zg_v = g_ok ? g : 0.f;
+    zs_v = s_ok ? z2 : 0.f;
+  }
   if (t < K) {
     sh.xe[t] = x_v;
     sh.F[t] = f_v;
@@ -483,6 +512,9 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   if (t <= K) sh.u[t] = u_v;
   if (t < K * sF) sh.sv[t] = sv_v;
   const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
+#if SSD_VERIFY_PRIO
+  __builtin_amdgcn_s_setprio(0);
+#endif
   __syncthreads();
   TRACE(1);
 
