@@ -186,7 +186,7 @@ def topf(z: np.ndarray, F: int, exclude: int = -1) -> np.ndarray:
     z = np.asarray(z, dtype=np.float64)
     V = z.shape[0]
     order = np.lexsort((np.arange(V), -z))
-    keep = [int(v) for v in order if v != exclude and z[v] > -np.inf]
+    keep = order[(order != exclude) & (z[order] > -np.inf)]
     out = np.full(F, -1, dtype=np.int64)
     take = keep[:F]
     out[: len(take)] = take

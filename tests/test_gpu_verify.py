@@ -92,7 +92,7 @@ def test_config_b1_k4_v32000_f32():
     report("b1_k4_v32000_f32 x32 seeds", st)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+@pytest.mark.parametrize("seed", range(32))
 def test_config_b16_k4_v128256_bf16_top3(seed):
     bt = synth.make_verify_batch(16, 4, 128256, synth.BF16, seed)
     check_batch(bt, f"b16_k4_v128256_bf16_top3 seed{seed}", topf_F_max=3)

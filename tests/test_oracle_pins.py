@@ -538,3 +538,59 @@ def test_backup_crossover_is_the_first_batch_where_the_fast_backup_wins(seed):
             assert all(wins[first - 1:])
         # the two speedups agree at the real crossing
         assert abs(O.batch_speedup(h, E_hit, Ef, Tp, Tf, bs) - O.batch_speedup(h, E_hit, En, Tp, Tn, bs)) < 1e-9
+
+
+def test_batch_speedup_matches_a_simulated_two_gpu_schedule():
+    """[SSD] "SSD 的核心思想": the speculator runs on its own GPU while the target verifies, so a round
+    ends when both have finished; a batch with any miss then waits for the backup. An event-by-event
+    simulation of that schedule (per-sequence random hits, the two GPUs' finish times, the backup's
+    wait) gives tokens per unit of verification time; over many rounds it must approach
+    batch_speedup, for a primary faster and slower than the verification."""
+    rng = np.random.default_rng(17)
+    for h, E_hit, E_miss, T_p, T_b, b in [(0.9, 4.0, 2.0, 0.5, 1.0, 4), (0.8, 3.0, 1.5, 1.7, 0.6, 3),
+                                           (0.95, 5.0, 1.0, 1.0, 2.0, 16)]:
+        rounds = 200000
+        tokens = 0.0
+        clock = 0.0
+        hits = rng.random((rounds, b)) < h
+        for r in range(rounds):
+            start = clock
+            verify_done = start + 1.0          # the target's verification, one unit
+            spec_done = start + T_p            # the speculator's cache, on the other GPU
+            clock = max(verify_done, spec_done)
+            if not hits[r].all():              # some sequence missed: everyone waits for the backup
+                clock += T_b
+            tokens += np.where(hits[r], E_hit, E_miss).sum() / b  # per sequence
+        sim = tokens / clock
+        assert abs(sim - O.batch_speedup(h, E_hit, E_miss, T_p, T_b, b)) < 0.01 * sim, (h, T_p, b, sim)
+
+
+def test_ssd_round_keys_outcome_k_with_the_guesses_of_draft_row_k():
+    """[SSD] "怎么猜奖励 token" with "SSD 的核心思想": the outcome (k, t) is looked up among the guesses
+    of draft position k (the extra draft row for k = K), which exclude the sampled token x_k. Rows
+    built so that the round ends at (k, t_k), t_k the best token of draft row k other than x_k and of
+    no other row: the lookup hits, at the first slot of position k (the second for the extra row,
+    whose favourite is not excluded), for every k."""
+    K, V, T = 3, 9, 1.0
+    F = [2, 2, 2, 2]
+    for k in range(K + 1):
+        draft = np.full((1, K + 1, V), -4.0, dtype=np.float32)
+        target = np.full((1, K + 1, V), -4.0, dtype=np.float32)
+        x = np.zeros((1, K), dtype=np.int64)             # every draft token is 0, the draft's favourite
+        for i in range(K + 1):
+            draft[0, i, 0] = 3.0
+            draft[0, i, 3 + i] = 2.0                     # t_i = 3 + i: row i's best other token
+            draft[0, i, 1] = 1.0
+        for i in range(k):
+            target[0, i] = draft[0, i]                   # p = q: accepted for any u < 1
+        # the target at position k (k < K: reject x_k = 0, residual on t_k; k = K: bonus drawn
+        # from p_K) puts its mass on t_k
+        target[0, k, :] = -20.0
+        target[0, k, 3 + k] = 20.0
+        u = np.full((1, K + 1), 0.5, dtype=np.float32)
+        res = O.ssd_round(draft, target, "f32", x, u, T, None, 1.0, F)[0]
+        assert (res["k"], res["bonus"]) == (k, 3 + k)
+        # row K has no sampled token to exclude: its favourite, token 0, is its first guess
+        want = sum(F[:k]) + (1 if k == K else 0)
+        assert res["slot"] == want, (k, res["slot"], res["keys_k"], res["keys_t"])
+        assert res["keys_k"][res["slot"]] == k and res["keys_t"][res["slot"]] == 3 + k
