@@ -13,7 +13,8 @@ from typing import Optional, Sequence
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd.so")
 TRACE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssd_trace.so")
 
-SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, SSD_ERR_SCRATCH_LIMIT = range(6)
+SSD_NOALLOC_SCRATCH_BYTES = 32 << 20
 SSD_F32, SSD_BF16 = 0, 1
 SSD_MAX_K, SSD_MAX_F, SSD_MAX_V, SSD_MAX_B = 16, 16, 1 << 20, 65535
 SSD_DEFAULT_WAIT_POLLS = 2048
@@ -30,7 +31,7 @@ EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify_tile
            "ssd_saguaro_sample_workspace_bytes", "ssd_saguaro_sample", "ssd_batch_speedup",
            "ssd_backup_crossover",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",
-           "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string"]
+           "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string", "ssd_verify_noalloc"]
 
 _lib = None
 P = ctypes.c_void_p
@@ -53,6 +54,9 @@ def _declare(L):
     L.ssd_verify.restype = ctypes.c_int
     L.ssd_verify.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32, P,
                              P, I32, P, P, P, P, P, P, SZ, P]
+    L.ssd_verify_noalloc.restype = ctypes.c_int
+    L.ssd_verify_noalloc.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32, P,
+                                     P, I32, P, P, P, P, P, P, P]
     L.ssd_verify_ex.restype = ctypes.c_int
     L.ssd_verify_ex.argtypes = [P, I64, P, I64, ctypes.c_int, I32, I32, I32, F32, P, P, P, I32, F32, P,
                                 P, I32, P, P, P, P, P, P, P, SZ, P]
@@ -241,7 +245,8 @@ class VerifyCall:
                  sag_set=None, sag_C=1.0, topf_F: Optional[Sequence[int]] = None,
                  topf_F_max: int = 0, topf_out=None, accepted_len=None, bonus_token=None,
                  accept_prob=None, residual_mass=None, workspace: Optional[Workspace] = None,
-                 stream=None, wait_polls: Optional[int] = None, topf_last_F: int = 0, topf_last_out=None):
+                 stream=None, wait_polls: Optional[int] = None, topf_last_F: int = 0, topf_last_out=None,
+                 noalloc_flags=None):
         torch = _torch()
         B, Kd, V, dstride = _rows3(draft, "draft", 1)
         Bt, Kt, Vt, tstride = _rows3(target, "target", 2)
@@ -293,7 +298,11 @@ class VerifyCall:
         if wait_polls is not None or topf_last_F > 0:
             self.opts = VerifyOpts(-1 if wait_polls is None else int(wait_polls), int(topf_last_F),
                                    _ptr(topf_last_out) if topf_last_F > 0 else None)
-        if workspace is None:
+        if noalloc_flags is not None:  # ssd_verify_noalloc: the library's static workspace
+            if self.opts is not None or workspace is not None:
+                raise ValueError("noalloc_flags excludes workspace, wait_polls and topf_last_F")
+            _need(noalloc_flags, torch.int32, (1,), "noalloc_flags")
+        elif workspace is None:
             workspace = Workspace(ssd_verify_workspace_bytes(B, K, V, max(topf_F_max, topf_last_F)), dev)
         self.B, self.K, self.V = B, K, V
         self.workspace = workspace
@@ -306,8 +315,13 @@ class VerifyCall:
             float(sag_C), None if self.sag_C_arr is None else ctypes.addressof(self.sag_C_arr),
             None if self.topf_F_arr is None else ctypes.addressof(self.topf_F_arr), int(topf_F_max),
             _ptr(topf_out), accepted_len.data_ptr(), bonus_token.data_ptr(), _ptr(accept_prob),
-            _ptr(residual_mass), workspace.ptr, workspace.nbytes, _stream(stream, dev))
-        if self.opts is not None:
+            _ptr(residual_mass), None if workspace is None else workspace.ptr,
+            0 if workspace is None else workspace.nbytes, _stream(stream, dev))
+        if noalloc_flags is not None:
+            self.args = self.args[:22] + (noalloc_flags.data_ptr(), self.args[24])
+            self._keep = self._keep + (noalloc_flags,)
+            self._fn = lib().ssd_verify_noalloc
+        elif self.opts is not None:
             self.args = self.args[:22] + (ctypes.addressof(self.opts),) + self.args[22:]
             self._fn = lib().ssd_verify_ex
         else:
@@ -319,6 +333,8 @@ class VerifyCall:
 
     def flags(self, clear: bool = True) -> int:
         """Device-error flags of this call's workspace (synchronises the stream)."""
+        if self.workspace is None:
+            raise ValueError("an allocation-free call reports its flags in its noalloc_flags word")
         return ssd_read_flags(self.workspace, clear)
 
     def checked(self):

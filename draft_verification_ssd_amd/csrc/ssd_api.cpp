@@ -46,6 +46,7 @@ const char* ssd_status_string(ssd_status s) {
     case SSD_ERR_UNSUPPORTED: return "unsupported dtype";
     case SSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case SSD_ERR_HIP: return "HIP launch error";
+    case SSD_ERR_SCRATCH_LIMIT: return "shape needs more than the allocation-free variant's static array holds";
   }
   return "unknown status";
 }
@@ -58,14 +59,19 @@ size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max) {
   return verify_layout(B, K, V, topf_F_max).total;
 }
 
-ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
-                         int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
-                         float temperature, const int32_t* draft_tokens, const float* uniforms,
-                         const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
-                         const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
-                         int32_t* accepted_len, int32_t* bonus_token, float* accept_prob,
-                         float* residual_mass, const ssd_verify_opts* opts, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// Both verify entry points: every argument is validated before any HIP call. `noalloc_flags`
+// non-null selects the allocation-free variant: the workspace is the library's static array of the
+// current device and the device-error flags go to the caller's word.
+static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
+                              int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
+                              float temperature, const int32_t* draft_tokens, const float* uniforms,
+                              const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                              const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                              int32_t* accepted_len, int32_t* bonus_token, float* accept_prob,
+                              float* residual_mass, const ssd_verify_opts* opts, void* workspace,
+                              size_t workspace_bytes, uint32_t* noalloc_flags, hipStream_t stream) {
   if (!dtype_ok(dtype)) return SSD_ERR_UNSUPPORTED;
   if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V)
     return SSD_ERR_INVALID_ARG;
@@ -92,6 +98,11 @@ ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride, con
       !bonus_token)
     return SSD_ERR_INVALID_ARG;
   const VerifyLayout L = verify_layout(B, K, V, std::max(topf_F_max, lastF));
+  if (noalloc_flags) {
+    if (L.total > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_SCRATCH_LIMIT;
+    if (noalloc_scratch(&workspace, L.off_stats, stream) != hipSuccess) return SSD_ERR_HIP;
+    workspace_bytes = SSD_NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws_ok(workspace, workspace_bytes, L.total)) return SSD_ERR_WORKSPACE;
 
   const bool bf16 = dtype == SSD_BF16;
@@ -126,7 +137,7 @@ ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride, con
   a.bonus_out = bonus_token;
   a.aprob_out = accept_prob;
   a.rmass_out = residual_mass;
-  a.flags = at<uint32_t>(workspace, 0);
+  a.flags = noalloc_flags ? noalloc_flags : at<uint32_t>(workspace, 0);
   a.gtag = at<uint32_t>(workspace, 4);
   a.gdone = at<uint32_t>(workspace, 8);
   a.seqctl = at<uint32_t>(workspace, L.off_seqctl);
@@ -141,6 +152,36 @@ ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride, con
   a.trace = static_cast<uint64_t*>(ssd_trace_buffer);
 #endif
   return hip_status(launch_verify(a, P, bf16, stream));
+}
+
+extern "C" {
+
+ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
+                         int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
+                         float temperature, const int32_t* draft_tokens, const float* uniforms,
+                         const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                         const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                         int32_t* accepted_len, int32_t* bonus_token, float* accept_prob,
+                         float* residual_mass, const ssd_verify_opts* opts, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return verify_impl(draft_logits, draft_seq_stride, target_logits, target_seq_stride, dtype, B, K, V,
+                     temperature, draft_tokens, uniforms, sag_set, sag_F, sag_C, sag_C_pos, topf_F, topf_F_max,
+                     topf_out, accepted_len, bonus_token, accept_prob, residual_mass, opts, workspace,
+                     workspace_bytes, nullptr, stream);
+}
+
+ssd_status ssd_verify_noalloc(const void* draft_logits, int64_t draft_seq_stride, const void* target_logits,
+                              int64_t target_seq_stride, ssd_dtype dtype, int B, int K, int V,
+                              float temperature, const int32_t* draft_tokens, const float* uniforms,
+                              const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                              const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                              int32_t* accepted_len, int32_t* bonus_token, float* accept_prob,
+                              float* residual_mass, uint32_t* device_flags, hipStream_t stream) {
+  if (!device_flags) return SSD_ERR_INVALID_ARG;
+  return verify_impl(draft_logits, draft_seq_stride, target_logits, target_seq_stride, dtype, B, K, V,
+                     temperature, draft_tokens, uniforms, sag_set, sag_F, sag_C, sag_C_pos, topf_F, topf_F_max,
+                     topf_out, accepted_len, bonus_token, accept_prob, residual_mass, nullptr, nullptr, 0,
+                     device_flags, stream);
 }
 
 #ifdef SSD_TRACE

@@ -124,6 +124,9 @@ struct VerifyPlan {
 };
 VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned);
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, bool bf16, hipStream_t st);
+// Device address of the allocation-free verification's static array on the current device; the
+// first call on a device looks it up and clears its first ctrl_bytes with a fill kernel on st.
+hipError_t noalloc_scratch(void** out, size_t ctrl_bytes, hipStream_t st);
 hipError_t launch_stream_read(const void* p, int64_t n16, uint32_t* out, hipStream_t st);
 hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);  // also ssd_saguaro_topf (a.sag)
 hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);

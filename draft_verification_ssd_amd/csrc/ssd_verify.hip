@@ -32,6 +32,10 @@
 // on a busy device; an idle one gets it sooner.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <mutex>
+
+#include "ssd.h"
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 #include "ssd_plan.hpp"
@@ -1249,6 +1253,48 @@ static hipError_t launch_verify_e(const VerifyArgs& a, const VerifyPlan& p, hipS
 
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, bool bf16, hipStream_t st) {
   return bf16 ? launch_verify_e<BF16T>(a, p, st) : launch_verify_e<F32T>(a, p, st);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The allocation-free variant's workspace: one array per device, part of the code object (zero when
+// it loads). Host code never uses the name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, and is what the kernels are given.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kScratchDevices];  // per device: the array's device address, once looked up
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+}  // namespace
+
+hipError_t noalloc_scratch(void** out, size_t ctrl_bytes, hipStream_t st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) % 256) != 0) return hipErrorInvalidValue;
+    // the control words (call tag, sequence count, arrival counters) must start at zero: cleared
+    // ahead of the first launch on this device (a fill kernel, not a memset, so that a capturing
+    // caller records no memset node)
+    const int64_t n = int64_t(std::min(ctrl_bytes, size_t(SSD_NOALLOC_SCRATCH_BYTES)) / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, st, static_cast<uint32_t*>(ptr), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace ssd

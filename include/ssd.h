@@ -51,7 +51,8 @@ typedef enum ssd_status {
   SSD_ERR_INVALID_ARG = 1,
   SSD_ERR_UNSUPPORTED = 2,
   SSD_ERR_WORKSPACE = 3,
-  SSD_ERR_HIP = 4
+  SSD_ERR_HIP = 4,
+  SSD_ERR_SCRATCH_LIMIT = 5 /* the shape needs more than SSD_NOALLOC_SCRATCH_BYTES (ssd_verify_noalloc) */
 } ssd_status;
 
 typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -156,6 +157,34 @@ ssd_status ssd_verify_ex(const void* draft_logits, int64_t draft_seq_stride,
                          int32_t* accepted_len, int32_t* bonus_token,
                          float* accept_prob, float* residual_mass, const ssd_verify_opts* opts,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ssd_verify_noalloc — ssd_verify for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * the same kernel, with its workspace taken from a static device array of the library instead of
+ * the caller.
+ *   Arguments as ssd_verify, without workspace / workspace_bytes, plus
+ *   device_flags  device uint32 [1], caller-owned: the call ORs its SSD_FLAG_* bits into it (sticky;
+ *                 the caller zeroes it, e.g. with ssd_read_flags(device_flags, &f, 1, stream)).
+ * Limit: shapes with ssd_verify_workspace_bytes(B, K, V, topf_F_max) <= SSD_NOALLOC_SCRATCH_BYTES;
+ * larger ones return SSD_ERR_SCRATCH_LIMIT before any HIP call. The array (one per device, 32 MiB,
+ * held until the process ends) is set up by the first call on each device (its address looked up,
+ * its control words cleared by a fill kernel on `stream`); no call allocates or frees anything.
+ * Every call on a device shares that device's array and leaves it ready for the next (counters back
+ * at zero, other words tagged with the call): calls that overlap on one device, on different
+ * streams, race and must not be issued.
+ * Errors: as ssd_verify, SSD_ERR_INVALID_ARG also for a null device_flags, SSD_ERR_SCRATCH_LIMIT.
+ * ------------------------------------------------------------------------------------------- */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ssd_status ssd_verify_noalloc(const void* draft_logits, int64_t draft_seq_stride,
+                              const void* target_logits, int64_t target_seq_stride,
+                              ssd_dtype dtype, int B, int K, int V, float temperature,
+                              const int32_t* draft_tokens, const float* uniforms,
+                              const int32_t* sag_set, int sag_F, float sag_C, const float* sag_C_pos,
+                              const int32_t* topf_F, int topf_F_max, int32_t* topf_out,
+                              int32_t* accepted_len, int32_t* bonus_token,
+                              float* accept_prob, float* residual_mass, uint32_t* device_flags,
+                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * ssd_topf_guess — top-F bonus-token guesses of R rows ([SSD] "怎么猜奖励 token"): per row the

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     L = ssd.lib()
-    for s in range(5):
+    for s in range(6):
         assert L.ssd_status_string(s)
     assert L.ssd_status_string(99) == b"unknown status"
 
@@ -257,3 +257,29 @@ def test_speedup_validation():
     assert L.ssd_batch_speedup(0.5, 1, 1, 0, 0, 1, None) == INV
     assert L.ssd_backup_crossover(0.5, 1, 1, 0, 1, 0, float("nan"), ctypes.byref(out), None) == INV
     assert L.ssd_backup_crossover(0.5, 1, 1, 0, 1, 0, 0, None, None) == INV
+
+
+def _verify_noalloc(**over):
+    B, K, V = 2, 4, 1000
+    a = dict(draft=FAKE, dstride=K * V, target=FAKE, tstride=(K + 1) * V, dtype=ssd.SSD_F32, B=B, K=K,
+             V=V, T=1.0, x=FAKE, u=FAKE, sset=None, sF=0, C=1.0, Cpos=None, topfF=None, topfFmax=0,
+             topf_out=None, k=FAKE, bonus=FAKE, aprob=None, rmass=None, flags=FAKE, stream=None)
+    a.update(over)
+    return ssd.lib().ssd_verify_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(flags=None), INV), (dict(dtype=7), UNS), (dict(B=-1), INV), (dict(T=0.0), INV),
+    (dict(k=None), INV),
+    # past the static array: B = 4096 sequences of K = 16 at V = 2^20 need far more than 32 MiB
+    (dict(B=4096, K=16, V=1 << 20, dstride=16 << 20, tstride=17 << 20), ssd.SSD_ERR_SCRATCH_LIMIT),
+])
+def test_verify_noalloc_rejects_before_any_launch(over, want):
+    assert _verify_noalloc(**over) == want
+
+
+def test_verify_noalloc_limit_matches_the_workspace_size():
+    # the headline shape fits the static array; the limit is the workspace size itself
+    assert ssd.ssd_verify_workspace_bytes(16, 4, 128256, 3) <= ssd.SSD_NOALLOC_SCRATCH_BYTES
+    assert ssd.ssd_verify_workspace_bytes(4096, 16, 1 << 20, 16) > ssd.SSD_NOALLOC_SCRATCH_BYTES
+    assert _verify_noalloc(B=0) == OK  # an empty batch is a no-op, before the array is touched
