@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--ablation", choices=["fanout"])
     ap.add_argument("--trace-timeline", action="store_true")
     ap.add_argument("--trace-out", default=None, help="with --trace-timeline: save the raw timestamps (.npy)")
+    ap.add_argument("--wait-polls", type=int, default=None,
+                    help="ssd_verify's wait_polls option (default: the library's)")
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="oracle worker processes for cpu_baseline (0: the usable cores, at most 16)")
     ap.add_argument("--temps", default="0.5,0.75,1.0,1.5,2.0")
@@ -184,7 +186,7 @@ def trace_timeline(args):
     esize = 2 if dtype == "bf16" else 4
     n_rep = max(1, math.ceil(ROTATE_BYTES / ((2 * K + 1) * B * V * esize)))
     ws = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, topf), dev)
-    calls = [make_replica(bt, dev, topf, ws) for _ in range(n_rep)]
+    calls = [make_replica(bt, dev, topf, ws, args.wait_polls) for _ in range(n_rep)]
     T = ssd.ssd_verify_tiles(B, K, V, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32)
     nwg = B * T
     buf = torch.zeros(nwg * TRACE_SLOTS, dtype=torch.int64, device=dev)
@@ -235,7 +237,7 @@ def algorithmic_bytes(B, K, V, esize, topf):
     return logits + small + outs
 
 
-def make_replica(bt, dev, topf, workspace):
+def make_replica(bt, dev, topf, workspace, wait_polls=None):
     import numpy as np
     import torch
 
@@ -251,55 +253,107 @@ def make_replica(bt, dev, topf, workspace):
     target = lg(bt.target)
     x = torch.from_numpy(bt.x).to(dev)
     u = torch.from_numpy(bt.u).to(dev)
-    return ssd.VerifyCall(draft, target, x, u, bt.T, topf_F_max=topf, workspace=workspace)
+    aprob = torch.empty((bt.B, bt.K), dtype=torch.float32, device=dev)
+    return ssd.VerifyCall(draft, target, x, u, bt.T, topf_F_max=topf, accept_prob=aprob, workspace=workspace,
+                          wait_polls=wait_polls)
 
 
-def cpu_baseline(bt, topf, seconds):
-    """The float64 oracle on a bounded sample of the same workload (single thread)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers(requested: int) -> int:
+    """Oracle worker processes: the host's cores, at most 16 (one GPU's share of the box)."""
+    if requested > 0:
+        return requested
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _one_thread():
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[v] = "1"
+
+
+def _oracle_verify_worker(job):
+    """One worker of the CPU baseline: whole sequences of the batch through the float64 oracle
+    (verification and top-F guesses) for `seconds`, starting at sequence `first`."""
     import oracle as O
 
+    draft, target, dtype, x, u, T, topf, first, seconds = job
+    B, K = x.shape
     t0 = time.perf_counter()
     seqs = 0
-    B, K = bt.B, bt.K
     while True:
-        b = seqs % B
-        zq = O.logits_f64(bt.draft[b, :K], bt.dtype)
-        zp = O.logits_f64(bt.target[b], bt.dtype)
-        O.verify_sequence(zq, zp, bt.x[b], bt.u[b], bt.T)
+        b = (first + seqs) % B
+        zq = O.logits_f64(draft[b, :K], dtype)
+        zp = O.logits_f64(target[b], dtype)
+        O.verify_sequence(zq, zp, x[b], u[b], T)
         for i in range(K):
-            O.topf(zq[i], topf, int(bt.x[b, i]))
+            O.topf(zq[i], topf, int(x[b, i]))
         seqs += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    rows = seqs * (2 * K + 1)
-    return dict(value=rows / el, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{seqs} sequences of the workload (seed 0), {rows} logit rows, "
-                       f"float64 NumPy oracle verify + top-{topf} guesses, {el:.1f} s on 1 thread")
+            return seqs, seqs * (2 * K + 1), el
 
 
-def cpu_baseline_round(bt, branch, branch_u, fan, seconds):
-    """The float64 oracle on a bounded sample of an SSD round (single thread): whole sequences,
-    each with its verification, guesses, keys, lookup and its branch rows' draft step (set,
-    Saguaro mass and normaliser, sampled token)."""
+def _oracle_round_worker(job):
+    """One worker of the round's CPU baseline: whole sequences of the round (verification, guesses,
+    keys, lookup and the branch rows' draft step) for `seconds`."""
     import oracle as O
 
+    draft, target, dtype, x, u, T, sets, C, fan, branch, branch_u, first, seconds = job
+    B, K = x.shape
+    nbr = branch.shape[1]
     t0 = time.perf_counter()
     seqs = 0
-    B, K = bt.B, bt.K
-    nbr = branch.shape[1]
     while True:
-        b = seqs % B
-        O.ssd_round(bt.draft[b:b + 1], bt.target[b:b + 1], bt.dtype, bt.x[b:b + 1], bt.u[b:b + 1], bt.T,
-                    bt.sets[b:b + 1], bt.C, fan, branch=branch[b:b + 1], branch_u=branch_u[b:b + 1])
+        b = (first + seqs) % B
+        O.ssd_round(draft[b:b + 1], target[b:b + 1], dtype, x[b:b + 1], u[b:b + 1], T, sets[b:b + 1], C, fan,
+                    branch=branch[b:b + 1], branch_u=branch_u[b:b + 1])
         seqs += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    rows = seqs * ((2 * K + 2) + nbr * K)
-    return dict(value=rows / el, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{seqs} whole sequences of the round (seed 0) with their {nbr} branches, {rows} logit "
-                       f"rows, float64 NumPy oracle, {el:.1f} s on 1 thread")
+            return seqs, seqs * ((2 * K + 2) + nbr * K), el
+
+
+def _run_workers(fn, jobs):
+    """The jobs in fresh interpreter processes (spawned: nothing of this process's GPU state is
+    inherited), one per job, each single-threaded."""
+    import multiprocessing as mp
+
+    with mp.get_context("spawn").Pool(len(jobs), initializer=_one_thread) as pool:
+        res = pool.map(fn, jobs)
+    return sum(r[0] for r in res), sum(r[1] for r in res), max(r[2] for r in res)
+
+
+def cpu_baseline(bt, topf, seconds, workers):
+    """The float64 oracle on a bounded sample of the same workload, over `workers` processes."""
+    K = bt.K
+    jobs = [(bt.draft[:, :K], bt.target, bt.dtype, bt.x, bt.u, bt.T, topf, (w * bt.B) // workers, seconds)
+            for w in range(workers)]
+    seqs, rows, el = _run_workers(_oracle_verify_worker, jobs)
+    return dict(value=round(rows / el, 1), unit="rows/s", cores=workers, kind="oracle", cpu=cpu_model(),
+                sample=f"{seqs} sequences of the workload (seed 0) over {workers} processes, {rows} logit "
+                       f"rows, float64 NumPy oracle verify + top-{topf} guesses, {el:.1f} s each")
+
+
+def cpu_baseline_round(bt, branch, branch_u, fan, seconds, workers):
+    """The float64 oracle on a bounded sample of an SSD round, over `workers` processes: whole
+    sequences, each with its verification, guesses, keys, lookup and its branch rows' draft step."""
+    jobs = [(bt.draft, bt.target, bt.dtype, bt.x, bt.u, bt.T, bt.sets, bt.C, fan, branch, branch_u,
+             (w * bt.B) // workers, seconds) for w in range(workers)]
+    seqs, rows, el = _run_workers(_oracle_round_worker, jobs)
+    nbr = branch.shape[1]
+    return dict(value=round(rows / el, 1), unit="rows/s", cores=workers, kind="oracle", cpu=cpu_model(),
+                sample=f"{seqs} whole sequences of the round (seed 0) with their {nbr} branches over "
+                       f"{workers} processes, {rows} logit rows, float64 NumPy oracle, {el:.1f} s each")
 
 
 def load_traffic(workload, khash):
@@ -474,7 +528,7 @@ def pipeline_bench(args, spec):
         st_out[st.name] = {"ms": round(ms, 5), "algorithmic_bytes": st.nbytes,
                            "GB/s": round(st.nbytes / (ms * 1e-3) / 1e9, 1)}
     dom = max(range(nst), key=lambda j: stage_ms[j])
-    cpu = None if args.no_cpu_baseline else cpu_baseline_round(bt, branch, branch_u, fan, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_round(bt, branch, branch_u, fan, args.cpu_seconds, cpu_workers(args.cpu_workers))
     line = {
         "metric": METRIC,
         "value": round(rows / (step_ms * 1e-3), 1),
@@ -542,7 +596,7 @@ def main():
     logit_bytes = (2 * K + 1) * B * V * esize
     n_rep = max(1, math.ceil(ROTATE_BYTES / logit_bytes))
     ws = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, topf), dev)
-    calls = [make_replica(bt, dev, topf, ws) for _ in range(n_rep)]
+    calls = [make_replica(bt, dev, topf, ws, args.wait_polls) for _ in range(n_rep)]
 
     for i in range(args.warmup):
         calls[i % n_rep]()
@@ -611,6 +665,26 @@ def main():
         print(f"device flags {flags:#x}", file=sys.stderr)
         sys.exit(3)
 
+    # the read-only streaming ceiling at this footprint: a plain read of as many bytes as the step's
+    # logits, rotating over as many buffers, timed the same way (outside the timed region above)
+    read_ceiling = None
+    if not args.copy_calibration:
+        bufs = [torch.empty(logit_bytes, dtype=torch.uint8, device=dev) for _ in range(n_rep)]
+        sink = torch.zeros(8192, dtype=torch.int32, device=dev)
+        for i in range(2 * n_rep):
+            ssd.ssd_stream_read(bufs[i % n_rep], sink, stream=stream)
+        n_read = max(n_rep * 20, 200)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record(stream)
+        for i in range(n_read):
+            ssd.ssd_stream_read(bufs[i % n_rep], sink, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        read_ms = r0.elapsed_time(r1) / n_read
+        read_ceiling = round(logit_bytes / (read_ms * 1e-3) / 1e9, 1)
+        del bufs, sink
+
     rows = (2 * K + 1) * B
     value = rows / (ms_per_step * 1e-3)
     # algorithmic bytes of one launch (a step's bytes over its launches, which run back to back) over
@@ -620,7 +694,9 @@ def main():
     khash = kernel_hash()
     traffic = load_traffic(args.workload, khash)
 
-    k_hist = np.bincount(calls[0].outputs["accepted_len"].cpu().numpy(), minlength=K + 1).tolist()
+    k_all = calls[0].outputs["accepted_len"].cpu().numpy()  # the replicas hold copies of one batch
+    a_all = calls[0].outputs["accept_prob"].cpu().numpy().ravel()
+    k_hist = np.bincount(k_all, minlength=K + 1).tolist()
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -639,14 +715,18 @@ def main():
                    "input_replicas": n_rep, "sequences_per_s": round(B / (ms_per_step * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "verify_fused_kernel",
+                     "kernel": VERIFY_KERNEL,
                      "launch_ms": round(launch_ms, 6), "launches_per_step": n_launch,
                      "isolated_launch_ms": round(isolated_ms, 6), "kernel_hash": khash,
+                     "read_ceiling_GBps": read_ceiling,
+                     "frac_of_read_ceiling": None if read_ceiling is None else round(achieved / read_ceiling, 4),
                      "device_copy_GBps": copy_gbs},
-        "accepted_len_hist": k_hist,
+        # [SD7.3] 7.3.7: the acceptance rate and the accepted length, over the replicas' sequences
+        "acceptance": {"alpha": round(float(a_all.mean()), 4), "mean_k": round(float(k_all.mean()), 4),
+                       "accepted_len_hist": k_hist},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(bt, topf, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(bt, topf, args.cpu_seconds, cpu_workers(args.cpu_workers))
     print(json.dumps(line), flush=True)
 
 

@@ -86,7 +86,7 @@ static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride
   if (topf_F)
     for (int i = 0; i < K; ++i)
       if (topf_F[i] < 0 || topf_F[i] > topf_F_max) return SSD_ERR_INVALID_ARG;
-  const int wait_polls = (opts && opts->wait_polls >= 0) ? opts->wait_polls : SSD_DEFAULT_WAIT_POLLS;
+  int wait_polls = (opts && opts->wait_polls >= 0) ? opts->wait_polls : -1;
   if (wait_polls > (1 << 20)) return SSD_ERR_INVALID_ARG;
   const int lastF = opts ? opts->topf_last_F : 0;
   if (lastF < 0 || lastF > SSD_MAX_F || (lastF > 0 && !opts->topf_last_out)) return SSD_ERR_INVALID_ARG;
@@ -110,6 +110,7 @@ static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride
   const bool aligned = aligned16(draft_logits) && aligned16(target_logits) && (int64_t(V) * es) % 16 == 0 &&
                        (draft_seq_stride * es) % 16 == 0 && (target_seq_stride * es) % 16 == 0;
   const VerifyPlan P = plan_verify(B, K, V, bf16, aligned);
+  if (wait_polls < 0) wait_polls = SSD_DEFAULT_WAIT_POLLS;
   VerifyArgs a;
   std::memset(&a, 0, sizeof(a));
   a.draft = draft_logits;

@@ -54,6 +54,7 @@ static_assert(kRegW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
 static_assert(kRegW <= 64, "a key-list region gives at most one entry per lane");
 // claim word states of a tile's residual chunk
 constexpr uint32_t kClaimOwner = 1, kClaimAbandoned = 2, kClaimCloser = 3;
+constexpr int kGroup = 4;  // chunks given up that the closer computes at once
 // decision record: 64-bit words (call tag << 32 | value)
 constexpr int kDecK = 0, kDecLp = 1, kDecLq = 2, kDecWout = 3, kDecWin = 4, kDecNset = 5, kDecSet = 6,
               kDecWords = kDecSet + kMaxF;
@@ -210,6 +211,8 @@ struct Shared {
   int role;  // bit 0 closer, bit 1 guess merger
   int go;    // the record (owners) or the masses (bonus) were read in time
   int todo, alldone, drawn;
+  int todo_list[kMaxT];       // chunks given up, listed for the closer
+  float wtg[kGroup][kWaves];  // per-wave masses of a group of such chunks
   // residual and bonus
   float wt[kWaves];
   float res[kMaxT];
@@ -1051,34 +1054,76 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   // chunks they gave up; an owner polls them (a bounded number of times)
   if (closer) {
     for (int spins = 0;;) {
+      // wave 0: masses that are in go to sh.res; the chunks given up are listed in ascending order
       if (t < 64) {
-        int first_ab = INT_MAX;
         bool all_in = true;
-        for (int c = lane; c < nT; c += 64) {
-          const uint64_t mw = ld_agent(chunk + 2 * c + 1);
-          if (tag_of(mw) == tag) {
-            sh.res[c] = val_f(mw);
-            continue;
+        int n_ab = 0;
+        for (int c0 = 0; c0 < nT; c0 += 64) {
+          const int c = c0 + lane;
+          bool ab = false;
+          if (c < nT) {
+            const uint64_t mw = ld_agent(chunk + 2 * c + 1);
+            if (tag_of(mw) == tag) {
+              sh.res[c] = val_f(mw);
+            } else {
+              all_in = false;
+              ab = ld_agent(chunk + 2 * c) == tagged(tag, kClaimAbandoned);
+            }
           }
-          all_in = false;
-          if (ld_agent(chunk + 2 * c) == tagged(tag, kClaimAbandoned)) first_ab = min(first_ab, c);
+          const uint64_t m = __ballot(ab);
+          if (ab)
+            sh.todo_list[n_ab + int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)))] = c;
+          n_ab += __popcll(m);
         }
-        first_ab = wave_min_i(first_ab);
         const bool all = __all(all_in);
         if (lane == 0) {
-          sh.todo = first_ab;
+          sh.todo = n_ab;
           sh.alldone = all ? 1 : 0;
         }
       }
       __syncthreads();
       if (sh.alldone) break;
-      const int c = sh.todo;
-      if (c != INT_MAX) {
-        if (t == 0) st_agent(chunk + 2 * c, tagged(tag, kClaimCloser));
-        float v2[E];
-        refetch_values(c, v2);
-        const float tot = tile_mass<E>(v2, sh.wt);
-        if (t == 0) st_agent(chunk + 2 * c + 1, tagged(tag, __float_as_uint(tot)));
+      const int n_ab = sh.todo;
+      if (n_ab > 0) {
+        // the chunks given up, kGroup at a time: both rows of every chunk of a group are read at
+        // once, then each chunk's mass is formed in tile_mass's order (the owner's bits)
+        for (int g0 = 0; g0 < n_ab; g0 += kGroup) {
+          const int gn = min(kGroup, n_ab - g0);
+          int cs[kGroup];
+          Raw<NV> rp[kGroup], rq[kGroup];
+#pragma unroll
+          for (int i = 0; i < kGroup; ++i) {
+            cs[i] = sh.todo_list[g0 + min(i, gn - 1)];
+            const int blq = cs[i] * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+            load_row<ET, NV, AL>(target + int64_t(k) * V, blq, V, rp[i]);
+            load_row<ET, NV, AL>(draft + int64_t(min(k, K - 1)) * V, blq, V, rq[i]);
+          }
+          if (t < gn) st_agent(chunk + 2 * cs[t], tagged(tag, kClaimCloser));
+          float part[kGroup];
+#pragma unroll
+          for (int i = 0; i < kGroup; ++i) {
+            const int blq = cs[i] * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+            const bool tq = AL && ((cs[i] + 1) * LY::TILE > V);
+            float zp[E], zq[E], v2[E];
+            unpack_row<ET, NV>(rp[i], blq, V, tq, zp);
+            unpack_row<ET, NV>(rq[i], blq, V, tq, zq);
+            residual_values<ET, NV>(zp, zq, k < K, blq, V, cc, sh.Lp, sh.Lq, sh.w_out, sh.w_in, sh.myset, nset, v2);
+            float sum = 0.f;
+#pragma unroll
+            for (int q = 0; q < E; ++q) sum += v2[q];
+            part[i] = wave_sum(sum);
+          }
+          if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) sh.wtg[i][w] = part[i];
+          }
+          __syncthreads();
+          if (t < gn) {
+            const float tot = (sh.wtg[t][0] + sh.wtg[t][1]) + (sh.wtg[t][2] + sh.wtg[t][3]);
+            st_agent(chunk + 2 * cs[t] + 1, tagged(tag, __float_as_uint(tot)));
+          }
+          __syncthreads();
+        }
         continue;
       }
       if (++spins > long_bound) {

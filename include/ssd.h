@@ -106,8 +106,9 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   workspace         device scratch of ssd_verify_workspace_bytes(B, K, V, topf_F_max) bytes.
  * Launch: one kernel of B * T workgroups (T tiles per row, ssd_verify_tiles). The tiles of a
  * sequence exchange partial results through the workspace, but no workgroup ever needs another to
- * be resident at the same time: a tile that has polled SSD_DEFAULT_WAIT_POLLS times for the rest of
- * its sequence hands its remaining work to the sequence's last tile and exits. The outputs are
+ * be resident at the same time: a tile that has polled for the rest of its sequence a bounded number
+ * of times (see ssd_verify_opts.wait_polls for the default) hands its remaining work to the
+ * sequence's last tile and exits. The outputs are
  * therefore the same on a device busy with other work; an idle device only gets them sooner.
  * Errors: SSD_ERR_INVALID_ARG (null required pointer, bad size/stride/T/C/F), SSD_ERR_UNSUPPORTED
  * (dtype), SSD_ERR_WORKSPACE (too small or misaligned), SSD_ERR_HIP.
@@ -133,11 +134,11 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Options of ssd_verify_ex (ssd_verify takes the defaults).
- *   wait_polls     < 0: SSD_DEFAULT_WAIT_POLLS. How many times a tile polls for the rest of its
- *                  sequence (its statistics, then its residual masses) before it leaves its work to
- *                  the sequence's last tile; 0 makes every tile but the last hand its work over at
- *                  once. Any value gives the same outputs; it only moves work between workgroups.
- *                  At most 1 << 20.
+ *   wait_polls     How many times a tile polls for the rest of its sequence (its statistics, then
+ *                  its residual masses) before it leaves its work to the sequence's last tile; 0
+ *                  makes every tile but the last hand its work over at once. < 0:
+ *                  SSD_DEFAULT_WAIT_POLLS. Any value gives the same outputs; it only moves work
+ *                  between workgroups. At most 1 << 20.
  *   topf_last_F    0..SSD_MAX_F: also the top guesses of draft row K (the row after the last drafted
  *                  token, [SSD] "怎么猜奖励 token": the outcome k = K), with no token excluded, read
  *                  in the same pass. Needs draft_seq_stride >= (K+1) V. 0: none.

@@ -52,3 +52,13 @@ def test_uniform_fanout_splits_the_budget_evenly():
         F = bench.uniform_fanout(K, budget)
         assert len(F) == K + 1 and sum(F) == budget and max(F) - min(F) <= 1
         assert F == sorted(F, reverse=True)  # the remainder goes to the smaller k
+
+
+def test_cpu_baseline_runs_the_oracle_over_worker_processes():
+    import bench
+    import synth
+    bt = synth.make_verify_batch(3, 2, 2000, synth.BF16, 0)
+    cb = bench.cpu_baseline(bt, 2, 0.3, 2)
+    assert cb["cores"] == 2 and cb["kind"] == "oracle" and cb["unit"] == "rows/s"
+    assert cb["value"] > 0 and cb["cpu"]
+    assert bench.cpu_workers(0) == max(1, min(os.cpu_count() or 1, 16))
