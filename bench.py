@@ -412,7 +412,8 @@ class _Stage:
 
 def pipeline_bench(args, spec):
     """One SSD round per step (the cache build and the full round): verification with Saguaro sets
-    and per-position top-F guesses, the guesses of draft row K, cache keys, lookup of the outcome,
+    and per-position top-F guesses, draft row K's guesses in the same pass, cache keys and the lookup
+    of the outcome in one launch,
     and, for the speculation-cache branches, the draft step of every branch row in one pass: its
     top-F set, Saguaro mass and normaliser, and a token drawn from q' (ssd_saguaro_sample). Each stage
     is timed on the GPU with an event pair per step; its algorithmic bytes (every logit it reads,
@@ -441,18 +442,19 @@ def pipeline_bench(args, spec):
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    b_verify = (2 * K + 1) * B * V * es + B * K * 4 + B * (K + 1) * 4 + B * K * Gm * 4 + 2 * B * 4 + B * K * Gm * 4
-    b_rowk = B * V * es + B * fan[K] * 4
+    # every logit row of the outer batch once (K + 1 draft rows, the extra one for its guesses, and
+    # K + 1 target rows), tokens, uniforms and sets in; k, bonus, top-F and row-K guesses out
+    b_verify = ((2 * K + 2) * B * V * es + B * K * 4 + B * (K + 1) * 4 + B * K * Gm * 4 + 2 * B * 4
+                + B * K * Gm * 4 + B * fan[K] * 4)
     # one read of every branch row; F and u in; set, sigma, N, token and q'(token) out
     b_branch = Rb * V * es + 2 * Rb * 4 + Rb * Gm * 4 + 4 * Rb * 4
-    b_keys = B * K * Gm * 4 + B * fan[K] * 4 + 2 * B * budget * 4
-    b_lookup = 2 * B * budget * 4 + 2 * B * 4 + B * 4 + 4
+    # guesses and outcomes in; keys, slots and the miss count out
+    b_keys_lookup = B * K * Gm * 4 + B * fan[K] * 4 + 2 * B * 4 + 2 * B * budget * 4 + B * 4 + 4
     total_logit_bytes = ((2 * K + 2) * B + Rb) * V * es
     n_rep = max(1, math.ceil(ROTATE_BYTES / total_logit_bytes))
 
     reps = []
     ws_v = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, Gm), dev)
-    ws_k = ssd.Workspace(ssd.ssd_topf_workspace_bytes(B, V, fan[K]), dev)
     ws_b = ssd.Workspace(ssd.ssd_saguaro_sample_workspace_bytes(Rb, V, Gm), dev)
     ub = torch.from_numpy(branch_u.reshape(-1)).to(dev)
     Fr = torch.tensor(fan[:K], dtype=torch.int32, device=dev).repeat(B * budget)
@@ -475,23 +477,21 @@ def pipeline_bench(args, spec):
         r["verify"] = ssd.VerifyCall(r["draft"], r["target"], torch.from_numpy(bt.x).to(dev),
                                      torch.from_numpy(bt.u).to(dev), T,
                                      sag_set=torch.from_numpy(bt.sets).to(dev), sag_C=bt.C, topf_F=fan[:K],
-                                     topf_F_max=Gm, topf_out=r["topf"], workspace=ws_v)
+                                     topf_F_max=Gm, topf_out=r["topf"], topf_last_F=fan[K],
+                                     topf_last_out=r["gk"], workspace=ws_v)
         reps.append(r)
 
     def stages(r):
         out = r["verify"].outputs
 
-        def keys():  # straight from ssd_verify's top-F output and the row-K guesses
-            ssd.ssd_cache_keys(r["topf"], fan, guesses_last=r["gk"], cache_k=r["ck"], cache_tok=r["ct"])
+        def keys_lookup():  # straight from ssd_verify's top-F outputs and its outcome
+            ssd.ssd_cache_keys_lookup(r["topf"], fan, out["accepted_len"], out["bonus_token"], guesses_last=r["gk"],
+                                      cache_k=r["ck"], cache_tok=r["ct"], out_slot=r["slot"],
+                                      out_miss_count=r["miss"])
 
         return [
-            _Stage("verify (ssd_verify, fused top-F and Saguaro)", b_verify, r["verify"]),
-            _Stage("row-K guesses (ssd_topf_guess)", b_rowk,
-                   lambda: ssd.ssd_topf_guess(r["draft"][:, K, :], fan[K], out=r["gk"], workspace=ws_k)),
-            _Stage("cache keys (ssd_cache_keys)", b_keys, keys),
-            _Stage("lookup (ssd_cache_lookup)", b_lookup,
-                   lambda: ssd.ssd_cache_lookup(r["ck"], r["ct"], out["accepted_len"], out["bonus_token"],
-                                                out_slot=r["slot"], out_miss_count=r["miss"])),
+            _Stage("verify (ssd_verify, fused top-F of rows 0..K and Saguaro)", b_verify, r["verify"]),
+            _Stage("cache keys + lookup (ssd_cache_keys_lookup)", b_keys_lookup, keys_lookup),
             _Stage("branch draft step (ssd_saguaro_sample)", b_branch,
                    lambda: ssd.ssd_saguaro_sample(r["bd"], T, Gm, bt.C, ub, F_per_row=Fr, out_token=r["btok"],
                                                   out_prob=r["bprob"], out_set=r["bsets"], out_set_mass=r["sig"],
@@ -516,12 +516,12 @@ def pipeline_bench(args, spec):
     stage_ms = [float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j in range(nst)]
     step_ms = float(np.median([ev[i][0].elapsed_time(ev[i][nst]) for i in range(args.steps)]))
-    flags = ssd.ssd_read_flags(ws_v) | ssd.ssd_read_flags(ws_k) | ssd.ssd_read_flags(ws_b)
+    flags = ssd.ssd_read_flags(ws_v) | ssd.ssd_read_flags(ws_b)
     if flags:
         print(f"device flags {flags:#x}", file=sys.stderr)
         sys.exit(3)
     rows = (2 * K + 2) * B + Rb
-    algo = b_verify + b_rowk + b_keys + b_lookup + b_branch
+    algo = b_verify + b_keys_lookup + b_branch
     miss = int(reps[0]["miss"].item())
     st_out = {}
     for st, ms in zip(plans[0], stage_ms):

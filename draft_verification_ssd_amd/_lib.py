@@ -31,7 +31,8 @@ EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify_tile
            "ssd_saguaro_sample_workspace_bytes", "ssd_saguaro_sample", "ssd_batch_speedup",
            "ssd_backup_crossover",
            "ssd_saguaro_workspace_bytes", "ssd_saguaro_adjust", "ssd_fanout_alloc", "ssd_cache_keys",
-           "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string", "ssd_verify_noalloc"]
+           "ssd_cache_lookup", "ssd_read_flags", "ssd_status_string", "ssd_verify_noalloc",
+           "ssd_cache_keys_lookup"]
 
 _lib = None
 P = ctypes.c_void_p
@@ -89,6 +90,8 @@ def _declare(L):
     L.ssd_fanout_alloc.argtypes = [I32, F64, F64, I32, P, P]
     L.ssd_cache_keys.restype = ctypes.c_int
     L.ssd_cache_keys.argtypes = [I32, I32, I32, P, P, I32, P, I32, P, P, P]
+    L.ssd_cache_keys_lookup.restype = ctypes.c_int
+    L.ssd_cache_keys_lookup.argtypes = [I32, I32, I32, P, P, I32, P, I32, P, P, P, P, P, P, P]
     L.ssd_cache_lookup.restype = ctypes.c_int
     L.ssd_cache_lookup.argtypes = [I32, I32, P, P, P, P, P, P, P]
     L.ssd_read_flags.restype = ctypes.c_int
@@ -556,3 +559,34 @@ def ssd_cache_lookup(cache_k, cache_tok, accepted_len, bonus_token, *, out_slot=
                                  accepted_len.data_ptr(), bonus_token.data_ptr(), out_slot.data_ptr(),
                                  out_miss_count.data_ptr(), _stream(stream, dev)), "ssd_cache_lookup")
     return out_slot, out_miss_count
+
+
+def ssd_cache_keys_lookup(guesses, fanout: Sequence[int], accepted_len, bonus_token, *, guesses_last=None,
+                          cache_k=None, cache_tok=None, out_slot=None, out_miss_count=None, stream=None):
+    """ssd_cache_keys and ssd_cache_lookup in one launch; returns (cache_k, cache_tok, slot, miss count)."""
+    torch = _torch()
+    B, Kg, G = guesses.shape
+    _need(guesses, torch.int32, (B, Kg, G), "guesses")
+    K = Kg if guesses_last is not None else Kg - 1
+    G_last = 0
+    if guesses_last is not None:
+        G_last = guesses_last.shape[1]
+        _need(guesses_last, torch.int32, (B, G_last), "guesses_last")
+    _need(accepted_len, torch.int32, (B,), "accepted_len")
+    _need(bonus_token, torch.int32, (B,), "bonus_token")
+    budget = int(sum(int(f) for f in fanout))
+    dev = guesses.device
+    if cache_k is None:
+        cache_k = torch.empty((B, budget), dtype=torch.int32, device=dev)
+    if cache_tok is None:
+        cache_tok = torch.empty((B, budget), dtype=torch.int32, device=dev)
+    if out_slot is None:
+        out_slot = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_miss_count is None:
+        out_miss_count = torch.empty(1, dtype=torch.int32, device=dev)
+    F = (ctypes.c_int32 * (K + 1))(*[int(f) for f in fanout])
+    check(lib().ssd_cache_keys_lookup(B, K, G, guesses.data_ptr(), _ptr(guesses_last), G_last, ctypes.addressof(F),
+                                      budget, accepted_len.data_ptr(), bonus_token.data_ptr(), cache_k.data_ptr(),
+                                      cache_tok.data_ptr(), out_slot.data_ptr(), out_miss_count.data_ptr(),
+                                      _stream(stream, dev)), "ssd_cache_keys_lookup")
+    return cache_k, cache_tok, out_slot, out_miss_count

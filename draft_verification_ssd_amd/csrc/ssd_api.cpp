@@ -90,8 +90,7 @@ static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride
   if (wait_polls > (1 << 20)) return SSD_ERR_INVALID_ARG;
   const int lastF = opts ? opts->topf_last_F : 0;
   if (lastF < 0 || lastF > SSD_MAX_F || (lastF > 0 && !opts->topf_last_out)) return SSD_ERR_INVALID_ARG;
-  if (lastF > 0) return SSD_ERR_UNSUPPORTED;
-  if (draft_seq_stride < int64_t(K) * V || target_seq_stride < int64_t(K + 1) * V)
+  if (draft_seq_stride < int64_t(lastF > 0 ? K + 1 : K) * V || target_seq_stride < int64_t(K + 1) * V)
     return SSD_ERR_INVALID_ARG;
   if (B == 0) return SSD_OK;
   if (!draft_logits || !target_logits || !draft_tokens || !uniforms || !accepted_len ||
@@ -480,14 +479,17 @@ ssd_status ssd_backup_crossover(double h, double E_hit, double E_miss_neural, do
 }
 
 // ------------------------------------------------------------------------------------------------
-ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
-                          int G_last, const int32_t* fanout, int budget, int32_t* cache_k,
-                          int32_t* cache_tok, hipStream_t stream) {
+}  // extern "C"
+
+// The keys' arguments, checked and packed (SSD_OK also for an empty batch or budget, with a.B or
+// a.budget 0: nothing to launch).
+static ssd_status keys_args(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
+                            int G_last, const int32_t* fanout, int budget, int32_t* cache_k, int32_t* cache_tok,
+                            CacheKeysArgs& a) {
+  std::memset(&a, 0, sizeof(a));
   if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || G_max < 1 || G_max > SSD_MAX_F ||
       budget < 0 || !fanout || (guesses_last && (G_last < 1 || G_last > SSD_MAX_F)))
     return SSD_ERR_INVALID_ARG;
-  CacheKeysArgs a;
-  std::memset(&a, 0, sizeof(a));
   int64_t off = 0;
   for (int k = 0; k <= K; ++k) {
     const int width = (guesses_last && k == K) ? G_last : G_max;
@@ -508,7 +510,41 @@ ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const
   a.Glast = G_last;
   a.cache_k = cache_k;
   a.cache_tok = cache_tok;
+  return SSD_OK;
+}
+
+extern "C" {
+
+ssd_status ssd_cache_keys(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
+                          int G_last, const int32_t* fanout, int budget, int32_t* cache_k,
+                          int32_t* cache_tok, hipStream_t stream) {
+  CacheKeysArgs a;
+  const ssd_status st = keys_args(B, K, G_max, guesses, guesses_last, G_last, fanout, budget, cache_k, cache_tok, a);
+  if (st != SSD_OK || a.B == 0 || a.budget == 0) return st;
   return hip_status(launch_cache_keys(a, stream));
+}
+
+ssd_status ssd_cache_keys_lookup(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
+                                 int G_last, const int32_t* fanout, int budget, const int32_t* accepted_len,
+                                 const int32_t* bonus_token, int32_t* cache_k, int32_t* cache_tok,
+                                 int32_t* out_slot, int32_t* out_miss_count, hipStream_t stream) {
+  CacheKeysArgs ka;
+  const ssd_status st = keys_args(B, K, G_max, guesses, guesses_last, G_last, fanout, budget, cache_k, cache_tok, ka);
+  if (st != SSD_OK) return st;
+  if (!out_miss_count || (B > 0 && (!accepted_len || !bonus_token || !out_slot))) return SSD_ERR_INVALID_ARG;
+  CacheLookupArgs la;
+  std::memset(&la, 0, sizeof(la));
+  la.B = B;
+  la.budget = budget;
+  la.cache_k = cache_k;
+  la.cache_tok = cache_tok;
+  la.k = accepted_len;
+  la.tok = bonus_token;
+  la.out_slot = out_slot;
+  la.out_miss = out_miss_count;
+  ka.B = B;  // an empty budget still writes every slot -1 and the miss count
+  ka.budget = budget;
+  return hip_status(launch_cache_keys_lookup(ka, la, stream));
 }
 
 ssd_status ssd_cache_lookup(int B, int budget, const int32_t* cache_k, const int32_t* cache_tok,

@@ -884,6 +884,62 @@ __global__ __launch_bounds__(kThreads) void cache_lookup_kernel(CacheLookupArgs 
   if (threadIdx.x == 0) a.out_miss[0] = shi[0] + shi[1] + shi[2] + shi[3];
 }
 
+// Keys and lookup in one launch (one workgroup): wave w takes sequences 4w .. 4w + 3, then 16 further
+// on; lane j forms the key of slot j of each of the four (64 slots a round) as cache_keys_kernel
+// does, with every read of the four issued together, writes it, and a ballot names the first slot
+// equal to the sequence's outcome. The miss count is summed in a fixed order.
+__global__ __launch_bounds__(kThreads) void cache_keys_lookup_kernel(CacheKeysArgs ka, CacheLookupArgs la) {
+  __shared__ int shi[kWaves];
+  constexpr int kSeq = 4;  // sequences per wave per round
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rows = ka.last ? ka.K : ka.K + 1;  // position rows in `guesses`
+  int miss = 0;  // lane 0 of each wave
+  for (int b0 = w * kSeq; b0 < ka.B; b0 += kWaves * kSeq) {
+    int kq[kSeq], tq[kSeq], slot[kSeq];
+#pragma unroll
+    for (int i = 0; i < kSeq; ++i) {
+      const int b = min(b0 + i, ka.B - 1);  // clamped: every read in bounds
+      kq[i] = la.k[b];
+      tq[i] = la.tok[b];
+      slot[i] = -1;
+    }
+    for (int j0 = 0; j0 < ka.budget; j0 += 64) {
+      const int j = min(j0 + lane, ka.budget - 1);  // clamped; lanes past the budget write nothing
+      int k = 0;
+      while (k < ka.K && j >= ka.off[k + 1]) ++k;
+      const int rank = j - ka.off[k];
+      int tok[kSeq];
+#pragma unroll
+      for (int i = 0; i < kSeq; ++i) {
+        const int64_t b = min(b0 + i, ka.B - 1);
+        tok[i] = (ka.last && k == ka.K) ? ka.last[b * ka.Glast + rank] : ka.guesses[(b * rows + k) * ka.Gmax + rank];
+      }
+#pragma unroll
+      for (int i = 0; i < kSeq; ++i) {
+        const bool mine = j0 + lane < ka.budget && b0 + i < ka.B;
+        if (mine) {
+          const int64_t g = int64_t(b0 + i) * ka.budget + j;
+          ka.cache_k[g] = (tok[i] >= 0) ? k : -1;
+          ka.cache_tok[g] = (tok[i] >= 0) ? tok[i] : -1;
+        }
+        const uint64_t m = __ballot(mine && tok[i] >= 0 && k == kq[i] && tok[i] == tq[i]);
+        if (slot[i] < 0 && m) slot[i] = j0 + __builtin_ctzll(m);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kSeq; ++i)
+        if (b0 + i < ka.B) {
+          la.out_slot[b0 + i] = slot[i];
+          miss += (slot[i] < 0);
+        }
+    }
+  }
+  if (lane == 0) shi[w] = miss;
+  __syncthreads();
+  if (threadIdx.x == 0) la.out_miss[0] = (shi[0] + shi[1]) + (shi[2] + shi[3]);
+}
+
 __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
 
 // Read-only streaming of n16 16-byte words, each read once, four loads in flight per thread: the
@@ -960,6 +1016,11 @@ hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(cache_keys_kernel, dim3(unsigned((n + kThreads - 1) / kThreads)), dim3(kThreads),
                      0, st, a);
+  return last_error();
+}
+
+hipError_t launch_cache_keys_lookup(const CacheKeysArgs& ka, const CacheLookupArgs& la, hipStream_t st) {
+  hipLaunchKernelGGL(cache_keys_lookup_kernel, dim3(1), dim3(kThreads), 0, st, ka, la);
   return last_error();
 }
 

@@ -132,6 +132,7 @@ hipError_t launch_topf(const TopfArgs& a, bool bf16, hipStream_t st);  // also s
 hipError_t launch_saguaro(const SagArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_cache_keys(const CacheKeysArgs& a, hipStream_t st);
 hipError_t launch_cache_lookup(const CacheLookupArgs& a, hipStream_t st);
+hipError_t launch_cache_keys_lookup(const CacheKeysArgs& ka, const CacheLookupArgs& la, hipStream_t st);
 hipError_t launch_clear_flags(uint32_t* flags, hipStream_t st);
 
 }  // namespace ssd

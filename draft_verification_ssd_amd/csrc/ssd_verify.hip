@@ -184,9 +184,9 @@ __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
 
 struct Shared {
   // per sequence, as given
-  int F[kMaxK + 1];       // guesses per draft row
+  int F[kMaxK + 1];       // guesses per draft row (row K: the extra draft row)
   float C[kMaxK];         // Saguaro factor per draft position
-  int xe[kMaxK];          // draft tokens
+  int xe[kMaxK + 1];      // draft tokens (-1 for the extra row: nothing excluded)
   float u[kMaxK + 1];     // uniforms
   int sv[kMaxK * kMaxF];  // Saguaro-set entries
   float zg[2 * kMaxK];    // logits at the draft tokens: draft rows 0..K-1, then target rows 0..K-1
@@ -197,10 +197,10 @@ struct Shared {
   float L[kMaxR2];                      // log2 normaliser of every row (merged over the tiles)
   // top-F candidates per draft row and wave: nseg < 0 means -nseg hot lanes copied their raw
   // chunks (lane ids in hl), nseg >= 0 that many key entries
-  uint64_t reg[kMaxK][kWaves][kRegW];
-  int nseg[kMaxK][kWaves];
-  int hl[kMaxK][kWaves][kHot];
-  uint32_t thr[kMaxK][kWaves];  // the copy's threshold key: smaller tokens are no candidates
+  uint64_t reg[kMaxK + 1][kWaves][kRegW];
+  int nseg[kMaxK + 1][kWaves];
+  int hl[kMaxK + 1][kWaves][kHot];
+  uint32_t thr[kMaxK + 1][kWaves];  // the copy's threshold key: smaller tokens are no candidates
   uint32_t fb[kWaves];          // draft rows the wave filters again (bit r)
   uint64_t spare[kWaves][64];   // where the compaction's failing tokens are written
   // the decision record, as this tile uses it
@@ -367,7 +367,11 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   // tile of the call has started, so every tile reads the same value here.
   const uint32_t tag_ld = ld_agent(a.gtag);
   TRACE(0);
-  const bool guesses = a.topfFmax > 0;
+  // guesses of draft rows 0..K-1 (the sampled token excluded) and of the extra draft row K (nothing
+  // excluded): KG rows go through the guess steps
+  const bool guess_rows = a.topfFmax > 0, guess_last = a.lastF > 0;
+  const bool guesses = guess_rows || guess_last;
+  const int KG = K + (guess_last ? 1 : 0);
   const bool tail = AL && (c0 + LY::TILE > V);  // aligned rows: chunks past V in this tile
 
   // per-sequence inputs, loaded before the rows and staged to LDS after them
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   if (t < K * sF) sv_v = a.sset[int64_t(b) * K * sF + t];
   const int xg = (t < 2 * K) ? a.x[b * K + (t < K ? t : t - K)] : -1;
   const float c_v = (t < K) ? a.Cpos[t] : 1.f;
-  const int f_v = (t < K) ? a.topfF[t] : 0;
+  const int f_v = (t <= K) ? a.topfF[t] : 0;
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the row loads
 
   // ---- the rows of the tile, in slot order (draft slots, then target): kAhead slots in flight at
@@ -394,8 +398,9 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   for (int s = 0; s < kAhead; ++s) issue(s);
   __builtin_amdgcn_sched_barrier(0);
 
-  const int Fp = a.topfFmax + 1;  // candidates kept per wave: one more than the guesses
-  if (lane == 0) sh.fb[w] = (guesses && !AL) ? (1u << K) - 1u : 0u;
+  const int Fp = max(a.topfFmax, a.lastF) + 1;  // candidates kept per wave: one more than the guesses
+  if (lane == 0)  // rows not 16-byte aligned: every guess row is filtered from memory
+    sh.fb[w] = AL ? 0u : ((guess_rows ? (1u << K) - 1u : 0u) | (guess_last ? 1u << K : 0u));
 
   // ---- statistics of every row, and the hot-lane copies of the draft rows
   // max and sum 2^(z c - max c) of one row over the lane's tokens, merged over 16-lane groups;
@@ -465,11 +470,15 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
       }
     }
   };
+  // The extra draft row K (its guesses only) is read where the row slots run out; without it the
+  // read repeats target row K (just loaded, a cache hit), so no branch surrounds the load.
+  Raw<NV> rk;
   {
     uint32_t mk[KM];
 #pragma unroll
     for (int s = 0; s < RM; ++s) {
       if (s + kAhead < RM) issue(s + kAhead);
+      if (s + kAhead == RM) load_row<ET, NV, AL>(guess_last ? draft + int64_t(K) * V : target + int64_t(K) * V, bl, V, rk);
 #if SSD_VERIFY_PRIO
       // A wave's issue priority falls as it gets through its rows, so the waves of the workgroups
       // that share a CU finish their statistics close together rather than the oldest first.
@@ -489,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
           unpack_row<ET, NV>(raw[s], bl, V, tail, z);
           mk[s] = row_stats(z, s);
         }
-        if (AL && s % 4 == 3 && s - 3 < K && guesses)
+        if (AL && s % 4 == 3 && s - 3 < K && guess_rows)
           draft_batch(raw + (s - 3), mk + (s - 3), s - 3, min(4, K - (s - 3)));
       } else if (s - KM <= K) {
         float z[E];
@@ -497,6 +506,15 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
         row_stats(z, K + (s - KM));
       }
     }
+  }
+  if (AL && guess_last) {
+    float z[E];
+    unpack_row<ET, NV>(rk, bl, V, tail, z);
+    float m = z[0];
+#pragma unroll
+    for (int q = 1; q < E; ++q) m = fmaxf(m, z[q]);
+    const uint32_t mkK = (m > -INFINITY) ? ordered_key(m) : 0u;
+    draft_batch(&rk, &mkK, K, 1);
   }
   // logits at the draft tokens and the Saguaro-set entries (the closer's accept tests): issued now,
   // read once the tile knows it is the closer
@@ -513,9 +531,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   }
   if (t < K) {
     sh.xe[t] = x_v;
-    sh.F[t] = f_v;
     sh.C[t] = c_v;
   }
+  if (t <= K) sh.F[t] = f_v;
+  if (t == K) sh.xe[K] = -1;
   if (t <= K) sh.u[t] = u_v;
   if (t < K * sF) sh.sv[t] = sv_v;
   const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
@@ -635,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
         const int r = __builtin_ctz(fbm);
         fbm &= fbm - 1u;
         Raw<NV> rr;
-        load_row<ET, NV, AL>(row_ptr(r), bl, V, rr);
+        load_row<ET, NV, AL>(draft + int64_t(r) * V, bl, V, rr);  // guess rows are draft rows
         float z[E];
         unpack_row<ET, NV>(rr, bl, V, tail, z);
         row_filter(z, r);
@@ -646,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
     // publishes them. Candidate round i reads the region of wave i / PARTS: a copy gives lane l
     // element l % E of slot l / E + SPR (i % PARTS); a key list gives lane l its entry
     // l + 64 (i % PARTS).
-    for (int r = w; r < K; r += kWaves) {
+    for (int r = w; r < KG; r += kWaves) {
       const int F = sh.F[r];
       const int e = lane % E;
       int n[kWaves];
@@ -771,9 +790,11 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   // writing it, so the wait for the tags ends.
   const int long_bound = a.wait_polls * 8 + 4096;  // waits on tiles known to have arrived
   auto merge_guesses = [&]() __attribute__((always_inline)) {
-    for (int r = w; r < K; r += kWaves) {
+    for (int r = w; r < KG; r += kWaves) {
+      if (r < K && !guess_rows) continue;
       const int F = sh.F[r];
-      int32_t* out = a.topf_out + (int64_t(b) * K + r) * a.topfFmax;
+      const int width = (r < K) ? a.topfFmax : a.lastF;
+      int32_t* out = (r < K) ? a.topf_out + (int64_t(b) * K + r) * a.topfFmax : a.topf_last_out + int64_t(b) * a.lastF;
       const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * Tc * a.Fcap * 2;
       const int n = nT * F;
       auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F), once tagged
@@ -840,7 +861,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
           prev = win;
         }
       }
-      for (int f = F + lane; f < a.topfFmax; f += 64) out[f] = -1;
+      for (int f = F + lane; f < width; f += 64) out[f] = -1;
     }
     if (t == 0) st_agent(ctr + 1, 0u);  // every tile has counted itself in: back to zero
   };

@@ -353,6 +353,17 @@ ssd_status ssd_cache_lookup(int B, int budget, const int32_t* cache_k, const int
                             int32_t* out_slot, int32_t* out_miss_count, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ssd_cache_keys_lookup — ssd_cache_keys and ssd_cache_lookup in one launch ([SSD] "SSD 的核心思想",
+ * "实现细节：缓存怎么建"): the same cache_k / cache_tok, out_slot and out_miss_count as the two
+ * calls in turn, with the keys formed and matched in registers. Arguments as the two calls'.
+ * Errors: SSD_ERR_INVALID_ARG as either call, SSD_ERR_HIP.
+ * ------------------------------------------------------------------------------------------- */
+ssd_status ssd_cache_keys_lookup(int B, int K, int G_max, const int32_t* guesses, const int32_t* guesses_last,
+                                 int G_last, const int32_t* fanout, int budget, const int32_t* accepted_len,
+                                 const int32_t* bonus_token, int32_t* cache_k, int32_t* cache_tok,
+                                 int32_t* out_slot, int32_t* out_miss_count, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * ssd_read_flags — copy a workspace's device-error flags to *out_flags (host) and, if clear != 0,
  * reset them. Synchronises `stream`.
  * ------------------------------------------------------------------------------------------- */

@@ -283,3 +283,16 @@ def test_verify_noalloc_limit_matches_the_workspace_size():
     assert ssd.ssd_verify_workspace_bytes(16, 4, 128256, 3) <= ssd.SSD_NOALLOC_SCRATCH_BYTES
     assert ssd.ssd_verify_workspace_bytes(4096, 16, 1 << 20, 16) > ssd.SSD_NOALLOC_SCRATCH_BYTES
     assert _verify_noalloc(B=0) == OK  # an empty batch is a no-op, before the array is touched
+
+
+def test_cache_keys_lookup_validates_like_its_two_calls():
+    L = ssd.lib()
+    F = (ctypes.c_int32 * 3)(2, 1, 1)
+    call = lambda B, K, G, g, budget, k, t, ck, ct, sl, m: L.ssd_cache_keys_lookup(
+        B, K, G, g, None, 0, ctypes.addressof(F), budget, k, t, ck, ct, sl, m, None)
+    assert call(2, 2, 2, FAKE, 3, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INV   # no miss-count output
+    assert call(2, 2, 2, FAKE, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == INV   # budget != sum(fanout)
+    assert call(2, 2, 1, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == INV   # F_0 = 2 > G_max = 1
+    assert call(2, 2, 2, None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == INV   # no guesses
+    assert call(2, 2, 2, FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE) == INV   # no outcomes
+    assert call(-1, 2, 2, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == INV

@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 
 
 def ssd_round_gpu(bt, fan, branch=None, branch_u=None):
-    """One SSD round through the library: guesses of the outer draft rows (verify-fused for rows
-    0..K-1, standalone for row K), cache keys, Saguaro verification, lookup; and the branch rows'
+    """One SSD round through the library: guesses of the outer draft rows (rows 0..K and the extra
+    row K, all in the verification's pass), cache keys, Saguaro verification, lookup; and the branch rows'
     draft step in one pass each (ssd_saguaro_sample: set = the row's top F_j, its mass and
     normaliser, and the token drawn from q' with the row's uniform)."""
     B, K, V = bt.B, bt.K, bt.V
@@ -37,18 +37,22 @@ def ssd_round_gpu(bt, fan, branch=None, branch_u=None):
     topf = torch.empty((B, K, Gm), dtype=torch.int32, device=DEV)
     # explicit workspaces, so that every call's device-error flags are read afterwards
     ws_v = ssd.Workspace(ssd.ssd_verify_workspace_bytes(B, K, V, Gm), DEV)
-    ws_t = ssd.Workspace(ssd.ssd_topf_workspace_bytes(B, V, max(1, fan[K])), DEV)
+    # draft row K's guesses (nothing excluded) come from the same pass as the verification
     out = ssd.ssd_verify(draft, target, x, u, bt.T, sag_set=sets, sag_C=bt.C, topf_F=fan[:K],
                          topf_F_max=Gm, topf_out=topf,
                          accept_prob=torch.empty((B, K), device=DEV), residual_mass=torch.empty(B, device=DEV),
-                         workspace=ws_v)
+                         topf_last_F=fan[K], workspace=ws_v)
     guesses[:, :K] = topf
-    last = ssd.ssd_topf_guess(draft[:, K, :], max(1, fan[K]), workspace=ws_t)
+    last = out["topf_last"]
     if fan[K] > 0:
         guesses[:, K, : fan[K]] = last[:, : fan[K]]
     # keys straight from the two calls' outputs (no copy into one buffer)
-    ck, ct = ssd.ssd_cache_keys(topf, fan, guesses_last=last)
-    slot, miss = ssd.ssd_cache_lookup(ck, ct, out["accepted_len"], out["bonus_token"])
+    ck, ct, slot, miss = ssd.ssd_cache_keys_lookup(topf, fan, out["accepted_len"], out["bonus_token"],
+                                                   guesses_last=last)
+    # the two-launch form gives the same keys and slots
+    ck2, ct2 = ssd.ssd_cache_keys(topf, fan, guesses_last=last)
+    slot2, miss2 = ssd.ssd_cache_lookup(ck2, ct2, out["accepted_len"], out["bonus_token"])
+    assert torch.equal(ck, ck2) and torch.equal(ct, ct2) and torch.equal(slot, slot2) and torch.equal(miss, miss2)
     res = dict(k=out["accepted_len"], bonus=out["bonus_token"], guesses=guesses, ck=ck, ct=ct,
                slot=slot, miss=miss, out=out)
     if branch is not None:
@@ -63,7 +67,6 @@ def ssd_round_gpu(bt, fan, branch=None, branch_u=None):
         assert ssd.ssd_read_flags(ws_s) == 0, "ssd_saguaro_sample device flags"
     torch.cuda.synchronize()
     assert ssd.ssd_read_flags(ws_v) == 0, "ssd_verify device flags"
-    assert ssd.ssd_read_flags(ws_t) == 0, "ssd_topf_guess device flags"
     return res
 
 

@@ -262,6 +262,14 @@ def test_cache_keys_and_lookup_match_oracle(B, K, G, fan):
     want = [O.cache_lookup(kk_all[b], tt_all[b], int(acc[b]), int(bon[b])) for b in range(B)]
     assert list(slot) == want
     assert int(miss.item()) == sum(s < 0 for s in want)
+    # keys and lookup in one launch: the same keys, slots and miss count, with position K's guesses
+    # in the array or held apart
+    for args in ((gd, fan), (gd[:, :K].contiguous(), fan)):
+        kw = {} if args[0] is gd else dict(guesses_last=gd[:, K, : max(1, fan[K])].contiguous())
+        fk, ft, fs, fm = ssd.ssd_cache_keys_lookup(args[0], args[1], torch.from_numpy(acc).to(DEV),
+                                                  torch.from_numpy(bon).to(DEV), **kw)
+        assert np.array_equal(fk.cpu().numpy(), ck) and np.array_equal(ft.cpu().numpy(), ct)
+        assert list(fs.cpu().numpy()) == want and int(fm.item()) == sum(s < 0 for s in want)
 
 
 def test_lookup_with_empty_cache_counts_every_miss():
