@@ -49,6 +49,17 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return make_uint4(r.x, r.y, r.z, r.w);
 }
 
+// Raw buffer reads: a resource over `bytes` bytes from `base` (uniform), read at 32-bit byte
+// offsets; a read past `bytes` returns zeros. The fourth descriptor word is the raw-buffer format
+// of the gfx9 family. The address of a read is one 32-bit register, not a 64-bit pair.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------------------------------------
 // DPP lane exchanges inside 16-lane rows: xor 1, xor 2 (quad permutes), then the half-row and row
 // mirrors. Applied in that order, a commutative combine leaves every lane of the row holding the

@@ -250,6 +250,15 @@ struct TopfWave {
   // the same with the lane maximum bm of z already formed
   template <int NB, class Idx>
   __device__ __forceinline__ void batch_bm(const float (&z)[NB], float bm, Idx idx_of) {
+    // a row with no excluded token skips the per-token index test (uniform)
+    if (exclude < 0)
+      batch_ex<false>(z, bm, idx_of);
+    else
+      batch_ex<true>(z, bm, idx_of);
+  }
+  template <bool EX, int NB, class Idx>
+  __device__ __forceinline__ void batch_ex(const float (&z)[NB], float bm, Idx idx_of) {
+    auto keep = [&](int e) __attribute__((always_inline)) { return !EX || idx_of(e) != exclude; };
     const int lane = threadIdx.x & 63;
     if (tau == -INFINITY && n == 0) {  // first batch: tau from the lane maxima
       const int Fp = F + 1;
@@ -268,20 +277,20 @@ struct TopfWave {
     if (__ballot(bm >= tau && bm > -INFINITY) == 0ull) return;  // nothing here reaches tau
     int cnt = 0;
 #pragma unroll
-    for (int e = 0; e < NB; ++e) cnt += (z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude) ? 1 : 0;
+    for (int e = 0; e < NB; ++e) cnt += (z[e] >= tau && z[e] > -INFINITY && keep(e)) ? 1 : 0;
     const int incl = wave_incl_scan_i(cnt);
     const int total = __builtin_amdgcn_readlane(incl, 63);
     if (n + total <= BUF) {
       int pos = n + incl - cnt;
 #pragma unroll
       for (int e = 0; e < NB; ++e)
-        if (z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude) buf[pos++] = cand_key64(z[e], idx_of(e));
+        if (z[e] >= tau && z[e] > -INFINITY && keep(e)) buf[pos++] = cand_key64(z[e], idx_of(e));
       n += total;
     } else {
       // too many to append at once (ties): one place of every lane at a time, cutting the buffer
       // (and raising tau) whenever the next place would not fit
       for (int e = 0; e < NB; ++e) {
-        bool c = z[e] >= tau && z[e] > -INFINITY && idx_of(e) != exclude;
+        bool c = z[e] >= tau && z[e] > -INFINITY && keep(e);
         uint64_t m = __ballot(c);
         if (m == 0ull) continue;
         if (n + __popcll(m) > BUF) {
@@ -501,18 +510,27 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
       const uint4* rv = reinterpret_cast<const uint4*>(p);
       const int v0 = c0 / N, v1 = v0 + (c1 - c0) / N;
       tail0 = v1 * N;
-      auto load_batch = [&](int vb, uint4 (&raw)[U]) __attribute__((always_inline)) {
+      // Batches are numbered by their first vector b0 (the same in every lane: loop control stays
+      // scalar). Every lane reads every vector of a batch from a clamped, valid address, so no
+      // branch surrounds a read and a wave waits only for the batch it is about to use; vectors
+      // past the chunk are replaced by -inf, which only the chunk's last batch needs.
+      const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(rv, uint32_t(v1) * 16u);
+      auto load_batch = [&](int b0, uint4 (&raw)[U]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int vi = vb + u * kThreads;
-          raw[u] = (vi < v1) ? load16(rv + vi)
-                             : make_uint4(ET::kNegInfWord, ET::kNegInfWord, ET::kNegInfWord, ET::kNegInfWord);
-        }
+        for (int u = 0; u < U; ++u) raw[u] = buffer_load16(rsrc, uint32_t(min(b0 + t + u * kThreads, v1 - 1)) * 16u);
       };
-      auto run_batch = [&](int vb, const uint4 (&raw)[U]) __attribute__((always_inline)) {
+      auto run_batch = [&](int b0, const uint4 (&raw)[U]) __attribute__((always_inline)) {
         float z[kTBatch];
 #pragma unroll
         for (int u = 0; u < U; ++u) ET::unpack(raw[u], z + u * N);
+        if (b0 + kThreads * U > v1) {  // uniform: the chunk ends inside this batch
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const bool in = b0 + t + u * kThreads < v1;
+#pragma unroll
+            for (int e = 0; e < N; ++e) z[u * N + e] = in ? z[u * N + e] : -INFINITY;
+          }
+        }
         float bm = z[0];
 #pragma unroll
         for (int e = 1; e < kTBatch; ++e) bm = fmaxf(bm, z[e]);
@@ -525,20 +543,22 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
           ++seg_batches;
         }
         if (SAG) ls.add(z, bm, cc);
-        if (F > 0) tw.batch_bm(z, bm, [&](int e) { return (vb + (e / N) * kThreads) * N + (e % N); });
+        if (F > 0) tw.batch_bm(z, bm, [&](int e) { return (b0 + t + (e / N) * kThreads) * N + (e % N); });
       };
-      // two batches in flight: the next one loads while this one is examined (the trip count is
-      // the same for every lane)
+      // two batches in flight: a buffer is read again as soon as it has been examined, so the other
+      // one is always on its way (reads past the last batch repeat the chunk's last vector)
       constexpr int kStep = kThreads * U;
-      uint4 ra[U], rb[U];
-      int vb = v0 + t;
-      if (vb - t < v1) load_batch(vb, ra);
-      for (; vb - t < v1; vb += 2 * kStep) {
-        if (vb + kStep - t < v1) load_batch(vb + kStep, rb);
-        run_batch(vb, ra);
-        if (vb + kStep - t >= v1) break;
-        if (vb + 2 * kStep - t < v1) load_batch(vb + 2 * kStep, ra);
-        run_batch(vb + kStep, rb);
+      if (v1 > v0) {
+        uint4 ra[U], rb[U];
+        load_batch(v0, ra);
+        load_batch(v0 + kStep, rb);
+        for (int b0 = v0; b0 < v1; b0 += 2 * kStep) {
+          run_batch(b0, ra);
+          if (b0 + kStep >= v1) break;
+          load_batch(b0 + 2 * kStep, ra);
+          run_batch(b0 + kStep, rb);
+          load_batch(b0 + 3 * kStep, rb);
+        }
       }
     }
     // elements after the last whole vector, or every element of an unaligned row, one per lane
