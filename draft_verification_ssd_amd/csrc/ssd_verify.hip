@@ -11,7 +11,8 @@
 //              and the sum of 2^(z c - max c) (c = log2(e) / T), merges them over the tile and
 //              publishes the tile's (max c, sum) as two words tagged with the call. Draft rows also
 //              mark the lanes that can hold one of the tile's best F+1 tokens and copy those lanes'
-//              values to LDS (the top-F candidates).
+//              values to LDS (the top-F candidates); so does the extra draft row K, read for its
+//              guesses only, when they are asked for.
 //  arrival     The tile claims its residual chunk and adds one to its sequence's arrival counter.
 //              The tile that brings the count to T, the closer, knows every tile has published.
 //  decide      The closer merges the T statistics of every row in one fixed order, takes the accept
