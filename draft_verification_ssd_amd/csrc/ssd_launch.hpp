@@ -122,7 +122,22 @@ struct VerifyPlan {
   int T;    // tiles per row
   bool AL;  // every row 16-byte aligned (vector loads)
 };
-VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned);
+constexpr int kVerifyThreads = 256;  // threads of a verification workgroup
+inline VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned) {
+  VerifyPlan p;
+  p.AL = aligned;
+  p.KM = (K <= 4) ? 4 : (K <= 8 ? 8 : 16);
+  // two chunks per lane and row keep 2 KM + 1 rows in at most 136 registers (one chunk for 33
+  // rows, for 17 rows of bf16, whose two chunks would spill, and for rows not 16-byte aligned,
+  // whose element loads hold a register per token in flight); a batch that would not give every CU
+  // a workgroup takes one chunk (twice the tiles)
+  p.NV = (!aligned || p.KM == 16 || (p.KM == 8 && bf16)) ? 1 : 2;
+  const int es = bf16 ? 2 : 4;
+  auto tiles = [&](int nv) { return int((int64_t(V) + kVerifyThreads * nv * (16 / es) - 1) / (kVerifyThreads * nv * (16 / es))); };
+  if (p.NV == 2 && int64_t(B) * tiles(2) < 256) p.NV = 1;
+  p.T = tiles(p.NV);
+  return p;
+}
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, bool bf16, hipStream_t st);
 // Device address of the allocation-free verification's static array on the current device; the
 // first call on a device looks it up and clears its first ctrl_bytes with a fill kernel on st.

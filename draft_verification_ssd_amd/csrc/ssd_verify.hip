@@ -1284,21 +1284,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
 // ---------------------------------------------------------------------------------------------
 // launch: one grid of every (sequence, tile); no workgroup needs another to be resident
 // ---------------------------------------------------------------------------------------------
-VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned) {
-  VerifyPlan p;
-  p.AL = aligned;
-  p.KM = (K <= 4) ? 4 : (K <= 8 ? 8 : 16);
-  // two chunks per lane and row keep 2 KM + 1 rows in at most 136 registers (one chunk for 33
-  // rows, for 17 rows of bf16, whose two chunks would spill, and for rows not 16-byte aligned,
-  // whose element loads hold a register per token in flight); a batch that would not give every CU
-  // a workgroup takes one chunk (twice the tiles)
-  p.NV = (!aligned || p.KM == 16 || (p.KM == 8 && bf16)) ? 1 : 2;
-  const int es = bf16 ? 2 : 4;
-  auto tiles = [&](int nv) { return int((int64_t(V) + kThreads * nv * (16 / es) - 1) / (kThreads * nv * (16 / es))); };
-  if (p.NV == 2 && int64_t(B) * tiles(2) < 256) p.NV = 1;
-  p.T = tiles(p.NV);
-  return p;
-}
+static_assert(kThreads == kVerifyThreads, "the host plan sizes tiles for this workgroup");
 
 template <class ET, int KM, int NV, bool AL>
 static hipError_t launch_v(const VerifyArgs& a, hipStream_t st) {
