@@ -22,7 +22,8 @@ SSD_DEFAULT_WAIT_POLLS = 2048
 
 class VerifyOpts(ctypes.Structure):
     """ssd_verify_opts of include/ssd.h."""
-    _fields_ = [("wait_polls", ctypes.c_int32), ("topf_last_F", ctypes.c_int32), ("topf_last_out", ctypes.c_void_p)]
+    _fields_ = [("wait_polls", ctypes.c_int32), ("topf_last_F", ctypes.c_int32), ("topf_last_out", ctypes.c_void_p),
+                ("launch_mode", ctypes.c_int32)]
 FLAG_BAD_TOKEN, FLAG_SAGUARO_NORM, FLAG_BAD_F, FLAG_TIMEOUT, FLAG_BAD_C = 0x1, 0x2, 0x4, 0x8, 0x10
 
 EXPORTS = ["ssd_verify_workspace_bytes", "ssd_verify_launches", "ssd_verify_tiles", "ssd_verify", "ssd_verify_ex",
@@ -200,7 +201,8 @@ def ssd_verify_workspace_bytes(B: int, K: int, V: int, topf_F_max: int = 0) -> i
 
 
 def ssd_verify_launches(B: int, K: int, V: int, dtype: int, topf_F_max: int = 0) -> int:
-    """Kernel launches ssd_verify issues for this shape (-1 if rejected)."""
+    """Kernel launches ssd_verify issues for this shape on the current device: 2 when the batch has
+    more tiles than the device runs at once, else 1 (-1 if rejected)."""
     return int(lib().ssd_verify_launches(B, K, V, dtype, topf_F_max))
 
 
@@ -249,7 +251,7 @@ class VerifyCall:
                  topf_F_max: int = 0, topf_out=None, accepted_len=None, bonus_token=None,
                  accept_prob=None, residual_mass=None, workspace: Optional[Workspace] = None,
                  stream=None, wait_polls: Optional[int] = None, topf_last_F: int = 0, topf_last_out=None,
-                 noalloc_flags=None):
+                 noalloc_flags=None, launch_mode: int = 0):
         torch = _torch()
         B, Kd, V, dstride = _rows3(draft, "draft", 1)
         Bt, Kt, Vt, tstride = _rows3(target, "target", 2)
@@ -298,12 +300,12 @@ class VerifyCall:
                 topf_last_out = torch.empty((B, topf_last_F), dtype=torch.int32, device=dev)
             _need(topf_last_out, torch.int32, (B, topf_last_F), "topf_last_out")
         self.opts = None
-        if wait_polls is not None or topf_last_F > 0:
+        if wait_polls is not None or topf_last_F > 0 or launch_mode != 0:
             self.opts = VerifyOpts(-1 if wait_polls is None else int(wait_polls), int(topf_last_F),
-                                   _ptr(topf_last_out) if topf_last_F > 0 else None)
+                                   _ptr(topf_last_out) if topf_last_F > 0 else None, int(launch_mode))
         if noalloc_flags is not None:  # ssd_verify_noalloc: the library's static workspace
             if self.opts is not None or workspace is not None:
-                raise ValueError("noalloc_flags excludes workspace, wait_polls and topf_last_F")
+                raise ValueError("noalloc_flags excludes workspace, wait_polls, topf_last_F and launch_mode")
             _need(noalloc_flags, torch.int32, (1,), "noalloc_flags")
         elif workspace is None:
             workspace = Workspace(ssd_verify_workspace_bytes(B, K, V, max(topf_F_max, topf_last_F)), dev)

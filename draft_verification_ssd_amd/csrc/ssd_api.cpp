@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -29,6 +30,23 @@ P* at(void* base, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(base) + off);
 }
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+// Verification workgroups the current device runs at once (its CU count, looked up once per
+// device, times the workgroups per CU); 256 CUs when no device answers.
+int verify_slots() {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cus[kDevs];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 256 * kVerifyWgPerCu;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n * kVerifyWgPerCu;
+}
+// The two-launch form: when the batch has more tiles than the device runs at once
+bool verify_split(int B, int T) { return int64_t(B) * T > verify_slots(); }
 
 
 }  // namespace
@@ -89,6 +107,8 @@ static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride
   int wait_polls = (opts && opts->wait_polls >= 0) ? opts->wait_polls : -1;
   if (wait_polls > (1 << 20)) return SSD_ERR_INVALID_ARG;
   const int lastF = opts ? opts->topf_last_F : 0;
+  const int launch_mode = opts ? opts->launch_mode : 0;
+  if (launch_mode < 0 || launch_mode > 2) return SSD_ERR_INVALID_ARG;
   if (lastF < 0 || lastF > SSD_MAX_F || (lastF > 0 && !opts->topf_last_out)) return SSD_ERR_INVALID_ARG;
   if (draft_seq_stride < int64_t(lastF > 0 ? K + 1 : K) * V || target_seq_stride < int64_t(K + 1) * V)
     return SSD_ERR_INVALID_ARG;
@@ -148,6 +168,7 @@ static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride
   a.Tcap = L.Tcap;
   a.wait_polls = wait_polls;
   a.aligned = aligned ? 1 : 0;
+  a.split = (launch_mode == 2 || (launch_mode == 0 && verify_split(B, P.T))) ? 1 : 0;
 #ifdef SSD_TRACE
   a.trace = static_cast<uint64_t*>(ssd_trace_buffer);
 #endif
@@ -207,7 +228,8 @@ int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max) {
   if (!dtype_ok(dtype)) return -1;
   if (B < 0 || B > SSD_MAX_B || K < 1 || K > SSD_MAX_K || V < 1 || V > SSD_MAX_V) return -1;
   if (topf_F_max < 0 || topf_F_max > SSD_MAX_F) return -1;
-  return B == 0 ? 0 : 1;
+  if (B == 0) return 0;
+  return verify_split(B, plan_verify(B, K, V, dtype == SSD_BF16, true).T) ? 2 : 1;
 }
 
 int ssd_verify_tiles(int B, int K, int V, ssd_dtype dtype) {

@@ -45,6 +45,7 @@ struct VerifyArgs {
   int Tcap;
   int wait_polls;    // polls a workgroup spends waiting on the others of its sequence
   int aligned;       // every logit row starts 16-byte aligned
+  int split;         // two launches: statistics, decision and guesses, then residual and bonus
   uint64_t* trace;   // per-workgroup phase timestamps (analysis builds only), or null
 };
 
@@ -123,6 +124,7 @@ struct VerifyPlan {
   bool AL;  // every row 16-byte aligned (vector loads)
 };
 constexpr int kVerifyThreads = 256;  // threads of a verification workgroup
+constexpr int kVerifyWgPerCu = 2;    // verification workgroups a CU runs at once (register budget)
 inline VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned) {
   VerifyPlan p;
   p.AL = aligned;

@@ -1,4 +1,5 @@
-// Batched lossless draft verification on gfx950: one launch per call.
+// Batched lossless draft verification on gfx950: one launch per call, or two for batches whose tiles
+// do not all fit on the device at once (the two-launch form, at the end of this file).
 //
 // Work unit: one 256-thread workgroup per (sequence b, tile of TILE tokens). A tile covers the same
 // token range of every row of its sequence (K draft rows, K+1 target rows) and keeps all of them
@@ -308,9 +309,9 @@ __device__ __forceinline__ void tile_prefix(const float (&rv)[Lay<ET, NV>::E], f
 // base + prefix exceeds target, or the last token of positive mass with clamp or when rounding
 // leaves the tile's prefixes short of target (the crossing is then the tile's end, within
 // rounding). Every thread returns the token (-1 when the tile holds no positive mass).
-template <class ET, int NV>
+template <class ET, int NV, class SH>
 __device__ __forceinline__ int tile_search(const float (&rv)[Lay<ET, NV>::E], const float (&pre)[Lay<ET, NV>::E],
-                                           int bl, float base, float target, bool clamp, Shared& sh) {
+                                           int bl, float base, float target, bool clamp, SH& sh) {
   using LY = Lay<ET, NV>;
   int first = INT_MAX, lastp = -1;
 #pragma unroll
@@ -338,10 +339,75 @@ __device__ __forceinline__ int tile_search(const float (&rv)[Lay<ET, NV>::E], co
   return r;
 }
 
+// The bonus scan over the T tile masses in sh.res (wave 0; every workgroup that runs it gets the same
+// bits): the tile where the cumulative mass first exceeds u_K R and the base before it, or the last
+// tile with mass when rounding leaves u_K R past the total, or the all-zero fallback.
+template <class SH>
+__device__ __forceinline__ void scan_masses(SH& sh, int nT, float uK) {
+  const int lane = threadIdx.x & 63;
+  const int per = (nT + 63) / 64;  // lane l takes consecutive tiles [l per, (l + 1) per)
+  const int q0 = min(lane * per, nT), q1 = min(nT, q0 + per);
+  float run = 0.f;
+  for (int q = q0; q < q1; ++q) run += sh.res[q];
+  const float inc = wave_incl_scan(run);
+  const float Rtot = readlane_f(inc, 63);
+  const float target_v = uK * Rtot;
+  int first = INT_MAX, lastpos = -1;
+  float p = wave_shift_up1(inc), base = 0.f;
+  for (int q = q0; q < q1; ++q) {
+    const float nxt = p + sh.res[q];
+    if (sh.res[q] > 0.f) lastpos = q;
+    if (first == INT_MAX && nxt > target_v) {
+      first = q;
+      base = p;
+    }
+    p = nxt;
+  }
+  const int cf = wave_min_i(first);
+  const int cl = wave_max_i(lastpos);
+  if (first != INT_MAX && first == cf) sh.base = base;
+  if (lane == 0) {
+    sh.cstar = (cf != INT_MAX) ? cf : cl;  // u R past the total by rounding: last tile with mass
+    sh.clamp = (cf == INT_MAX);
+    sh.fallback = (cf == INT_MAX && cl < 0);  // all-zero residual (rounding only)
+    sh.target = target_v;
+    sh.R = Rtot;
+  }
+}
+
+// Residual identically zero (rounding only): the bonus is drawn from the target row p_k itself
+// (prow, whose log2 normaliser is Lp), tile by tile in token order. Every thread returns the token.
+template <class ET, int NV, bool AL, class SH>
+__device__ __forceinline__ int fallback_draw(const typename ET::T* prow, int V, int nT, float cc, float Lp, float uK,
+                                             SH& sh) {
+  using LY = Lay<ET, NV>;
+  constexpr int E = LY::E;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float run = 0.f;
+  int found = -1, lastp = -1;
+  for (int q = 0; q < nT && found < 0; ++q) {
+    const int blq = q * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+    const bool tq = AL && ((q + 1) * LY::TILE > V);
+    Raw<NV> rp;
+    load_row<ET, NV, AL>(prow, blq, V, rp);
+    float zp[E], v2[E], p2[E];
+    unpack_row<ET, NV>(rp, blq, V, tq, zp);
+    residual_values<ET, NV>(zp, zp, false, blq, V, cc, Lp, 0.f, 1.f, 1.f, sh.myset, 0, v2);
+    tile_prefix<ET, NV>(v2, sh.wt, p2);
+    const float tot = tile_mass<E>(v2, sh.wt);
+    const int tk = tile_search<ET, NV>(v2, p2, blq, run, uK, false, sh);
+    // a crossing in this tile (the search's first token), or its last positive token
+    if (sh.first != INT_MAX) found = tk;
+    if (tk >= 0) lastp = tk;
+    run += tot;
+  }
+  return (found >= 0) ? found : lastp;
+}
+
 // KM: register rows per tile are 2 KM + 1 (draft slots 0..KM-1, target slots KM..2KM), K <= KM.
 // NV: 16-byte chunks per lane and row. AL: every row 16-byte aligned.
 template <class ET, int KM, int NV, bool AL>
-__global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(VerifyArgs a) {
   using T = typename ET::T;
   using LY = Lay<ET, NV>;
   constexpr int E = LY::E;
@@ -569,7 +635,8 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
       role = 1;
       // the closer counts its guesses in now and publishes them later, off its path to the bonus:
       // the merger (usually another tile) waits for them, and the closer has arrived, so it ends
-      if (guesses && add_agent(ctr + 1, 1u) + 1u == uint32_t(nT)) role |= 2;
+      // (in the two-launch form nothing waits, and the closer counts in after its guesses)
+      if (guesses && !a.split && add_agent(ctr + 1, 1u) + 1u == uint32_t(nT)) role |= 2;
     }
     sh.role = role;
   }
@@ -992,7 +1059,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
         if (f >= 0 && f < kMaxF) sh.myset[f] = sv;
       }
     if (t == 0) sh.go = 1;
-  } else {
+  } else if (!a.split) {
     if (guesses) tile_guesses(true);
       // wave 0 polls the record until every word it needs carries this call's tag
       if (t < 64) {
@@ -1025,6 +1092,12 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
       }
   }
   __syncthreads();
+  if (a.split) {  // two-launch form: the residual and the bonus are mass_kernel's
+    if (guesses) tile_guesses(true);
+    if ((sh.role & 2) != 0) merge_guesses();
+    TRACE(9);
+    return;
+  }
   TRACE(4);
   TRACEV(12, uint64_t(sh.role) | (uint64_t(sh.go) << 8));
 
@@ -1184,41 +1257,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   __syncthreads();
   TRACE(closer ? 7 : 6);
 
-  // ---- the bonus (one copy for every role): scan of the T masses (wave 0, the same bits in every
-  // tile that runs it): the tile where the cumulative mass first exceeds u_K R and the base before
-  // it, or the last tile with mass when rounding leaves u_K R past the total, or the all-zero
-  // fallback; the tile whose range holds u_K R draws the token from its registers.
+  // ---- the bonus (one copy for every role): the scan of the T masses, then the tile whose range
+  // holds u_K R draws the token from its registers.
   if (sh.go) {
-    if (t < 64) {
-      const int per = (nT + 63) / 64;  // lane l takes consecutive tiles [l per, (l + 1) per)
-      const int q0 = min(lane * per, nT), q1 = min(nT, q0 + per);
-      float run = 0.f;
-      for (int q = q0; q < q1; ++q) run += sh.res[q];
-      const float inc = wave_incl_scan(run);
-      const float Rtot = readlane_f(inc, 63);
-      const float target_v = sh.u[K] * Rtot;
-      int first = INT_MAX, lastpos = -1;
-      float p = wave_shift_up1(inc), base = 0.f;
-      for (int q = q0; q < q1; ++q) {
-        const float nxt = p + sh.res[q];
-        if (sh.res[q] > 0.f) lastpos = q;
-        if (first == INT_MAX && nxt > target_v) {
-          first = q;
-          base = p;
-        }
-        p = nxt;
-      }
-      const int cf = wave_min_i(first);
-      const int cl = wave_max_i(lastpos);
-      if (first != INT_MAX && first == cf) sh.base = base;
-      if (lane == 0) {
-        sh.cstar = (cf != INT_MAX) ? cf : cl;  // u R past the total by rounding: last tile with mass
-        sh.clamp = (cf == INT_MAX);
-        sh.fallback = (cf == INT_MAX && cl < 0);  // all-zero residual (rounding only)
-        sh.target = target_v;
-        sh.R = Rtot;
-      }
-    }
+    if (t < 64) scan_masses(sh, nT, sh.u[K]);
     __syncthreads();
     if (!sh.fallback && sh.cstar == tile) {
       const int tok = tile_search<ET, NV>(rv, pre, bl, sh.base, sh.target, sh.clamp != 0, sh);
@@ -1232,29 +1274,10 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
   }
 
   if (closer) {
-    if (sh.fallback) {
-      // residual identically zero (rounding only): draw from the target row p_k itself, R = 0
-      const float target_v = sh.u[K];
-      float run = 0.f;
-      int found = -1, lastp = -1;
-      for (int q = 0; q < nT && found < 0; ++q) {
-        const int blq = q * LY::TILE + w * LY::WTOK + lane * LY::VEC;
-        const bool tq = AL && ((q + 1) * LY::TILE > V);
-        Raw<NV> rp;
-        load_row<ET, NV, AL>(target + int64_t(k) * V, blq, V, rp);
-        float zp[E], v2[E], p2[E];
-        unpack_row<ET, NV>(rp, blq, V, tq, zp);
-        residual_values<ET, NV>(zp, zp, false, blq, V, cc, sh.Lp, 0.f, 1.f, 1.f, sh.myset, 0, v2);
-        tile_prefix<ET, NV>(v2, sh.wt, p2);
-        const float tot = tile_mass<E>(v2, sh.wt);
-        const int tk = tile_search<ET, NV>(v2, p2, blq, run, target_v, false, sh);
-        // a crossing in this tile (the search's first token), or its last positive token
-        if (sh.first != INT_MAX) found = tk;
-        if (tk >= 0) lastp = tk;
-        run += tot;
-      }
+    if (sh.fallback) {  // residual identically zero (rounding only): drawn from p_k itself, R = 0
+      const int tok = fallback_draw<ET, NV, AL>(target + int64_t(k) * V, V, nT, cc, sh.Lp, sh.u[K], sh);
       if (t == 0) {
-        a.bonus_out[b] = (found >= 0) ? found : lastp;
+        a.bonus_out[b] = tok;
         if (a.rmass_out) a.rmass_out[b] = 0.f;
       }
     } else if (sh.cstar != tile && ld_agent(chunk + 2 * sh.cstar) == tagged(tag, kClaimCloser)) {
@@ -1282,13 +1305,165 @@ __global__ __launch_bounds__(kThreads, 2) void verify_kernel(VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// The two-launch form. When a batch has more tiles than the device runs at once, the workgroups go
+// through it in waves, and a tile that waits for its sequence's decision holds a slot that a tile
+// not yet started could stream in: the waits add up over the waves. So verify_kernel (a.split) ends
+// every tile once its statistics and guesses are published, the last tile of each sequence taking
+// the decision, and mass_kernel, a second grid of the same tiles, reads the decision record, reads
+// the tile's two residual rows again (2 of the 2K+1 rows), publishes the tile's mass and counts
+// itself in; the last tile of each sequence to arrive scans the masses and draws the bonus. No
+// workgroup waits for one that has not arrived. Tiles, merge orders, mass sums and the search are
+// those of the one-launch form, so the two forms give the same bits.
+// ---------------------------------------------------------------------------------------------
+struct MassShared {
+  int k, nset;
+  float Lp, Lq, w_out, w_in;
+  int myset[kMaxF];
+  int last;  // this tile is the last of its sequence to arrive
+  float wt[kWaves];
+  float res[kMaxT];
+  int cstar, clamp, fallback, first, lastp;
+  float base, target, R;
+};
+
+template <class ET, int NV, bool AL>
+__global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
+  using T = typename ET::T;
+  using LY = Lay<ET, NV>;
+  constexpr int E = LY::E;
+  __shared__ MassShared sh;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int K = a.K, V = a.V, nT = a.T, sF = a.sF, Tc = a.Tcap;
+  const float cc = a.c2;
+  const int tile = blockIdx.x % nT;
+  const int b = int(blockIdx.x) / nT;
+  const int bl = tile * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+  const T* draft = reinterpret_cast<const T*>(a.draft) + int64_t(b) * a.dstride;
+  const T* target = reinterpret_cast<const T*>(a.target) + int64_t(b) * a.tstride;
+  uint32_t* ctr = a.seqctl + int64_t(b) * kPlanSeqCtlWords;
+  uint64_t* chunk = a.chunk + int64_t(b) * Tc * 2;
+  const uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
+  // the tag of the call: verify_kernel left the last call's tag in place; the last sequence to
+  // finish here advances it, once every tile of this grid has read it
+  const uint32_t tag_ld = ld_agent(a.gtag);
+  const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
+  const float uK = a.u[b * (K + 1) + K];
+  const int long_bound = a.wait_polls * 8 + 4096;
+
+  // the decision record (the first launch has ended, so the words are in; the poll only checks)
+  if (t < 64) {
+    const int nw = kDecSet + sF;
+    uint64_t v = 0;
+    for (int n = 0;; ++n) {
+      v = (lane < nw) ? ld_agent(dec + lane) : tagged(tag, 0u);
+      if (__all(tag_of(v) == tag)) break;
+      if (n >= long_bound) {
+        if (lane == 0) atomicOr(a.flags, kFlagTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const uint32_t x = uint32_t(v);
+    if (lane == kDecK) sh.k = int(x);
+    if (lane == kDecLp) sh.Lp = __uint_as_float(x);
+    if (lane == kDecLq) sh.Lq = __uint_as_float(x);
+    if (lane == kDecWout) sh.w_out = __uint_as_float(x);
+    if (lane == kDecWin) sh.w_in = __uint_as_float(x);
+    if (lane == kDecNset) sh.nset = int(x);
+    if (lane >= kDecSet && lane < kDecSet + kMaxF) sh.myset[lane - kDecSet] = (lane < nw) ? int(x) : -1;
+  }
+  __syncthreads();
+  const int k = min(max(__builtin_amdgcn_readfirstlane(sh.k), 0), K);
+  const int nset = (k < K) ? min(max(sh.nset, 0), kMaxF) : 0;
+
+  // the tile's residual values (target row k, draft row k) and its mass
+  auto values = [&](int q, float (&rv)[E]) __attribute__((always_inline)) -> int {
+    const int blq = q * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+    const bool tq = AL && ((q + 1) * LY::TILE > V);
+    Raw<NV> rp, rq;
+    load_row<ET, NV, AL>(target + int64_t(k) * V, blq, V, rp);
+    // no draft row when every draft passed (r = p_K): the target row's address again, a cache hit
+    load_row<ET, NV, AL>((k < K) ? draft + int64_t(k) * V : target + int64_t(k) * V, blq, V, rq);
+    float zp[E], zq[E];
+    unpack_row<ET, NV>(rp, blq, V, tq, zp);
+    unpack_row<ET, NV>(rq, blq, V, tq, zq);
+    residual_values<ET, NV>(zp, zq, k < K, blq, V, cc, sh.Lp, sh.Lq, sh.w_out, sh.w_in, sh.myset, nset, rv);
+    return blq;
+  };
+  float rv[E];
+  values(tile, rv);
+  const float total = tile_mass<E>(rv, sh.wt);
+  if (t == 0) {
+    st_agent(chunk + 2 * tile + 1, tagged(tag, __float_as_uint(total)));
+    const bool last = add_agent(ctr, 1u) + 1u == uint32_t(nT);
+    if (last) st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
+    sh.last = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!sh.last) return;
+
+  // ---- the last tile of the sequence: every mass has been published (the polls only wait for the
+  // words to be seen), the scan, the draw
+  if (t < 64) {
+    bool ok = false;
+    for (int n = 0;; ++n) {
+      bool in = true;
+      for (int c = lane; c < nT; c += 64) {
+        const uint64_t mw = ld_agent(chunk + 2 * c + 1);
+        in = in && tag_of(mw) == tag;
+        sh.res[c] = val_f(mw);
+      }
+      if (__all(in)) {
+        ok = true;
+        break;
+      }
+      if (n >= long_bound) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok && lane == 0) atomicOr(a.flags, kFlagTimeout);
+  }
+  __syncthreads();
+  if (t < 64) scan_masses(sh, nT, uK);
+  __syncthreads();
+  int tok;
+  float rm;
+  if (sh.fallback) {
+    tok = fallback_draw<ET, NV, AL>(target + int64_t(k) * V, V, nT, cc, sh.Lp, uK, sh);
+    rm = 0.f;
+  } else {
+    const int cs = sh.cstar;
+    int blq = bl;
+    if (cs != tile) blq = values(cs, rv);  // another tile's range: its two rows read again
+    float pre[E];
+    tile_prefix<ET, NV>(rv, sh.wt, pre);
+    tok = tile_search<ET, NV>(rv, pre, blq, sh.base, sh.target, sh.clamp != 0, sh);
+    rm = (k < K) ? sh.R : 1.f;
+  }
+  if (t == 0) {
+    a.bonus_out[b] = tok;
+    if (a.rmass_out) a.rmass_out[b] = rm;
+    if (add_agent(a.gdone, 1u) + 1u == uint32_t(a.B)) {  // the last sequence of the call
+      st_agent(a.gdone, 0u);
+      st_agent(a.gtag, tag);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // launch: one grid of every (sequence, tile); no workgroup needs another to be resident
 // ---------------------------------------------------------------------------------------------
 static_assert(kThreads == kVerifyThreads, "the host plan sizes tiles for this workgroup");
 
 template <class ET, int KM, int NV, bool AL>
 static hipError_t launch_v(const VerifyArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((verify_kernel<ET, KM, NV, AL>), dim3(unsigned(int64_t(a.B) * a.T)), dim3(kThreads), 0, st, a);
+  const dim3 grid(unsigned(int64_t(a.B) * a.T));
+  hipLaunchKernelGGL((verify_kernel<ET, KM, NV, AL>), grid, dim3(kThreads), 0, st, a);
+  if (!a.split) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mass_kernel<ET, NV, AL>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -76,6 +76,33 @@ def test_verify_argument_validation(over, want):
     assert _verify(**over) == want
 
 
+def _verify_ex(opts, **over):
+    B, K, V = 2, 4, 1000
+    a = dict(draft=FAKE, dstride=K * V, target=FAKE, tstride=(K + 1) * V, dtype=ssd.SSD_F32, B=B, K=K,
+             V=V, T=1.0, x=FAKE, u=FAKE, sset=None, sF=0, C=1.0, Cpos=None, topfF=None, topfFmax=0,
+             topf_out=None, k=FAKE, bonus=FAKE, aprob=None, rmass=None, opts=ctypes.addressof(opts), ws=None,
+             wsb=0, stream=None)
+    a.update(over)
+    return ssd.lib().ssd_verify_ex(*a.values())
+
+
+@pytest.mark.parametrize("fields,over,want", [
+    (dict(launch_mode=3), {}, INV), (dict(launch_mode=-1), {}, INV),
+    (dict(wait_polls=(1 << 20) + 1), {}, INV),
+    (dict(topf_last_F=17, topf_last_out=FAKE), dict(dstride=5000), INV),
+    (dict(topf_last_F=2), dict(dstride=5000), INV),                   # no output for the extra row
+    (dict(topf_last_F=2, topf_last_out=FAKE), {}, INV),                # draft stride without row K
+    (dict(topf_last_F=2, topf_last_out=FAKE), dict(dstride=5000), WS),  # valid: fails at the workspace
+    (dict(launch_mode=0), {}, WS), (dict(launch_mode=1), {}, WS), (dict(launch_mode=2), {}, WS),
+    (dict(wait_polls=-5), {}, WS),                                     # < 0: the default
+])
+def test_verify_options_are_checked(fields, over, want):
+    o = ssd.VerifyOpts(-1, 0, None, 0)
+    for k, v in fields.items():
+        setattr(o, k, v)
+    assert _verify_ex(o, **over) == want
+
+
 def test_verify_per_position_c_is_checked():
     good = (ctypes.c_float * 4)(0.5, 0.3, 1.0, 0.0)
     bad = (ctypes.c_float * 4)(0.5, 1.2, 1.0, 0.0)
@@ -195,6 +222,16 @@ def test_verify_launch_count_rejects_what_verify_rejects():
                  (1, 4, 1000, ssd.SSD_BF16, 17), (1, 4, 1000, ssd.SSD_BF16, -1)]:
         assert ssd.ssd_verify_launches(*args) == -1, args
     assert ssd.ssd_verify_launches(0, 4, 1000, ssd.SSD_BF16, 3) == 0
+
+
+def test_verify_launch_count_follows_the_tiles_the_device_runs_at_once():
+    # 256 CUs x 2 workgroups (the count the library assumes when no device answers, and MI355X's):
+    # 16 x 32 tiles fit, 17 x 32 do not
+    assert ssd.ssd_verify_tiles(16, 4, 128256, ssd.SSD_BF16) == 32
+    assert ssd.ssd_verify_launches(16, 4, 128256, ssd.SSD_BF16, 3) == 1
+    assert ssd.ssd_verify_launches(17, 4, 128256, ssd.SSD_BF16, 3) == 2
+    assert ssd.ssd_verify_launches(128, 8, 152064, ssd.SSD_F32, 4) == 2
+    assert ssd.ssd_verify_launches(1, 4, 32000, ssd.SSD_F32, 0) == 1
 
 
 @pytest.mark.parametrize("K,a,r,budget", [(4, 0.7, 1.0, 12), (4, 0.7, 1.0, 32), (8, 0.55, 0.5, 100),

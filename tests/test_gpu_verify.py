@@ -193,10 +193,11 @@ def test_empty_batch_is_a_no_op():
 
 
 def test_launch_count_and_tiles():
-    # one launch per call whatever the batch; tiles per row follow the plan (bf16 4096-token tiles
-    # for the headline shape, smaller tiles when the batch alone would leave CUs idle)
+    # one launch while the batch's tiles fit on the device at once (MI355X: 256 CUs x 2), two beyond;
+    # tiles per row follow the plan (bf16 4096-token tiles for the headline shape, smaller tiles when
+    # the batch alone would leave CUs idle)
     assert ssd.ssd_verify_launches(16, 4, 128256, ssd.SSD_BF16, 3) == 1
-    assert ssd.ssd_verify_launches(4096, 4, 128256, ssd.SSD_BF16, 3) == 1
+    assert ssd.ssd_verify_launches(4096, 4, 128256, ssd.SSD_BF16, 3) == 2
     assert ssd.ssd_verify_launches(0, 4, 128256, ssd.SSD_BF16, 3) == 0
     assert ssd.ssd_verify_tiles(16, 4, 128256, ssd.SSD_BF16) == 32
     assert ssd.ssd_verify_tiles(1, 4, 32000, ssd.SSD_F32) == 32
