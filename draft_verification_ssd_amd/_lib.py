@@ -201,8 +201,8 @@ def ssd_verify_workspace_bytes(B: int, K: int, V: int, topf_F_max: int = 0) -> i
 
 
 def ssd_verify_launches(B: int, K: int, V: int, dtype: int, topf_F_max: int = 0) -> int:
-    """Kernel launches ssd_verify issues for this shape on the current device: 2 when the batch has
-    more tiles than the device runs at once, else 1 (-1 if rejected)."""
+    """Kernel launches ssd_verify issues for this shape on the current device: 2 (the streaming
+    form) when the batch has more tiles than the device runs at once, else 1 (-1 if rejected)."""
     return int(lib().ssd_verify_launches(B, K, V, dtype, topf_F_max))
 
 

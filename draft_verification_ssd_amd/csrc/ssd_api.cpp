@@ -45,7 +45,7 @@ int verify_slots() {
   }
   return n * kVerifyWgPerCu;
 }
-// The two-launch form: when the batch has more tiles than the device runs at once
+// The streaming form (two launches): when the batch has more tiles than the device runs at once
 bool verify_split(int B, int T) { return int64_t(B) * T > verify_slots(); }
 
 
@@ -169,6 +169,8 @@ static ssd_status verify_impl(const void* draft_logits, int64_t draft_seq_stride
   a.wait_polls = wait_polls;
   a.aligned = aligned ? 1 : 0;
   a.split = (launch_mode == 2 || (launch_mode == 0 && verify_split(B, P.T))) ? 1 : 0;
+  // the streaming form's second grid: about one workgroup per slot, each over a run of tiles
+  a.groups = int(std::min<int64_t>(P.T, std::max<int64_t>(1, (verify_slots() + B - 1) / B)));
 #ifdef SSD_TRACE
   a.trace = static_cast<uint64_t*>(ssd_trace_buffer);
 #endif

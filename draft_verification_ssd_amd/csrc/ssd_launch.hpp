@@ -45,7 +45,8 @@ struct VerifyArgs {
   int Tcap;
   int wait_polls;    // polls a workgroup spends waiting on the others of its sequence
   int aligned;       // every logit row starts 16-byte aligned
-  int split;         // two launches: statistics, decision and guesses, then residual and bonus
+  int split;         // the streaming form: statistics and guesses, then decision, residual and bonus
+  int groups;        // the streaming form: workgroups per sequence of its second grid
   uint64_t* trace;   // per-workgroup phase timestamps (analysis builds only), or null
 };
 
@@ -125,6 +126,7 @@ struct VerifyPlan {
 };
 constexpr int kVerifyThreads = 256;  // threads of a verification workgroup
 constexpr int kVerifyWgPerCu = 2;    // verification workgroups a CU runs at once (register budget)
+constexpr int kStreamWgPerCu = 3;    // the same for the streaming form's first grid
 inline VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned) {
   VerifyPlan p;
   p.AL = aligned;

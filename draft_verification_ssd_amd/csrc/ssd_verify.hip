@@ -1,5 +1,5 @@
 // Batched lossless draft verification on gfx950: one launch per call, or two for batches whose tiles
-// do not all fit on the device at once (the two-launch form, at the end of this file).
+// do not all fit on the device at once (the streaming form, at the end of this file).
 //
 // Work unit: one 256-thread workgroup per (sequence b, tile of TILE tokens). A tile covers the same
 // token range of every row of its sequence (K draft rows, K+1 target rows) and keeps all of them
@@ -17,16 +17,17 @@
 //  arrival     The tile claims its residual chunk and adds one to its sequence's arrival counter.
 //              The tile that brings the count to T, the closer, knows every tile has published.
 //  decide      The closer merges the T statistics of every row in one fixed order, takes the accept
-//              decisions (k and the rows of the residual) and publishes them as a small record of
+//              decisions (k and the terms of the residual) and publishes them as a small record of
 //              tagged words.
 //  guesses     Meanwhile every other tile selects its best F per draft row from the copies and
 //              publishes them; the last tile of the sequence to do so merges them all.
 //  residual    Each tile, once it has read the record (a bounded number of polls), forms
 //              r = max(p_k - q'_k, 0) (p_K when every draft passes) from the rows in registers and
 //              publishes its mass, tagged.
-//  bonus       The closer collects the T masses, finds the tile whose range holds u_K R and the
-//              token inside it (from its registers, or reading that tile's two rows again), and
-//              returns the sequence's counters to zero; the last sequence advances the call tag.
+//  bonus       Every tile reads the T masses and finds the tile whose range holds u_K R; that tile
+//              finds the token inside it from its registers (the closer, reading its two rows
+//              again, if it gave its chunk up). The closer returns the sequence's counters to zero;
+//              the last sequence advances the call tag.
 //
 // The closer waits only on tiles that have arrived, never on one that may not have started, and a
 // tile that has polled for the record its bound gives its chunk up and exits; the closer computes
@@ -54,13 +55,13 @@ constexpr int kRegW = 48;
 constexpr int kHot = 8;
 static_assert(kRegW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
 static_assert(kRegW <= 64, "a key-list region gives at most one entry per lane");
-// claim word states of a tile's residual chunk
-constexpr uint32_t kClaimOwner = 1, kClaimAbandoned = 2, kClaimCloser = 3;
-constexpr int kGroup = 4;  // chunks given up that the closer computes at once
 // decision record: 64-bit words (call tag << 32 | value)
 constexpr int kDecK = 0, kDecLp = 1, kDecLq = 2, kDecWout = 3, kDecWin = 4, kDecNset = 5, kDecSet = 6,
               kDecWords = kDecSet + kMaxF;
 static_assert(kDecWords <= kPlanDecWords, "decision record exceeds its workspace slot");
+// claim word states of a tile's residual chunk
+constexpr uint32_t kClaimOwner = 1, kClaimAbandoned = 2, kClaimCloser = 3;
+constexpr int kGroup = 4;  // chunks given up that the closer computes at once
 
 #ifndef SSD_VERIFY_PRIO
 #define SSD_VERIFY_PRIO 1  // phase-1 issue priority by progress
@@ -404,10 +405,248 @@ __device__ __forceinline__ int fallback_draw(const typename ET::T* prow, int V, 
   return (found >= 0) ? found : lastp;
 }
 
+// The merge of sequence b's guesses (every thread of one workgroup calls it, once every tile of the
+// sequence has published its own). Keys are unique (a token lives in one tile), so round f picks the
+// largest key below round f-1's. Each key is two words tagged with the call; the caller knows that
+// every tile has written its keys, so the polls only wait for the words to be seen. kM: keys per
+// lane held in registers (more keys per row: every round reads them again). The workgroup merges
+// guess rows first, first + step, ... (wave w takes the w-th of them, then every kWaves-th).
+template <int kM>
+__device__ __forceinline__ void merge_guesses_seq(const VerifyArgs& a, const Shared& sh, int b, uint32_t tag,
+                                                  int long_bound, int first = 0, int step = 1) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = a.K, nT = a.T, Tc = a.Tcap;
+  const bool guess_rows = a.topfFmax > 0;
+  const int KG = K + (a.lastF > 0 ? 1 : 0);
+  for (int r = first + w * step; r < KG; r += kWaves * step) {
+    if (r < K && !guess_rows) continue;
+    const int F = sh.F[r];
+    const int width = (r < K) ? a.topfFmax : a.lastF;
+    int32_t* out = (r < K) ? a.topf_out + (int64_t(b) * K + r) * a.topfFmax : a.topf_last_out + int64_t(b) * a.lastF;
+    const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * Tc * a.Fcap * 2;
+    const int n = nT * F;
+    auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F), once tagged
+      const int tl = q / F, ff = q - tl * F;
+      const uint64_t* cw = cd + (int64_t(tl) * a.Fcap + ff) * 2;
+      uint64_t hi = 0, lo = 0;
+      for (int spins = 0;; ++spins) {
+        hi = ld_agent(cw);
+        lo = ld_agent(cw + 1);
+        if (tag_of(hi) == tag && tag_of(lo) == tag) break;
+        if (spins > long_bound) {
+          atomicOr(a.flags, kFlagTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+    };
+    if (n <= 64 * kM) {
+      // every key's two words loaded at once, then the tags checked (read again if not yet in)
+      uint64_t hi[kM], lo[kM];
+      for (int spins = 0;; ++spins) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+          const int q = lane + 64 * i;
+          const int tl = q / max(F, 1), ff = q - tl * max(F, 1);
+          const uint64_t* cw = cd + (int64_t(min(tl, nT - 1)) * a.Fcap + ff) * 2;
+          hi[i] = (q < n) ? ld_agent(cw) : tagged(tag, 0u);
+          lo[i] = (q < n) ? ld_agent(cw + 1) : tagged(tag, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < kM; ++i) ok = ok && tag_of(hi[i]) == tag && tag_of(lo[i]) == tag;
+        if (__all(ok)) break;
+        if (spins > long_bound) {
+          if (!ok) atomicOr(a.flags, kFlagTimeout);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      uint64_t key[kM];
+#pragma unroll
+      for (int i = 0; i < kM; ++i) key[i] = (uint64_t(uint32_t(hi[i])) << 32) | uint32_t(lo[i]);
+      for (int f = 0; f < F; ++f) {
+        uint64_t mine = key[0];
+#pragma unroll
+        for (int i = 1; i < kM; ++i) mine = max_u64(mine, key[i]);
+        const uint64_t win = wave_max_u64(mine);
+        if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+#pragma unroll
+        for (int i = 0; i < kM; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
+      }
+    } else {  // many tiles: every round reads the keys again, taking the largest below the last
+      uint64_t prev = ~0ull;
+      for (int f = 0; f < F; ++f) {
+        uint64_t best = 0;
+        for (int q = lane; q < n; q += 64) {
+          const uint64_t kq = cand_at(q);
+          best = (kq < prev && kq > best) ? kq : best;
+        }
+        const uint64_t win = wave_max_u64(best);
+        if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+        prev = win;
+      }
+    }
+    for (int f = F + lane; f < width; f += 64) out[f] = -1;
+  }
+}
+
+// The inputs of the accept tests that the decision reads from LDS: the logits at the draft tokens
+// (draft rows, then target rows) and at the Saguaro-set entries, and the set entries that count (in
+// range, first occurrence). Thread t holds its values; sh.sv must be staged and visible.
+__device__ __forceinline__ void stage_accept_inputs(Shared& sh, int K, int sF, int V, float zg_v, float zs_v, int sv_v) {
+  const int t = threadIdx.x;
+  if (t < 2 * K) sh.zg[t] = zg_v;
+  if (t < K * sF) {
+    sh.zs[t] = zs_v;
+    const int i = t / sF, f = t - i * sF;
+    int set_v = (unsigned(sv_v) < unsigned(V)) ? sv_v : -1;
+    for (int g = 0; g < f && set_v >= 0; ++g)
+      if (sh.sv[i * sF + g] == set_v) set_v = -1;
+    sh.set[t] = set_v;
+  }
+}
+
+// The decision of sequence b by one workgroup (every thread calls it, once sh.xe, sh.C, sh.u, sh.zg,
+// sh.zs and sh.set are staged): every tile's statistics merged in one fixed order, then the accept
+// tests (wave 0), the decision left in sh (k, the residual's normalisers, weights and set). Each
+// statistic is read once its two words carry the call's tag, polling at most `bound` times; false
+// if some word was not seen by then (nothing decided; with flag_timeout the device flag is set).
+// tr: this workgroup writes trace slot 3; record: it publishes the decision as the sequence's
+// record; outputs: it writes k and the accept probabilities.
+__device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, Shared& sh, int b, uint32_t tag, int bound,
+                                                bool flag_timeout, bool tr, bool record, bool outputs) {
+  const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
+  const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF, Tc = a.Tcap;
+  const float cc = a.c2;
+  uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
+  bool miss = false;
+  // Merge every tile's statistics in one fixed order: 16-lane group g merges rows g, g + 16, ...;
+  // lane l takes tiles l, l + 16, ... in order, then the group combines its lanes with DPP.
+  for (int r = grp; r < R2; r += kGroupsPerBlock) {
+    const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * Tc * 2;
+    float M = -INFINITY, S = 0.f;
+    constexpr int kAhead = 4;  // tiles per lane per round of loads
+    for (int q0 = (t & 15); q0 < nT; q0 += kAhead * 16) {
+      uint64_t mv[kAhead], sv[kAhead];
+      for (int spins = 0;; ++spins) {  // until both words of each tile carry this call's tag
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) {
+          const int q = q0 + i * 16;
+          mv[i] = (q < nT) ? ld_agent(st + 2 * q) : tagged(tag, 0xFF800000u);
+          sv[i] = (q < nT) ? ld_agent(st + 2 * q + 1) : tagged(tag, 0u);
+          ok = ok && tag_of(mv[i]) == tag && tag_of(sv[i]) == tag;
+        }
+        if (__all(ok)) break;
+        if (spins >= bound) {
+          miss = miss || !ok;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) {
+        const float m = val_f(mv[i]), s = val_f(sv[i]);
+        if (s > 0.f) {
+          if (m > M) {
+            S = S * ex2(M - m) + s;
+            M = m;
+          } else {
+            S += s * ex2(m - M);
+          }
+        }
+      }
+    }
+    const float Mr = row16_max(M);
+    const float Sr = row16_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
+    if ((t & 15) == 0) sh.L[r] = Mr + lg2(Sr);
+  }
+  if (__syncthreads_or(miss ? 1 : 0)) {
+    if (flag_timeout && t == 0) atomicOr(a.flags, kFlagTimeout);
+    return false;
+  }
+  if (tr) TRACE(3);
+  if (t < 64) {  // wave 0: lane i takes the accept test of position i
+    const int i = min(lane, K - 1);
+    const float C = sh.C[i];  // Saguaro factor of position i
+    const float Lq = sh.L[i], Lp = sh.L[K + i];
+    const int xi = sh.xe[i];
+    const bool xok = unsigned(xi) < unsigned(V);
+    if (lane < K && !xok) atomicOr(a.flags, kFlagBadToken);
+    float Nn = 1.f;
+    bool xin = false;
+    if (sF > 0) {  // Saguaro: N = 1 - (1 - C) sigma, sigma = q mass of the set
+      float sig = 0.f;
+      for (int f = 0; f < sF; ++f) {
+        const int sv = sh.set[i * sF + f];
+        if (sv < 0) continue;
+        sig += ex2(fmaf(sh.zs[i * sF + f], cc, -Lq));
+        if (sv == xi) xin = true;
+      }
+      Nn = 1.f - (1.f - C) * sig;
+      if (lane < K && !(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+    }
+    bool accept;
+    float ai;
+    if (!xok) {
+      accept = false;
+      ai = 0.f;
+    } else {
+      const float wx = xin ? C : 1.f;
+      const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
+      const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
+      if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
+        accept = dp > -INFINITY;
+        ai = accept ? 1.f : 0.f;
+      } else {
+        const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
+        accept = sh.u[i] < ratio;
+        ai = fminf(1.f, ratio);
+      }
+    }
+    if (outputs && a.aprob_out && lane < K) a.aprob_out[b * K + lane] = ai;
+    const uint64_t rej = __ballot(lane < K && !accept);
+    const int kk = rej ? __builtin_ctzll(rej) : K;  // first rejection
+    const float Nk = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), kk)) : 1.f;
+    const float Ck = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(C), kk)) : 1.f;
+    // the residual's terms, published as the record straight from registers: lane j writes word j
+    // (the set of row k keeps its -1 holes: duplicates and out-of-range entries, which the residual
+    // skips)
+    const int nset = (kk < K) ? sF : 0;
+    const float Lpk = sh.L[K + kk], Lqk = (kk < K) ? sh.L[kk] : 0.f;
+    const int f = lane - kDecSet;
+    const int sv = (f >= 0 && f < nset) ? sh.set[kk * sF + f] : -1;
+    uint32_t v = uint32_t(sv);
+    if (lane == kDecK) v = uint32_t(kk);
+    if (lane == kDecLp) v = __float_as_uint(Lpk);
+    if (lane == kDecLq) v = __float_as_uint(Lqk);
+    if (lane == kDecWout) v = __float_as_uint(1.f / Nk);
+    if (lane == kDecWin) v = __float_as_uint(Ck / Nk);
+    if (lane == kDecNset) v = uint32_t(nset);
+    if (record && lane < kDecSet + sF) st_agent(dec + lane, tagged(tag, v));
+    if (lane == 0) {
+      if (outputs) a.k_out[b] = kk;
+      sh.k = kk;
+      sh.nset = nset;
+      sh.Lp = Lpk;
+      sh.Lq = Lqk;
+      sh.w_out = 1.f / Nk;
+      sh.w_in = Ck / Nk;
+    }
+    if (lane < kMaxF) sh.myset[lane] = (lane < nset) ? sh.set[kk * sF + lane] : -1;
+  }
+  __syncthreads();
+  return true;
+}
+
 // KM: register rows per tile are 2 KM + 1 (draft slots 0..KM-1, target slots KM..2KM), K <= KM.
-// NV: 16-byte chunks per lane and row. AL: every row 16-byte aligned.
-template <class ET, int KM, int NV, bool AL>
-__global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(VerifyArgs a) {
+// NV: 16-byte chunks per lane and row. AL: every row 16-byte aligned. SPLIT: the streaming form's
+// first grid (statistics and guesses of every tile, nothing else; see the end of this file).
+template <class ET, int KM, int NV, bool AL, bool SPLIT>
+__global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) void verify_kernel(VerifyArgs a) {
   using T = typename ET::T;
   using LY = Lay<ET, NV>;
   constexpr int E = LY::E;
@@ -460,7 +699,9 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
     const int r = (s < KM) ? min(s, K - 1) : K + min(s - KM, K);
     load_row<ET, NV, AL>(row_ptr(r), bl, V, raw[s]);
   };
-  constexpr int kAhead = (SSD_VERIFY_AHEAD < RM) ? SSD_VERIFY_AHEAD : RM;
+  // (the streaming form issues every row at once: its rows' registers are held anyway, and no
+  // workgroup of it waits for another)
+  constexpr int kAhead = SPLIT ? RM : ((SSD_VERIFY_AHEAD < RM) ? SSD_VERIFY_AHEAD : RM);
 #pragma unroll
   for (int s = 0; s < kAhead; ++s) issue(s);
   __builtin_amdgcn_sched_barrier(0);
@@ -549,7 +790,7 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
 #if SSD_VERIFY_PRIO
       // A wave's issue priority falls as it gets through its rows, so the waves of the workgroups
       // that share a CU finish their statistics close together rather than the oldest first.
-      {
+      if constexpr (!SPLIT) {
         const int q = (4 * s) / RM;  // a constant once the loop is unrolled
         if (q == 0) __builtin_amdgcn_s_setprio(3);
         else if (q == 1) __builtin_amdgcn_s_setprio(2);
@@ -587,8 +828,8 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
   // read once the tile knows it is the closer
   // Every lane reads (an idle or out-of-range lane the row's first token) and the value is selected
   // afterwards, so no branch makes the wave wait for the read where it is issued.
-  float zg_v, zs_v;
-  {
+  float zg_v = 0.f, zs_v = 0.f;
+  if constexpr (!SPLIT) {  // (the streaming form's decision reads them itself)
     const bool g_ok = t < 2 * K && unsigned(xg) < unsigned(V);
     const float g = ET::one(row_ptr(t < 2 * K ? t : 0), g_ok ? xg : 0);
     const bool s_ok = t < K * sF && unsigned(sv_v) < unsigned(V);
@@ -606,7 +847,7 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
   if (t < K * sF) sh.sv[t] = sv_v;
   const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
 #if SSD_VERIFY_PRIO
-  __builtin_amdgcn_s_setprio(0);
+  if constexpr (!SPLIT) __builtin_amdgcn_s_setprio(0);
 #endif
   __syncthreads();
   TRACE(1);
@@ -627,16 +868,17 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
     st_agent(st + 1, tagged(tag, __float_as_uint(S)));
   }
   if (t == 0) {
-    st_agent(chunk + 2 * tile, tagged(tag, kClaimOwner));
-    const bool last = add_agent(ctr, 1u) + 1u == uint32_t(nT);
     int role = 0;
-    if (last) {
-      st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
-      role = 1;
-      // the closer counts its guesses in now and publishes them later, off its path to the bonus:
-      // the merger (usually another tile) waits for them, and the closer has arrived, so it ends
-      // (in the two-launch form nothing waits, and the closer counts in after its guesses)
-      if (guesses && !a.split && add_agent(ctr + 1, 1u) + 1u == uint32_t(nT)) role |= 2;
+    if constexpr (!SPLIT) {
+      st_agent(chunk + 2 * tile, tagged(tag, kClaimOwner));
+      if (add_agent(ctr, 1u) + 1u == uint32_t(nT)) {
+        st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
+        role = 1;
+        // the closer counts its guesses in now and publishes them later, off its path to the
+        // bonus: the merger (usually another tile) waits for them, and the closer has arrived, so
+        // it ends
+        if (guesses && add_agent(ctr + 1, 1u) + 1u == uint32_t(nT)) role |= 2;
+      }
     }
     sh.role = role;
   }
@@ -852,252 +1094,58 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
       __syncthreads();
     }
   };
-  // ---- guess merger: the last tile of the sequence to publish its guesses merges them. Keys are
-  // unique (a token lives in one tile), so round f picks the largest key below round f-1's. Each
-  // key is two words tagged with the call; every tile that wrote one has counted itself in after
-  // writing it, so the wait for the tags ends.
+  // ---- guess merger: the last tile of the sequence to publish its guesses merges them
   const int long_bound = a.wait_polls * 8 + 4096;  // waits on tiles known to have arrived
   auto merge_guesses = [&]() __attribute__((always_inline)) {
-    for (int r = w; r < KG; r += kWaves) {
-      if (r < K && !guess_rows) continue;
-      const int F = sh.F[r];
-      const int width = (r < K) ? a.topfFmax : a.lastF;
-      int32_t* out = (r < K) ? a.topf_out + (int64_t(b) * K + r) * a.topfFmax : a.topf_last_out + int64_t(b) * a.lastF;
-      const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * Tc * a.Fcap * 2;
-      const int n = nT * F;
-      auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F), once tagged
-        const int tl = q / F, ff = q - tl * F;
-        const uint64_t* cw = cd + (int64_t(tl) * a.Fcap + ff) * 2;
-        uint64_t hi = 0, lo = 0;
-        for (int spins = 0;; ++spins) {
-          hi = ld_agent(cw);
-          lo = ld_agent(cw + 1);
-          if (tag_of(hi) == tag && tag_of(lo) == tag) break;
-          if (spins > long_bound) {
-            atomicOr(a.flags, kFlagTimeout);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
-      };
-      constexpr int kM = 4;  // keys per lane held in registers
-      if (n <= 64 * kM) {
-        // every key's two words loaded at once, then the tags checked (read again if not yet in)
-        uint64_t hi[kM], lo[kM];
-        for (int spins = 0;; ++spins) {
-          bool ok = true;
-#pragma unroll
-          for (int i = 0; i < kM; ++i) {
-            const int q = lane + 64 * i;
-            const int tl = q / max(F, 1), ff = q - tl * max(F, 1);
-            const uint64_t* cw = cd + (int64_t(min(tl, nT - 1)) * a.Fcap + ff) * 2;
-            hi[i] = (q < n) ? ld_agent(cw) : tagged(tag, 0u);
-            lo[i] = (q < n) ? ld_agent(cw + 1) : tagged(tag, 0u);
-          }
-#pragma unroll
-          for (int i = 0; i < kM; ++i) ok = ok && tag_of(hi[i]) == tag && tag_of(lo[i]) == tag;
-          if (__all(ok)) break;
-          if (spins > long_bound) {
-            if (!ok) atomicOr(a.flags, kFlagTimeout);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        uint64_t key[kM];
-#pragma unroll
-        for (int i = 0; i < kM; ++i) key[i] = (uint64_t(uint32_t(hi[i])) << 32) | uint32_t(lo[i]);
-        for (int f = 0; f < F; ++f) {
-          uint64_t mine = key[0];
-#pragma unroll
-          for (int i = 1; i < kM; ++i) mine = max_u64(mine, key[i]);
-          const uint64_t win = wave_max_u64(mine);
-          if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
-#pragma unroll
-          for (int i = 0; i < kM; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
-        }
-      } else {  // many tiles: every round reads the keys again, taking the largest below the last
-        uint64_t prev = ~0ull;
-        for (int f = 0; f < F; ++f) {
-          uint64_t best = 0;
-          for (int q = lane; q < n; q += 64) {
-            const uint64_t kq = cand_at(q);
-            best = (kq < prev && kq > best) ? kq : best;
-          }
-          const uint64_t win = wave_max_u64(best);
-          if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
-          prev = win;
-        }
-      }
-      for (int f = F + lane; f < width; f += 64) out[f] = -1;
-    }
+    merge_guesses_seq<4>(a, sh, b, tag, long_bound);
     if (t == 0) st_agent(ctr + 1, 0u);  // every tile has counted itself in: back to zero
   };
+
+  if constexpr (SPLIT) {  // the streaming form: resid_kernel takes the rest
+    if (guesses) tile_guesses(false);
+    TRACE(9);
+    return;
+  }
 
   // ---- the decision: the closer merges the statistics and publishes the record; every other tile
   // selects its guesses meanwhile, then reads the record (or gives its chunk up)
   if (closer) {
-      if (t < 2 * K) sh.zg[t] = zg_v;
-      if (t < K * sF) {
-        sh.zs[t] = zs_v;
-        // the set entries that count: in range, first occurrence
-        const int i = t / sF, f = t - i * sF;
-        int set_v = (unsigned(sv_v) < unsigned(V)) ? sv_v : -1;
-        for (int g = 0; g < f && set_v >= 0; ++g)
-          if (sh.sv[i * sF + g] == set_v) set_v = -1;
-        sh.set[t] = set_v;
-      }
-      // Merge every tile's statistics in one fixed order: 16-lane group g merges rows g, g + 16, ...;
-      // lane l takes tiles l, l + 16, ... in order, then the group combines its lanes with DPP.
-      for (int r = grp; r < R2; r += kGroupsPerBlock) {
-        const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * Tc * 2;
-        float M = -INFINITY, S = 0.f;
-        constexpr int kAhead = 4;  // tiles per lane per round of loads
-        for (int q0 = (t & 15); q0 < nT; q0 += kAhead * 16) {
-          uint64_t mv[kAhead], sv[kAhead];
-          for (int spins = 0;; ++spins) {  // until both words of each tile carry this call's tag
-            bool ok = true;
-  #pragma unroll
-            for (int i = 0; i < kAhead; ++i) {
-              const int q = q0 + i * 16;
-              mv[i] = (q < nT) ? ld_agent(st + 2 * q) : tagged(tag, 0xFF800000u);
-              sv[i] = (q < nT) ? ld_agent(st + 2 * q + 1) : tagged(tag, 0u);
-              ok = ok && tag_of(mv[i]) == tag && tag_of(sv[i]) == tag;
-            }
-            if (__all(ok)) break;
-            if (spins > long_bound) {
-              if (!ok) atomicOr(a.flags, kFlagTimeout);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-  #pragma unroll
-          for (int i = 0; i < kAhead; ++i) {
-            const float m = val_f(mv[i]), s = val_f(sv[i]);
-            if (s > 0.f) {
-              if (m > M) {
-                S = S * ex2(M - m) + s;
-                M = m;
-              } else {
-                S += s * ex2(m - M);
-              }
-            }
-          }
-        }
-        const float Mr = row16_max(M);
-        const float Sr = row16_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
-        if ((t & 15) == 0) sh.L[r] = Mr + lg2(Sr);
-      }
-      __syncthreads();
-      TRACE(3);
-      if (t < 64) {  // wave 0: lane i takes the accept test of position i
-        const int i = min(lane, K - 1);
-        const float C = sh.C[i];  // Saguaro factor of position i
-        const float Lq = sh.L[i], Lp = sh.L[K + i];
-        const int xi = sh.xe[i];
-        const bool xok = unsigned(xi) < unsigned(V);
-        if (lane < K && !xok) atomicOr(a.flags, kFlagBadToken);
-        float Nn = 1.f;
-        bool xin = false;
-        if (sF > 0) {  // Saguaro: N = 1 - (1 - C) sigma, sigma = q mass of the set
-          float sig = 0.f;
-          for (int f = 0; f < sF; ++f) {
-            const int sv = sh.set[i * sF + f];
-            if (sv < 0) continue;
-            sig += ex2(fmaf(sh.zs[i * sF + f], cc, -Lq));
-            if (sv == xi) xin = true;
-          }
-          Nn = 1.f - (1.f - C) * sig;
-          if (lane < K && !(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
-        }
-        bool accept;
-        float ai;
-        if (!xok) {
-          accept = false;
-          ai = 0.f;
-        } else {
-          const float wx = xin ? C : 1.f;
-          const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
-          const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
-          if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
-            accept = dp > -INFINITY;
-            ai = accept ? 1.f : 0.f;
-          } else {
-            const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
-            accept = sh.u[i] < ratio;
-            ai = fminf(1.f, ratio);
-          }
-        }
-        if (a.aprob_out && lane < K) a.aprob_out[b * K + lane] = ai;
-        const uint64_t rej = __ballot(lane < K && !accept);
-        const int kk = rej ? __builtin_ctzll(rej) : K;  // first rejection
-        const float Nk = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), kk)) : 1.f;
-        const float Ck = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(C), kk)) : 1.f;
-        // the record, straight from registers: lane j publishes word j (the set of row k keeps its
-        // -1 holes: duplicates and out-of-range entries, which the residual skips)
-        const int nset = (kk < K) ? sF : 0;
-        const float Lpk = sh.L[K + kk], Lqk = (kk < K) ? sh.L[kk] : 0.f;
-        const int f = lane - kDecSet;
-        const int sv = (f >= 0 && f < nset) ? sh.set[kk * sF + f] : -1;
-        uint32_t v = uint32_t(sv);
-        if (lane == kDecK) v = uint32_t(kk);
-        if (lane == kDecLp) v = __float_as_uint(Lpk);
-        if (lane == kDecLq) v = __float_as_uint(Lqk);
-        if (lane == kDecWout) v = __float_as_uint(1.f / Nk);
-        if (lane == kDecWin) v = __float_as_uint(Ck / Nk);
-        if (lane == kDecNset) v = uint32_t(nset);
-        if (lane < kDecSet + sF) st_agent(dec + lane, tagged(tag, v));
-        if (lane == 0) {
-          a.k_out[b] = kk;
-          sh.k = kk;
-          sh.nset = nset;
-          sh.Lp = Lpk;
-          sh.Lq = Lqk;
-          sh.w_out = 1.f / Nk;
-          sh.w_in = Ck / Nk;
-        }
-        if (f >= 0 && f < kMaxF) sh.myset[f] = sv;
-      }
+    stage_accept_inputs(sh, K, sF, V, zg_v, zs_v, sv_v);
+    decide_sequence(a, sh, b, tag, long_bound, true, true, true, true);
     if (t == 0) sh.go = 1;
-  } else if (!a.split) {
+  } else {
     if (guesses) tile_guesses(true);
-      // wave 0 polls the record until every word it needs carries this call's tag
-      if (t < 64) {
-        const int nw = kDecSet + sF;
-        bool ok = false;
-        uint64_t v = 0;
-        for (int n = 0;; ++n) {
-          v = (lane < nw) ? ld_agent(dec + lane) : tagged(tag, 0u);
-          if (__all(tag_of(v) == tag)) {
-            ok = true;
-            break;
-          }
-          if (n >= a.wait_polls) break;
-          __builtin_amdgcn_s_sleep(2);
+    // wave 0 polls the record until every word it needs carries this call's tag
+    if (t < 64) {
+      const int nw = kDecSet + sF;
+      bool ok = false;
+      uint64_t v = 0;
+      for (int n = 0;; ++n) {
+        v = (lane < nw) ? ld_agent(dec + lane) : tagged(tag, 0u);
+        if (__all(tag_of(v) == tag)) {
+          ok = true;
+          break;
         }
-        if (ok) {
-          const uint32_t x = uint32_t(v);
-          if (lane == kDecK) sh.k = int(x);
-          if (lane == kDecLp) sh.Lp = __uint_as_float(x);
-          if (lane == kDecLq) sh.Lq = __uint_as_float(x);
-          if (lane == kDecWout) sh.w_out = __uint_as_float(x);
-          if (lane == kDecWin) sh.w_in = __uint_as_float(x);
-          if (lane == kDecNset) sh.nset = int(x);
-          if (lane >= kDecSet && lane < kDecSet + kMaxF) sh.myset[lane - kDecSet] = (lane < nw) ? int(x) : -1;
-        }
-        if (lane == 0) {
-          sh.go = ok ? 1 : 0;
-          if (!ok) st_agent(chunk + 2 * tile, tagged(tag, kClaimAbandoned));  // the closer computes it
-        }
+        if (n >= a.wait_polls) break;
+        __builtin_amdgcn_s_sleep(2);
       }
+      if (ok) {
+        const uint32_t x = uint32_t(v);
+        if (lane == kDecK) sh.k = int(x);
+        if (lane == kDecLp) sh.Lp = __uint_as_float(x);
+        if (lane == kDecLq) sh.Lq = __uint_as_float(x);
+        if (lane == kDecWout) sh.w_out = __uint_as_float(x);
+        if (lane == kDecWin) sh.w_in = __uint_as_float(x);
+        if (lane == kDecNset) sh.nset = int(x);
+        if (lane >= kDecSet && lane < kDecSet + kMaxF) sh.myset[lane - kDecSet] = (lane < nw) ? int(x) : -1;
+      }
+      if (lane == 0) {
+        sh.go = ok ? 1 : 0;
+        if (!ok) st_agent(chunk + 2 * tile, tagged(tag, kClaimAbandoned));  // the closer computes it
+      }
+    }
   }
   __syncthreads();
-  if (a.split) {  // two-launch form: the residual and the bonus are mass_kernel's
-    if (guesses) tile_guesses(true);
-    if ((sh.role & 2) != 0) merge_guesses();
-    TRACE(9);
-    return;
-  }
   TRACE(4);
   TRACEV(12, uint64_t(sh.role) | (uint64_t(sh.go) << 8));
 
@@ -1267,7 +1315,6 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
       if (t == 0) {
         a.bonus_out[b] = tok;
         if (a.rmass_out) a.rmass_out[b] = (k < K) ? sh.R : 1.f;
-        st_agent(dec + kPlanDecWords - 1, tagged(tag, uint32_t(tok)));  // the done word
       }
       TRACE(8);
     }
@@ -1305,107 +1352,123 @@ __global__ __launch_bounds__(kThreads, kVerifyWgPerCu) void verify_kernel(Verify
 }
 
 // ---------------------------------------------------------------------------------------------
-// The two-launch form. When a batch has more tiles than the device runs at once, the workgroups go
+// The streaming form. When a batch has more tiles than the device runs at once, the workgroups go
 // through it in waves, and a tile that waits for its sequence's decision holds a slot that a tile
-// not yet started could stream in: the waits add up over the waves. So verify_kernel (a.split) ends
-// every tile once its statistics and guesses are published, the last tile of each sequence taking
-// the decision, and mass_kernel, a second grid of the same tiles, reads the decision record, reads
-// the tile's two residual rows again (2 of the 2K+1 rows), publishes the tile's mass and counts
-// itself in; the last tile of each sequence to arrive scans the masses and draws the bonus. No
-// workgroup waits for one that has not arrived. Tiles, merge orders, mass sums and the search are
-// those of the one-launch form, so the two forms give the same bits.
+// not yet started could stream in: the waits add up over the waves. So the work is cut where a
+// tile would wait, into two grids whose workgroups never wait for ones that have not arrived:
+//   verify_kernel<SPLIT>  every tile: every row read once, statistics and guesses published; no
+//                         counter, no decision (its rows are issued all at once)
+//   resid_kernel          G workgroups per sequence, each over a run of consecutive tiles: the
+//                         statistics merged and the accept decisions taken (every workgroup of the
+//                         sequence takes the same ones, from the same words in the same order), the
+//                         run's residual masses published (the tile's two residual rows read
+//                         again, 2 of the 2K+1 rows, the next tile's in flight), a share of the
+//                         guesses merged; the last workgroup of the sequence to arrive scans the
+//                         masses and draws the bonus
+// Tiles, merge orders, mass sums and the search are those of the one-launch form, so both forms give
+// the same bits.
 // ---------------------------------------------------------------------------------------------
-struct MassShared {
-  int k, nset;
-  float Lp, Lq, w_out, w_in;
-  int myset[kMaxF];
-  int last;  // this tile is the last of its sequence to arrive
-  float wt[kWaves];
-  float res[kMaxT];
-  int cstar, clamp, fallback, first, lastp;
-  float base, target, R;
-};
-
 template <class ET, int NV, bool AL>
-__global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
   using T = typename ET::T;
   using LY = Lay<ET, NV>;
   constexpr int E = LY::E;
-  __shared__ MassShared sh;
+  __shared__ Shared sh;
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int K = a.K, V = a.V, nT = a.T, sF = a.sF, Tc = a.Tcap;
+  const int K = a.K, V = a.V, nT = a.T, sF = a.sF, Tc = a.Tcap, G = a.groups;
   const float cc = a.c2;
-  const int tile = blockIdx.x % nT;
-  const int b = int(blockIdx.x) / nT;
-  const int bl = tile * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+  const int b = int(blockIdx.x) / G, g = int(blockIdx.x) - b * G;
+  const int run = (nT + G - 1) / G;  // tiles per workgroup
+  const int q0 = min(g * run, nT), q1 = min(nT, q0 + run);
   const T* draft = reinterpret_cast<const T*>(a.draft) + int64_t(b) * a.dstride;
   const T* target = reinterpret_cast<const T*>(a.target) + int64_t(b) * a.tstride;
+  auto row_ptr = [&](int r) -> const T* { return (r < K) ? draft + int64_t(r) * V : target + int64_t(r - K) * V; };
   uint32_t* ctr = a.seqctl + int64_t(b) * kPlanSeqCtlWords;
   uint64_t* chunk = a.chunk + int64_t(b) * Tc * 2;
-  const uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
-  // the tag of the call: verify_kernel left the last call's tag in place; the last sequence to
-  // finish here advances it, once every tile of this grid has read it
+  // the call's tag: the first grid left the last call's tag in place; the last sequence to finish
+  // here advances it, once every workgroup of this grid has read it
   const uint32_t tag_ld = ld_agent(a.gtag);
   const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
-  const float uK = a.u[b * (K + 1) + K];
   const int long_bound = a.wait_polls * 8 + 4096;
 
-  // the decision record (the first launch has ended, so the words are in; the poll only checks)
-  if (t < 64) {
-    const int nw = kDecSet + sF;
-    uint64_t v = 0;
-    for (int n = 0;; ++n) {
-      v = (lane < nw) ? ld_agent(dec + lane) : tagged(tag, 0u);
-      if (__all(tag_of(v) == tag)) break;
-      if (n >= long_bound) {
-        if (lane == 0) atomicOr(a.flags, kFlagTimeout);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    const uint32_t x = uint32_t(v);
-    if (lane == kDecK) sh.k = int(x);
-    if (lane == kDecLp) sh.Lp = __uint_as_float(x);
-    if (lane == kDecLq) sh.Lq = __uint_as_float(x);
-    if (lane == kDecWout) sh.w_out = __uint_as_float(x);
-    if (lane == kDecWin) sh.w_in = __uint_as_float(x);
-    if (lane == kDecNset) sh.nset = int(x);
-    if (lane >= kDecSet && lane < kDecSet + kMaxF) sh.myset[lane - kDecSet] = (lane < nw) ? int(x) : -1;
+  // ---- the decision (the sequence's inputs, the logits the accept tests read, every statistic)
+  const int x_v = (t < K) ? a.x[b * K + t] : -1;
+  const float u_v = (t <= K) ? a.u[b * (K + 1) + t] : 0.f;
+  const int sv_v = (t < K * sF) ? a.sset[int64_t(b) * K * sF + t] : -1;
+  const int xg = (t < 2 * K) ? a.x[b * K + (t < K ? t : t - K)] : -1;
+  const bool g_ok = t < 2 * K && unsigned(xg) < unsigned(V);
+  const float zg = ET::one(row_ptr(t < 2 * K ? t : 0), g_ok ? xg : 0);
+  const bool s_ok = t < K * sF && unsigned(sv_v) < unsigned(V);
+  const float zs = ET::one(row_ptr(t < K * sF ? t / sF : 0), s_ok ? sv_v : 0);
+  if (t < K) {
+    sh.xe[t] = x_v;
+    sh.C[t] = a.Cpos[t];
   }
+  if (t <= K) {
+    sh.F[t] = a.topfF[t];
+    sh.u[t] = u_v;
+  }
+  if (t == K) sh.xe[K] = -1;
+  if (t < K * sF) sh.sv[t] = sv_v;
   __syncthreads();
+  stage_accept_inputs(sh, K, sF, V, g_ok ? zg : 0.f, s_ok ? zs : 0.f, sv_v);
+  decide_sequence(a, sh, b, tag, long_bound, true, false, false, g == 0);
   const int k = min(max(__builtin_amdgcn_readfirstlane(sh.k), 0), K);
   const int nset = (k < K) ? min(max(sh.nset, 0), kMaxF) : 0;
+  const float uK = sh.u[K];
 
-  // the tile's residual values (target row k, draft row k) and its mass
-  auto values = [&](int q, float (&rv)[E]) __attribute__((always_inline)) -> int {
-    const int blq = q * LY::TILE + w * LY::WTOK + lane * LY::VEC;
+  // ---- the run's residual masses: target row k, draft row k (none when every draft passed: the
+  // target row's address again, a cache hit); the next tile's rows load while one is summed
+  const T* prow = target + int64_t(k) * V;
+  const T* qrow = (k < K) ? draft + int64_t(k) * V : prow;
+  auto lane_base = [&](int q) { return q * LY::TILE + w * LY::WTOK + lane * LY::VEC; };
+  auto load2 = [&](int q, Raw<NV>& rp, Raw<NV>& rq) __attribute__((always_inline)) {
+    load_row<ET, NV, AL>(prow, lane_base(q), V, rp);
+    load_row<ET, NV, AL>(qrow, lane_base(q), V, rq);
+  };
+  auto values = [&](int q, const Raw<NV>& rp, const Raw<NV>& rq, float (&rv)[E]) __attribute__((always_inline)) {
+    const int blq = lane_base(q);
     const bool tq = AL && ((q + 1) * LY::TILE > V);
-    Raw<NV> rp, rq;
-    load_row<ET, NV, AL>(target + int64_t(k) * V, blq, V, rp);
-    // no draft row when every draft passed (r = p_K): the target row's address again, a cache hit
-    load_row<ET, NV, AL>((k < K) ? draft + int64_t(k) * V : target + int64_t(k) * V, blq, V, rq);
     float zp[E], zq[E];
     unpack_row<ET, NV>(rp, blq, V, tq, zp);
     unpack_row<ET, NV>(rq, blq, V, tq, zq);
     residual_values<ET, NV>(zp, zq, k < K, blq, V, cc, sh.Lp, sh.Lq, sh.w_out, sh.w_in, sh.myset, nset, rv);
-    return blq;
   };
-  float rv[E];
-  values(tile, rv);
-  const float total = tile_mass<E>(rv, sh.wt);
+  auto mass = [&](int q, const Raw<NV>& rp, const Raw<NV>& rq) __attribute__((always_inline)) {
+    float rv[E];
+    values(q, rp, rq, rv);
+    const float total = tile_mass<E>(rv, sh.wt);
+    if (t == 0) st_agent(chunk + 2 * q + 1, tagged(tag, __float_as_uint(total)));
+  };
+  if (q0 < q1) {
+    // two buffers; a tile index past the run loads the run's last tile again (in bounds, unused),
+    // so no branch surrounds a load
+    Raw<NV> pa, qa, pb, qb;
+    load2(q0, pa, qa);
+    for (int q = q0; q < q1; q += 2) {
+      load2(min(q + 1, q1 - 1), pb, qb);
+      mass(q, pa, qa);
+      if (q + 1 < q1) {
+        load2(min(q + 2, q1 - 1), pa, qa);
+        mass(q + 1, pb, qb);
+      }
+    }
+  }
+  // a share of the guess merge: guess rows g, g + G, ...
+  if (a.topfFmax > 0 || a.lastF > 0) merge_guesses_seq<8>(a, sh, b, tag, long_bound, g, G);
+  __syncthreads();
   if (t == 0) {
-    st_agent(chunk + 2 * tile + 1, tagged(tag, __float_as_uint(total)));
-    const bool last = add_agent(ctr, 1u) + 1u == uint32_t(nT);
-    if (last) st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
-    sh.last = last ? 1 : 0;
+    const bool last = add_agent(ctr, 1u) + 1u == uint32_t(G);
+    if (last) st_agent(ctr, 0u);  // every workgroup has counted itself in: back to zero
+    sh.role = last ? 1 : 0;
   }
   __syncthreads();
-  if (!sh.last) return;
+  if (!sh.role) return;
 
-  // ---- the last tile of the sequence: every mass has been published (the polls only wait for the
-  // words to be seen), the scan, the draw
+  // ---- the last workgroup of the sequence: every mass has been published (the polls only wait for
+  // the words to be seen), the scan, the draw
   if (t < 64) {
     bool ok = false;
     for (int n = 0;; ++n) {
@@ -1430,15 +1493,16 @@ __global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
   int tok;
   float rm;
   if (sh.fallback) {
-    tok = fallback_draw<ET, NV, AL>(target + int64_t(k) * V, V, nT, cc, sh.Lp, uK, sh);
+    tok = fallback_draw<ET, NV, AL>(prow, V, nT, cc, sh.Lp, uK, sh);
     rm = 0.f;
-  } else {
+  } else {  // the tile whose range holds u_K R: its two rows read again
     const int cs = sh.cstar;
-    int blq = bl;
-    if (cs != tile) blq = values(cs, rv);  // another tile's range: its two rows read again
-    float pre[E];
+    Raw<NV> rp, rq;
+    load2(cs, rp, rq);
+    float rv[E], pre[E];
+    values(cs, rp, rq, rv);
     tile_prefix<ET, NV>(rv, sh.wt, pre);
-    tok = tile_search<ET, NV>(rv, pre, blq, sh.base, sh.target, sh.clamp != 0, sh);
+    tok = tile_search<ET, NV>(rv, pre, lane_base(cs), sh.base, sh.target, sh.clamp != 0, sh);
     rm = (k < K) ? sh.R : 1.f;
   }
   if (t == 0) {
@@ -1459,11 +1523,14 @@ static_assert(kThreads == kVerifyThreads, "the host plan sizes tiles for this wo
 template <class ET, int KM, int NV, bool AL>
 static hipError_t launch_v(const VerifyArgs& a, hipStream_t st) {
   const dim3 grid(unsigned(int64_t(a.B) * a.T));
-  hipLaunchKernelGGL((verify_kernel<ET, KM, NV, AL>), grid, dim3(kThreads), 0, st, a);
-  if (!a.split) return hipGetLastError();
+  if (!a.split) {
+    hipLaunchKernelGGL((verify_kernel<ET, KM, NV, AL, false>), grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((verify_kernel<ET, KM, NV, AL, true>), grid, dim3(kThreads), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mass_kernel<ET, NV, AL>), grid, dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((resid_kernel<ET, NV, AL>), dim3(unsigned(int64_t(a.B) * a.groups)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

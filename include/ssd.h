@@ -104,9 +104,9 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
  *   residual_mass     device fp32 [B] out or NULL: R (1 when k = K; 0 when the residual was all zero
  *                     and the bonus came from p_k).
  *   workspace         device scratch of ssd_verify_workspace_bytes(B, K, V, topf_F_max) bytes.
- * Launch: one kernel of B * T workgroups (T tiles per row, ssd_verify_tiles), or two such grids
- * when the batch has more tiles than the device runs at once (ssd_verify_launches,
- * ssd_verify_opts.launch_mode). The tiles of a sequence exchange partial results through the
+ * Launch: one kernel of B * T workgroups (T tiles per row, ssd_verify_tiles), or, when the batch
+ * has more tiles than the device runs at once, that grid followed by one of a few workgroups per
+ * sequence (ssd_verify_launches, ssd_verify_opts.launch_mode). The tiles of a sequence exchange partial results through the
  * workspace, but no workgroup ever needs another to be resident at the same time: a tile that has
  * polled for the rest of its sequence a bounded number of times (see ssd_verify_opts.wait_polls for
  * the default) hands its remaining work to the sequence's last tile and exits. The outputs are
@@ -118,9 +118,9 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 /* Workspace bytes for calls of this shape; topf_F_max is the largest number of guesses per row
  * the calls make (including ssd_verify_opts.topf_last_F). */
 size_t ssd_verify_workspace_bytes(int B, int K, int V, int topf_F_max);
-/* Kernel launches ssd_verify issues for 16-byte aligned rows on the current device: 1, or 2 when the
- * batch has more tiles (B x ssd_verify_tiles) than the device runs at once (2 per CU); 0 for B = 0,
- * -1 for arguments it rejects. */
+/* Kernel launches ssd_verify issues for 16-byte aligned rows on the current device: 1, or 2 (the
+ * streaming form) when the batch has more tiles (B x ssd_verify_tiles) than the device runs at once
+ * (2 per CU); 0 for B = 0, -1 for arguments it rejects. */
 int ssd_verify_launches(int B, int K, int V, ssd_dtype dtype, int topf_F_max);
 /* Tiles per logit row (workgroups per sequence) of ssd_verify for this shape with 16-byte aligned
  * rows (rows that are not take 1024-token fp32 / 2048-token bf16 tiles), -1 if rejected. */
@@ -146,13 +146,14 @@ ssd_status ssd_verify(const void* draft_logits, int64_t draft_seq_stride,
  *                  token, [SSD] "怎么猜奖励 token": the outcome k = K), with no token excluded, read
  *                  in the same pass. Needs draft_seq_stride >= (K+1) V. 0: none.
  *   topf_last_out  device int32 [B, topf_last_F] (-1 padded) when topf_last_F > 0.
- *   launch_mode    0: by shape (below); 1: one launch; 2: two launches. One launch keeps every row of
- *                  a tile in registers from its statistics to its residual, the tile waiting for
- *                  its sequence's decision; two launches end each tile after its statistics and
- *                  guesses and read the two residual rows again in a second grid, so no tile waits.
- *                  By shape, a batch with more tiles than the device runs at once (where waiting
- *                  tiles would hold slots that others could stream in) takes two. Both give the
- *                  same outputs, bit for bit. Other values: SSD_ERR_INVALID_ARG. */
+ *   launch_mode    0: by shape (below); 1: one launch; 2: the streaming form, two launches. One
+ *                  launch keeps every row of a tile in registers from its statistics to its
+ *                  residual, the tile waiting for its sequence's decision. The streaming form ends
+ *                  each tile once its statistics and guesses are out; a second grid takes the
+ *                  decision and reads the two residual rows again, so no tile waits. By shape, a batch with more tiles than the device runs at
+ *                  once (where waiting tiles would hold slots that others could stream in) takes
+ *                  the streaming form. Both give the same outputs, bit for bit. Other values:
+ *                  SSD_ERR_INVALID_ARG. */
 typedef struct ssd_verify_opts {
   int32_t wait_polls;
   int32_t topf_last_F;

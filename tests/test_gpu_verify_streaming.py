@@ -1,7 +1,7 @@
-"""GPU tests of ssd_verify's two-launch form (statistics, decision and guesses in one grid; residual
-mass and bonus in a second): forced on small shapes it gives the one-launch form's bits, and the
-oracle's results; chosen by shape for a batch with more tiles than the device runs at once; one
-workspace serves both forms in turn."""
+"""GPU tests of ssd_verify's streaming form (two grids: statistics and guesses of every tile; then,
+over runs of tiles, the decision, the residual masses, the guess merge and the bonus): forced on
+small shapes it gives the one-launch form's bits, and the oracle's results; chosen by shape for a
+batch with more tiles than the device runs at once; one workspace serves both forms in turn."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +13,7 @@ from gpu_helpers import DEV, batch_to_device, compare_verify, report
 
 pytestmark = pytest.mark.gpu
 
-ONE, TWO, BY_SHAPE = 1, 2, 0
+ONE, STREAM, BY_SHAPE = 1, 2, 0
 
 
 def call_verify(bt, topf_F_max, launch_mode, workspace=None, last_F=0, stream=None):
@@ -53,7 +53,7 @@ def check_oracle(bt, out, aprob, rmass, topf_F_max, name, last_F=0):
 def same_bits(h1, h2, name):
     assert len(h1) == len(h2)
     for n, (x, y) in enumerate(zip(h1, h2)):
-        assert np.array_equal(x, y), f"{name}: output {n} differs between the one- and two-launch forms"
+        assert np.array_equal(x, y), f"{name}: output {n} differs between the one-launch and streaming forms"
 
 
 FORCED = [
@@ -73,65 +73,65 @@ FORCED = [
 
 
 @pytest.mark.parametrize("B,K,V,dtype,T,topf,sag,last_F", FORCED)
-def test_two_launches_give_the_one_launch_bits(B, K, V, dtype, T, topf, sag, last_F):
+def test_streaming_form_gives_the_one_launch_bits(B, K, V, dtype, T, topf, sag, last_F):
     kw = dict(sag_sizes=[3] * K, C=0.4) if sag else {}
     bt = synth.make_verify_batch(B, K, V, dtype, 13, T=T, **kw)
-    name = f"two launches B{B} K{K} V{V} {dtype} F{topf} last{last_F}"
+    name = f"streaming B{B} K{K} V{V} {dtype} F{topf} last{last_F}"
     print(f"[case] {name}", flush=True)
     _, _, _, h1 = call_verify(bt, topf, ONE, last_F=last_F)
-    o2, a2, r2, h2 = call_verify(bt, topf, TWO, last_F=last_F)
+    o2, a2, r2, h2 = call_verify(bt, topf, STREAM, last_F=last_F)
     same_bits(h1, h2, name)
     check_oracle(bt, o2, a2, r2, topf, name, last_F)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_two_launches_all_zero_residual_falls_back_to_the_target_row(dtype):
+def test_streaming_all_zero_residual_falls_back_to_the_target_row(dtype):
     """Identical draft and target rows with u_0 = 1: position 0 rejects and max(p - q, 0) is zero
-    everywhere, so the last tile of the second grid draws the bonus from p_0 (R reported 0)."""
+    everywhere, so the last workgroup of the sequence in the second grid draws the bonus from p_0 (R reported 0)."""
     B, K, V = 6, 4, 20011
     bt = synth.make_verify_batch(B, K, V, dtype, 42)
     bt.target[:, :K] = bt.draft[:, :K]
     bt.u[:, 0] = np.float32(1.0)
     ref = O.verify_batch(bt.draft, bt.target, bt.dtype, bt.x, bt.u, bt.T)
     assert all(r.fallback and r.k == 0 and r.R == 0.0 for r in ref.values())
-    print(f"[case] two launches, all-zero residual {dtype}", flush=True)
+    print(f"[case] streaming, all-zero residual {dtype}", flush=True)
     _, _, _, h1 = call_verify(bt, 2, ONE)
-    o2, a2, r2, h2 = call_verify(bt, 2, TWO)
+    o2, a2, r2, h2 = call_verify(bt, 2, STREAM)
     same_bits(h1, h2, f"all-zero residual {dtype}")
     assert np.all(r2.cpu().numpy() == 0.0)
-    check_oracle(bt, o2, a2, r2, 2, f"two launches, all-zero residual {dtype}")
+    check_oracle(bt, o2, a2, r2, 2, f"streaming, all-zero residual {dtype}")
 
 
-def test_identical_rows_accept_everything_in_two_launches():
+def test_identical_rows_accept_everything_in_the_streaming_form():
     bt = synth.make_verify_batch(8, 6, 7777, synth.BF16, 3)
     bt.target[:, : bt.K] = bt.draft[:, : bt.K]
     bt.u[:, : bt.K] = np.float32(1 - 2 ** -24)
-    print("[case] two launches, every draft accepted", flush=True)
+    print("[case] streaming, every draft accepted", flush=True)
     _, _, _, h1 = call_verify(bt, 3, ONE)
-    o2, a2, r2, h2 = call_verify(bt, 3, TWO)
+    o2, a2, r2, h2 = call_verify(bt, 3, STREAM)
     same_bits(h1, h2, "every draft accepted")
     assert np.all(o2["accepted_len"].cpu().numpy() == bt.K)
-    check_oracle(bt, o2, a2, r2, 3, "two launches, every draft accepted")
+    check_oracle(bt, o2, a2, r2, 3, "streaming, every draft accepted")
 
 
 @pytest.mark.parametrize("B", [17, 24])
-def test_batch_beyond_the_device_takes_two_launches(B):
+def test_batch_beyond_the_device_takes_the_streaming_form(B):
     """17 and 24 sequences of the headline rows (32 tiles each): more tiles than 256 CUs run at once,
-    so the shape picks two launches; the bits are the forced one-launch call's, and the oracle's."""
+    so the shape picks the streaming form; the bits are the forced one-launch call's, and the oracle's."""
     assert ssd.ssd_verify_launches(B, 4, 128256, ssd.SSD_BF16, 3) == 2
     bt = synth.make_verify_batch(B, 4, 128256, synth.BF16, 30 + B)
     print(f"[case] B={B} headline rows by shape", flush=True)
     o0, a0, r0, h0 = call_verify(bt, 3, BY_SHAPE)
     _, _, _, h1 = call_verify(bt, 3, ONE)
     same_bits(h0, h1, f"B={B} by shape")
-    check_oracle(bt, o0, a0, r0, 3, f"B={B} headline rows, two launches by shape")
+    check_oracle(bt, o0, a0, r0, 3, f"B={B} headline rows, streaming form by shape")
 
 
 def test_one_workspace_serves_both_forms_in_turn():
     """Calls of both forms and of different shapes on one workspace, every one against the oracle:
-    the second grid's tag and counters must leave the workspace as a one-launch call expects it."""
-    calls = [(16, 4, 128256, "bf16", ONE), (16, 4, 128256, "bf16", TWO), (8, 4, 128256, "bf16", TWO),
-             (16, 4, 128256, "bf16", ONE), (6, 2, 70001, "f32", TWO), (9, 8, 40000, "bf16", ONE),
+    the streaming form's tag and counters must leave the workspace as a one-launch call expects it."""
+    calls = [(16, 4, 128256, "bf16", ONE), (16, 4, 128256, "bf16", STREAM), (8, 4, 128256, "bf16", STREAM),
+             (16, 4, 128256, "bf16", ONE), (6, 2, 70001, "f32", STREAM), (9, 8, 40000, "bf16", ONE),
              (24, 4, 128256, "bf16", BY_SHAPE), (16, 4, 128256, "bf16", BY_SHAPE)]
     need = max(ssd.ssd_verify_workspace_bytes(B, K, V, 3) for B, K, V, _, _ in calls)
     ws = ssd.Workspace(need, DEV)
@@ -143,17 +143,17 @@ def test_one_workspace_serves_both_forms_in_turn():
         check_oracle(bt, o, a, r, 3, name)
 
 
-def test_two_launches_while_another_stream_holds_the_device():
+def test_streaming_form_while_another_stream_holds_the_device():
     """A long read-only kernel on a second stream occupies the CUs while both grids are launched."""
     bt = synth.make_verify_batch(16, 4, 128256, synth.BF16, 5)
     busy = torch.empty(6 << 30, dtype=torch.uint8, device=DEV)  # ~1 ms of streaming
     sink = torch.zeros(8192, dtype=torch.int32, device=DEV)
     side = torch.cuda.Stream(device=DEV)
     torch.cuda.synchronize()
-    print("[case] two launches on a busy device", flush=True)
+    print("[case] streaming form on a busy device", flush=True)
     for rep in range(2):
         with torch.cuda.stream(side):
             ssd.ssd_stream_read(busy, sink, stream=side)
-        o, a, r, _ = call_verify(bt, 3, TWO)
-        check_oracle(bt, o, a, r, 3, f"two launches, busy device rep {rep}")
+        o, a, r, _ = call_verify(bt, 3, STREAM)
+        check_oracle(bt, o, a, r, 3, f"streaming form, busy device rep {rep}")
     del busy
