@@ -49,10 +49,10 @@ constexpr int kMaxR2 = 2 * kMaxK + 1;
 constexpr int kMaxT = kMaxV / kPlanMinTile;  // tiles of the longest row at the smallest tile
 constexpr int kGroupsPerBlock = kThreads / 16;
 // Per draft row and wave, the top-F candidates live in an LDS region of kRegW 64-bit words: either
-// the raw chunks of the wave's hot lanes (at most kHot of them), or a list of
+// the raw chunks of the wave's hot lanes (at most Lay::HOT of them, kHot for any type), or a list of
 // (float bits << 32 | ~token) entries from the compaction filter.
-constexpr int kRegW = 48;
-constexpr int kHot = 8;
+constexpr int kRegW = 64;
+constexpr int kHot = 16;
 static_assert(kRegW >= kMaxF + 1, "a wave region must hold an exact top-(F+1)");
 static_assert(kRegW <= 64, "a key-list region gives at most one entry per lane");
 // decision record: 64-bit words (call tag << 32 | value)
@@ -107,9 +107,13 @@ struct Lay {
   static constexpr int TILE = kThreads * E;        // tokens per tile
   // hot-lane copies: lanes of one selection round per slot, slots per round, rounds per wave region
   static constexpr int SPR = 64 / E;
-  static constexpr int PARTS = (kHot + SPR - 1) / SPR;
+  // hot lanes a wave copies: 16 for fp32 (16 guesses take the copy), 8 for bf16, whose rounds read
+  // every slot
+  static constexpr int HOT = (sizeof(T) == 4) ? 16 : 8;
+  static_assert(HOT <= kHot, "the lane-id table holds kHot lanes per wave");
+  static constexpr int PARTS = (HOT + SPR - 1) / SPR;
   static constexpr int SEL = kWaves * PARTS;
-  static_assert(kHot * NV * 2 <= kRegW, "a wave region must hold kHot lanes' chunks");
+  static_assert(HOT * NV * 2 <= kRegW, "a wave region must hold HOT lanes' chunks");
   // token of element q of a lane whose first token is bl
   __device__ static __forceinline__ int tok(int bl, int q) { return bl + (q / VEC) * CTOK + (q % VEC); }
 };
@@ -738,7 +742,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   // every non-empty lane is hot. Hot lanes copy their raw chunks into the row's region (chunks past
   // V are dropped at selection); a row with more hot lanes than slots is filtered again later.
   auto draft_batch = [&](const Raw<NV>* rw, const uint32_t* mk, int r0, int nb) __attribute__((always_inline)) {
-    if (Fp > kHot) {  // more guesses than slots: every row of the batch is filtered later
+    if (Fp > LY::HOT) {  // more guesses than slots: every row of the batch is filtered later
       if (lane == 0)
         for (int i = 0; i < nb; ++i) sh.fb[w] |= 1u << (r0 + i);
       return;
@@ -760,7 +764,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
         const bool hot = mk[i] >= thr && mk[i] != 0u;
         const uint64_t hm = __ballot(hot);
         const int n = __popcll(hm);
-        if (n <= kHot) {
+        if (n <= LY::HOT) {
           if (hot) {
             const int sl = __builtin_amdgcn_mbcnt_hi(uint32_t(hm >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(hm), 0u));
             uint4* dst = reinterpret_cast<uint4*>(&sh.reg[r][w][0]) + sl * NV;
@@ -994,7 +998,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
         int hlv[LY::SEL];
 #pragma unroll
         for (int i = 0; i < LY::SEL; ++i) {
-          const int ww = i / LY::PARTS, slc = min(lane / E + LY::SPR * (i % LY::PARTS), kHot - 1);
+          const int ww = i / LY::PARTS, slc = min(lane / E + LY::SPR * (i % LY::PARTS), LY::HOT - 1);
           rawv[i] = reinterpret_cast<const uint16_t*>(&sh.reg[r][ww][0])[slc * E + e];
           hlv[i] = sh.hl[r][ww][slc];
         }
@@ -1041,7 +1045,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
           key[i] = 0;
           const int sl = lane / E + LY::SPR * part;
           if (n[ww] < 0 && LY::SPR * part < -n[ww]) {  // uniform: some slot of this part holds a copy
-            const int slc = min(sl, kHot - 1);
+            const int slc = min(sl, LY::HOT - 1);
             const float v = ET::one(reinterpret_cast<const T*>(&sh.reg[r][ww][0]) + slc * E, e);
             const int tok = c0 + ww * LY::WTOK + sh.hl[r][ww][slc] * LY::VEC + LY::tok(0, e);
             const uint32_t kv = ordered_key(v);
