@@ -275,16 +275,37 @@ struct TopfWave {
       if (taken >= Fp) tau = thr;
     }
     if (__ballot(bm >= tau && bm > -INFINITY) == 0ull) return;  // nothing here reaches tau
+    // Groups of GS places: only a group where some lane of the wave reaches tau is examined (a
+    // batch that reaches tau mostly does so in one or two places of a few lanes). The candidates
+    // are the same, appended in the same order.
+    constexpr int GS = (NB % 8 == 0) ? 8 : 1, NG = NB / GS;
+    uint32_t gmask = 0;  // wave-uniform: groups with a place at or above tau in some lane
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float gm = z[g * GS];
+#pragma unroll
+      for (int e = 1; e < GS; ++e) gm = fmaxf(gm, z[g * GS + e]);
+      if (__ballot(gm >= tau && gm > -INFINITY) != 0ull) gmask |= 1u << g;
+    }
+    auto pass = [&](int e) __attribute__((always_inline)) { return z[e] >= tau && z[e] > -INFINITY && keep(e); };
     int cnt = 0;
 #pragma unroll
-    for (int e = 0; e < NB; ++e) cnt += (z[e] >= tau && z[e] > -INFINITY && keep(e)) ? 1 : 0;
+    for (int g = 0; g < NG; ++g)
+      if ((gmask >> g) & 1u) {
+#pragma unroll
+        for (int e = g * GS; e < (g + 1) * GS; ++e) cnt += pass(e) ? 1 : 0;
+      }
     const int incl = wave_incl_scan_i(cnt);
     const int total = __builtin_amdgcn_readlane(incl, 63);
     if (n + total <= BUF) {
       int pos = n + incl - cnt;
 #pragma unroll
-      for (int e = 0; e < NB; ++e)
-        if (z[e] >= tau && z[e] > -INFINITY && keep(e)) buf[pos++] = cand_key64(z[e], idx_of(e));
+      for (int g = 0; g < NG; ++g)
+        if ((gmask >> g) & 1u) {
+#pragma unroll
+          for (int e = g * GS; e < (g + 1) * GS; ++e)
+            if (pass(e)) buf[pos++] = cand_key64(z[e], idx_of(e));
+        }
       n += total;
     } else {
       // too many to append at once (ties): one place of every lane at a time, cutting the buffer
@@ -545,20 +566,31 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
         if (SAG) ls.add(z, bm, cc);
         if (F > 0) tw.batch_bm(z, bm, [&](int e) { return (b0 + t + (e / N) * kThreads) * N + (e % N); });
       };
-      // two batches in flight: a buffer is read again as soon as it has been examined, so the other
-      // one is always on its way (reads past the last batch repeat the chunk's last vector)
+      // NBUF batches in flight (a third slowed the bf16 pass): a buffer is read again as soon as it
+      // has been examined, so the other is always on its way (reads past the last batch repeat the
+      // chunk's last vector). The scheduling barriers keep the reads in this order, so a batch waits
+      // only for its own reads: were the batches' reads issued in another order before the loop,
+      // the loop's first wait would have to cover them all.
+      constexpr int NBUF = 2;
       constexpr int kStep = kThreads * U;
       if (v1 > v0) {
-        uint4 ra[U], rb[U];
-        load_batch(v0, ra);
-        load_batch(v0 + kStep, rb);
-        for (int b0 = v0; b0 < v1; b0 += 2 * kStep) {
-          run_batch(b0, ra);
-          if (b0 + kStep >= v1) break;
-          load_batch(b0 + 2 * kStep, ra);
-          run_batch(b0 + kStep, rb);
-          load_batch(b0 + 3 * kStep, rb);
+        uint4 rbuf[NBUF][U];
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) {
+          load_batch(v0 + i * kStep, rbuf[i]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        for (int b0 = v0;; b0 += NBUF * kStep) {
+#pragma unroll
+          for (int i = 0; i < NBUF; ++i) {
+            run_batch(b0 + i * kStep, rbuf[i]);
+            if (b0 + (i + 1) * kStep >= v1) goto chunk_done;
+            __builtin_amdgcn_sched_barrier(0);
+            load_batch(b0 + (i + NBUF) * kStep, rbuf[i]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      chunk_done:;
       }
     }
     // elements after the last whole vector, or every element of an unaligned row, one per lane

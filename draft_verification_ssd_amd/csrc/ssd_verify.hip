@@ -1446,19 +1446,18 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
     const float total = tile_mass<E>(rv, sh.wt);
     if (t == 0) st_agent(chunk + 2 * q + 1, tagged(tag, __float_as_uint(total)));
   };
-  if (q0 < q1) {
-    // two buffers; a tile index past the run loads the run's last tile again (in bounds, unused),
-    // so no branch surrounds a load
-    Raw<NV> pa, qa, pb, qb;
-    load2(q0, pa, qa);
-    for (int q = q0; q < q1; q += 2) {
-      load2(min(q + 1, q1 - 1), pb, qb);
-      mass(q, pa, qa);
-      if (q + 1 < q1) {
-        load2(min(q + 2, q1 - 1), pa, qa);
-        mass(q + 1, pb, qb);
-      }
-    }
+  // kRunGroup tiles at a time: every read of the group is issued, then the tiles are summed in
+  // order (a tile index past the run reads the run's last tile again: in bounds, unused, so no
+  // branch surrounds a read); nothing is carried from one group to the next, so no buffer has to be
+  // copied while its reads are in flight
+  constexpr int kRunGroup = 4;
+  for (int qg = q0; qg < q1; qg += kRunGroup) {
+    Raw<NV> rp[kRunGroup], rq[kRunGroup];
+#pragma unroll
+    for (int i = 0; i < kRunGroup; ++i) load2(min(qg + i, q1 - 1), rp[i], rq[i]);
+#pragma unroll
+    for (int i = 0; i < kRunGroup; ++i)
+      if (qg + i < q1) mass(qg + i, rp[i], rq[i]);
   }
   // a share of the guess merge: guess rows g, g + G, ...
   if (a.topfFmax > 0 || a.lastF > 0) merge_guesses_seq<8>(a, sh, b, tag, long_bound, g, G);
