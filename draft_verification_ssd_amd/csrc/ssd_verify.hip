@@ -175,6 +175,10 @@ __device__ __forceinline__ void unpack_row(const Raw<NV>& r, int bl, int V, bool
 }
 
 __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) { return (uint64_t(tag) << 32) | v; }
+// An empty instruction that takes v and gives it back: arithmetic on v cannot move above it. Used on
+// a value a returning atomic brings back inside a one-lane branch, so the wave waits for the atomic
+// where the value is read, not where it is issued.
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return uint32_t(w >> 32); }
 __device__ __forceinline__ float val_f(uint64_t w) { return __uint_as_float(uint32_t(w)); }
 template <class P>
@@ -189,7 +193,11 @@ __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-struct Shared {
+// LDS of a workgroup. RK: the draft rows whose top-F candidates it keeps (K + 1 at most, the extra
+// row included; sized by the kernel's row budget, so a kernel for short drafts leaves room for more
+// workgroups on a CU).
+template <int RK>
+struct SharedT {
   // per sequence, as given
   int F[kMaxK + 1];       // guesses per draft row (row K: the extra draft row)
   float C[kMaxK];         // Saguaro factor per draft position
@@ -200,14 +208,14 @@ struct Shared {
   float zs[kMaxK * kMaxF];  // draft logits at the set entries
   int set[kMaxK * kMaxF];   // de-duplicated in-range set entries, -1 elsewhere
   // statistics
-  float2 g16[kMaxR2][kGroupsPerBlock];  // (max c, sum) per 16-lane group
+  float2 g16[2 * RK - 1][kGroupsPerBlock];  // (max c, sum) per 16-lane group and row
   float L[kMaxR2];                      // log2 normaliser of every row (merged over the tiles)
   // top-F candidates per draft row and wave: nseg < 0 means -nseg hot lanes copied their raw
   // chunks (lane ids in hl), nseg >= 0 that many key entries
-  uint64_t reg[kMaxK + 1][kWaves][kRegW];
-  int nseg[kMaxK + 1][kWaves];
-  int hl[kMaxK + 1][kWaves][kHot];
-  uint32_t thr[kMaxK + 1][kWaves];  // the copy's threshold key: smaller tokens are no candidates
+  uint64_t reg[RK][kWaves][kRegW];
+  int nseg[RK][kWaves];
+  int hl[RK][kWaves][kHot];
+  uint32_t thr[RK][kWaves];  // the copy's threshold key: smaller tokens are no candidates
   uint32_t fb[kWaves];          // draft rows the wave filters again (bit r)
   uint64_t spare[kWaves][64];   // where the compaction's failing tokens are written
   // the decision record, as this tile uses it
@@ -415,8 +423,8 @@ __device__ __forceinline__ int fallback_draw(const typename ET::T* prow, int V, 
 // every tile has written its keys, so the polls only wait for the words to be seen. kM: keys per
 // lane held in registers (more keys per row: every round reads them again). The workgroup merges
 // guess rows first, first + step, ... (wave w takes the w-th of them, then every kWaves-th).
-template <int kM>
-__device__ __forceinline__ void merge_guesses_seq(const VerifyArgs& a, const Shared& sh, int b, uint32_t tag,
+template <int kM, class SH>
+__device__ __forceinline__ void merge_guesses_seq(const VerifyArgs& a, const SH& sh, int b, uint32_t tag,
                                                   int long_bound, int first = 0, int step = 1) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -500,7 +508,8 @@ __device__ __forceinline__ void merge_guesses_seq(const VerifyArgs& a, const Sha
 // The inputs of the accept tests that the decision reads from LDS: the logits at the draft tokens
 // (draft rows, then target rows) and at the Saguaro-set entries, and the set entries that count (in
 // range, first occurrence). Thread t holds its values; sh.sv must be staged and visible.
-__device__ __forceinline__ void stage_accept_inputs(Shared& sh, int K, int sF, int V, float zg_v, float zs_v, int sv_v) {
+template <class SH>
+__device__ __forceinline__ void stage_accept_inputs(SH& sh, int K, int sF, int V, float zg_v, float zs_v, int sv_v) {
   const int t = threadIdx.x;
   if (t < 2 * K) sh.zg[t] = zg_v;
   if (t < K * sF) {
@@ -520,7 +529,8 @@ __device__ __forceinline__ void stage_accept_inputs(Shared& sh, int K, int sF, i
 // if some word was not seen by then (nothing decided; with flag_timeout the device flag is set).
 // tr: this workgroup writes trace slot 3; record: it publishes the decision as the sequence's
 // record; outputs: it writes k and the accept probabilities.
-__device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, Shared& sh, int b, uint32_t tag, int bound,
+template <class SH>
+__device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
                                                 bool flag_timeout, bool tr, bool record, bool outputs) {
   const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
   const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF, Tc = a.Tcap;
@@ -655,7 +665,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   using LY = Lay<ET, NV>;
   constexpr int E = LY::E;
   constexpr int RM = 2 * KM + 1;
-  __shared__ Shared sh;
+  __shared__ SharedT<KM + 1> sh;
 
   const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, in a scalar register
@@ -871,12 +881,17 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     st_agent(st, tagged(tag, __float_as_uint(M)));
     st_agent(st + 1, tagged(tag, __float_as_uint(S)));
   }
+  // (thread 0 of the closer: the sequences of the call counted before this one. Every tile of the
+  // sequence has read the call's tag once the closer arrives, so the closer counts the sequence in
+  // now; the count comes back while it works, and the last sequence advances the tag at its end)
+  uint32_t seqs_before = 0;
   if (t == 0) {
     int role = 0;
     if constexpr (!SPLIT) {
       st_agent(chunk + 2 * tile, tagged(tag, kClaimOwner));
       if (add_agent(ctr, 1u) + 1u == uint32_t(nT)) {
         st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
+        seqs_before = add_agent(a.gdone, 1u);
         role = 1;
         // the closer counts its guesses in now and publishes them later, off its path to the
         // bonus: the merger (usually another tile) waits for them, and the closer has arrived, so
@@ -1348,9 +1363,12 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   }
   if ((sh.role & 2) != 0) merge_guesses();
   // ---- the sequence is done; the last sequence of the call advances the call tag
-  if (closer && t == 0 && add_agent(a.gdone, 1u) + 1u == uint32_t(a.B)) {
-    st_agent(a.gdone, 0u);
-    st_agent(a.gtag, tag);
+  if (closer && t == 0) {
+    opaque(seqs_before);
+    if (seqs_before + 1u == uint32_t(a.B)) {
+      st_agent(a.gdone, 0u);
+      st_agent(a.gtag, tag);
+    }
   }
   TRACE(9);
 }
@@ -1377,7 +1395,7 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
   using T = typename ET::T;
   using LY = Lay<ET, NV>;
   constexpr int E = LY::E;
-  __shared__ Shared sh;
+  __shared__ SharedT<1> sh;  // (no candidate regions: the first grid selected the guesses)
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -1462,9 +1480,13 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
   // a share of the guess merge: guess rows g, g + G, ...
   if (a.topfFmax > 0 || a.lastF > 0) merge_guesses_seq<8>(a, sh, b, tag, long_bound, g, G);
   __syncthreads();
+  uint32_t seqs_before = 0;  // (as in verify_kernel: the sequence counted in once all have arrived)
   if (t == 0) {
     const bool last = add_agent(ctr, 1u) + 1u == uint32_t(G);
-    if (last) st_agent(ctr, 0u);  // every workgroup has counted itself in: back to zero
+    if (last) {
+      st_agent(ctr, 0u);  // every workgroup has counted itself in: back to zero
+      seqs_before = add_agent(a.gdone, 1u);
+    }
     sh.role = last ? 1 : 0;
   }
   __syncthreads();
@@ -1511,7 +1533,8 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
   if (t == 0) {
     a.bonus_out[b] = tok;
     if (a.rmass_out) a.rmass_out[b] = rm;
-    if (add_agent(a.gdone, 1u) + 1u == uint32_t(a.B)) {  // the last sequence of the call
+    opaque(seqs_before);
+    if (seqs_before + 1u == uint32_t(a.B)) {  // the last sequence of the call
       st_agent(a.gdone, 0u);
       st_agent(a.gtag, tag);
     }
