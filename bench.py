@@ -157,6 +157,7 @@ TRACE_PHASES = [  # slot: what the workgroup has just finished
     (1, "statistics of every row computed"),
     (2, "statistics published, arrived (role known)"),
     (3, "closer: every tile's statistics merged"),
+    (11, "others: guesses published (then the decision is polled)"),
     (4, "decision published (closer) / guesses out and decision read (others)"),
     (5, "residual mass published"),
     (6, "others: every residual mass seen"),

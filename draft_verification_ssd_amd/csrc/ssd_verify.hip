@@ -37,6 +37,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "ssd.h"
 #include "ssd_device.hpp"
@@ -522,6 +523,23 @@ __device__ __forceinline__ void stage_accept_inputs(SH& sh, int K, int sF, int V
   }
 }
 
+// One round of a workgroup's merge reads: for row r, tiles q0, q0 + 16, ... (kMergeAhead of them,
+// both words of each; a tile past the row's tiles reads as an empty statistic).
+constexpr int kMergeAhead = 4;
+struct StatsRound {
+  uint64_t m[kMergeAhead], s[kMergeAhead];
+};
+__device__ __forceinline__ void load_stats_round(const VerifyArgs& a, int b, uint32_t tag, int r, int q0, StatsRound& v) {
+  const int R2 = 2 * a.K + 1, nT = a.T;
+  const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * a.Tcap * 2;
+#pragma unroll
+  for (int i = 0; i < kMergeAhead; ++i) {
+    const int q = q0 + i * 16;
+    v.m[i] = (q < nT) ? ld_agent(st + 2 * q) : tagged(tag, 0xFF800000u);
+    v.s[i] = (q < nT) ? ld_agent(st + 2 * q + 1) : tagged(tag, 0u);
+  }
+}
+
 // The decision of sequence b by one workgroup (every thread calls it, once sh.xe, sh.C, sh.u, sh.zg,
 // sh.zs and sh.set are staged): every tile's statistics merged in one fixed order, then the accept
 // tests (wave 0), the decision left in sh (k, the residual's normalisers, weights and set). Each
@@ -533,27 +551,21 @@ template <class SH>
 __device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
                                                 bool flag_timeout, bool tr, bool record, bool outputs) {
   const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
-  const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF, Tc = a.Tcap;
+  const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF;
   const float cc = a.c2;
   uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
   bool miss = false;
   // Merge every tile's statistics in one fixed order: 16-lane group g merges rows g, g + 16, ...;
   // lane l takes tiles l, l + 16, ... in order, then the group combines its lanes with DPP.
   for (int r = grp; r < R2; r += kGroupsPerBlock) {
-    const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * Tc * 2;
     float M = -INFINITY, S = 0.f;
-    constexpr int kAhead = 4;  // tiles per lane per round of loads
-    for (int q0 = (t & 15); q0 < nT; q0 += kAhead * 16) {
-      uint64_t mv[kAhead], sv[kAhead];
+    for (int q0 = (t & 15); q0 < nT; q0 += kMergeAhead * 16) {
+      StatsRound v;
       for (int spins = 0;; ++spins) {  // until both words of each tile carry this call's tag
+        load_stats_round(a, b, tag, r, q0, v);
         bool ok = true;
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i) {
-          const int q = q0 + i * 16;
-          mv[i] = (q < nT) ? ld_agent(st + 2 * q) : tagged(tag, 0xFF800000u);
-          sv[i] = (q < nT) ? ld_agent(st + 2 * q + 1) : tagged(tag, 0u);
-          ok = ok && tag_of(mv[i]) == tag && tag_of(sv[i]) == tag;
-        }
+        for (int i = 0; i < kMergeAhead; ++i) ok = ok && tag_of(v.m[i]) == tag && tag_of(v.s[i]) == tag;
         if (__all(ok)) break;
         if (spins >= bound) {
           miss = miss || !ok;
@@ -562,8 +574,8 @@ __device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, SH& sh, int
         __builtin_amdgcn_s_sleep(1);
       }
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) {
-        const float m = val_f(mv[i]), s = val_f(sv[i]);
+      for (int i = 0; i < kMergeAhead; ++i) {
+        const float m = val_f(v.m[i]), s = val_f(v.s[i]);
         if (s > 0.f) {
           if (m > M) {
             S = S * ex2(M - m) + s;
@@ -1007,50 +1019,62 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
       if constexpr (sizeof(T) == 2) {
         // bf16: 32-bit keys, the value's 16-bit order key above 0xFFFF - (token - c0), so a larger
         // key is a larger value, then a smaller token; 0 = none (every real key is above 2^23).
-        // Every read is issued first (clamped, in bounds), then the keys are formed.
+        // Every read is issued first (clamped, in bounds), then the keys are formed. NP parts of
+        // every wave's slots are read: the second only when some wave copied more than SPR lanes
+        // (a key list never needs it), so the usual row forms half the keys.
         const uint32_t xs_l = uint32_t(sh.xe[r] - c0);  // the sampled token, relative to the tile
-        uint32_t rawv[LY::SEL];
-        int hlv[LY::SEL];
+        auto select = [&](auto np) __attribute__((always_inline)) {
+          constexpr int NP = decltype(np)::value, NSEL = kWaves * NP;
+          uint32_t rawv[NSEL];
+          int hlv[NSEL];
 #pragma unroll
-        for (int i = 0; i < LY::SEL; ++i) {
-          const int ww = i / LY::PARTS, slc = min(lane / E + LY::SPR * (i % LY::PARTS), LY::HOT - 1);
-          rawv[i] = reinterpret_cast<const uint16_t*>(&sh.reg[r][ww][0])[slc * E + e];
-          hlv[i] = sh.hl[r][ww][slc];
-        }
-        uint32_t key[LY::SEL];
-#pragma unroll
-        for (int i = 0; i < LY::SEL; ++i) {
-          const int ww = i / LY::PARTS, part = i % LY::PARTS;
-          const int sl = lane / E + LY::SPR * part;
-          const uint32_t raw16 = rawv[i];
-          const uint32_t ok16 = (raw16 & 0x8000u) ? (~raw16 & 0xFFFFu) : (raw16 | 0x8000u);
-          const uint32_t tl = uint32_t(ww * LY::WTOK + hlv[i] * LY::VEC + LY::tok(0, e));
-          // th is above the key of -inf; the sampled token is never a guess
-          const bool ok = (n[ww] < 0) & (sl < -n[ww]) & (ok16 >= (th[ww] >> 16)) & (int(tl) < V - c0) & (tl != xs_l);
-          key[i] = ok ? (ok16 << 16) | (0xFFFFu - tl) : 0u;
-          if (n[ww] > 64 * part) {  // uniform: a key list (its tokens lie in this tile)
-            const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
-            const uint32_t tk = uint32_t(int(~uint32_t(ent)) - c0);
-            const uint32_t o16 = ordered_key(__uint_as_float(uint32_t(ent >> 32))) >> 16;
-            key[i] = (lane + 64 * part < n[ww] && uint32_t(ent) != 0u && tk != xs_l)  // lo 0 = none
-                         ? (o16 << 16) | (0xFFFFu - tk)
-                         : 0u;
+          for (int i = 0; i < NSEL; ++i) {
+            const int ww = i / NP, slc = min(lane / E + LY::SPR * (i % NP), LY::HOT - 1);
+            rawv[i] = reinterpret_cast<const uint16_t*>(&sh.reg[r][ww][0])[slc * E + e];
+            hlv[i] = sh.hl[r][ww][slc];
           }
-        }
-        for (int f = 0; f < F; ++f) {
-          uint32_t mine = key[0];
+          uint32_t key[NSEL];
 #pragma unroll
-          for (int i = 1; i < LY::SEL; ++i) mine = max(mine, key[i]);
-          const uint32_t win = wave_max_u32(mine);
-#pragma unroll
-          for (int i = 0; i < LY::SEL; ++i) key[i] = (key[i] == win) ? 0u : key[i];  // keys are unique
-          if (lane == 0) {  // back to the 64-bit (order key of the float, ~token) form
-            const uint32_t h = win >> 16;
-            const uint32_t okf = (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
-            publish_guess(r, f, win ? (uint64_t(okf) << 32) | uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
-                                    : 0ull);
+          for (int i = 0; i < NSEL; ++i) {
+            const int ww = i / NP, part = i % NP;
+            const int sl = lane / E + LY::SPR * part;
+            const uint32_t raw16 = rawv[i];
+            const uint32_t ok16 = (raw16 & 0x8000u) ? (~raw16 & 0xFFFFu) : (raw16 | 0x8000u);
+            const uint32_t tl = uint32_t(ww * LY::WTOK + hlv[i] * LY::VEC + LY::tok(0, e));
+            // th is above the key of -inf; the sampled token is never a guess
+            const bool ok = (n[ww] < 0) & (sl < -n[ww]) & (ok16 >= (th[ww] >> 16)) & (int(tl) < V - c0) & (tl != xs_l);
+            key[i] = ok ? (ok16 << 16) | (0xFFFFu - tl) : 0u;
+            if (n[ww] > 64 * part) {  // uniform: a key list (its tokens lie in this tile)
+              const uint64_t ent = sh.reg[r][ww][min(lane + 64 * part, kRegW - 1)];
+              const uint32_t tk = uint32_t(int(~uint32_t(ent)) - c0);
+              const uint32_t o16 = ordered_key(__uint_as_float(uint32_t(ent >> 32))) >> 16;
+              key[i] = (lane + 64 * part < n[ww] && uint32_t(ent) != 0u && tk != xs_l)  // lo 0 = none
+                           ? (o16 << 16) | (0xFFFFu - tk)
+                           : 0u;
+            }
           }
-        }
+          for (int f = 0; f < F; ++f) {
+            uint32_t mine = key[0];
+#pragma unroll
+            for (int i = 1; i < NSEL; ++i) mine = max(mine, key[i]);
+            const uint32_t win = wave_max_u32(mine);
+#pragma unroll
+            for (int i = 0; i < NSEL; ++i) key[i] = (key[i] == win) ? 0u : key[i];  // keys are unique
+            if (lane == 0) {  // back to the 64-bit (order key of the float, ~token) form
+              const uint32_t h = win >> 16;
+              const uint32_t okf = (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
+              publish_guess(r, f, win ? (uint64_t(okf) << 32) | uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
+                                      : 0ull);
+            }
+          }
+        };
+        bool wide = false;  // uniform: some wave copied more lanes than one part holds
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) wide = wide || n[ww] < -LY::SPR;
+        if (LY::PARTS > 1 && wide)
+          select(std::integral_constant<int, LY::PARTS>{});
+        else
+          select(std::integral_constant<int, 1>{});
       } else {
         const int xs = sh.xe[r];
         uint64_t key[LY::SEL];
@@ -1134,6 +1158,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     if (t == 0) sh.go = 1;
   } else {
     if (guesses) tile_guesses(true);
+    TRACE(11);
     // wave 0 polls the record until every word it needs carries this call's tag
     if (t < 64) {
       const int nw = kDecSet + sF;
