@@ -63,6 +63,10 @@ static_assert(kDecWords <= kPlanDecWords, "decision record exceeds its workspace
 // claim word states of a tile's residual chunk
 constexpr uint32_t kClaimOwner = 1, kClaimAbandoned = 2, kClaimCloser = 3;
 constexpr int kGroup = 4;  // chunks given up that the closer computes at once
+// The thread that counts its tile in and publishes the tile's mass: lane 0 of wave 1. A wave's stores
+// retire in order with its reads, so a wave waiting for a read (an atomic's count, a poll) also
+// waits for every store it issued before; wave 0 publishes the statistics and polls, wave 1 does not.
+constexpr int kSignalThread = 64;
 
 #ifndef SSD_VERIFY_PRIO
 #define SSD_VERIFY_PRIO 1  // phase-1 issue priority by progress
@@ -896,8 +900,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   // (thread 0 of the closer: the sequences of the call counted before this one. Every tile of the
   // sequence has read the call's tag once the closer arrives, so the closer counts the sequence in
   // now; the count comes back while it works, and the last sequence advances the tag at its end)
-  uint32_t seqs_before = 0;
-  if (t == 0) {
+  uint32_t seqs_before = 0, guesses_before = 0;
+  if (t == kSignalThread) {
     int role = 0;
     if constexpr (!SPLIT) {
       st_agent(chunk + 2 * tile, tagged(tag, kClaimOwner));
@@ -907,8 +911,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
         role = 1;
         // the closer counts its guesses in now and publishes them later, off its path to the
         // bonus: the merger (usually another tile) waits for them, and the closer has arrived, so
-        // it ends
-        if (guesses && add_agent(ctr + 1, 1u) + 1u == uint32_t(nT)) role |= 2;
+        // it ends. The count is read at the end.
+        if (guesses) guesses_before = add_agent(ctr + 1, 1u);
       }
     }
     sh.role = role;
@@ -918,7 +922,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   TRACE(2);
 
   // ---- the tile's guesses: its best F per draft row, published as tagged halves of 64-bit keys
-  // (order key of the value << 32 | ~token), then the guess-arrival counter
+  // (order key of the value << 32 | ~token), then the guess-arrival counter (its count is read at
+  // the end, so no wave waits for it)
   // Draft row r of a wave the hot-lane copy could not take: compaction of the tokens at or above
   // the threshold into the wave's region (exact top Fp from registers if too many pass).
   auto lane_thr = [&](float m, int& n) __attribute__((always_inline)) -> float {
@@ -1132,10 +1137,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
       }
     }
     __syncthreads();  // every guess of the tile issued
-    if (count_in) {
-      if (t == 0 && add_agent(ctr + 1, 1u) + 1u == uint32_t(nT)) sh.role |= 2;
-      __syncthreads();
-    }
+    if (count_in && t == kSignalThread) guesses_before = add_agent(ctr + 1, 1u);  // read at the end
   };
   // ---- guess merger: the last tile of the sequence to publish its guesses merges them
   const int long_bound = a.wait_polls * 8 + 4096;  // waits on tiles known to have arrived
@@ -1215,7 +1217,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     unpack_row<ET, NV>(rq, bl, V, tail, zq);
     residual_values<ET, NV>(zp, zq, k < K, bl, V, cc, sh.Lp, sh.Lq, sh.w_out, sh.w_in, sh.myset, nset, rv);
     const float total = tile_mass<E>(rv, sh.wt);
-    if (t == 0) st_agent(chunk + 2 * tile + 1, tagged(tag, __float_as_uint(total)));
+    if (t == kSignalThread) st_agent(chunk + 2 * tile + 1, tagged(tag, __float_as_uint(total)));
     TRACE(5);
     tile_prefix<ET, NV>(rv, sh.wt, pre);
   }
@@ -1386,9 +1388,16 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
       TRACE(8);
     }
   }
-  if ((sh.role & 2) != 0) merge_guesses();
+  if (guesses) {  // the last tile of the sequence to count its guesses in merges them
+    if (t == kSignalThread) {
+      opaque(guesses_before);
+      if (guesses_before + 1u == uint32_t(nT)) sh.role |= 2;
+    }
+    __syncthreads();
+    if ((sh.role & 2) != 0) merge_guesses();
+  }
   // ---- the sequence is done; the last sequence of the call advances the call tag
-  if (closer && t == 0) {
+  if (closer && t == kSignalThread) {
     opaque(seqs_before);
     if (seqs_before + 1u == uint32_t(a.B)) {
       st_agent(a.gdone, 0u);
