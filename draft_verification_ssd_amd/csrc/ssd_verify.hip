@@ -236,7 +236,8 @@ struct SharedT {
   // residual and bonus
   float wt[kWaves];
   float res[kMaxT];
-  int cstar, clamp, fallback, first, lastp;
+  int cstar, clamp, fallback;
+  int wfirst[kWaves], wlastp[kWaves];  // the tile search's per-wave crossing and last token of mass
   float base, target, R;
 };
 
@@ -326,10 +327,12 @@ __device__ __forceinline__ void tile_prefix(const float (&rv)[Lay<ET, NV>::E], f
 // The workgroup's search of its tile for the bonus token: the first token (ascending id) whose
 // base + prefix exceeds target, or the last token of positive mass with clamp or when rounding
 // leaves the tile's prefixes short of target (the crossing is then the tile's end, within
-// rounding). Every thread returns the token (-1 when the tile holds no positive mass).
+// rounding). Every thread returns the token (-1 when the tile holds no positive mass); *crossed, when
+// asked, tells whether it is a crossing rather than the last token of mass.
 template <class ET, int NV, class SH>
 __device__ __forceinline__ int tile_search(const float (&rv)[Lay<ET, NV>::E], const float (&pre)[Lay<ET, NV>::E],
-                                           int bl, float base, float target, bool clamp, SH& sh) {
+                                           int bl, float base, float target, bool clamp, SH& sh,
+                                           bool* crossed = nullptr) {
   using LY = Lay<ET, NV>;
   int first = INT_MAX, lastp = -1;
 #pragma unroll
@@ -341,20 +344,21 @@ __device__ __forceinline__ int tile_search(const float (&rv)[Lay<ET, NV>::E], co
     }
   first = wave_min_i(first);
   lastp = wave_max_i(lastp);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    sh.first = INT_MAX;
-    sh.lastp = -1;
-  }
-  __syncthreads();
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    if (first != INT_MAX) atomicMin(&sh.first, first);
-    if (lastp >= 0) atomicMax(&sh.lastp, lastp);
+    sh.wfirst[w] = first;
+    sh.wlastp[w] = lastp;
   }
   __syncthreads();
-  const int r = (sh.first != INT_MAX) ? sh.first : sh.lastp;
-  __syncthreads();
-  return r;
+  int f = sh.wfirst[0], l = sh.wlastp[0];
+#pragma unroll
+  for (int ww = 1; ww < kWaves; ++ww) {
+    f = min(f, sh.wfirst[ww]);
+    l = max(l, sh.wlastp[ww]);
+  }
+  __syncthreads();  // the slots are written again by the next search
+  if (crossed) *crossed = f != INT_MAX;
+  return (f != INT_MAX) ? f : l;
 }
 
 // The bonus scan over the T tile masses in sh.res (wave 0; every workgroup that runs it gets the same
@@ -381,9 +385,13 @@ __device__ __forceinline__ void scan_masses(SH& sh, int nT, float uK) {
     }
     p = nxt;
   }
-  const int cf = wave_min_i(first);
-  const int cl = wave_max_i(lastpos);
-  if (first != INT_MAX && first == cf) sh.base = base;
+  // lanes hold ascending runs of tiles: the first crossing is the lowest such lane's, the last tile
+  // of mass the highest such lane's
+  const uint64_t fm = __ballot(first != INT_MAX), lm = __ballot(lastpos >= 0);
+  const int fl = fm ? int(__builtin_ctzll(fm)) : -1, ll = lm ? 63 - int(__builtin_clzll(lm)) : -1;
+  const int cf = (fl >= 0) ? __builtin_amdgcn_readlane(first, fl) : INT_MAX;
+  const int cl = (ll >= 0) ? __builtin_amdgcn_readlane(lastpos, ll) : -1;
+  if (lane == fl) sh.base = base;
   if (lane == 0) {
     sh.cstar = (cf != INT_MAX) ? cf : cl;  // u R past the total by rounding: last tile with mass
     sh.clamp = (cf == INT_MAX);
@@ -413,9 +421,10 @@ __device__ __forceinline__ int fallback_draw(const typename ET::T* prow, int V, 
     residual_values<ET, NV>(zp, zp, false, blq, V, cc, Lp, 0.f, 1.f, 1.f, sh.myset, 0, v2);
     tile_prefix<ET, NV>(v2, sh.wt, p2);
     const float tot = tile_mass<E>(v2, sh.wt);
-    const int tk = tile_search<ET, NV>(v2, p2, blq, run, uK, false, sh);
+    bool crossed;
+    const int tk = tile_search<ET, NV>(v2, p2, blq, run, uK, false, sh, &crossed);
     // a crossing in this tile (the search's first token), or its last positive token
-    if (sh.first != INT_MAX) found = tk;
+    if (crossed) found = tk;
     if (tk >= 0) lastp = tk;
     run += tot;
   }
@@ -1356,6 +1365,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   if (sh.go) {
     if (t < 64) scan_masses(sh, nT, sh.u[K]);
     __syncthreads();
+    TRACE(13);
     if (!sh.fallback && sh.cstar == tile) {
       const int tok = tile_search<ET, NV>(rv, pre, bl, sh.base, sh.target, sh.clamp != 0, sh);
       if (t == 0) {
