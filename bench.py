@@ -157,9 +157,10 @@ TRACE_PHASES = [  # slot: what the workgroup has just finished
     (1, "statistics of every row computed"),
     (2, "statistics published, arrived (role known)"),
     (3, "closer: every tile's statistics merged"),
-    (11, "others: guesses published (then the decision is polled)"),
+    (11, "waves 1-3: the tile's guesses published"),
     (4, "decision published (closer) / guesses out and decision read (others)"),
     (5, "residual mass published"),
+    (10, "merger (tile r mod T): guess row r merged"),
     (6, "others: every residual mass seen"),
     (7, "closer: every residual mass in"),
     (8, "bonus token drawn (the tile that drew it)"),

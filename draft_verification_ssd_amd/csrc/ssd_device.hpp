@@ -78,6 +78,16 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
 }
+// maximum and sum over each quad of lanes (every lane of the quad ends with the same bits: the
+// pairs are added in either order, then the two pair sums)
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  return fmaxf(v, dpp_f<kDppXor2>(v));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  return v + dpp_f<kDppXor2>(v);
+}
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f<kDppXor1>(v));
   v = fmaxf(v, dpp_f<kDppXor2>(v));
@@ -179,20 +189,8 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
   return (uint64_t(h) << 32) | l;
 }
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-// unsigned 64-bit maximum over the wave, all in vector registers: DPP inside 16-lane rows, then
-// row_bcast:15 and row_bcast:31 carry rows 0..2 into row 3, whose last lane holds the result
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<kDppXor1>(v));
-  v = max_u64(v, dpp_u64<kDppXor2>(v));
-  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
-  v = max_u64(v, dpp_u64<kDppMirror>(v));
-  v = max_u64(v, dpp_u64<0x142, 0xA>(v));  // row_bcast:15 into rows 1 and 3
-  v = max_u64(v, dpp_u64<0x143, 0xC>(v));  // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
-  return (uint64_t(hi) << 32) | lo;
-}
-// unsigned 32-bit maximum over the wave, the same way (one DPP operand per step)
+// unsigned 32-bit maximum over the wave: DPP maxima inside 16-lane rows, then row_bcast:15 and
+// row_bcast:31 carry rows 0..2 into row 3, whose last lane holds the result (each step one DPP max)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u<kDppXor1>(v));
   v = max(v, dpp_u<kDppXor2>(v));
@@ -201,6 +199,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x142, 0xA, 0xF, false)));
   v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x143, 0xC, 0xF, false)));
   return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+// unsigned 64-bit maximum over the wave as two 32-bit maxima: the high words, then the low words of
+// the lanes whose high word is that maximum (a 64-bit step would take a compare and two selects)
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = uint32_t(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? uint32_t(v) : 0u);
+  return (uint64_t(mh) << 32) | ml;
 }
 // lexicographic max of (hi, lo) key pairs over the wave
 __device__ __forceinline__ void wave_max_key(uint32_t& hi, uint32_t& lo) {

@@ -37,7 +37,7 @@ struct VerifyArgs {
   uint32_t* flags;   // sticky device-error flags
   uint32_t* gtag;    // the last call's tag
   uint32_t* gdone;   // sequences finished by the running call
-  uint32_t* seqctl;  // [kSeqCtlMax][kPlanSeqCtlWords] arrivals, guess arrivals
+  uint32_t* seqctl;  // [kSeqCtlMax][kPlanSeqCtlWords] arrivals (word 0)
   uint64_t* stats;   // [B][2K+1][Tcap][2]
   uint64_t* chunk;   // [B][Tcap][2] claim word, mass word
   uint64_t* dec;     // [B][kPlanDecWords] decision record

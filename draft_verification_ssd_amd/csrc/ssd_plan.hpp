@@ -43,7 +43,7 @@ inline RowPlan plan_rows(int64_t rows, int V) {
 // ceil(V / 1024) tiles: the workspace is sized for that many whatever tile the call takes.
 constexpr int kPlanMinTile = 1024;
 constexpr int kSeqCtlMax = 65536;     // per-sequence counter slots: one for every sequence index
-constexpr int kPlanSeqCtlWords = 8;   // 32 bytes per sequence: arrivals, guess arrivals, spare
+constexpr int kPlanSeqCtlWords = 8;   // 32 bytes per sequence: arrivals (word 0), then spare
 constexpr int kPlanDecWords = 32;     // decision record: 256 bytes per sequence
 
 struct VerifyLayout {
@@ -55,7 +55,7 @@ struct VerifyLayout {
 // Workspace of ssd_verify:
 //   [0, 256)      word 0 sticky flags, word 1 the last call's tag, word 2 sequences finished by the
 //                 running call
-//   seqctl        counters per sequence index (arrivals of its tiles, tiles whose guesses are in),
+//   seqctl        counters per sequence index (the arrivals of its tiles in word 0),
 //                 at a fixed place for every sequence index 0 .. kSeqCtlMax-1, so no call of any
 //                 shape writes data where another call keeps a counter
 //   stats         [B][2K+1][Tcap][2] tagged (max c, sum) per row and tile

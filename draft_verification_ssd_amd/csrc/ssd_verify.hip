@@ -16,18 +16,21 @@
 //              guesses only, when they are asked for.
 //  arrival     The tile claims its residual chunk and adds one to its sequence's arrival counter.
 //              The tile that brings the count to T, the closer, knows every tile has published.
-//  decide      The closer merges the T statistics of every row in one fixed order, takes the accept
-//              decisions (k and the terms of the residual) and publishes them as a small record of
-//              tagged words.
-//  guesses     Meanwhile every other tile selects its best F per draft row from the copies and
-//              publishes them; the last tile of the sequence to do so merges them all.
-//  residual    Each tile, once it has read the record (a bounded number of polls), forms
-//              r = max(p_k - q'_k, 0) (p_K when every draft passes) from the rows in registers and
-//              publishes its mass, tagged.
+//  decide      Wave 0 of the closer, alone, merges the T statistics of every row in one fixed
+//              order, takes the accept decisions (k and the terms of the residual) and publishes
+//              them as a small record of tagged words; wave 0 of every other tile polls the record.
+//  guesses     Meanwhile waves 1 .. 3 of every tile select its best F per draft row from the copies
+//              and publish them (waves 2 and 3 from the arrival on, wave 1 once it has learned the
+//              tile's role and handed it to wave 0 through LDS).
+//  residual    Each tile, once it has the decision (the record read within a bounded number of
+//              polls), forms r = max(p_k - q'_k, 0) (p_K when every draft passes) from the rows in
+//              registers and publishes its mass, tagged.
 //  bonus       Every tile reads the T masses and finds the tile whose range holds u_K R; that tile
 //              finds the token inside it from its registers (the closer, reading its two rows
 //              again, if it gave its chunk up). The closer returns the sequence's counters to zero;
 //              the last sequence advances the call tag.
+//  merge       Guess row r of the sequence is merged by tile r mod T (waves 2 and 3), from every
+//              tile's published keys, once its bonus work is done.
 //
 // The closer waits only on tiles that have arrived, never on one that may not have started, and a
 // tile that has polled for the record its bound gives its chunk up and exits; the closer computes
@@ -93,7 +96,14 @@ __device__ __forceinline__ uint64_t trace_clock() {
   do {                                                                                       \
     if (threadIdx.x == 0 && a.trace) a.trace[int64_t(blockIdx.x) * kTraceSlots + (i)] = (v); \
   } while (0)
+#define TRACE_AT(i, thr)                                                                               \
+  do {                                                                                                 \
+    if (threadIdx.x == (thr) && a.trace) a.trace[int64_t(blockIdx.x) * kTraceSlots + (i)] = trace_clock(); \
+  } while (0)
 #else
+#define TRACE_AT(i, thr) \
+  do {                   \
+  } while (0)
 #define TRACE(i) \
   do {           \
   } while (0)
@@ -228,10 +238,12 @@ struct SharedT {
   float Lp, Lq, w_out, w_in;
   int myset[kMaxF];
   // roles and waits
-  int role;  // bit 0 closer, bit 1 guess merger
+  int role;   // bit 0 closer
+  int ready;  // waves 1 .. 3 that have staged their inputs (wave 1: and published the role)
   int go;    // the record (owners) or the masses (bonus) were read in time
   int todo, alldone, drawn;
   int todo_list[kMaxT];       // chunks given up, listed for the closer
+  uint32_t took[(kMaxT + 31) / 32];  // bit q: the closer computed chunk q
   float wtg[kGroup][kWaves];  // per-wave masses of a group of such chunks
   // residual and bonus
   float wt[kWaves];
@@ -431,151 +443,177 @@ __device__ __forceinline__ int fallback_draw(const typename ET::T* prow, int V, 
   return (found >= 0) ? found : lastp;
 }
 
-// The merge of sequence b's guesses (every thread of one workgroup calls it, once every tile of the
-// sequence has published its own). Keys are unique (a token lives in one tile), so round f picks the
-// largest key below round f-1's. Each key is two words tagged with the call; the caller knows that
-// every tile has written its keys, so the polls only wait for the words to be seen. kM: keys per
-// lane held in registers (more keys per row: every round reads them again). The workgroup merges
-// guess rows first, first + step, ... (wave w takes the w-th of them, then every kWaves-th).
+// The two words of every key of guess row r, requested by one wave (lane l takes keys l, l + 64,
+// ...: key q is guess q mod F of tile q / F): every lane reads a clamped, valid address; the keys
+// past the row's are replaced by the merge.
+template <int kM>
+__device__ __forceinline__ void request_guess_row(const VerifyArgs& a, int b, int r, uint64_t (&hi)[kM], uint64_t (&lo)[kM]) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.K, nT = a.T;
+  const int F1 = max(a.topfF[r], 1), nk = (nT * F1 + 63) >> 6;  // key slots a lane needs
+  const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * a.Tcap * a.Fcap * 2;
+#pragma unroll
+  for (int i = 0; i < kM; ++i) {
+    if (i >= nk) break;
+    const int q = lane + 64 * i;
+    const int tl = q / F1, ff = q - tl * F1;
+    const uint64_t* cw = cd + (int64_t(min(tl, nT - 1)) * a.Fcap + ff) * 2;
+    hi[i] = ld_agent(cw);
+    lo[i] = ld_agent(cw + 1);
+  }
+}
+
+// The merge of sequence b's guesses of draft row r by one wave, once every tile of the sequence
+// has published its own best F of the row (each key two words tagged with the call; the polls only
+// wait for the words to be seen). Keys are unique (a token lives in one tile), so round f picks the
+// largest key below round f-1's. kM: keys per lane held in registers (more keys per row: every round
+// reads them again). hi/lo: the row's words if `requested` already (request_guess_row).
+template <int kM, class SH>
+__device__ __forceinline__ void merge_guess_row(const VerifyArgs& a, const SH& sh, int b, uint32_t tag,
+                                                int long_bound, int r, uint64_t (&hi)[kM], uint64_t (&lo)[kM],
+                                                bool requested) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.K, nT = a.T, Tc = a.Tcap;
+  const int F = __builtin_amdgcn_readfirstlane(sh.F[r]), F1 = max(F, 1);
+  const int width = (r < K) ? a.topfFmax : a.lastF;
+  int32_t* out = (r < K) ? a.topf_out + (int64_t(b) * K + r) * a.topfFmax : a.topf_last_out + int64_t(b) * a.lastF;
+  const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * Tc * a.Fcap * 2;
+  const int n = nT * F;
+  if (n <= 64 * kM) {
+    // every request in flight before any value is looked at, then the tags checked (the words
+    // requested again if not yet in); slots past the row's keys (beyond nk a lane, or past n) are
+    // empty keys
+    const int nk = (nT * F1 + 63) >> 6;
+    if (!requested) request_guess_row<kM>(a, b, r, hi, lo);
+    for (int spins = 0;; ++spins) {
+      __builtin_amdgcn_sched_barrier(0);
+      bool ok = true;
+#pragma unroll
+      for (int i = 0; i < kM; ++i) {
+        const bool in = i < nk && lane + 64 * i < n;
+        hi[i] = in ? hi[i] : tagged(tag, 0u);
+        lo[i] = in ? lo[i] : tagged(tag, 0u);
+        ok = ok && tag_of(hi[i]) == tag && tag_of(lo[i]) == tag;
+      }
+      if (__all(ok)) break;
+      if (spins > long_bound) {
+        if (!ok) atomicOr(a.flags, kFlagTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      request_guess_row<kM>(a, b, r, hi, lo);
+    }
+    uint64_t key[kM];
+#pragma unroll
+    for (int i = 0; i < kM; ++i) key[i] = (uint64_t(uint32_t(hi[i])) << 32) | uint32_t(lo[i]);
+    for (int f = 0; f < F; ++f) {
+      uint64_t mine = key[0];
+#pragma unroll
+      for (int i = 1; i < kM; ++i)
+        if (i < nk) mine = max_u64(mine, key[i]);
+      const uint64_t win = wave_max_u64(mine);
+      if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+#pragma unroll
+      for (int i = 0; i < kM; ++i)
+        if (i < nk) key[i] = (key[i] == win) ? 0ull : key[i];
+    }
+  } else {  // many tiles: every round reads the keys again, taking the largest below the last
+    uint64_t prev = ~0ull;
+    for (int f = 0; f < F; ++f) {
+      uint64_t best = 0;
+      for (int q = lane; q < n; q += 64) {
+        const int tl = q / F1, ff = q - tl * F1;
+        const uint64_t* cw = cd + (int64_t(tl) * a.Fcap + ff) * 2;
+        uint64_t h = 0, l = 0;
+        for (int spins = 0;; ++spins) {
+          h = ld_agent(cw);
+          l = ld_agent(cw + 1);
+          if (tag_of(h) == tag && tag_of(l) == tag) break;
+          if (spins > long_bound) {
+            atomicOr(a.flags, kFlagTimeout);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t kq = (uint64_t(uint32_t(h)) << 32) | uint32_t(l);
+        best = (kq < prev && kq > best) ? kq : best;
+      }
+      const uint64_t win = wave_max_u64(best);
+      if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+      prev = win;
+    }
+  }
+  for (int f = F + lane; f < width; f += 64) out[f] = -1;
+}
+
+// The merge of sequence b's guess rows first, first + step, ... by one workgroup (wave w takes the
+// w-th of them, then every kWaves-th).
 template <int kM, class SH>
 __device__ __forceinline__ void merge_guesses_seq(const VerifyArgs& a, const SH& sh, int b, uint32_t tag,
                                                   int long_bound, int first = 0, int step = 1) {
-  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = a.K, nT = a.T, Tc = a.Tcap;
+  const int K = a.K;
   const bool guess_rows = a.topfFmax > 0;
   const int KG = K + (a.lastF > 0 ? 1 : 0);
   for (int r = first + w * step; r < KG; r += kWaves * step) {
     if (r < K && !guess_rows) continue;
-    const int F = sh.F[r];
-    const int width = (r < K) ? a.topfFmax : a.lastF;
-    int32_t* out = (r < K) ? a.topf_out + (int64_t(b) * K + r) * a.topfFmax : a.topf_last_out + int64_t(b) * a.lastF;
-    const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * Tc * a.Fcap * 2;
-    const int n = nT * F;
-    auto cand_at = [&](int q) -> uint64_t {  // key q = (tile q / F, guess q % F), once tagged
-      const int tl = q / F, ff = q - tl * F;
-      const uint64_t* cw = cd + (int64_t(tl) * a.Fcap + ff) * 2;
-      uint64_t hi = 0, lo = 0;
-      for (int spins = 0;; ++spins) {
-        hi = ld_agent(cw);
-        lo = ld_agent(cw + 1);
-        if (tag_of(hi) == tag && tag_of(lo) == tag) break;
-        if (spins > long_bound) {
-          atomicOr(a.flags, kFlagTimeout);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
-    };
-    if (n <= 64 * kM) {
-      // every key's two words loaded at once, then the tags checked (read again if not yet in)
-      uint64_t hi[kM], lo[kM];
-      for (int spins = 0;; ++spins) {
-        bool ok = true;
-#pragma unroll
-        for (int i = 0; i < kM; ++i) {
-          const int q = lane + 64 * i;
-          const int tl = q / max(F, 1), ff = q - tl * max(F, 1);
-          const uint64_t* cw = cd + (int64_t(min(tl, nT - 1)) * a.Fcap + ff) * 2;
-          hi[i] = (q < n) ? ld_agent(cw) : tagged(tag, 0u);
-          lo[i] = (q < n) ? ld_agent(cw + 1) : tagged(tag, 0u);
-        }
-#pragma unroll
-        for (int i = 0; i < kM; ++i) ok = ok && tag_of(hi[i]) == tag && tag_of(lo[i]) == tag;
-        if (__all(ok)) break;
-        if (spins > long_bound) {
-          if (!ok) atomicOr(a.flags, kFlagTimeout);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      uint64_t key[kM];
-#pragma unroll
-      for (int i = 0; i < kM; ++i) key[i] = (uint64_t(uint32_t(hi[i])) << 32) | uint32_t(lo[i]);
-      for (int f = 0; f < F; ++f) {
-        uint64_t mine = key[0];
-#pragma unroll
-        for (int i = 1; i < kM; ++i) mine = max_u64(mine, key[i]);
-        const uint64_t win = wave_max_u64(mine);
-        if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
-#pragma unroll
-        for (int i = 0; i < kM; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
-      }
-    } else {  // many tiles: every round reads the keys again, taking the largest below the last
-      uint64_t prev = ~0ull;
-      for (int f = 0; f < F; ++f) {
-        uint64_t best = 0;
-        for (int q = lane; q < n; q += 64) {
-          const uint64_t kq = cand_at(q);
-          best = (kq < prev && kq > best) ? kq : best;
-        }
-        const uint64_t win = wave_max_u64(best);
-        if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
-        prev = win;
-      }
-    }
-    for (int f = F + lane; f < width; f += 64) out[f] = -1;
+    uint64_t hi[kM], lo[kM];
+    merge_guess_row<kM>(a, sh, b, tag, long_bound, r, hi, lo, false);
   }
 }
 
-// The inputs of the accept tests that the decision reads from LDS: the logits at the draft tokens
-// (draft rows, then target rows) and at the Saguaro-set entries, and the set entries that count (in
-// range, first occurrence). Thread t holds its values; sh.sv must be staged and visible.
-template <class SH>
-__device__ __forceinline__ void stage_accept_inputs(SH& sh, int K, int sF, int V, float zg_v, float zs_v, int sv_v) {
-  const int t = threadIdx.x;
-  if (t < 2 * K) sh.zg[t] = zg_v;
-  if (t < K * sF) {
-    sh.zs[t] = zs_v;
-    const int i = t / sF, f = t - i * sF;
-    int set_v = (unsigned(sv_v) < unsigned(V)) ? sv_v : -1;
-    for (int g = 0; g < f && set_v >= 0; ++g)
-      if (sh.sv[i * sF + g] == set_v) set_v = -1;
-    sh.set[t] = set_v;
-  }
-}
-
-// One round of a workgroup's merge reads: for row r, tiles q0, q0 + 16, ... (kMergeAhead of them,
-// both words of each; a tile past the row's tiles reads as an empty statistic).
-constexpr int kMergeAhead = 4;
+// One round of the decision's merge reads: row r, tiles q0, q0 + 4, ... (kMergeAhead of them, both
+// words of each; a tile past the row's tiles reads the last tile's words, in bounds, and counts as an
+// empty statistic).
+constexpr int kMergeAhead = 8;
 struct StatsRound {
   uint64_t m[kMergeAhead], s[kMergeAhead];
 };
-__device__ __forceinline__ void load_stats_round(const VerifyArgs& a, int b, uint32_t tag, int r, int q0, StatsRound& v) {
-  const int R2 = 2 * a.K + 1, nT = a.T;
-  const uint64_t* st = a.stats + (int64_t(b) * R2 + r) * a.Tcap * 2;
+__device__ __forceinline__ void load_stats_round(const uint64_t* st, int nT, uint32_t tag, int q0, StatsRound& v) {
+  // every lane reads (a clamped tile); every read is issued before any value is selected, so the
+  // wave waits once for all of them
 #pragma unroll
   for (int i = 0; i < kMergeAhead; ++i) {
-    const int q = q0 + i * 16;
-    v.m[i] = (q < nT) ? ld_agent(st + 2 * q) : tagged(tag, 0xFF800000u);
-    v.s[i] = (q < nT) ? ld_agent(st + 2 * q + 1) : tagged(tag, 0u);
+    const int qc = min(q0 + 4 * i, nT - 1);
+    v.m[i] = ld_agent(st + 2 * qc);
+    v.s[i] = ld_agent(st + 2 * qc + 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kMergeAhead; ++i) {
+    const bool in = q0 + 4 * i < nT;
+    v.m[i] = in ? v.m[i] : tagged(tag, 0xFF800000u);
+    v.s[i] = in ? v.s[i] : tagged(tag, 0u);
   }
 }
 
-// The decision of sequence b by one workgroup (every thread calls it, once sh.xe, sh.C, sh.u, sh.zg,
-// sh.zs and sh.set are staged): every tile's statistics merged in one fixed order, then the accept
-// tests (wave 0), the decision left in sh (k, the residual's normalisers, weights and set). Each
-// statistic is read once its two words carry the call's tag, polling at most `bound` times; false
-// if some word was not seen by then (nothing decided; with flag_timeout the device flag is set).
-// tr: this workgroup writes trace slot 3; record: it publishes the decision as the sequence's
-// record; outputs: it writes k and the accept probabilities.
+// The decision of sequence b, taken by wave 0 alone (no barrier: the caller makes sh visible to the
+// other waves). Inputs in LDS, visible to wave 0: sh.xe, sh.C, sh.u, sh.sv, sh.zg (logits at the
+// draft tokens: draft rows, then target rows) and sh.zs (draft logits at the set entries).
+// Every tile's statistics are merged in one fixed order: quad g of the wave merges rows g, g + 16,
+// ...; lane l of the quad takes tiles l, l + 4, l + 8, ... in ascending order, then the quad combines
+// its lanes. Each statistic is read once its two words carry the call's tag, polling at most `bound`
+// times; false if some word was not seen by then (nothing decided; with flag_timeout the device
+// flag is set). Then the accept tests (lane i = position i), the decision left in sh (k, the
+// residual's normalisers, weights and set); record: published as the sequence's record; outputs: k
+// and the accept probabilities written.
 template <class SH>
-__device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
-                                                bool flag_timeout, bool tr, bool record, bool outputs) {
-  const int t = threadIdx.x, lane = t & 63, grp = t >> 4;
+__device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
+                                             bool flag_timeout, bool record, bool outputs) {
+  const int lane = threadIdx.x & 63, grp = lane >> 2, sub = lane & 3;
   const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF;
   const float cc = a.c2;
   uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
+  const uint64_t* stb = a.stats + int64_t(b) * R2 * a.Tcap * 2;
   bool miss = false;
-  // Merge every tile's statistics in one fixed order: 16-lane group g merges rows g, g + 16, ...;
-  // lane l takes tiles l, l + 16, ... in order, then the group combines its lanes with DPP.
-  for (int r = grp; r < R2; r += kGroupsPerBlock) {
+  for (int r0 = 0; r0 < R2; r0 += 16) {
+    const int r = min(r0 + grp, R2 - 1);  // quads past the rows merge the last row again, unused
+    const uint64_t* st = stb + int64_t(r) * a.Tcap * 2;
     float M = -INFINITY, S = 0.f;
-    for (int q0 = (t & 15); q0 < nT; q0 += kMergeAhead * 16) {
+    for (int qb = 0; qb < nT; qb += 4 * kMergeAhead) {
       StatsRound v;
       for (int spins = 0;; ++spins) {  // until both words of each tile carry this call's tag
-        load_stats_round(a, b, tag, r, q0, v);
+        load_stats_round(st, nT, tag, qb + sub, v);
         bool ok = true;
 #pragma unroll
         for (int i = 0; i < kMergeAhead; ++i) ok = ok && tag_of(v.m[i]) == tag && tag_of(v.s[i]) == tag;
@@ -586,98 +624,106 @@ __device__ __forceinline__ bool decide_sequence(const VerifyArgs& a, SH& sh, int
         }
         __builtin_amdgcn_s_sleep(1);
       }
+      // the round's maximum first, then every sum scaled to it (independent terms; a tile without
+      // mass adds nothing)
+      float Mn = M;
+#pragma unroll
+      for (int i = 0; i < kMergeAhead; ++i)
+        if (val_f(v.s[i]) > 0.f) Mn = fmaxf(Mn, val_f(v.m[i]));
+      float Sn = (S > 0.f) ? S * ex2(M - Mn) : 0.f;
 #pragma unroll
       for (int i = 0; i < kMergeAhead; ++i) {
         const float m = val_f(v.m[i]), s = val_f(v.s[i]);
-        if (s > 0.f) {
-          if (m > M) {
-            S = S * ex2(M - m) + s;
-            M = m;
-          } else {
-            S += s * ex2(m - M);
-          }
-        }
+        Sn += (s > 0.f) ? s * ex2(m - Mn) : 0.f;
       }
+      M = Mn;
+      S = Sn;
     }
-    const float Mr = row16_max(M);
-    const float Sr = row16_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
-    if ((t & 15) == 0) sh.L[r] = Mr + lg2(Sr);
+    const float Mr = quad_max(M);
+    const float Sr = quad_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
+    if (sub == 0 && r0 + grp < R2) sh.L[r0 + grp] = Mr + lg2(Sr);
   }
-  if (__syncthreads_or(miss ? 1 : 0)) {
-    if (flag_timeout && t == 0) atomicOr(a.flags, kFlagTimeout);
+  if (__any(miss)) {
+    if (flag_timeout && lane == 0) atomicOr(a.flags, kFlagTimeout);
     return false;
   }
-  if (tr) TRACE(3);
-  if (t < 64) {  // wave 0: lane i takes the accept test of position i
-    const int i = min(lane, K - 1);
-    const float C = sh.C[i];  // Saguaro factor of position i
-    const float Lq = sh.L[i], Lp = sh.L[K + i];
-    const int xi = sh.xe[i];
-    const bool xok = unsigned(xi) < unsigned(V);
-    if (lane < K && !xok) atomicOr(a.flags, kFlagBadToken);
-    float Nn = 1.f;
-    bool xin = false;
-    if (sF > 0) {  // Saguaro: N = 1 - (1 - C) sigma, sigma = q mass of the set
-      float sig = 0.f;
-      for (int f = 0; f < sF; ++f) {
-        const int sv = sh.set[i * sF + f];
-        if (sv < 0) continue;
-        sig += ex2(fmaf(sh.zs[i * sF + f], cc, -Lq));
-        if (sv == xi) xin = true;
-      }
-      Nn = 1.f - (1.f - C) * sig;
-      if (lane < K && !(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
-    }
-    bool accept;
-    float ai;
-    if (!xok) {
-      accept = false;
-      ai = 0.f;
-    } else {
-      const float wx = xin ? C : 1.f;
-      const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
-      const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
-      if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
-        accept = dp > -INFINITY;
-        ai = accept ? 1.f : 0.f;
-      } else {
-        const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
-        accept = sh.u[i] < ratio;
-        ai = fminf(1.f, ratio);
-      }
-    }
-    if (outputs && a.aprob_out && lane < K) a.aprob_out[b * K + lane] = ai;
-    const uint64_t rej = __ballot(lane < K && !accept);
-    const int kk = rej ? __builtin_ctzll(rej) : K;  // first rejection
-    const float Nk = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), kk)) : 1.f;
-    const float Ck = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(C), kk)) : 1.f;
-    // the residual's terms, published as the record straight from registers: lane j writes word j
-    // (the set of row k keeps its -1 holes: duplicates and out-of-range entries, which the residual
-    // skips)
-    const int nset = (kk < K) ? sF : 0;
-    const float Lpk = sh.L[K + kk], Lqk = (kk < K) ? sh.L[kk] : 0.f;
-    const int f = lane - kDecSet;
-    const int sv = (f >= 0 && f < nset) ? sh.set[kk * sF + f] : -1;
-    uint32_t v = uint32_t(sv);
-    if (lane == kDecK) v = uint32_t(kk);
-    if (lane == kDecLp) v = __float_as_uint(Lpk);
-    if (lane == kDecLq) v = __float_as_uint(Lqk);
-    if (lane == kDecWout) v = __float_as_uint(1.f / Nk);
-    if (lane == kDecWin) v = __float_as_uint(Ck / Nk);
-    if (lane == kDecNset) v = uint32_t(nset);
-    if (record && lane < kDecSet + sF) st_agent(dec + lane, tagged(tag, v));
-    if (lane == 0) {
-      if (outputs) a.k_out[b] = kk;
-      sh.k = kk;
-      sh.nset = nset;
-      sh.Lp = Lpk;
-      sh.Lq = Lqk;
-      sh.w_out = 1.f / Nk;
-      sh.w_in = Ck / Nk;
-    }
-    if (lane < kMaxF) sh.myset[lane] = (lane < nset) ? sh.set[kk * sF + lane] : -1;
+  // the Saguaro set entries that count (in range, first occurrence in their position's set)
+  for (int j = lane; j < K * sF; j += 64) {
+    const int i = j / sF, f = j - i * sF;
+    const int sv = sh.sv[j];
+    int set_v = (unsigned(sv) < unsigned(V)) ? sv : -1;
+    for (int g = 0; g < f && set_v >= 0; ++g)
+      if (sh.sv[i * sF + g] == set_v) set_v = -1;
+    sh.set[j] = set_v;
   }
-  __syncthreads();
+  // lane i takes the accept test of position i
+  const int i = min(lane, K - 1);
+  const float C = sh.C[i];  // Saguaro factor of position i
+  const float Lq = sh.L[i], Lp = sh.L[K + i];
+  const int xi = sh.xe[i];
+  const bool xok = unsigned(xi) < unsigned(V);
+  if (lane < K && !xok) atomicOr(a.flags, kFlagBadToken);
+  float Nn = 1.f;
+  bool xin = false;
+  if (sF > 0) {  // Saguaro: N = 1 - (1 - C) sigma, sigma = q mass of the set
+    float sig = 0.f;
+    for (int f = 0; f < sF; ++f) {
+      const int sv = sh.set[i * sF + f];
+      if (sv < 0) continue;
+      sig += ex2(fmaf(sh.zs[i * sF + f], cc, -Lq));
+      if (sv == xi) xin = true;
+    }
+    Nn = 1.f - (1.f - C) * sig;
+    if (lane < K && !(Nn > 0.f)) atomicOr(a.flags, kFlagSaguaroNorm);
+  }
+  bool accept;
+  float ai;
+  if (!xok) {
+    accept = false;
+    ai = 0.f;
+  } else {
+    const float wx = xin ? C : 1.f;
+    const float dp = fmaf(sh.zg[K + i], cc, -Lp);  // log2 p(x)
+    const float dq = fmaf(sh.zg[i], cc, -Lq);      // log2 q(x)
+    if (wx == 0.f || dq == -INFINITY) {            // q'(x) = 0: accept iff p(x) > 0
+      accept = dp > -INFINITY;
+      ai = accept ? 1.f : 0.f;
+    } else {
+      const float ratio = ex2(dp - dq) * (Nn / wx);  // p(x) / q'(x)
+      accept = sh.u[i] < ratio;
+      ai = fminf(1.f, ratio);
+    }
+  }
+  if (outputs && a.aprob_out && lane < K) a.aprob_out[b * K + lane] = ai;
+  const uint64_t rej = __ballot(lane < K && !accept);
+  const int kk = rej ? __builtin_ctzll(rej) : K;  // first rejection
+  const float Nk = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Nn), kk)) : 1.f;
+  const float Ck = (kk < K) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(C), kk)) : 1.f;
+  // the residual's terms, published as the record straight from registers: lane j writes word j
+  // (the set of row k keeps its -1 holes: duplicates and out-of-range entries, which the residual
+  // skips)
+  const int nset = (kk < K) ? sF : 0;
+  const float Lpk = sh.L[K + kk], Lqk = (kk < K) ? sh.L[kk] : 0.f;
+  const int f = lane - kDecSet;
+  const int sv = (f >= 0 && f < nset) ? sh.set[kk * sF + f] : -1;
+  uint32_t v = uint32_t(sv);
+  if (lane == kDecK) v = uint32_t(kk);
+  if (lane == kDecLp) v = __float_as_uint(Lpk);
+  if (lane == kDecLq) v = __float_as_uint(Lqk);
+  if (lane == kDecWout) v = __float_as_uint(1.f / Nk);
+  if (lane == kDecWin) v = __float_as_uint(Ck / Nk);
+  if (lane == kDecNset) v = uint32_t(nset);
+  if (record && lane < kDecSet + sF) st_agent(dec + lane, tagged(tag, v));
+  if (lane == 0) {
+    if (outputs) a.k_out[b] = kk;
+    sh.k = kk;
+    sh.nset = nset;
+    sh.Lp = Lpk;
+    sh.Lq = Lqk;
+    sh.w_out = 1.f / Nk;
+    sh.w_in = Ck / Nk;
+  }
+  if (lane < kMaxF) sh.myset[lane] = (lane < nset) ? sh.set[kk * sF + lane] : -1;
   return true;
 }
 
@@ -705,7 +751,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   auto row_ptr = [&](int r) -> const T* {  // logical row r: draft rows 0..K-1, target rows K..2K
     return (r < K) ? draft + int64_t(r) * V : target + int64_t(r - K) * V;
   };
-  uint32_t* ctr = a.seqctl + int64_t(b) * kPlanSeqCtlWords;  // [0] arrivals, [1] guess arrivals
+  uint32_t* ctr = a.seqctl + int64_t(b) * kPlanSeqCtlWords;  // [0] arrivals
   uint64_t* chunk = a.chunk + int64_t(b) * Tc * 2;
   uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
   // The call's tag is one past the last call's. The last sequence to finish stores it, after every
@@ -725,6 +771,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   int sv_v = -1;
   if (t < K * sF) sv_v = a.sset[int64_t(b) * K * sF + t];
   const int xg = (t < 2 * K) ? a.x[b * K + (t < K ? t : t - K)] : -1;
+
   const float c_v = (t < K) ? a.Cpos[t] : 1.f;
   const int f_v = (t <= K) ? a.topfF[t] : 0;
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the row loads
@@ -863,19 +910,6 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     const uint32_t mkK = (m > -INFINITY) ? ordered_key(m) : 0u;
     draft_batch(&rk, &mkK, K, 1);
   }
-  // logits at the draft tokens and the Saguaro-set entries (the closer's accept tests): issued now,
-  // read once the tile knows it is the closer
-  // Every lane reads (an idle or out-of-range lane the row's first token) and the value is selected
-  // afterwards, so no branch makes the wave wait for the read where it is issued.
-  float zg_v = 0.f, zs_v = 0.f;
-  if constexpr (!SPLIT) {  // (the streaming form's decision reads them itself)
-    const bool g_ok = t < 2 * K && unsigned(xg) < unsigned(V);
-    const float g = ET::one(row_ptr(t < 2 * K ? t : 0), g_ok ? xg : 0);
-    const bool s_ok = t < K * sF && unsigned(sv_v) < unsigned(V);
-    const float z2 = ET::one(row_ptr(t < K * sF ? t / sF : 0), s_ok ? sv_v : 0);
-    zg_v = g_ok ? g : 0.f;
-    zs_v = s_ok ? z2 : 0.f;
-  }
   if (t < K) {
     sh.xe[t] = x_v;
     sh.C[t] = c_v;
@@ -884,6 +918,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   if (t == K) sh.xe[K] = -1;
   if (t <= K) sh.u[t] = u_v;
   if (t < K * sF) sh.sv[t] = sv_v;
+  if (t == 0) sh.ready = 0;
   const uint32_t tag = (tag_ld + 1u == 0u) ? 1u : tag_ld + 1u;
 #if SSD_VERIFY_PRIO
   if constexpr (!SPLIT) __builtin_amdgcn_s_setprio(0);
@@ -891,8 +926,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   __syncthreads();
   TRACE(1);
 
-  // ---- publish the tile's statistics, claim the residual chunk, arrive
-  if (t < R2) {
+  // the tile's (max c, sum) of every row, tagged with the call (thread t < R2: row t)
+  auto publish_stats = [&]() __attribute__((always_inline)) {
     float M = -INFINITY;
 #pragma unroll
     for (int q = 0; q < kGroupsPerBlock; ++q) M = fmaxf(M, sh.g16[t][q].x);
@@ -905,34 +940,9 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     uint64_t* st = a.stats + ((int64_t(b) * R2 + t) * Tc + tile) * 2;
     st_agent(st, tagged(tag, __float_as_uint(M)));
     st_agent(st + 1, tagged(tag, __float_as_uint(S)));
-  }
-  // (thread 0 of the closer: the sequences of the call counted before this one. Every tile of the
-  // sequence has read the call's tag once the closer arrives, so the closer counts the sequence in
-  // now; the count comes back while it works, and the last sequence advances the tag at its end)
-  uint32_t seqs_before = 0, guesses_before = 0;
-  if (t == kSignalThread) {
-    int role = 0;
-    if constexpr (!SPLIT) {
-      st_agent(chunk + 2 * tile, tagged(tag, kClaimOwner));
-      if (add_agent(ctr, 1u) + 1u == uint32_t(nT)) {
-        st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
-        seqs_before = add_agent(a.gdone, 1u);
-        role = 1;
-        // the closer counts its guesses in now and publishes them later, off its path to the
-        // bonus: the merger (usually another tile) waits for them, and the closer has arrived, so
-        // it ends. The count is read at the end.
-        if (guesses) guesses_before = add_agent(ctr + 1, 1u);
-      }
-    }
-    sh.role = role;
-  }
-  __syncthreads();
-  const bool closer = (sh.role & 1) != 0;
-  TRACE(2);
-
+  };
   // ---- the tile's guesses: its best F per draft row, published as tagged halves of 64-bit keys
-  // (order key of the value << 32 | ~token), then the guess-arrival counter (its count is read at
-  // the end, so no wave waits for it)
+  // (order key of the value << 32 | ~token)
   // Draft row r of a wave the hot-lane copy could not take: compaction of the tokens at or above
   // the threshold into the wave's region (exact top Fp from registers if too many pass).
   auto lane_thr = [&](float m, int& n) __attribute__((always_inline)) -> float {
@@ -1000,9 +1010,9 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     st_agent(cw, tagged(tag, uint32_t(kv >> 32)));
     st_agent(cw + 1, tagged(tag, uint32_t(kv)));
   };
-  auto tile_guesses = [&](bool count_in) __attribute__((always_inline)) {
-    // rows the hot-lane copy could not take (ties, more guesses than copy slots, rows not 16-byte
-    // aligned): read again from cache and filtered
+  // rows the hot-lane copy could not take (ties, more guesses than copy slots, rows not 16-byte
+  // aligned): read again from cache and filtered (every thread calls it)
+  auto refilter = [&]() __attribute__((always_inline)) {
     if ((sh.fb[0] | sh.fb[1] | sh.fb[2] | sh.fb[3]) != 0u) {
       uint32_t fbm = __builtin_amdgcn_readfirstlane(sh.fb[w]);
       while (fbm) {
@@ -1016,11 +1026,13 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
       }
       __syncthreads();
     }
-    // Wave w selects the F best candidates (value desc, index asc) of rows w, w + 4, ... and
-    // publishes them. Candidate round i reads the region of wave i / PARTS: a copy gives lane l
-    // element l % E of slot l / E + SPR (i % PARTS); a key list gives lane l its entry
-    // l + 64 (i % PARTS).
-    for (int r = w; r < KG; r += kWaves) {
+  };
+  // The wave selects the F best candidates (value desc, index asc) of draft row r and hands each
+  // to emit(r, f, key) on lane 0, in descending order (no barrier). Candidate round i reads the
+  // region of wave i / PARTS: a copy gives lane l element l % E of slot l / E + SPR (i % PARTS); a
+  // key list gives lane l its entry l + 64 (i % PARTS).
+  auto select_row = [&](int r, auto&& emit) __attribute__((always_inline)) {
+    {
       const int F = sh.F[r];
       const int e = lane % E;
       int n[kWaves];
@@ -1077,8 +1089,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
             if (lane == 0) {  // back to the 64-bit (order key of the float, ~token) form
               const uint32_t h = win >> 16;
               const uint32_t okf = (h << 16) | ((h & 0x8000u) ? 0u : 0xFFFFu);
-              publish_guess(r, f, win ? (uint64_t(okf) << 32) | uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
-                                      : 0ull);
+              emit(r, f, win ? (uint64_t(okf) << 32) | uint64_t(~uint32_t(c0 + int(0xFFFFu - (win & 0xFFFFu))))
+                             : 0ull);
             }
           }
         };
@@ -1129,7 +1141,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
           uint64_t mine = (lane < N) ? lst[lane] : 0ull;
           for (int f = 0; f < F; ++f) {
             const uint64_t win = wave_max_u64(mine);
-            if (lane == 0) publish_guess(r, f, win);
+            if (lane == 0) emit(r, f, win);
             mine = (mine == win) ? 0ull : mine;  // keys are unique: only the winner is cleared
           }
         } else {
@@ -1138,40 +1150,102 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
 #pragma unroll
             for (int i = 1; i < LY::SEL; ++i) mine = max_u64(mine, key[i]);
             const uint64_t win = wave_max_u64(mine);
-            if (lane == 0) publish_guess(r, f, win);
+            if (lane == 0) emit(r, f, win);
 #pragma unroll
             for (int i = 0; i < LY::SEL; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
           }
         }
       }
     }
-    __syncthreads();  // every guess of the tile issued
-    if (count_in && t == kSignalThread) guesses_before = add_agent(ctr + 1, 1u);  // read at the end
   };
-  // ---- guess merger: the last tile of the sequence to publish its guesses merges them
+  // the streaming form: every row's best F published, wave w taking rows w, w + 4, ...
+  auto tile_guesses = [&]() __attribute__((always_inline)) {
+    refilter();
+    for (int r = w; r < KG; r += kWaves) select_row(r, publish_guess);
+  };
   const int long_bound = a.wait_polls * 8 + 4096;  // waits on tiles known to have arrived
-  auto merge_guesses = [&]() __attribute__((always_inline)) {
-    merge_guesses_seq<4>(a, sh, b, tag, long_bound);
-    if (t == 0) st_agent(ctr + 1, 0u);  // every tile has counted itself in: back to zero
-  };
 
-  if constexpr (SPLIT) {  // the streaming form: resid_kernel takes the rest
-    if (guesses) tile_guesses(false);
+
+  if constexpr (SPLIT) {  // the streaming form: statistics and guesses, resid_kernel takes the rest
+    if (t < R2) publish_stats();
+    if (guesses) tile_guesses();
     TRACE(9);
     return;
   }
 
-  // ---- the decision: the closer merges the statistics and publishes the record; every other tile
-  // selects its guesses meanwhile, then reads the record (or gives its chunk up)
-  if (closer) {
-    stage_accept_inputs(sh, K, sF, V, zg_v, zs_v, sv_v);
-    decide_sequence(a, sh, b, tag, long_bound, true, true, true, true);
-    if (t == 0) sh.go = 1;
-  } else {
-    if (guesses) tile_guesses(true);
-    TRACE(11);
-    // wave 0 polls the record until every word it needs carries this call's tag
-    if (t < 64) {
+  // rows the hot-lane copy could not take are filtered again before the tile arrives: the waves
+  // that select below run beside the decision and meet no barrier until the residual
+  if (guesses) refilter();
+
+  // ---- publish the tile's statistics, claim the residual chunk, arrive (the signalling thread; the
+  // closer also counts the sequence in: every tile of the sequence has read the call's tag once the
+  // closer arrives; the count comes back while it works, and the last sequence advances the tag at
+  // its end)
+  if (t < R2) publish_stats();
+  uint32_t seqs_before = 0;
+  int role = 0;
+  if (t == kSignalThread) {
+    st_agent(chunk + 2 * tile, tagged(tag, kClaimOwner));
+    if (add_agent(ctr, 1u) + 1u == uint32_t(nT)) {
+      st_agent(ctr, 0u);  // every tile has counted itself in: back to zero
+      seqs_before = add_agent(a.gdone, 1u);
+      role = 1;
+    }
+  }
+  // The logits at the draft tokens and at the Saguaro-set entries (the closer's accept tests),
+  // requested once the arrival is out (a request ahead of it would hold the arrival's answer back).
+  // Every lane of every wave reads (a lane without an entry reads the row's first token) and only
+  // the closer's wave 0 uses them: lane i the draft token of row i (i < 2K), and the set entries
+  // lane, lane + 64, ... (K sF <= 4 * 64; set entry ids from LDS).
+  constexpr int kSetSlots = (kMaxK * kMaxF + 63) / 64;
+  const int nss = (K * sF + 63) >> 6;  // set slots a lane takes
+  const bool g_ok = lane < 2 * K && unsigned(xg) < unsigned(V);
+  const float zg_r = ET::one(row_ptr(lane < 2 * K ? lane : 0), g_ok ? xg : 0);
+  float zs_r[kSetSlots];
+  int sv_r[kSetSlots];
+#pragma unroll
+  for (int m = 0; m < kSetSlots; ++m) {
+    zs_r[m] = 0.f;
+    sv_r[m] = -1;
+    if (m < nss) {
+      const int j = lane + 64 * m;
+      sv_r[m] = (j < K * sF) ? sh.sv[j] : -1;
+      const bool s_ok = unsigned(sv_r[m]) < unsigned(V);
+      zs_r[m] = ET::one(row_ptr(j < K * sF ? j / sF : 0), s_ok ? sv_r[m] : 0);
+    }
+  }
+  // Waves 1 .. 3 check in (wave 1 once it knows the role and has put it in LDS), and wave 0, alone,
+  // then takes the decision (the closer: its lanes put the point reads' logits in LDS first) or
+  // reads the record (every other tile). Meanwhile waves 1 .. 3 select the tile's guesses: row r by
+  // wave 2, 3, 1 for r = 0, 1, 2 (mod 3), waves 2 and 3 from the arrival on, wave 1 once the role
+  // is known.
+  if (w == 1) {
+    const int rl = __builtin_amdgcn_readlane(role, 0);
+    if (lane == 0) sh.role = rl;
+    TRACE_AT(14, 64);
+  }
+  if (w == 2) TRACE_AT(15, 128);
+  // (LDS ordering only: a release of every address space would make the wave wait for its own
+  // requests in flight, the closer's count of finished sequences among them)
+  if (w != 0 && lane == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __hip_atomic_fetch_add(&sh.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  if (w == 0) {
+    while (__hip_atomic_load(&sh.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < kWaves - 1)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    TRACE(2);
+    if ((sh.role & 1) != 0) {
+      if (lane < 2 * K) sh.zg[lane] = g_ok ? zg_r : 0.f;
+#pragma unroll
+      for (int m = 0; m < kSetSlots; ++m)
+        if (m < nss && lane + 64 * m < K * sF) sh.zs[lane + 64 * m] = (unsigned(sv_r[m]) < unsigned(V)) ? zs_r[m] : 0.f;
+      decide_wave0(a, sh, b, tag, long_bound, true, true, true);
+      TRACE(3);
+      if (lane == 0) sh.go = 1;
+    } else {
+      // poll the record until every word it needs carries this call's tag
       const int nw = kDecSet + sF;
       bool ok = false;
       uint64_t v = 0;
@@ -1199,8 +1273,12 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
         if (!ok) st_agent(chunk + 2 * tile, tagged(tag, kClaimAbandoned));  // the closer computes it
       }
     }
+  } else if (guesses) {
+    for (int r = (w == 2) ? 0 : (w == 3) ? 1 : 2; r < KG; r += 3) select_row(r, publish_guess);
+    TRACE_AT(11, 64 * w);
   }
   __syncthreads();
+  const bool closer = (sh.role & 1) != 0;
   TRACE(4);
   TRACEV(12, uint64_t(sh.role) | (uint64_t(sh.go) << 8));
 
@@ -1230,8 +1308,18 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     TRACE(5);
     tile_prefix<ET, NV>(rv, sh.wt, pre);
   }
-  // the closer's own guesses, while the owners' masses come in
-  if (closer && guesses) tile_guesses(false);
+  // the merger waves (guess row r is merged by tile r mod T, waves 2 and 3 taking its rows in turn)
+  // request their first row's keys now: every tile published its own before it read the record,
+  // and the merge itself waits until the tile's bonus work is done
+  uint64_t mhi[4], mlo[4];
+  int mrow = -1;
+  if (guesses && w >= 2) {
+    const int r = tile + (w - 2) * nT;
+    if (r < KG && !(r < K && !guess_rows)) {
+      request_guess_row<4>(a, b, r, mhi, mlo);
+      mrow = r;
+    }
+  }
   const bool go = sh.go != 0;
 
   // the residual values of tile q, its two rows read again
@@ -1251,6 +1339,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
   // ---- the masses of all T tiles into sh.res: the closer waits for the owners and computes the
   // chunks they gave up; an owner polls them (a bounded number of times)
   if (closer) {
+    for (int i = t; i < (nT + 31) / 32; i += kThreads) sh.took[i] = 0u;  // ordered by the loop's barrier
     for (int spins = 0;;) {
       // wave 0: masses that are in go to sh.res; the chunks given up are listed in ascending order
       if (t < 64) {
@@ -1296,7 +1385,10 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
             load_row<ET, NV, AL>(target + int64_t(k) * V, blq, V, rp[i]);
             load_row<ET, NV, AL>(draft + int64_t(min(k, K - 1)) * V, blq, V, rq[i]);
           }
-          if (t < gn) st_agent(chunk + 2 * cs[t], tagged(tag, kClaimCloser));
+          if (t < gn) {
+            st_agent(chunk + 2 * cs[t], tagged(tag, kClaimCloser));
+            atomicOr(&sh.took[cs[t] >> 5], 1u << (cs[t] & 31));
+          }
           float part[kGroup];
 #pragma unroll
           for (int i = 0; i < kGroup; ++i) {
@@ -1383,7 +1475,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
         a.bonus_out[b] = tok;
         if (a.rmass_out) a.rmass_out[b] = 0.f;
       }
-    } else if (sh.cstar != tile && ld_agent(chunk + 2 * sh.cstar) == tagged(tag, kClaimCloser)) {
+    } else if (sh.cstar != tile && ((sh.took[sh.cstar >> 5] >> (sh.cstar & 31)) & 1u) != 0u) {
       // the owning tile gave its chunk up (computed here): the closer reads its two rows again and
       // draws; any other owner draws from its registers, having read the record
       const int cs = sh.cstar;
@@ -1398,20 +1490,21 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
       TRACE(8);
     }
   }
-  if (guesses) {  // the last tile of the sequence to count its guesses in merges them
-    if (t == kSignalThread) {
-      opaque(guesses_before);
-      if (guesses_before + 1u == uint32_t(nT)) sh.role |= 2;
-    }
-    __syncthreads();
-    if ((sh.role & 2) != 0) merge_guesses();
-  }
   // ---- the sequence is done; the last sequence of the call advances the call tag
   if (closer && t == kSignalThread) {
     opaque(seqs_before);
     if (seqs_before + 1u == uint32_t(a.B)) {
       st_agent(a.gdone, 0u);
       st_agent(a.gtag, tag);
+    }
+  }
+  // ---- the guess rows of the merger waves, now that the tile's bonus work is done
+  if (guesses && w >= 2) {
+    int turn = 0;
+    for (int r = tile; r < KG; r += nT, ++turn) {
+      if ((turn & 1) != w - 2 || (r < K && !guess_rows)) continue;
+      merge_guess_row<4>(a, sh, b, tag, long_bound, r, mhi, mlo, r == mrow);
+      TRACE_AT(10, 64 * w);
     }
   }
   TRACE(9);
@@ -1477,10 +1570,14 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
     sh.u[t] = u_v;
   }
   if (t == K) sh.xe[K] = -1;
-  if (t < K * sF) sh.sv[t] = sv_v;
+  if (t < K * sF) {
+    sh.sv[t] = sv_v;
+    sh.zs[t] = s_ok ? zs : 0.f;
+  }
+  if (t < 2 * K) sh.zg[t] = g_ok ? zg : 0.f;
   __syncthreads();
-  stage_accept_inputs(sh, K, sF, V, g_ok ? zg : 0.f, s_ok ? zs : 0.f, sv_v);
-  decide_sequence(a, sh, b, tag, long_bound, true, false, false, g == 0);
+  if (w == 0) decide_wave0(a, sh, b, tag, long_bound, true, false, g == 0);
+  __syncthreads();
   const int k = min(max(__builtin_amdgcn_readfirstlane(sh.k), 0), K);
   const int nset = (k < K) ? min(max(sh.nset, 0), kMaxF) : 0;
   const float uK = sh.u[K];
