@@ -78,6 +78,15 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
 }
+// Orders one wave's LDS writes before its later LDS reads when its lanes pass values through LDS
+// without a workgroup barrier: every write issued before it is done, and no read after it is
+// moved above it (the compiler may otherwise place a branch's reads before another branch's
+// writes: lanes are independent threads to it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 // maximum and sum over each quad of lanes (every lane of the quad ends with the same bits: the
 // pairs are added in either order, then the two pair sums)
 __device__ __forceinline__ float quad_max(float v) {

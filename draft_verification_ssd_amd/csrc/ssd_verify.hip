@@ -643,6 +643,7 @@ __device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b,
     const float Sr = quad_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
     if (sub == 0 && r0 + grp < R2) sh.L[r0 + grp] = Mr + lg2(Sr);
   }
+  wave_lds_sync();  // sh.L (and the caller's staged inputs) before the lanes read them
   if (__any(miss)) {
     if (flag_timeout && lane == 0) atomicOr(a.flags, kFlagTimeout);
     return false;
@@ -656,6 +657,7 @@ __device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b,
       if (sh.sv[i * sF + g] == set_v) set_v = -1;
     sh.set[j] = set_v;
   }
+  wave_lds_sync();
   // lane i takes the accept test of position i
   const int i = min(lane, K - 1);
   const float C = sh.C[i];  // Saguaro factor of position i
@@ -1137,6 +1139,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
             N += __popcll(m);
           }
         }
+        wave_lds_sync();  // the list's entries come from other lanes
         if (N <= 64) {
           uint64_t mine = (lane < N) ? lst[lane] : 0ull;
           for (int f = 0; f < F; ++f) {
