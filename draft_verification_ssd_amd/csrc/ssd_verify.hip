@@ -443,15 +443,31 @@ __device__ __forceinline__ int fallback_draw(const typename ET::T* prow, int V, 
   return (found >= 0) ? found : lastp;
 }
 
-// The two words of every key of guess row r, requested by one wave (lane l takes keys l, l + 64,
-// ...: key q is guess q mod F of tile q / F): every lane reads a clamped, valid address; the keys
-// past the row's are replaced by the merge.
+// Two layouts of a guess row's keys across one wave: by tile (T <= 64 tiles and F <= 4 guesses:
+// lane q holds tile q's F keys, which its selection published in descending order) or spread (lane
+// l holds keys l, l + 64, ...: key q is guess q mod F of tile q / F).
+__device__ __forceinline__ bool guess_row_by_tile(int nT, int F) { return nT <= 64 && F <= 4; }
+
+// The two words of every key of guess row r, requested by one wave in the row's layout: every lane
+// reads a clamped, valid address; the keys past the row's are replaced by the merge.
 template <int kM>
 __device__ __forceinline__ void request_guess_row(const VerifyArgs& a, int b, int r, uint64_t (&hi)[kM], uint64_t (&lo)[kM]) {
+  static_assert(kM >= 4, "the by-tile layout holds 4 keys a lane");
   const int lane = threadIdx.x & 63;
   const int K = a.K, nT = a.T;
-  const int F1 = max(a.topfF[r], 1), nk = (nT * F1 + 63) >> 6;  // key slots a lane needs
+  const int F = a.topfF[r], F1 = max(F, 1);
   const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * a.Tcap * a.Fcap * 2;
+  if (guess_row_by_tile(nT, F)) {
+    const uint64_t* ct = cd + int64_t(min(lane, nT - 1)) * a.Fcap * 2;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      if (f >= F) break;
+      hi[f] = ld_agent(ct + 2 * f);
+      lo[f] = ld_agent(ct + 2 * f + 1);
+    }
+    return;
+  }
+  const int nk = (nT * F1 + 63) >> 6;  // key slots a lane needs
 #pragma unroll
   for (int i = 0; i < kM; ++i) {
     if (i >= nk) break;
@@ -479,7 +495,42 @@ __device__ __forceinline__ void merge_guess_row(const VerifyArgs& a, const SH& s
   int32_t* out = (r < K) ? a.topf_out + (int64_t(b) * K + r) * a.topfFmax : a.topf_last_out + int64_t(b) * a.lastF;
   const uint64_t* cd = a.cand + (int64_t(b) * (K + 1) + r) * Tc * a.Fcap * 2;
   const int n = nT * F;
-  if (n <= 64 * kM) {
+  if (guess_row_by_tile(nT, F)) {
+    // lane q: tile q's keys in descending order; round f takes the wave maximum of the lanes' heads
+    // and the lane that held it moves its head on
+    if (!requested) request_guess_row<kM>(a, b, r, hi, lo);
+    for (int spins = 0;; ++spins) {
+      __builtin_amdgcn_sched_barrier(0);
+      bool ok = true;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const bool in = f < F && lane < nT;
+        hi[f] = in ? hi[f] : tagged(tag, 0u);
+        lo[f] = in ? lo[f] : tagged(tag, 0u);
+        ok = ok && tag_of(hi[f]) == tag && tag_of(lo[f]) == tag;
+      }
+      if (__all(ok)) break;
+      if (spins > long_bound) {
+        if (!ok) atomicOr(a.flags, kFlagTimeout);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      request_guess_row<kM>(a, b, r, hi, lo);
+    }
+    uint64_t key[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) key[f] = (uint64_t(uint32_t(hi[f])) << 32) | uint32_t(lo[f]);
+    int h = 0;
+    uint64_t head = key[0];
+    for (int f = 0; f < F; ++f) {
+      const uint64_t win = wave_max_u64(head);
+      if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
+      if (head == win) {  // keys are unique: only the winner's lane moves on (0 stays 0)
+        ++h;
+        head = (h == 1) ? key[1] : (h == 2) ? key[2] : (h == 3) ? key[3] : 0ull;
+      }
+    }
+  } else if (n <= 64 * kM) {
     // every request in flight before any value is looked at, then the tags checked (the words
     // requested again if not yet in); slots past the row's keys (beyond nk a lane, or past n) are
     // empty keys
@@ -589,7 +640,9 @@ __device__ __forceinline__ void load_stats_round(const uint64_t* st, int nT, uin
 
 // The decision of sequence b, taken by wave 0 alone (no barrier: the caller makes sh visible to the
 // other waves). Inputs in LDS, visible to wave 0: sh.xe, sh.C, sh.u, sh.sv, sh.zg (logits at the
-// draft tokens: draft rows, then target rows) and sh.zs (draft logits at the set entries).
+// draft tokens: draft rows, then target rows) and sh.zs (draft logits at the set entries); the
+// last two may instead be written by `stage`, which runs once the statistics' requests are out
+// (so the requests of both are in flight together).
 // Every tile's statistics are merged in one fixed order: quad g of the wave merges rows g, g + 16,
 // ...; lane l of the quad takes tiles l, l + 4, l + 8, ... in ascending order, then the quad combines
 // its lanes. Each statistic is read once its two words carry the call's tag, polling at most `bound`
@@ -597,9 +650,12 @@ __device__ __forceinline__ void load_stats_round(const uint64_t* st, int nT, uin
 // flag is set). Then the accept tests (lane i = position i), the decision left in sh (k, the
 // residual's normalisers, weights and set); record: published as the sequence's record; outputs: k
 // and the accept probabilities written.
-template <class SH>
+struct NoStage {
+  __device__ void operator()() const {}
+};
+template <class SH, class Stage = NoStage>
 __device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
-                                             bool flag_timeout, bool record, bool outputs) {
+                                             bool flag_timeout, bool record, bool outputs, Stage&& stage = Stage{}) {
   const int lane = threadIdx.x & 63, grp = lane >> 2, sub = lane & 3;
   const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF;
   const float cc = a.c2;
@@ -643,7 +699,8 @@ __device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b,
     const float Sr = quad_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
     if (sub == 0 && r0 + grp < R2) sh.L[r0 + grp] = Mr + lg2(Sr);
   }
-  wave_lds_sync();  // sh.L (and the caller's staged inputs) before the lanes read them
+  stage();          // the caller's inputs of the accept tests, put in LDS now (stage: the caller's)
+  wave_lds_sync();  // sh.L and those inputs before the lanes read them
   if (__any(miss)) {
     if (flag_timeout && lane == 0) atomicOr(a.flags, kFlagTimeout);
     return false;
@@ -1195,28 +1252,6 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
       role = 1;
     }
   }
-  // The logits at the draft tokens and at the Saguaro-set entries (the closer's accept tests),
-  // requested once the arrival is out (a request ahead of it would hold the arrival's answer back).
-  // Every lane of every wave reads (a lane without an entry reads the row's first token) and only
-  // the closer's wave 0 uses them: lane i the draft token of row i (i < 2K), and the set entries
-  // lane, lane + 64, ... (K sF <= 4 * 64; set entry ids from LDS).
-  constexpr int kSetSlots = (kMaxK * kMaxF + 63) / 64;
-  const int nss = (K * sF + 63) >> 6;  // set slots a lane takes
-  const bool g_ok = lane < 2 * K && unsigned(xg) < unsigned(V);
-  const float zg_r = ET::one(row_ptr(lane < 2 * K ? lane : 0), g_ok ? xg : 0);
-  float zs_r[kSetSlots];
-  int sv_r[kSetSlots];
-#pragma unroll
-  for (int m = 0; m < kSetSlots; ++m) {
-    zs_r[m] = 0.f;
-    sv_r[m] = -1;
-    if (m < nss) {
-      const int j = lane + 64 * m;
-      sv_r[m] = (j < K * sF) ? sh.sv[j] : -1;
-      const bool s_ok = unsigned(sv_r[m]) < unsigned(V);
-      zs_r[m] = ET::one(row_ptr(j < K * sF ? j / sF : 0), s_ok ? sv_r[m] : 0);
-    }
-  }
   // Waves 1 .. 3 check in (wave 1 once it knows the role and has put it in LDS), and wave 0, alone,
   // then takes the decision (the closer: its lanes put the point reads' logits in LDS first) or
   // reads the record (every other tile). Meanwhile waves 1 .. 3 select the tile's guesses: row r by
@@ -1240,11 +1275,32 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     TRACE(2);
     if ((sh.role & 1) != 0) {
-      if (lane < 2 * K) sh.zg[lane] = g_ok ? zg_r : 0.f;
+      // the logits at the draft tokens and at the Saguaro-set entries, requested ahead of the
+      // statistics (every lane reads: a lane without an entry the row's first token): lane i the
+      // draft token of row i (i < 2K), and the set entries lane, lane + 64, ... (K sF <= 4 * 64)
+      constexpr int kSetSlots = (kMaxK * kMaxF + 63) / 64;
+      const int nss = (K * sF + 63) >> 6;  // set slots a lane takes
+      const bool g_ok = lane < 2 * K && unsigned(xg) < unsigned(V);
+      const float zg_r = ET::one(row_ptr(lane < 2 * K ? lane : 0), g_ok ? xg : 0);
+      float zs_r[kSetSlots];
+      bool s_ok[kSetSlots];
 #pragma unroll
-      for (int m = 0; m < kSetSlots; ++m)
-        if (m < nss && lane + 64 * m < K * sF) sh.zs[lane + 64 * m] = (unsigned(sv_r[m]) < unsigned(V)) ? zs_r[m] : 0.f;
-      decide_wave0(a, sh, b, tag, long_bound, true, true, true);
+      for (int m = 0; m < kSetSlots; ++m) {
+        zs_r[m] = 0.f;
+        s_ok[m] = false;
+        if (m < nss) {
+          const int j = lane + 64 * m;
+          const int sv = (j < K * sF) ? sh.sv[j] : -1;
+          s_ok[m] = unsigned(sv) < unsigned(V);
+          zs_r[m] = ET::one(row_ptr(j < K * sF ? j / sF : 0), s_ok[m] ? sv : 0);
+        }
+      }
+      decide_wave0(a, sh, b, tag, long_bound, true, true, true, [&]() __attribute__((always_inline)) {
+        if (lane < 2 * K) sh.zg[lane] = g_ok ? zg_r : 0.f;
+#pragma unroll
+        for (int m = 0; m < kSetSlots; ++m)
+          if (m < nss && lane + 64 * m < K * sF) sh.zs[lane + 64 * m] = s_ok[m] ? zs_r[m] : 0.f;
+      });
       TRACE(3);
       if (lane == 0) sh.go = 1;
     } else {
