@@ -127,6 +127,7 @@ struct VerifyPlan {
 constexpr int kVerifyThreads = 256;  // threads of a verification workgroup
 constexpr int kVerifyWgPerCu = 2;    // verification workgroups a CU runs at once (register budget)
 constexpr int kStreamWgPerCu = 3;    // the same for the streaming form's first grid
+constexpr int kResidWgPerCu = 2;     // and for its second grid (residual masses, draw, guess merge)
 inline VerifyPlan plan_verify(int B, int K, int V, bool bf16, bool aligned) {
   VerifyPlan p;
   p.AL = aligned;

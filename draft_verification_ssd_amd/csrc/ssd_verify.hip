@@ -465,18 +465,8 @@ __device__ __forceinline__ void request_guess_row(const VerifyArgs& a, int b, in
       hi[f] = ld_agent(ct + 2 * f);
       lo[f] = ld_agent(ct + 2 * f + 1);
     }
-    return;
   }
-  const int nk = (nT * F1 + 63) >> 6;  // key slots a lane needs
-#pragma unroll
-  for (int i = 0; i < kM; ++i) {
-    if (i >= nk) break;
-    const int q = lane + 64 * i;
-    const int tl = q / F1, ff = q - tl * F1;
-    const uint64_t* cw = cd + (int64_t(min(tl, nT - 1)) * a.Fcap + ff) * 2;
-    hi[i] = ld_agent(cw);
-    lo[i] = ld_agent(cw + 1);
-  }
+  // (the spread layout requests its keys in the merge itself)
 }
 
 // The merge of sequence b's guesses of draft row r by one wave, once every tile of the sequence
@@ -531,42 +521,38 @@ __device__ __forceinline__ void merge_guess_row(const VerifyArgs& a, const SH& s
       }
     }
   } else if (n <= 64 * kM) {
-    // every request in flight before any value is looked at, then the tags checked (the words
-    // requested again if not yet in); slots past the row's keys (beyond nk a lane, or past n) are
-    // empty keys
-    const int nk = (nT * F1 + 63) >> 6;
-    if (!requested) request_guess_row<kM>(a, b, r, hi, lo);
+    // every key's two words requested at once, then the tags checked (read again if not yet in)
+    uint64_t hk[kM], lk[kM];
     for (int spins = 0;; ++spins) {
-      __builtin_amdgcn_sched_barrier(0);
       bool ok = true;
 #pragma unroll
       for (int i = 0; i < kM; ++i) {
-        const bool in = i < nk && lane + 64 * i < n;
-        hi[i] = in ? hi[i] : tagged(tag, 0u);
-        lo[i] = in ? lo[i] : tagged(tag, 0u);
-        ok = ok && tag_of(hi[i]) == tag && tag_of(lo[i]) == tag;
+        const int q = lane + 64 * i;
+        const int tl = q / F1, ff = q - tl * F1;
+        const uint64_t* cw = cd + (int64_t(min(tl, nT - 1)) * a.Fcap + ff) * 2;
+        hk[i] = (q < n) ? ld_agent(cw) : tagged(tag, 0u);
+        lk[i] = (q < n) ? ld_agent(cw + 1) : tagged(tag, 0u);
       }
+#pragma unroll
+      for (int i = 0; i < kM; ++i) ok = ok && tag_of(hk[i]) == tag && tag_of(lk[i]) == tag;
       if (__all(ok)) break;
       if (spins > long_bound) {
         if (!ok) atomicOr(a.flags, kFlagTimeout);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-      request_guess_row<kM>(a, b, r, hi, lo);
     }
     uint64_t key[kM];
 #pragma unroll
-    for (int i = 0; i < kM; ++i) key[i] = (uint64_t(uint32_t(hi[i])) << 32) | uint32_t(lo[i]);
+    for (int i = 0; i < kM; ++i) key[i] = (uint64_t(uint32_t(hk[i])) << 32) | uint32_t(lk[i]);
     for (int f = 0; f < F; ++f) {
       uint64_t mine = key[0];
 #pragma unroll
-      for (int i = 1; i < kM; ++i)
-        if (i < nk) mine = max_u64(mine, key[i]);
+      for (int i = 1; i < kM; ++i) mine = max_u64(mine, key[i]);
       const uint64_t win = wave_max_u64(mine);
       if (lane == 0) out[f] = win ? int(~uint32_t(win)) : -1;
 #pragma unroll
-      for (int i = 0; i < kM; ++i)
-        if (i < nk) key[i] = (key[i] == win) ? 0ull : key[i];
+      for (int i = 0; i < kM; ++i) key[i] = (key[i] == win) ? 0ull : key[i];
     }
   } else {  // many tiles: every round reads the keys again, taking the largest below the last
     uint64_t prev = ~0ull;
@@ -653,16 +639,17 @@ __device__ __forceinline__ void load_stats_round(const uint64_t* st, int nT, uin
 struct NoStage {
   __device__ void operator()() const {}
 };
-template <class SH, class Stage = NoStage>
-__device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
-                                             bool flag_timeout, bool record, bool outputs, Stage&& stage = Stage{}) {
+// One wave's part of the merge of every tile's statistics: rows 16 wi + 64 i + g (quad g), i >= 0,
+// of a merge that nw waves share (wi = 0, nw = 1: every row). Each row's arithmetic is the same
+// whichever wave takes it. Returns whether some word was not seen within the bound.
+template <class SH>
+__device__ __forceinline__ bool merge_stats_part(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
+                                                 int wi, int nw) {
   const int lane = threadIdx.x & 63, grp = lane >> 2, sub = lane & 3;
-  const int K = a.K, V = a.V, R2 = 2 * K + 1, nT = a.T, sF = a.sF;
-  const float cc = a.c2;
-  uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
+  const int R2 = 2 * a.K + 1, nT = a.T;
   const uint64_t* stb = a.stats + int64_t(b) * R2 * a.Tcap * 2;
   bool miss = false;
-  for (int r0 = 0; r0 < R2; r0 += 16) {
+  for (int r0 = 16 * wi; r0 < R2; r0 += 16 * nw) {
     const int r = min(r0 + grp, R2 - 1);  // quads past the rows merge the last row again, unused
     const uint64_t* st = stb + int64_t(r) * a.Tcap * 2;
     float M = -INFINITY, S = 0.f;
@@ -699,9 +686,22 @@ __device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b,
     const float Sr = quad_sum((S > 0.f) ? S * ex2(M - Mr) : 0.f);
     if (sub == 0 && r0 + grp < R2) sh.L[r0 + grp] = Mr + lg2(Sr);
   }
+  return __any(miss);
+}
+
+template <class SH, class Stage = NoStage>
+__device__ __forceinline__ bool decide_wave0(const VerifyArgs& a, SH& sh, int b, uint32_t tag, int bound,
+                                             bool flag_timeout, bool record, bool outputs, Stage&& stage = Stage{},
+                                             bool merged = false, bool merge_miss = false) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.K, V = a.V, sF = a.sF;
+  const float cc = a.c2;
+  uint64_t* dec = a.dec + int64_t(b) * kPlanDecWords;
+  // the statistics merged here, or already by several waves (merged: sh.L is visible)
+  const bool miss = merged ? merge_miss : merge_stats_part(a, sh, b, tag, bound, 0, 1);
   stage();          // the caller's inputs of the accept tests, put in LDS now (stage: the caller's)
   wave_lds_sync();  // sh.L and those inputs before the lanes read them
-  if (__any(miss)) {
+  if (miss) {
     if (flag_timeout && lane == 0) atomicOr(a.flags, kFlagTimeout);
     return false;
   }
@@ -1587,7 +1587,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
 // the same bits.
 // ---------------------------------------------------------------------------------------------
 template <class ET, int NV, bool AL>
-__global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads, kResidWgPerCu) void resid_kernel(VerifyArgs a) {
   using T = typename ET::T;
   using LY = Lay<ET, NV>;
   constexpr int E = LY::E;
@@ -1635,7 +1635,10 @@ __global__ __launch_bounds__(kThreads) void resid_kernel(VerifyArgs a) {
   }
   if (t < 2 * K) sh.zg[t] = g_ok ? zg : 0.f;
   __syncthreads();
-  if (w == 0) decide_wave0(a, sh, b, tag, long_bound, true, false, g == 0);
+  // every wave merges its share of the rows (the same arithmetic per row as the one-launch form's
+  // wave 0), then wave 0 decides
+  const bool miss = __syncthreads_or(merge_stats_part(a, sh, b, tag, long_bound, w, kWaves) ? 1 : 0) != 0;
+  if (w == 0) decide_wave0(a, sh, b, tag, long_bound, true, false, g == 0, NoStage{}, true, miss);
   __syncthreads();
   const int k = min(max(__builtin_amdgcn_readfirstlane(sh.k), 0), K);
   const int nset = (k < K) ? min(max(sh.nset, 0), kMaxF) : 0;
