@@ -237,6 +237,19 @@ struct TopfWave {
   int n;          // keys in buf (wave-uniform)
   float tau;      // lower bound of the F-th best so far (wave-uniform); -inf: none yet
   int F, exclude;
+  // The workgroup's bound in LDS (order key; 0: none): every wave raises it to its own tau and
+  // takes it up before each batch. A wave's tau has F tokens of its own at or above it (F + 1 from
+  // the first batch's lane maxima, one of which may be the excluded token), so no token below it is
+  // among the row's best F, whichever wave holds the token; the bound only prunes sooner.
+  uint32_t* shared_tau;
+  __device__ __forceinline__ void take_shared() {
+    const uint32_t k = __hip_atomic_load(shared_tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (k > ordered_key(tau)) tau = key_to_float(k);
+  }
+  __device__ __forceinline__ void give_shared() {
+    if ((threadIdx.x & 63) == 0 && tau > -INFINITY)
+      __hip_atomic_fetch_max(shared_tau, ordered_key(tau), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 
   // one batch: lane tokens z[0..NB) (-inf for a place past the chunk), token index of place e
   // from idx_of(e) (evaluated only for batches that reach tau)
@@ -260,6 +273,7 @@ struct TopfWave {
   __device__ __forceinline__ void batch_ex(const float (&z)[NB], float bm, Idx idx_of) {
     auto keep = [&](int e) __attribute__((always_inline)) { return !EX || idx_of(e) != exclude; };
     const int lane = threadIdx.x & 63;
+    take_shared();
     if (tau == -INFINITY && n == 0) {  // first batch: tau from the lane maxima
       const int Fp = F + 1;
       float mm = bm, thr = -INFINITY;
@@ -272,7 +286,10 @@ struct TopfWave {
         if (taken >= Fp) break;
         mm = (mm == cur) ? -INFINITY : mm;
       }
-      if (taken >= Fp) tau = thr;
+      if (taken >= Fp) {
+        tau = thr;
+        give_shared();
+      }
     }
     if (__ballot(bm >= tau && bm > -INFINITY) == 0ull) return;  // nothing here reaches tau
     // Groups of GS places: only a group where some lane of the wave reaches tau is examined (a
@@ -316,7 +333,10 @@ struct TopfWave {
         if (m == 0ull) continue;
         if (n + __popcll(m) > BUF) {
           n = wave_cut_keys<BUF>(buf, n, F);
-          if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
+          if (n == F) {
+            tau = key_to_float(uint32_t(buf[F - 1] >> 32));
+            give_shared();
+          }
           c = c && z[e] >= tau;
           m = __ballot(c);
         }
@@ -327,7 +347,10 @@ struct TopfWave {
     }
     if (n > max(2 * F, kTReduce)) {
       n = wave_cut_keys<BUF>(buf, n, F);
-      if (n == F) tau = key_to_float(uint32_t(buf[F - 1] >> 32));
+      if (n == F) {
+        tau = key_to_float(uint32_t(buf[F - 1] >> 32));
+        give_shared();
+      }
     }
   }
 };
@@ -508,12 +531,16 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
   const T* p = reinterpret_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
   const int c0 = chunk * a.chunk1;
   const int c1 = min(a.V, c0 + a.chunk1);
+  __shared__ uint32_t s_tau;
+  if (t == 0) s_tau = 0u;
+  __syncthreads();
   TopfWave<ET, BUF> tw;
   tw.buf = sbuf[w];
   tw.n = 0;
   tw.tau = -INFINITY;
   tw.F = F;
   tw.exclude = ex;
+  tw.shared_tau = &s_tau;
   // SMP: a lane's statistics cover the current segment only; at a segment's end the lane's pair
   // goes to LDS (every lane takes part in every batch, so each segment of the chunk gets all 256)
   // and the lane starts again; the pairs are merged once, after the pass
