@@ -412,28 +412,49 @@ __device__ void block_sample(const typename ET::T* __restrict__ p, int V, bool a
                              int ns, int seg_len, float L, float cc, float Cr, float Nn, const int* set,
                              const float* zs, int F, float u, float* shf, int* shi, int32_t* out_token,
                              float* out_prob, uint32_t* flags) {
-  const int t = threadIdx.x;
-  float m = 0.f;
-  if (t < ns) {
-    const float2 r = segm[t];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  // q' mass of segment i (i < ns)
+  auto seg_mass = [&](int i) {
+    const float2 r = segm[i];
     const float mq = (r.y > 0.f) ? r.y * ex2(r.x - L) : 0.f;
     float in_set = 0.f;
     for (int f = 0; f < F; ++f)
-      if (set[f] >= 0 && set[f] / seg_len == t) in_set += ex2(fmaf(zs[f], cc, -L));
+      if (set[f] >= 0 && set[f] / seg_len == i) in_set += ex2(fmaf(zs[f], cc, -L));
     const float mp = mq - (1.f - Cr) * in_set;
-    m = (mp > kSegEps * mq) ? mp : 0.f;
-  }
-  float Z;
-  const float excl = block_excl_scan(m, shf, Z);
-  const float tau = u * Z;
-  int sg = block_min_i((m > 0.f && excl + m > tau) ? t : INT_MAX, shi);
+    return (mp > kSegEps * mq) ? mp : 0.f;
+  };
+  int sg;
   float rem = INFINITY;  // tau less the mass before the segment; +inf: its last token of mass
-  if (sg == INT_MAX) {
-    sg = block_max_i(m > 0.f ? t : -1, shi);
+  if (ns <= 64) {
+    // Every wave finds the segment by itself, lane i taking segment i: no barrier. These are the
+    // sums the block-wide scan below forms, as every segment sits in its first wave.
+    const float m = (lane < ns) ? seg_mass(lane) : 0.f;
+    const float inc = wave_incl_scan(m);
+    const float prev = wave_shift_up1(inc);  // outside the select: every lane takes part
+    const float base = 0.f;
+    const float excl = (lane == 0) ? base : base + prev;
+    const float tau = u * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+    const uint64_t hit = __ballot(m > 0.f && excl + m > tau);
+    if (hit) {
+      sg = __builtin_ctzll(hit);
+      rem = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tau - excl), sg));
+    } else {
+      const uint64_t pos = __ballot(m > 0.f);
+      sg = pos ? 63 - __builtin_clzll(pos) : -1;
+    }
   } else {
-    if (t == sg) shf[kWaves + 1] = tau - excl;
-    __syncthreads();
-    rem = shf[kWaves + 1];
+    const float m = (t < ns) ? seg_mass(t) : 0.f;
+    float Z;
+    const float excl = block_excl_scan(m, shf, Z);
+    const float tau = u * Z;
+    sg = block_min_i((m > 0.f && excl + m > tau) ? t : INT_MAX, shi);
+    if (sg == INT_MAX) {
+      sg = block_max_i(m > 0.f ? t : -1, shi);
+    } else {
+      if (t == sg) shf[kWaves + 1] = tau - excl;
+      __syncthreads();
+      rem = shf[kWaves + 1];
+    }
   }
   if (sg < 0 || !(Nn > 0.f)) {  // no mass: a masked row, or C = 0 with the set holding it all
     if (t == 0) {
@@ -456,35 +477,98 @@ __device__ void block_sample(const typename ET::T* __restrict__ p, int V, bool a
   const int a0 = sg * seg_len, a1 = min(V, a0 + seg_len);
   const int run = seg_len / kThreads;
   const int b0 = min(a1, a0 + t * run), b1 = min(a1, b0 + run);
-  float sum = 0.f;
+  // A run of exactly kRunTok tokens of an aligned row (a one-batch segment: the usual case) is read
+  // with all its loads in flight at once and its masses kept in registers, so the walk below reads
+  // nothing again; any other run streams through for_run. Both take the same steps in the same
+  // order, so the result does not depend on which one a thread takes.
+  constexpr int N = ET::kVec;
+  constexpr int kRunTok = kPlanSampleSpan / kThreads;
+  const bool held = aligned && b1 - b0 == kRunTok;  // b0 is a multiple of kRunTok: 16-byte aligned
+  float qr[kRunTok];
+  float sum = 0.f, qlp = 0.f;
   int lp = -1;
-  for_run<ET>(p, b0, b1, aligned, [&](float z, int e) {
-    const float q = mass(z, e);
-    sum += q;
-    if (q > 0.f) lp = e;
-  });
-  float Ts;
-  const float ex = block_excl_scan(sum, shf, Ts);
-  const int owner = block_min_i((sum > 0.f && ex + sum > rem) ? t : INT_MAX, shi);
+  if (held) {
+    uint4 raw[kRunTok / N];
+#pragma unroll
+    for (int j = 0; j < kRunTok / N; ++j) raw[j] = load16(p + b0 + j * N);
+    uint32_t in_set = 0;  // bit j: token b0 + j is a set member (weight Cr, as in mass)
+    for (int f = 0; f < F; ++f) {
+      const int d = set[f] - b0;
+      if (set[f] >= 0 && d >= 0 && d < kRunTok) in_set |= 1u << d;
+    }
+#pragma unroll
+    for (int j = 0; j < kRunTok / N; ++j) ET::unpack(raw[j], qr + j * N);
+#pragma unroll
+    for (int j = 0; j < kRunTok; ++j) {
+      const float q = (((in_set >> j) & 1u) ? Cr : 1.f) * ex2(fmaf(qr[j], cc, -L));
+      qr[j] = q;
+      sum += q;
+      if (q > 0.f) {
+        lp = b0 + j;
+        qlp = q;
+      }
+    }
+  } else {
+    for_run<ET>(p, b0, b1, aligned, [&](float z, int e) {
+      const float q = mass(z, e);
+      sum += q;
+      if (q > 0.f) lp = e;
+    });
+  }
+  // the run holding the target: an exclusive scan of the runs' masses over the block (each wave's
+  // total after the earlier waves' totals, in order), then the first run whose end passes it
+  const float inc = wave_incl_scan(sum);
+  if (lane == 63) shf[w] = inc;
+  __syncthreads();
+  float base = 0.f;
+  for (int i = 0; i < w; ++i) base += shf[i];
+  // the cross-lane read outside the select: a lane inside a branch that leaves lane 0 out would
+  // read 0 from it
+  const float prev = wave_shift_up1(inc);
+  const float ex = (lane == 0) ? base : base + prev;
+  const uint64_t own = __ballot(sum > 0.f && ex + sum > rem);
+  if (lane == 0) shi[w] = own ? w * 64 + __builtin_ctzll(own) : INT_MAX;
+  __syncthreads();
+  const int owner = min(min(shi[0], shi[1]), min(shi[2], shi[3]));
   int x = -1;
-  bool writer = false;
+  bool writer = false, have_q = false;
+  float qx = 0.f;  // q mass of x, when this thread holds it
   if (owner == INT_MAX) {
     x = block_max_i(lp, shi);
     writer = (t == 0);
   } else if (t == owner) {
     float c = ex;
-    for_run<ET>(p, b0, b1, aligned, [&](float z, int e) {
-      if (x < 0) {
-        c += mass(z, e);
-        if (c > rem) x = e;
+    if (held) {
+#pragma unroll
+      for (int j = 0; j < kRunTok; ++j) {  // the running sum stops at the first crossing
+        const bool live = x < 0;
+        c = live ? c + qr[j] : c;
+        const bool hit = live && c > rem;
+        x = hit ? b0 + j : x;
+        qx = hit ? qr[j] : qx;
       }
-    });
-    if (x < 0) x = lp;
+      if (x < 0) {
+        x = lp;
+        qx = qlp;
+      }
+      have_q = true;
+    } else {
+      for_run<ET>(p, b0, b1, aligned, [&](float z, int e) {
+        if (x < 0) {
+          c += mass(z, e);
+          if (c > rem) x = e;
+        }
+      });
+      if (x < 0) x = lp;
+    }
     writer = true;
   }
   if (writer) {
     *out_token = x;
-    if (out_prob) *out_prob = (x >= 0) ? mass(ET::one(p, x), x) / Nn : 0.f;
+    if (out_prob) {
+      if (x >= 0 && !have_q) qx = mass(ET::one(p, x), x);
+      *out_prob = (x >= 0) ? qx / Nn : 0.f;
+    }
   }
 }
 
