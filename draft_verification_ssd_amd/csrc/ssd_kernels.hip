@@ -386,6 +386,25 @@ struct LaneStats {
 constexpr float kSegEps = 9.5367431640625e-07f;  // 2^-20: a segment's q' mass below this share of
                                                  // its q mass is cancellation left over, not mass
 static_assert(kPlanSampleSpan == kThreads * kTBatch, "a sampling segment is whole top-F batches");
+// tokens of one thread's run when a segment is one batch (the register-held case below)
+constexpr int kRunTok = kPlanSampleSpan / kThreads;
+
+// The segment a row's draw falls in, from the segments' q masses alone (the set's down-weighting
+// left out): every wave finds it by itself, lane i taking segment i (ns <= 64); -1 if none. Only a
+// guess of the draw's segment, good for requesting its tokens early.
+__device__ __forceinline__ int guess_segment(const float2* segm, int ns, float L, float u) {
+  const int lane = threadIdx.x & 63;
+  float m = 0.f;
+  if (lane < ns) {
+    const float2 r = segm[lane];
+    m = (r.y > 0.f) ? r.y * ex2(r.x - L) : 0.f;
+  }
+  const float inc = wave_incl_scan(m);
+  const float prev = wave_shift_up1(inc);
+  const float tau = u * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), 63));
+  const uint64_t hit = __ballot(m > 0.f && prev + m > tau);
+  return hit ? int(__builtin_ctzll(hit)) : -1;
+}
 
 // tokens [b0, b1) of row p in ascending order, 16-byte loads when aligned (b0 % kVec == 0)
 template <class ET, class Fn>
@@ -407,11 +426,14 @@ __device__ __forceinline__ void for_run(const typename ET::T* __restrict__ p, in
 // Whole block. segm: ns <= 256 segment pairs (LDS); set / zs: the F set members and their logits
 // (LDS, -1 for an empty place); L = log2 of the row's normaliser in the units of z c. Writes the
 // token (-1 when q' has no mass) and q' of it. shf >= kWaves + 2 floats, shi >= kWaves ints.
+// sg0 / pre: a segment guessed earlier and this thread's run of it, already requested (sg0 = -1:
+// none); used when the draw does fall in that segment.
 template <class ET>
-__device__ void block_sample(const typename ET::T* __restrict__ p, int V, bool aligned, const float2* segm,
-                             int ns, int seg_len, float L, float cc, float Cr, float Nn, const int* set,
-                             const float* zs, int F, float u, float* shf, int* shi, int32_t* out_token,
-                             float* out_prob, uint32_t* flags) {
+__device__ __forceinline__ void block_sample(const typename ET::T* __restrict__ p, int V, bool aligned,
+                                             const float2* segm, int ns, int seg_len, float L, float cc, float Cr,
+                                             float Nn, const int* set, const float* zs, int F, float u, float* shf,
+                                             int* shi, int32_t* out_token, float* out_prob, uint32_t* flags,
+                                             int sg0, const uint4 (&pre)[kRunTok / ET::kVec]) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   // q' mass of segment i (i < ns)
   auto seg_mass = [&](int i) {
@@ -419,7 +441,7 @@ __device__ void block_sample(const typename ET::T* __restrict__ p, int V, bool a
     const float mq = (r.y > 0.f) ? r.y * ex2(r.x - L) : 0.f;
     float in_set = 0.f;
     for (int f = 0; f < F; ++f)
-      if (set[f] >= 0 && set[f] / seg_len == i) in_set += ex2(fmaf(zs[f], cc, -L));
+      if (set[f] >= i * seg_len && set[f] < (i + 1) * seg_len) in_set += ex2(fmaf(zs[f], cc, -L));
     const float mp = mq - (1.f - Cr) * in_set;
     return (mp > kSegEps * mq) ? mp : 0.f;
   };
@@ -482,15 +504,19 @@ __device__ void block_sample(const typename ET::T* __restrict__ p, int V, bool a
   // nothing again; any other run streams through for_run. Both take the same steps in the same
   // order, so the result does not depend on which one a thread takes.
   constexpr int N = ET::kVec;
-  constexpr int kRunTok = kPlanSampleSpan / kThreads;
   const bool held = aligned && b1 - b0 == kRunTok;  // b0 is a multiple of kRunTok: 16-byte aligned
   float qr[kRunTok];
   float sum = 0.f, qlp = 0.f;
   int lp = -1;
   if (held) {
     uint4 raw[kRunTok / N];
+    if (sg == sg0) {  // requested already
 #pragma unroll
-    for (int j = 0; j < kRunTok / N; ++j) raw[j] = load16(p + b0 + j * N);
+      for (int j = 0; j < kRunTok / N; ++j) raw[j] = pre[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRunTok / N; ++j) raw[j] = load16(p + b0 + j * N);
+    }
     uint32_t in_set = 0;  // bit j: token b0 + j is a set member (weight Cr, as in mass)
     for (int f = 0; f < F; ++f) {
       const int d = set[f] - b0;
@@ -758,6 +784,22 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
     for (int q = 0; q < NS; ++q)
       if (segm[q].y > 0.f) S += segm[q].y * ex2(segm[q].x - MXc);
   }
+  // One chunk: this thread's run of the segment the draw most likely falls in (the set, merged
+  // next, moves it only near a segment's edge) is requested now, to arrive during that merge.
+  int sg0 = -1;
+  uint4 pre[kRunTok / N];
+#pragma unroll
+  for (int j = 0; j < kRunTok / N; ++j) pre[j] = make_uint4(0u, 0u, 0u, 0u);
+  if (SMP && a.n1 == 1 && a.aligned && a.seg_len == kPlanSampleSpan) {
+    const int ns = (a.V + a.seg_len - 1) / a.seg_len;
+    sg0 = guess_segment(segm, ns, MXc + lg2(S), u_row);
+    const int a0 = sg0 * a.seg_len, a1 = min(a.V, a0 + a.seg_len);
+    const int b0 = min(a1, a0 + t * kRunTok);
+    if (sg0 >= 0 && min(a1, b0 + kRunTok) - b0 == kRunTok) {
+#pragma unroll
+      for (int j = 0; j < kRunTok / N; ++j) pre[j] = load16(p + b0 + j * N);
+    }
+  }
   if (w == 0) {  // the chunk's top F from the waves' lists
     uint64_t k = 0ull;
     if (F > 0 && lane < kWaves * F) k = stop[lane / F][lane % F];
@@ -807,7 +849,7 @@ __global__ __launch_bounds__(kThreads) void topf_rows_kernel(TopfArgs a) {
     const int ns = (a.V + a.seg_len - 1) / a.seg_len;
     block_sample<ET>(p, a.V, a.aligned != 0, segm, ns, a.seg_len, s_lnc[0], cc, s_lnc[2], s_lnc[1], s_set, s_zs,
                      F, u_row, shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
-                     a.flags);
+                     a.flags, sg0, pre);
   }
 }
 
@@ -869,9 +911,12 @@ __global__ __launch_bounds__(kThreads) void topf_merge_kernel(TopfArgs a) {
   }
   if (SMP) {
     __syncthreads();
+    uint4 none[kRunTok / ET::kVec];
+#pragma unroll
+    for (int j = 0; j < kRunTok / ET::kVec; ++j) none[j] = make_uint4(0u, 0u, 0u, 0u);
     block_sample<ET>(p, a.V, a.aligned != 0, s_segm, ns, a.seg_len, s_lnc[0], a.c2, s_lnc[2], s_lnc[1], s_set,
                      s_zs, F, u_row, shf, shi, a.out_token + row, a.out_prob ? a.out_prob + row : nullptr,
-                     a.flags);
+                     a.flags, -1, none);
   }
 }
 
