@@ -379,9 +379,10 @@ struct LaneStats {
 // =============================================================================================
 // The streaming pass leaves every segment of seg_len tokens its q mass as a (max c, sum) pair. The
 // segment where the cumulative q' mass first exceeds u times the total is found from those pairs
-// (one segment per thread; the set members' share of a segment is scaled by C), then only that
-// segment is read again, each thread owning seg_len / 256 consecutive tokens: a block scan of the
-// runs' masses names the run, whose thread walks it token by token. When rounding leaves the
+// (one segment per lane, every wave on its own when there are at most 64, else one per thread over
+// the block; the set members' share of a segment is scaled by C), then only that segment is read
+// again, each thread owning seg_len / 256 consecutive tokens: a block scan of the runs' masses
+// names the run, whose thread walks it token by token. When rounding leaves the
 // target past the last crossing, the last token of positive mass is taken (segment, then run).
 constexpr float kSegEps = 9.5367431640625e-07f;  // 2^-20: a segment's q' mass below this share of
                                                  // its q mass is cancellation left over, not mass
