@@ -282,18 +282,19 @@ __device__ __forceinline__ void residual_values(const float (&zp)[Lay<ET, NV>::E
 }
 
 // The tile's mass in one fixed order (lane, then DPP over the wave, then the waves in order); every
-// thread returns the same bits.
-template <int E>
+// thread returns the same bits. FENCED: barriers before and after keep wt_sh's other uses apart;
+// without, the caller has a barrier right before and one right after (its next user's).
+template <int E, bool FENCED = true>
 __device__ __forceinline__ float tile_mass(const float (&rv)[E], float* wt_sh) {
   float s = 0.f;
 #pragma unroll
   for (int q = 0; q < E; ++q) s += rv[q];
   s = wave_sum(s);
-  __syncthreads();
+  if (FENCED) __syncthreads();
   if ((threadIdx.x & 63) == 0) wt_sh[threadIdx.x >> 6] = s;
   __syncthreads();
   const float tot = (wt_sh[0] + wt_sh[1]) + (wt_sh[2] + wt_sh[3]);
-  __syncthreads();
+  if (FENCED) __syncthreads();
   return tot;
 }
 
@@ -1362,7 +1363,8 @@ __global__ __launch_bounds__(kThreads, SPLIT ? kStreamWgPerCu : kVerifyWgPerCu) 
     unpack_row<ET, NV>(rp, bl, V, tail, zp);
     unpack_row<ET, NV>(rq, bl, V, tail, zq);
     residual_values<ET, NV>(zp, zq, k < K, bl, V, cc, sh.Lp, sh.Lq, sh.w_out, sh.w_in, sh.myset, nset, rv);
-    const float total = tile_mass<E>(rv, sh.wt);
+    // (the barrier before the residual, and tile_prefix's first one, keep sh.wt's uses apart)
+    const float total = tile_mass<E, false>(rv, sh.wt);
     if (t == kSignalThread) st_agent(chunk + 2 * tile + 1, tagged(tag, __float_as_uint(total)));
     TRACE(5);
     tile_prefix<ET, NV>(rv, sh.wt, pre);
